@@ -1,0 +1,231 @@
+"""CPU oracle for the MoE token permute / unpermute path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+CPU-baseline leg of the benchmark may import this package.  The product path
+(the HIP library and its Python binding) never imports, links or runs it, and
+the two share no code.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, scalar loops, built with
+``-O2 -ffp-contract=off``); this module only marshals numpy arrays into it.
+bfloat16 arrays travel as their ``uint16`` bit patterns because numpy has no
+bfloat16 type.
+
+Definitions followed (see the comments in ``moe_oracle.c`` for the passage
+behind each step):
+
+* vLLM PR #14568, "permute/unpermute kernel for moe optimization", PR
+  description -- what permute and unpermute compute.
+* prhub summary of vLLM PR #43014, section "key code snippets"
+  (MoEPermuteScratch) -- names, dtypes and lengths of every buffer, and the
+  numbering of expanded rows as an arange viewed ``[n_token, topk]``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# A test that plants mistakes in a copy of the oracle points this at the copy.
+_LIB_OVERRIDE = os.environ.get("MOE_ORACLE_LIB")
+
+OK = 0
+BAD_ID = -1
+BAD_ARG = -2
+BAD_INV = -3
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = False) -> str:
+    """Compile ``moe_oracle.c`` with gcc into ``libmoe_oracle.so``."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(
+            ["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            lib = ctypes.CDLL(_LIB)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        i32 = ctypes.c_int32
+        lib.oracle_expert_counts.argtypes = [p, i64, i32, i32, p]
+        lib.oracle_expert_counts.restype = ctypes.c_int
+        lib.oracle_expert_first_token_offset.argtypes = [p, i32, p]
+        lib.oracle_expert_first_token_offset.restype = None
+        lib.oracle_stable_expert_order.argtypes = [p, i64, i32, p, p, p]
+        lib.oracle_stable_expert_order.restype = ctypes.c_int
+        lib.oracle_gather_rows.argtypes = [p, i64, p, p, i64, i32, p, p]
+        lib.oracle_gather_rows.restype = None
+        lib.oracle_moe_permute.argtypes = [p, i64, p, p, i64, i32, i32, p, p, p, p, p]
+        lib.oracle_moe_permute.restype = ctypes.c_int
+        lib.oracle_unpermute_f32.argtypes = [p, p, p, i64, i32, i64, p]
+        lib.oracle_unpermute_f32.restype = ctypes.c_int
+        lib.oracle_unpermute_bf16.argtypes = [p, p, p, i64, i32, i64, p]
+        lib.oracle_unpermute_bf16.restype = ctypes.c_int
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(status: int):
+    if status != OK:
+        raise OracleError({BAD_ID: "expert id out of range", BAD_ARG: "bad argument",
+                           BAD_INV: "inv_permuted_idx out of range"}.get(status, str(status)))
+
+
+def _ids2d(topk_ids) -> np.ndarray:
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    if ids.ndim != 2:
+        raise ValueError("topk_ids must be [num_tokens, topk]")
+    return ids
+
+
+# --------------------------------------------------------------------------
+# Permute, step by step
+# --------------------------------------------------------------------------
+def expert_counts(topk_ids, num_experts: int) -> np.ndarray:
+    """Step 1: expanded rows routed to each expert (int64 [E])."""
+    ids = _ids2d(topk_ids)
+    counts = np.zeros(num_experts, dtype=np.int64)
+    _check(_load().oracle_expert_counts(_ptr(ids), ids.shape[0], ids.shape[1], num_experts, _ptr(counts)))
+    return counts
+
+
+def expert_first_token_offset(counts) -> np.ndarray:
+    """Step 2: exclusive prefix sum of the counts (int64 [E+1])."""
+    counts = np.ascontiguousarray(counts, dtype=np.int64)
+    off = np.zeros(counts.shape[0] + 1, dtype=np.int64)
+    _load().oracle_expert_first_token_offset(_ptr(counts), counts.shape[0], _ptr(off))
+    return off
+
+
+def stable_expert_order(topk_ids, num_experts: int, offsets) -> tuple[np.ndarray, np.ndarray]:
+    """Step 3: (permuted_idx, inv_permuted_idx), both int32 [N*topk]."""
+    ids = _ids2d(topk_ids)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    rows = ids.size
+    perm = np.zeros(rows, dtype=np.int32)
+    inv = np.zeros(rows, dtype=np.int32)
+    _check(_load().oracle_stable_expert_order(_ptr(ids), rows, num_experts, _ptr(offsets),
+                                              _ptr(perm), _ptr(inv)))
+    return perm, inv
+
+
+def gather_rows(hidden_bytes: np.ndarray, permuted_idx, topk: int, token_scale=None):
+    """Step 4: permuted rows (raw bytes) and, if given, permuted per-token scales."""
+    hb = np.ascontiguousarray(hidden_bytes, dtype=np.uint8)
+    perm = np.ascontiguousarray(permuted_idx, dtype=np.int32)
+    rows = perm.shape[0]
+    out = np.zeros((rows, hb.shape[1]), dtype=np.uint8)
+    scale = None if token_scale is None else np.ascontiguousarray(token_scale, dtype=np.float32)
+    out_scale = None if scale is None else np.zeros(rows, dtype=np.float32)
+    _load().oracle_gather_rows(_ptr(hb), hb.shape[1], _ptr(scale), _ptr(perm), rows, topk,
+                               _ptr(out), _ptr(out_scale))
+    return out, out_scale
+
+
+def as_row_bytes(hidden: np.ndarray) -> np.ndarray:
+    """View a C-contiguous [N, H] array of any element type as [N, H*itemsize] bytes."""
+    h = np.ascontiguousarray(hidden)
+    return h.view(np.uint8).reshape(h.shape[0], -1)
+
+
+def permute(hidden: np.ndarray, topk_ids, num_experts: int, token_scale=None) -> dict:
+    """The whole permute (steps 1-4).
+
+    ``hidden`` is [N, H] of any element type (float32, bf16 bits as uint16, or
+    fp8 codes as uint8); the permuted rows come back with the same element
+    type.  Returns a dict with ``expert_first_token_offset``, ``permuted_idx``,
+    ``inv_permuted_idx``, ``permuted_hidden_states`` and ``permuted_scale``.
+    """
+    ids = _ids2d(topk_ids)
+    n, topk = ids.shape
+    h = np.ascontiguousarray(hidden)
+    if h.shape[0] != n:
+        raise ValueError("hidden and topk_ids disagree on num_tokens")
+    hb = as_row_bytes(h) if h.size else np.zeros((n, 0), dtype=np.uint8)
+    rows = n * topk
+    off = np.zeros(num_experts + 1, dtype=np.int64)
+    perm = np.zeros(rows, dtype=np.int32)
+    inv = np.zeros(rows, dtype=np.int32)
+    out = np.zeros((rows, hb.shape[1]), dtype=np.uint8)
+    scale = None if token_scale is None else np.ascontiguousarray(token_scale, dtype=np.float32)
+    out_scale = None if scale is None else np.zeros(rows, dtype=np.float32)
+    _check(_load().oracle_moe_permute(_ptr(hb), hb.shape[1], _ptr(scale), _ptr(ids), n, topk,
+                                      num_experts, _ptr(out), _ptr(out_scale), _ptr(off),
+                                      _ptr(perm), _ptr(inv)))
+    return {
+        "expert_first_token_offset": off,
+        "permuted_idx": perm,
+        "inv_permuted_idx": inv,
+        "permuted_hidden_states": out.view(h.dtype).reshape((rows,) + h.shape[1:]) if h.ndim == 2 else out,
+        "permuted_scale": out_scale,
+    }
+
+
+# --------------------------------------------------------------------------
+# Unpermute
+# --------------------------------------------------------------------------
+def unpermute(expanded_output: np.ndarray, topk_weights, inv_permuted_idx, dtype: str) -> np.ndarray:
+    """out[t] = sum_k w[t,k] * Y[inv[t*topk+k]], double-precision sum rounded once.
+
+    ``dtype`` is ``"f32"`` (Y float32) or ``"bf16"`` (Y as uint16 bit patterns);
+    the output has the same representation as Y.
+    """
+    w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("topk_weights must be [num_tokens, topk]")
+    n, topk = w.shape
+    inv = np.ascontiguousarray(inv_permuted_idx, dtype=np.int32).reshape(-1)
+    lib = _load()
+    if dtype == "f32":
+        y = np.ascontiguousarray(expanded_output, dtype=np.float32)
+        out = np.zeros((n, y.shape[1]), dtype=np.float32)
+        _check(lib.oracle_unpermute_f32(_ptr(y), _ptr(w), _ptr(inv), n, topk, y.shape[1], _ptr(out)))
+    elif dtype == "bf16":
+        y = np.ascontiguousarray(expanded_output, dtype=np.uint16)
+        out = np.zeros((n, y.shape[1]), dtype=np.uint16)
+        _check(lib.oracle_unpermute_bf16(_ptr(y), _ptr(w), _ptr(inv), n, topk, y.shape[1], _ptr(out)))
+    else:
+        raise ValueError("unpermute dtype must be 'f32' or 'bf16'")
+    return out
+
+
+def bf16_to_double(bits: int) -> float:
+    return float(_load().oracle_bf16_to_double(int(bits) & 0xFFFF))
+
+
+def double_to_bf16(x: float) -> int:
+    return int(_load().oracle_double_to_bf16(float(x)))

@@ -1,0 +1,273 @@
+/*
+ * moe_oracle.c -- plain, slow, obviously correct CPU definition of the MoE
+ * token permute / unpermute path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file or the library built from it.  Its users are the tests, the
+ * small smoke check and the CPU-baseline leg of the benchmark.  It shares no
+ * code, header, table or helper with the HIP implementation.
+ *
+ * Sources (the three pages on the subject):
+ *   [P1] vLLM PR #14568, "permute/unpermute kernel for moe optimization",
+ *        PR description: permute expands each token to its topk copies and
+ *        orders them so that every expert's tokens are contiguous for the
+ *        grouped GEMM; unpermute reduces the expanded grouped-GEMM output back
+ *        per token, scaling by topk_weight.
+ *   [P3] prhub summary of vLLM PR #43014 (preallocated MoE permute buffers),
+ *        section "key code snippets", class MoEPermuteScratch: buffer names,
+ *        dtypes and lengths (token_expert_indices = arange of the expanded
+ *        rows viewed [n_token, topk]; expert_first_token_offset int64 of
+ *        length num_local_experts+1; permuted_idx, inv_permuted_idx int32 of
+ *        length max_expanded_rows; permuted_hidden_states of hidden_dtype).
+ *
+ * Readings taken where the pages are silent (each is listed with its reason
+ * in the design notes of the repository):
+ *   - expanded row r of token t, slot k is r = t*topk + k (the arange view);
+ *   - rows with the same expert keep ascending r (a stable sort);
+ *   - permuted_idx[j] = r, the expanded row that lands in permuted slot j;
+ *     inv_permuted_idx[r] = j, its inverse;
+ *   - unpermute computes out[t] = sum_k w[t,k] * Y[inv[t*topk+k]]: here the
+ *     sum is formed in double precision in ascending k and rounded once to the
+ *     output type (round to nearest, ties to even).
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared -o libmoe_oracle.so moe_oracle.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ID (-1)  /* an expert id outside [0, num_experts) */
+#define ORACLE_BAD_ARG (-2) /* a size or pointer that makes no sense */
+#define ORACLE_BAD_INV (-3) /* an inv_permuted_idx entry outside [0, N*topk) */
+
+/* ------------------------------------------------------------------------ */
+/* Permute, step 1 -- tokens per expert.                                      */
+/* [P3] key code snippets, MoEPermuteScratch: expert_first_token_offset has   */
+/* one entry per local expert plus one, so the permute needs the number of    */
+/* expanded rows routed to each expert.  The expanded rows are the topk_ids   */
+/* entries taken in row-major order (token_expert_indices is an arange viewed */
+/* as [n_token, topk]).                                                       */
+/* ------------------------------------------------------------------------ */
+int oracle_expert_counts(const int32_t *topk_ids, int64_t num_tokens,
+                         int32_t topk, int32_t num_experts, int64_t *counts)
+{
+    if (num_tokens < 0 || topk < 1 || num_experts < 1)
+        return ORACLE_BAD_ARG;
+    for (int32_t e = 0; e < num_experts; ++e)
+        counts[e] = 0;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        for (int32_t k = 0; k < topk; ++k) {
+            int32_t id = topk_ids[t * topk + k];
+            if (id < 0 || id >= num_experts)
+                return ORACLE_BAD_ID;
+            counts[id] += 1;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Permute, step 2 -- expert_first_token_offset.                              */
+/* [P3] key code snippets: int64, num_experts + 1 entries.  Entry e is the    */
+/* first permuted slot of expert e; the last entry is the number of expanded  */
+/* rows.  This is the exclusive prefix sum of the counts.                     */
+/* ------------------------------------------------------------------------ */
+void oracle_expert_first_token_offset(const int64_t *counts, int32_t num_experts,
+                                      int64_t *expert_first_token_offset)
+{
+    expert_first_token_offset[0] = 0;
+    for (int32_t e = 0; e < num_experts; ++e)
+        expert_first_token_offset[e + 1] = expert_first_token_offset[e] + counts[e];
+}
+
+/* ------------------------------------------------------------------------ */
+/* Permute, step 3 -- stable order of the expanded rows by expert.            */
+/* [P1] PR description: the expanded tokens are ordered so that each expert's */
+/* tokens become contiguous.  [P3] key code snippets: permuted_idx and        */
+/* inv_permuted_idx, int32, one entry per expanded row.                       */
+/* A counting sort: walk the expanded rows in ascending r and hand each the   */
+/* next free slot of its expert.  The ascending walk is what makes rows of    */
+/* one expert keep ascending r.                                               */
+/* ------------------------------------------------------------------------ */
+int oracle_stable_expert_order(const int32_t *topk_ids, int64_t num_rows,
+                               int32_t num_experts,
+                               const int64_t *expert_first_token_offset,
+                               int32_t *permuted_idx, int32_t *inv_permuted_idx)
+{
+    int64_t *next_slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)num_experts);
+    if (next_slot == NULL)
+        return ORACLE_BAD_ARG;
+    for (int32_t e = 0; e < num_experts; ++e)
+        next_slot[e] = expert_first_token_offset[e];
+    for (int64_t r = 0; r < num_rows; ++r) {
+        int32_t id = topk_ids[r];
+        if (id < 0 || id >= num_experts) {
+            free(next_slot);
+            return ORACLE_BAD_ID;
+        }
+        int64_t j = next_slot[id];
+        next_slot[id] = j + 1;
+        permuted_idx[j] = (int32_t)r;
+        inv_permuted_idx[r] = (int32_t)j;
+    }
+    free(next_slot);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Permute, step 4 -- gather the hidden rows into the permuted layout.        */
+/* [P1] PR description: the permute gathers the tokens that are not          */
+/* contiguous for an expert into one contiguous block.  [P3] key code         */
+/* snippets: permuted_hidden_states has max_expanded_rows * hidden_size       */
+/* elements of hidden_dtype.  Expanded row r belongs to token r / topk.       */
+/* The copy is of raw bytes, so any element type (fp32, bf16, fp8 codes) is   */
+/* moved unchanged.  A per-token activation scale, when present, moves with   */
+/* its row ([P2] vLLM PR #19636 "[Kernels] MoE refactor", highlights:         */
+/* per-token activation quantisation parameters).                             */
+/* ------------------------------------------------------------------------ */
+void oracle_gather_rows(const uint8_t *hidden_states, int64_t row_bytes,
+                        const float *token_scale, const int32_t *permuted_idx,
+                        int64_t num_rows, int32_t topk,
+                        uint8_t *permuted_hidden_states, float *permuted_scale)
+{
+    for (int64_t j = 0; j < num_rows; ++j) {
+        int64_t t = permuted_idx[j] / topk;
+        memcpy(permuted_hidden_states + j * row_bytes, hidden_states + t * row_bytes,
+               (size_t)row_bytes);
+        if (token_scale != NULL && permuted_scale != NULL)
+            permuted_scale[j] = token_scale[t];
+    }
+}
+
+/* The whole permute: steps 1 to 4 in order. */
+int oracle_moe_permute(const uint8_t *hidden_states, int64_t row_bytes,
+                       const float *token_scale, const int32_t *topk_ids,
+                       int64_t num_tokens, int32_t topk, int32_t num_experts,
+                       uint8_t *permuted_hidden_states, float *permuted_scale,
+                       int64_t *expert_first_token_offset, int32_t *permuted_idx,
+                       int32_t *inv_permuted_idx)
+{
+    int64_t *counts = (int64_t *)malloc(sizeof(int64_t) * (size_t)(num_experts > 0 ? num_experts : 1));
+    if (counts == NULL)
+        return ORACLE_BAD_ARG;
+    int status = oracle_expert_counts(topk_ids, num_tokens, topk, num_experts, counts);
+    if (status == ORACLE_OK) {
+        oracle_expert_first_token_offset(counts, num_experts, expert_first_token_offset);
+        status = oracle_stable_expert_order(topk_ids, num_tokens * topk, num_experts,
+                                            expert_first_token_offset, permuted_idx,
+                                            inv_permuted_idx);
+    }
+    if (status == ORACLE_OK && row_bytes > 0)
+        oracle_gather_rows(hidden_states, row_bytes, token_scale, permuted_idx,
+                           num_tokens * topk, topk, permuted_hidden_states,
+                           permuted_scale);
+    free(counts);
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* bfloat16, written from the format: 1 sign bit, 8 exponent bits (bias 127), */
+/* 7 fraction bits.  Exponent field 0 holds zero and the subnormals          */
+/* (fraction * 2^-133); field 255 holds infinities (fraction 0) and NaNs.    */
+/* ------------------------------------------------------------------------ */
+double oracle_bf16_to_double(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int expo = (bits >> 7) & 0xFF;
+    int frac = bits & 0x7F;
+    double mag;
+    if (expo == 0xFF)
+        mag = frac ? NAN : INFINITY;
+    else if (expo == 0)
+        mag = ldexp((double)frac, -133);
+    else
+        mag = ldexp(128.0 + (double)frac, expo - 127 - 7);
+    return sign ? -mag : mag;
+}
+
+/* Round a double to the nearest bfloat16, ties to the even fraction; values */
+/* whose rounded magnitude reaches 2^128 become infinity.  NaN maps to the    */
+/* quiet NaN 0x7FC0 with the input's sign.                                    */
+uint16_t oracle_double_to_bf16(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(x);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return (uint16_t)(sign | 0x7F80u);
+    int e2;
+    frexp(a, &e2);              /* a lies in [2^(e2-1), 2^e2) */
+    int p = e2 - 1;             /* binade exponent */
+    if (p < -126)
+        p = -126;               /* below the normal range the spacing stays 2^-133 */
+    double quantum = ldexp(1.0, p - 7); /* spacing of bf16 values in this binade */
+    double q = nearbyint(a / quantum);  /* a / quantum is exact; default mode is nearest-even */
+    double v = q * quantum;
+    if (v >= ldexp(1.0, 128))
+        return (uint16_t)(sign | 0x7F80u);
+    if (v < ldexp(1.0, -126))  /* subnormal (or rounded up to exactly 2^-126, handled below) */
+        return (uint16_t)(sign | (uint16_t)(v / ldexp(1.0, -133)));
+    frexp(v, &e2);
+    int expo = e2 - 1 + 127;
+    int frac = (int)(v / ldexp(1.0, e2 - 1 - 7)) - 128;
+    return (uint16_t)(sign | (uint16_t)(expo << 7) | (uint16_t)frac);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Unpermute.                                                                 */
+/* [P1] PR description: reduce the expanded grouped-GEMM output back per      */
+/* token and scale each contribution by its topk_weight:                      */
+/*     out[t, h] = sum_{k=0}^{topk-1} w[t, k] * Y[inv_permuted_idx[t*topk+k], h] */
+/* Y is in permuted order, so the row holding token t's slot k is             */
+/* inv_permuted_idx[t*topk+k].  The sum is formed in double precision in      */
+/* ascending k and rounded once to the output type.                          */
+/* ------------------------------------------------------------------------ */
+int oracle_unpermute_f32(const float *expanded_output, const float *topk_weights,
+                         const int32_t *inv_permuted_idx, int64_t num_tokens,
+                         int32_t topk, int64_t hidden_size, float *output)
+{
+    int64_t num_rows = num_tokens * topk;
+    for (int64_t r = 0; r < num_rows; ++r)
+        if (inv_permuted_idx[r] < 0 || inv_permuted_idx[r] >= num_rows)
+            return ORACLE_BAD_INV;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        for (int64_t h = 0; h < hidden_size; ++h) {
+            double acc = 0.0;
+            for (int32_t k = 0; k < topk; ++k) {
+                int64_t r = t * topk + k;
+                int64_t j = inv_permuted_idx[r];
+                acc += (double)topk_weights[r] * (double)expanded_output[j * hidden_size + h];
+            }
+            output[t * hidden_size + h] = (float)acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+int oracle_unpermute_bf16(const uint16_t *expanded_output, const float *topk_weights,
+                          const int32_t *inv_permuted_idx, int64_t num_tokens,
+                          int32_t topk, int64_t hidden_size, uint16_t *output)
+{
+    int64_t num_rows = num_tokens * topk;
+    for (int64_t r = 0; r < num_rows; ++r)
+        if (inv_permuted_idx[r] < 0 || inv_permuted_idx[r] >= num_rows)
+            return ORACLE_BAD_INV;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        for (int64_t h = 0; h < hidden_size; ++h) {
+            double acc = 0.0;
+            for (int32_t k = 0; k < topk; ++k) {
+                int64_t r = t * topk + k;
+                int64_t j = inv_permuted_idx[r];
+                acc += (double)topk_weights[r] *
+                       oracle_bf16_to_double(expanded_output[j * hidden_size + h]);
+            }
+            output[t * hidden_size + h] = oracle_double_to_bf16(acc);
+        }
+    }
+    return ORACLE_OK;
+}

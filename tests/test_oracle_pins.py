@@ -1,0 +1,350 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+What pins what:
+* a pure-Python brute force written from the definition on exhaustive tiny
+  grids (ids, counts, offsets, order, gathered rows);
+* numpy library routines: ``bincount``/``cumsum`` for the offsets,
+  ``argsort(kind="stable")`` for the order, fancy indexing for the gather,
+  ``einsum`` in float64 for the unpermute sum;
+* invariants that hold at any size (offsets, bijection, inverse, sortedness);
+* a hand-worked example whose every number is derived in the comments;
+* exact special cases of unpermute (topk=1 with weight 1; the round trip with
+  identity experts and equal power-of-two weights);
+* bfloat16 decoding against torch on all 65536 patterns, and bfloat16
+  rounding against an exact brute-force nearest-value search.
+
+The definition being pinned: vLLM PR #14568 "permute/unpermute kernel for moe
+optimization" (PR description) and the buffer contract in the prhub summary
+of vLLM PR #43014, section "key code snippets" (MoEPermuteScratch).
+"""
+
+import bisect
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+hypothesis = pytest.importorskip("hypothesis")
+from hypothesis import given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+
+# --------------------------------------------------------------------------
+# Brute force, written independently from the definition.
+# --------------------------------------------------------------------------
+def brute_permute(ids2d, num_experts, hidden_rows):
+    flat = [int(v) for row in ids2d for v in row]  # expanded row r = t*topk + k
+    topk = len(ids2d[0]) if len(ids2d) else 1
+    rows = len(flat)
+    perm = [r for e in range(num_experts) for r in range(rows) if flat[r] == e]
+    inv = [0] * rows
+    for j, r in enumerate(perm):
+        inv[r] = j
+    off = [0]
+    for e in range(num_experts):
+        off.append(off[-1] + sum(1 for v in flat if v == e))
+    gathered = [hidden_rows[r // topk] for r in perm]
+    return off, perm, inv, gathered
+
+
+def _grid_ids(rng, n, k, e, mode):
+    if mode == "random":
+        return rng.integers(0, e, size=(n, k))
+    if mode == "one_expert":
+        return np.full((n, k), e - 1)
+    if mode == "distinct" and k <= e:
+        return np.stack([rng.permutation(e)[:k] for _ in range(n)]) if n else np.zeros((0, k), int)
+    if mode == "skip_first_last" and e >= 3:
+        return rng.integers(1, e - 1, size=(n, k))
+    return rng.integers(0, e, size=(n, k))
+
+
+@pytest.mark.parametrize("n,k,e", list(itertools.product([0, 1, 2, 3, 5, 16], [1, 2, 3, 8], [1, 2, 3, 8])))
+def test_oracle_permute_matches_brute_force(n, k, e):
+    rng = np.random.default_rng(1000 + 97 * n + 13 * k + e)
+    for mode in ("random", "one_expert", "distinct", "skip_first_last"):
+        ids = _grid_ids(rng, n, k, e, mode).astype(np.int32).reshape(n, k)
+        hidden = rng.standard_normal((n, 3)).astype(np.float32)
+        got = oracle.permute(hidden, ids, e)
+        off, perm, inv, gathered = brute_permute(ids.tolist(), e, [row.tobytes() for row in hidden])
+        assert got["expert_first_token_offset"].tolist() == off
+        assert got["permuted_idx"].tolist() == perm
+        assert got["inv_permuted_idx"].tolist() == inv
+        assert [row.tobytes() for row in got["permuted_hidden_states"]] == gathered
+
+
+def test_hand_worked_example():
+    # N=3 tokens, topk=2, E=3 experts; token 2 picks expert 2 twice (allowed).
+    ids = np.array([[2, 0], [0, 1], [2, 2]], dtype=np.int32)
+    # expanded rows r = t*2+k carry experts [2, 0, 0, 1, 2, 2]
+    # counts: e0 <- rows 1,2 (2); e1 <- row 3 (1); e2 <- rows 0,4,5 (3)
+    # offsets: [0, 2, 3, 6]
+    # stable order: slots 0,1 <- rows 1,2; slot 2 <- row 3; slots 3,4,5 <- rows 0,4,5
+    # inverse: r0->3, r1->0, r2->1, r3->2, r4->4, r5->5
+    # source tokens of the slots: perm // 2 = [0, 1, 1, 0, 2, 2]
+    x = np.array([[10, 11], [20, 21], [30, 31]], dtype=np.float32)
+    got = oracle.permute(x, ids, 3)
+    assert got["expert_first_token_offset"].tolist() == [0, 2, 3, 6]
+    assert got["permuted_idx"].tolist() == [1, 2, 3, 0, 4, 5]
+    assert got["inv_permuted_idx"].tolist() == [3, 0, 1, 2, 4, 5]
+    assert got["permuted_hidden_states"].tolist() == [[10, 11], [20, 21], [20, 21], [10, 11], [30, 31], [30, 31]]
+    # Unpermute with Y[j] = (j+1) * [1, -1] and weights [[.5,.25],[1,2],[.75,-1]]:
+    # out[0] = .5*Y[inv[0]=3] + .25*Y[inv[1]=0] = .5*4 + .25*1 = 2.25
+    # out[1] = 1*Y[inv[2]=1] + 2*Y[inv[3]=2] = 1*2 + 2*3 = 8
+    # out[2] = .75*Y[inv[4]=4] + (-1)*Y[inv[5]=5] = .75*5 - 6 = -2.25
+    y = np.array([[j + 1, -(j + 1)] for j in range(6)], dtype=np.float32)
+    w = np.array([[0.5, 0.25], [1.0, 2.0], [0.75, -1.0]], dtype=np.float32)
+    out = oracle.unpermute(y, w, got["inv_permuted_idx"], "f32")
+    assert out.tolist() == [[2.25, -2.25], [8.0, -8.0], [-2.25, 2.25]]
+    yb = (y.view(np.uint32) >> 16).astype(np.uint16)  # these values are exact in bf16
+    outb = oracle.unpermute(yb, w, got["inv_permuted_idx"], "bf16")
+    assert ((outb.astype(np.uint32) << 16).view(np.float32)).tolist() == [[2.25, -2.25], [8.0, -8.0], [-2.25, 2.25]]
+
+
+def test_bad_ids_rejected():
+    with pytest.raises(oracle.OracleError):
+        oracle.permute(np.zeros((2, 4), np.float32), np.array([[0, 3]], np.int32).repeat(2, 0), 3)
+    with pytest.raises(oracle.OracleError):
+        oracle.permute(np.zeros((1, 4), np.float32), np.array([[-1, 0]], np.int32), 3)
+    with pytest.raises(oracle.OracleError):
+        oracle.unpermute(np.zeros((2, 4), np.float32), np.ones((1, 2), np.float32), np.array([0, 2], np.int32), "f32")
+
+
+# --------------------------------------------------------------------------
+# Invariants at any size, and library cross-checks on every workload.
+# --------------------------------------------------------------------------
+def check_permute_invariants(ids2d, num_experts, res):
+    flat = np.asarray(ids2d, dtype=np.int64).reshape(-1)
+    rows = flat.shape[0]
+    off = res["expert_first_token_offset"]
+    perm = res["permuted_idx"].astype(np.int64)
+    inv = res["inv_permuted_idx"].astype(np.int64)
+    assert off.dtype == np.int64 and off.shape == (num_experts + 1,)
+    assert off[0] == 0 and off[-1] == rows and np.all(np.diff(off) >= 0)
+    assert np.array_equal(np.sort(perm), np.arange(rows))  # bijection on [0, R)
+    assert np.array_equal(inv[perm], np.arange(rows))  # inv o perm = identity
+    assert np.array_equal(perm[inv], np.arange(rows))  # perm o inv = identity
+    keys = flat[perm]
+    assert np.all(np.diff(keys) >= 0)
+    for e in range(num_experts):
+        seg = perm[off[e]:off[e + 1]]
+        assert np.all(keys[off[e]:off[e + 1]] == e)
+        assert np.all(np.diff(seg) > 0)  # ties keep ascending expanded row
+
+
+@settings(max_examples=150, deadline=None)
+@given(
+    n=st.integers(0, 40),
+    k=st.integers(1, 6),
+    e=st.integers(1, 12),
+    seed=st.integers(0, 2**31 - 1),
+)
+def test_oracle_invariants_property(n, k, e, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, e, size=(n, k)).astype(np.int32)
+    res = oracle.permute(rng.standard_normal((n, 2)).astype(np.float32), ids, e)
+    check_permute_invariants(ids, e, res)
+    np.testing.assert_array_equal(res["expert_first_token_offset"],
+                                  np.concatenate([[0], np.cumsum(np.bincount(ids.ravel(), minlength=e))]))
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "qwen3", "dsv3", "decode"])
+def test_oracle_order_matches_numpy_at_workload_sizes(name):
+    w = W.WORKLOADS[name]
+    ids, _ = W.make_routing(w)
+    counts = oracle.expert_counts(ids, w.num_experts)
+    np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=w.num_experts))
+    off = oracle.expert_first_token_offset(counts)
+    np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(counts)]))
+    perm, inv = oracle.stable_expert_order(ids, w.num_experts, off)
+    np.testing.assert_array_equal(perm, np.argsort(ids.ravel(), kind="stable"))
+    check_permute_invariants(ids, w.num_experts, {"expert_first_token_offset": off,
+                                                  "permuted_idx": perm, "inv_permuted_idx": inv})
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.uint16, np.uint8])
+def test_oracle_gather_matches_fancy_indexing(dtype):
+    rng = np.random.default_rng(7)
+    n, k, e, h = 37, 3, 5, 48
+    ids = rng.integers(0, e, size=(n, k)).astype(np.int32)
+    x = rng.integers(0, 255, size=(n, h)).astype(dtype)
+    scale = rng.random(n).astype(np.float32)
+    res = oracle.permute(x, ids, e, token_scale=scale)
+    src = res["permuted_idx"] // k
+    np.testing.assert_array_equal(res["permuted_hidden_states"], x[src])
+    np.testing.assert_array_equal(res["permuted_scale"], scale[src])
+
+
+# --------------------------------------------------------------------------
+# bfloat16 decoding and rounding.
+# --------------------------------------------------------------------------
+def test_bf16_decode_all_patterns_against_torch():
+    torch = pytest.importorskip("torch")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def _finite_bf16_table():
+    vals = []
+    for b in range(0x0000, 0x7F80):  # +0 .. largest finite
+        vals.append(oracle.bf16_to_double(b))
+    return vals  # ascending, patterns 0..0x7F7F
+
+
+_TABLE = None
+
+
+def brute_nearest_bf16(x: float) -> int:
+    """Nearest bf16 by exhaustive search with exact rational arithmetic (ties -> even pattern)."""
+    global _TABLE
+    if _TABLE is None:
+        _TABLE = _finite_bf16_table()
+    sign = 0x8000 if np.signbit(x) else 0
+    a = abs(x)
+    fa = Fraction(a)
+    max_finite = Fraction(_TABLE[-1])
+    overflow_at = max_finite + (Fraction(2) ** 128 - max_finite) / 2
+    if fa >= overflow_at:
+        return sign | 0x7F80
+    i = bisect.bisect_left(_TABLE, a)
+    if i < len(_TABLE) and _TABLE[i] == a:
+        return sign | i
+    lo, hi = i - 1, i
+    dlo = fa - Fraction(_TABLE[lo])
+    dhi = Fraction(_TABLE[hi]) - fa
+    if dlo < dhi:
+        return sign | lo
+    if dhi < dlo:
+        return sign | hi
+    return sign | (lo if lo % 2 == 0 else hi)
+
+
+def test_bf16_rounding_against_exhaustive_nearest():
+    rng = np.random.default_rng(3)
+    tests = [0.0, -0.0, 1.0, -1.0, 1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, 1.0 + 2.0**-8 + 2.0**-40,
+             1.0 + 2.0**-8 - 2.0**-40, 2.0**-126, 2.0**-133, 2.0**-134, 3 * 2.0**-134, 2.0**-135,
+             2.0**-126 - 2.0**-134, 65504.0, 3.0e38, 3.4e38, 3.3895313892515355e38, 2.0**128, 1e300, -1e-300]
+    # exact midpoints between neighbours, and points just beside them
+    table = _finite_bf16_table()
+    for i in rng.integers(0, len(table) - 1, size=200):
+        mid = (table[i] + table[i + 1]) / 2.0
+        tests += [mid, np.nextafter(mid, 0.0), np.nextafter(mid, np.inf), -mid]
+    tests += list(rng.standard_normal(300) * 10.0 ** rng.integers(-40, 38, size=300))
+    for x in tests:
+        assert oracle.double_to_bf16(float(x)) == brute_nearest_bf16(float(x)), x
+
+
+def test_bf16_rounding_of_floats_against_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(4)
+    xs = np.concatenate([rng.standard_normal(4000).astype(np.float32),
+                         (rng.standard_normal(1000) * 1e-38).astype(np.float32),
+                         np.array([1 + 2**-8, 1 + 3 * 2**-8, 3.3895e38, -3.39e38], dtype=np.float32)])
+    ref = torch.from_numpy(xs).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.double_to_bf16(float(x)) for x in xs], dtype=np.uint16)
+    np.testing.assert_array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# Unpermute.
+# --------------------------------------------------------------------------
+def _bf16_bits_from_f32(x):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _f32_from_bf16_bits(b):
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unpermute_topk1_weight1_is_a_gather(dtype):
+    rng = np.random.default_rng(5)
+    n, h = 29, 40
+    inv = rng.permutation(n).astype(np.int32)
+    y = rng.standard_normal((n, h)).astype(np.float32)
+    if dtype == "bf16":
+        y = _bf16_bits_from_f32(y)
+    out = oracle.unpermute(y, np.ones((n, 1), np.float32), inv, dtype)
+    np.testing.assert_array_equal(out, y[inv])
+
+
+@pytest.mark.parametrize("dtype,topk", [("f32", 1), ("f32", 2), ("bf16", 1), ("bf16", 2), ("bf16", 4), ("bf16", 8)])
+def test_round_trip_identity_experts_is_exact(dtype, topk):
+    # With identity experts (Y = permuted X) and all weights 1/topk, every partial sum
+    # j*x/topk is exact in fp32 for bf16 x (8 significant bits + log2(topk) <= 24), and
+    # for fp32 x when topk <= 2; the double sum is exact as well, so out == x bit for bit.
+    rng = np.random.default_rng(6)
+    n, e, h = 50, 9, 24
+    ids = np.stack([rng.permutation(e)[:topk] for _ in range(n)]).astype(np.int32)
+    x = rng.standard_normal((n, h)).astype(np.float32)
+    if dtype == "bf16":
+        x = _bf16_bits_from_f32(x)
+    p = oracle.permute(x, ids, e)
+    w = np.full((n, topk), 1.0 / topk, np.float32)
+    out = oracle.unpermute(p["permuted_hidden_states"], w, p["inv_permuted_idx"], dtype)
+    np.testing.assert_array_equal(out, x)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_round_trip_weights_sum_to_one(dtype):
+    rng = np.random.default_rng(8)
+    n, e, k, h = 64, 16, 6, 32
+    ids = np.stack([rng.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    x = rng.standard_normal((n, h)).astype(np.float32)
+    wt = rng.random((n, k))
+    wt = (wt / wt.sum(1, keepdims=True)).astype(np.float32)
+    if dtype == "bf16":
+        x = _bf16_bits_from_f32(x)
+    p = oracle.permute(x, ids, e)
+    out = oracle.unpermute(p["permuted_hidden_states"], wt, p["inv_permuted_idx"], dtype)
+    xf = _f32_from_bf16_bits(x) if dtype == "bf16" else x
+    of = _f32_from_bf16_bits(out) if dtype == "bf16" else out
+    # weights sum to 1 up to float32 rounding of each weight (k * 2^-24) plus one output rounding
+    tol = (2.0**-8 if dtype == "bf16" else 2.0**-23) * np.abs(xf) + k * 2.0**-23 * np.abs(xf) + 1e-30
+    assert np.all(np.abs(of - xf) <= tol)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unpermute_against_float64_einsum(dtype):
+    rng = np.random.default_rng(9)
+    n, e, k, h = 41, 7, 3, 35
+    ids = np.stack([rng.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    p = oracle.permute(np.zeros((n, 1), np.float32), ids, e)
+    inv = p["inv_permuted_idx"]
+    y32 = rng.standard_normal((n * k, h)).astype(np.float32)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    y = _bf16_bits_from_f32(y32) if dtype == "bf16" else y32
+    yv = _f32_from_bf16_bits(y) if dtype == "bf16" else y
+    ref = np.einsum("tk,tkh->th", w.astype(np.float64), yv.astype(np.float64)[inv.reshape(n, k)])
+    out = oracle.unpermute(y, w, inv, dtype)
+    if dtype == "f32":
+        np.testing.assert_array_equal(out, ref.astype(np.float32))
+    else:
+        # every output is the nearest bf16 of the exact sum
+        flat_ref = ref.reshape(-1)
+        flat_out = out.reshape(-1)
+        for i in range(0, flat_ref.shape[0], 7):
+            assert flat_out[i] == brute_nearest_bf16(float(flat_ref[i]))
+        of = _f32_from_bf16_bits(out).astype(np.float64)
+        assert np.all(np.abs(of - ref) <= 2.0**-8 * np.abs(ref) + 2.0**-133)
+
+
+def test_unpermute_weight_index_is_token_major():
+    # w[t, k] multiplies the row of expanded row r = t*topk + k (not w[k, t]).
+    n, k, h = 3, 2, 1
+    inv = np.arange(n * k, dtype=np.int32)
+    y = np.arange(1, n * k + 1, dtype=np.float32).reshape(n * k, h)
+    w = np.array([[1, 10], [100, 1000], [10000, 100000]], np.float32)
+    out = oracle.unpermute(y, w, inv, "f32")
+    assert out.reshape(-1).tolist() == [1 * 1 + 10 * 2, 100 * 3 + 1000 * 4, 10000 * 5 + 100000 * 6]
