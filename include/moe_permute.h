@@ -1,0 +1,159 @@
+/*
+ * moe_permute.h -- C ABI of the MI355X (gfx950) MoE token permute / unpermute
+ * library, libmoe_permute.so.
+ *
+ * What is computed (the three pages on the subject):
+ *   - vLLM PR #14568, "permute/unpermute kernel for moe optimization", PR
+ *     description: permute expands every token into its topk copies and
+ *     orders the copies so that the tokens of each expert are contiguous, as
+ *     the grouped GEMM wants them; unpermute folds the expanded grouped-GEMM
+ *     output back into one row per token, weighting each copy by its
+ *     topk_weight.
+ *   - prhub summary of vLLM PR #43014 (preallocated MoE permute buffers),
+ *     section "key code snippets", MoEPermuteScratch: the buffers and their
+ *     types -- expert_first_token_offset int64 [num_experts + 1];
+ *     permuted_idx and inv_permuted_idx int32 [num_tokens * topk];
+ *     permuted_hidden_states [num_tokens * topk, hidden_size] of the hidden
+ *     type; a sort workspace whose size is queried up front; expanded rows
+ *     numbered by an arange viewed [num_tokens, topk].
+ *   - same summary, sections "implementation breakdown" and "review
+ *     highlights": callers preallocate every buffer once and reuse it; the
+ *     library must write into the caller's buffers (never a hidden copy); the
+ *     size query must be safe to call anywhere.
+ *
+ * Definitions used throughout (N = num_tokens, K = topk, E = num_experts):
+ *   expanded row     r = t*K + k  holds topk_ids[t][k]           (0 <= r < N*K)
+ *   offsets          expert_first_token_offset[e] = number of expanded rows
+ *                    whose expert is < e; entry E equals N*K
+ *   order            rows of one expert keep ascending r (a stable sort)
+ *   permuted_idx[j]  = r, the expanded row placed at permuted position j
+ *   inv_permuted_idx[r] = j, so inv[perm[j]] = j and perm[inv[r]] = r
+ *   permute rows     permuted_hidden_states[j] = hidden_states[permuted_idx[j] / K]
+ *   unpermute        output[t] = sum over k = 0..K-1, ascending, of
+ *                    topk_weights[t][k] * expanded_output[inv_permuted_idx[t*K+k]]
+ *                    accumulated in fp32 and rounded once (round to nearest even)
+ *
+ * Conventions for every entry point:
+ *   - Stateless and reentrant.  No call allocates memory, frees memory,
+ *     memsets, synchronises the host or copies host<->device.  Work is
+ *     enqueued on `stream` (a hipStream_t; NULL is the null stream) and the
+ *     call returns after enqueueing.  Buffers must stay valid until the
+ *     stream reaches the work.
+ *   - Every pointer is a device pointer owned by the caller, C-contiguous,
+ *     row-major.  Outputs must not overlap inputs or each other.
+ *   - Arguments are checked on the host before anything is enqueued; a
+ *     failed check returns its status and leaves every buffer untouched.
+ *   - Alignment: hidden / expanded / output row pointers 16 bytes, and the
+ *     row length in bytes (hidden_size * element size) a multiple of 16;
+ *     int32 and float arrays 4 bytes; int64 arrays 8 bytes.
+ *   - Limits: 1 <= num_experts <= MOE_MAX_EXPERTS; 1 <= topk <= num_experts;
+ *     num_tokens >= 0; num_tokens * topk < 2^31 (int32 indices).
+ */
+#ifndef MOE_PERMUTE_H
+#define MOE_PERMUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,         /* a size, pointer or combination is invalid */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 2, /* workspace_bytes < the size this call needs */
+    MOE_ERR_MISALIGNED = 3,          /* pointer or row pitch breaks the alignment rules */
+    MOE_ERR_UNSUPPORTED = 4,         /* element type not supported by this operation */
+    MOE_ERR_HIP = 5                  /* the HIP runtime refused a launch */
+} moe_status_t;
+
+typedef enum moe_dtype {
+    MOE_DTYPE_F32 = 0,     /* IEEE binary32 */
+    MOE_DTYPE_BF16 = 1,    /* bfloat16 */
+    MOE_DTYPE_FP8_E4M3 = 2 /* OCP fp8 E4M3FN codes (permute moves them as bytes) */
+} moe_dtype_t;
+
+#define MOE_MAX_EXPERTS 1024
+
+/*
+ * moe_permute_supported -- 1 if `device` exists and is a gfx950 GPU, else 0.
+ * Never fails or aborts, including on a host with no GPU or no HIP driver.
+ * (Summary of vLLM PR #43014, "review highlights": the size query crashed on
+ * platforms without the kernel, so callers need a guard that is always safe.)
+ */
+int moe_permute_supported(int device);
+
+/*
+ * moe_permute_workspace_size -- bytes of device workspace that moe_permute
+ * needs for any num_tokens <= max_num_tokens with this topk and num_experts.
+ * A pure host function: no HIP call, no device needed, monotone
+ * non-decreasing in max_num_tokens.  Returns 0 when the arguments are outside
+ * the limits above.  (Summary of vLLM PR #43014, "key code snippets": the sort
+ * workspace is sized once, from the largest expanded-row count and the expert
+ * count, and allocated as bytes.)
+ */
+size_t moe_permute_workspace_size(int64_t max_num_tokens, int32_t topk, int32_t num_experts);
+
+/*
+ * moe_permute -- expert histogram, exclusive-scan offsets, stable order of
+ * the expanded rows by expert, and the gather of hidden rows into the
+ * per-expert contiguous layout (vLLM PR #14568, PR description; buffers per
+ * the summary of vLLM PR #43014, "key code snippets").
+ *
+ *   hidden_states            [N, hidden_size] of `dtype`; ignored when hidden_size == 0
+ *   dtype                    MOE_DTYPE_F32 / BF16 / FP8_E4M3 (rows are moved as raw bytes)
+ *   token_scale              [N] float, per-token activation scale, or NULL
+ *   topk_ids                 [N, topk] int32, every value in [0, num_experts)
+ *   num_tokens, hidden_size, topk, num_experts   sizes (hidden_size 0: indices only)
+ *   permuted_hidden_states   [N*topk, hidden_size] of `dtype` (out); ignored when hidden_size == 0
+ *   permuted_scale           [N*topk] float (out); non-NULL exactly when token_scale is
+ *   expert_first_token_offset [num_experts + 1] int64 (out)
+ *   permuted_idx             [N*topk] int32 (out)
+ *   inv_permuted_idx         [N*topk] int32 (out)
+ *   workspace                device scratch of workspace_bytes bytes (16-byte aligned);
+ *                            may be NULL if moe_permute_workspace_size(N, topk, E) is 0.
+ *                            Its contents on entry do not matter and are not preserved.
+ *   stream                   hipStream_t
+ *
+ * Results never depend on earlier contents of the outputs or the workspace.
+ * With num_tokens == 0 only the offsets are written (all zero).
+ * An expert id outside [0, num_experts) is detected on the device: then every
+ * entry of expert_first_token_offset is set to -1 and nothing else is
+ * written; no out-of-bounds access happens.
+ */
+moe_status_t moe_permute(const void *hidden_states, int32_t dtype, const float *token_scale,
+                         const int32_t *topk_ids, int64_t num_tokens, int64_t hidden_size,
+                         int32_t topk, int32_t num_experts, void *permuted_hidden_states,
+                         float *permuted_scale, int64_t *expert_first_token_offset,
+                         int32_t *permuted_idx, int32_t *inv_permuted_idx, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
+ * moe_unpermute -- weighted top-k reduction of the expanded grouped-GEMM
+ * output back to one row per token (vLLM PR #14568, PR description):
+ *     output[t] = sum_{k=0}^{topk-1} topk_weights[t][k] * expanded_output[inv_permuted_idx[t*topk+k]]
+ * accumulated in fp32 in ascending k, rounded once to `dtype`.
+ *
+ *   expanded_output   [N*topk, hidden_size] of `dtype`, in permuted order
+ *   dtype             MOE_DTYPE_F32 or MOE_DTYPE_BF16 (else MOE_ERR_UNSUPPORTED)
+ *   topk_weights      [N, topk] float
+ *   inv_permuted_idx  [N*topk] int32, as written by moe_permute
+ *   output            [N, hidden_size] of `dtype` (out)
+ *
+ * An inv_permuted_idx entry outside [0, N*topk) is detected on the device:
+ * that token's output row is filled with NaN and no out-of-bounds read happens.
+ * Needs no workspace.
+ */
+moe_status_t moe_unpermute(const void *expanded_output, int32_t dtype, const float *topk_weights,
+                           const int32_t *inv_permuted_idx, int64_t num_tokens,
+                           int64_t hidden_size, int32_t topk, void *output, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *moe_status_string(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_PERMUTE_H */

@@ -1,0 +1,226 @@
+"""Python binding of libmoe_permute.so (argument marshalling only).
+
+Every step of the path runs in the HIP library; this module turns torch
+tensors into raw device pointers and sizes, passes the caller's current HIP
+stream, and raises on a non-OK status.  There is no fallback: if the library
+is missing the first call raises.
+
+The entry points carry the C names: ``moe_permute_supported``,
+``moe_permute_workspace_size``, ``moe_permute``, ``moe_unpermute``.
+``MoEPermuteScratch`` follows the preallocated-buffer design of the prhub
+summary of vLLM PR #43014 (section "key code snippets", MoEPermuteScratch):
+every buffer is allocated once for ``max_num_tokens`` and reused by each call.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_permute.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_WORKSPACE_TOO_SMALL = 2
+MOE_ERR_MISALIGNED = 3
+MOE_ERR_UNSUPPORTED = 4
+MOE_ERR_HIP = 5
+
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
+MOE_DTYPE_FP8_E4M3 = 2
+MOE_MAX_EXPERTS = 1024
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (what, _status_name(status)))
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmoe_permute.so; raises FileNotFoundError if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                "libmoe_permute.so is not built (%s); run "
+                "`python -m mixture_experts_token_amd.build_lib`" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.moe_permute_supported.argtypes = [ctypes.c_int]
+        lib.moe_permute_supported.restype = ctypes.c_int
+        lib.moe_permute_workspace_size.argtypes = [i64, i32, i32]
+        lib.moe_permute_workspace_size.restype = sz
+        lib.moe_permute.argtypes = [p, i32, p, p, i64, i64, i32, i32, p, p, p, p, p, p, sz, p]
+        lib.moe_permute.restype = ctypes.c_int
+        lib.moe_unpermute.argtypes = [p, i32, p, p, i64, i64, i32, p, p]
+        lib.moe_unpermute.restype = ctypes.c_int
+        lib.moe_status_string.argtypes = [ctypes.c_int]
+        lib.moe_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _status_name(status: int) -> str:
+    try:
+        return load_library().moe_status_string(status).decode()
+    except Exception:
+        return str(status)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return MOE_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MOE_DTYPE_FP8_E4M3
+    raise TypeError("unsupported element type %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else None
+
+
+def _stream(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def moe_permute_supported(device: int = 0) -> bool:
+    return bool(load_library().moe_permute_supported(int(device)))
+
+
+def moe_permute_workspace_size(max_num_tokens: int, topk: int, num_experts: int) -> int:
+    return int(load_library().moe_permute_workspace_size(int(max_num_tokens), int(topk), int(num_experts)))
+
+
+def moe_permute(hidden_states, topk_ids, num_experts: int, permuted_hidden_states,
+                expert_first_token_offset, permuted_idx, inv_permuted_idx, workspace=None,
+                token_scale=None, permuted_scale=None, stream=None) -> None:
+    """Enqueue the permute on ``stream`` (default: torch's current stream).
+
+    ``hidden_states`` [N, H] (float32, bfloat16, or fp8 codes as uint8 /
+    float8_e4m3fn) or None for an index-only permute; ``topk_ids`` int32
+    [N, topk].  Outputs are written in place.
+    """
+    import torch
+
+    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
+        raise TypeError("topk_ids must be an int32 [num_tokens, topk] tensor")
+    n, topk = topk_ids.shape
+    if hidden_states is None:
+        hidden, code, hsize = None, MOE_DTYPE_BF16, 0
+    else:
+        hidden, code, hsize = hidden_states, _dtype_code(hidden_states), hidden_states.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = load_library().moe_permute(
+        _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), n, hsize, topk, int(num_experts),
+        _ptr(permuted_hidden_states) if hsize else None, _ptr(permuted_scale),
+        _ptr(expert_first_token_offset), _ptr(permuted_idx), _ptr(inv_permuted_idx),
+        _ptr(workspace), ws_bytes, _stream(stream, topk_ids.device))
+    if status != MOE_OK:
+        raise MoEError(status, "moe_permute")
+
+
+def moe_unpermute(expanded_output, topk_weights, inv_permuted_idx, output, stream=None) -> None:
+    """Enqueue the unpermute on ``stream`` (default: torch's current stream).
+
+    ``expanded_output`` [N*topk, H] float32 or bfloat16 in permuted order,
+    ``topk_weights`` float32 [N, topk], ``inv_permuted_idx`` int32 [N*topk],
+    ``output`` [N, H] of the same type as ``expanded_output``.
+    """
+    n, topk = topk_weights.shape
+    status = load_library().moe_unpermute(
+        _ptr(expanded_output), _dtype_code(expanded_output), _ptr(topk_weights), _ptr(inv_permuted_idx),
+        n, expanded_output.shape[-1], topk, _ptr(output), _stream(stream, output.device))
+    if status != MOE_OK:
+        raise MoEError(status, "moe_unpermute")
+
+
+class MoEPermuteScratch:
+    """Every permute buffer, allocated once for ``max_num_tokens`` and reused.
+
+    Mirrors MoEPermuteScratch in the prhub summary of vLLM PR #43014 (section
+    "key code snippets"): offsets int64 [num_experts + 1]; permuted_idx and
+    inv_permuted_idx int32 [max_num_tokens * topk]; permuted_hidden_states
+    only when ``hidden_size`` is given; an opaque workspace sized by the
+    library's size query.  ``validate`` performs the same checks the summary
+    lists (device, token count, topk, hidden size and type).
+    """
+
+    def __init__(self, max_num_tokens: int, topk: int, num_experts: int, device, hidden_size: int | None = None,
+                 hidden_dtype=None, with_scale: bool = False):
+        import torch
+
+        self.max_num_tokens = int(max_num_tokens)
+        self.topk = int(topk)
+        self.num_experts = int(num_experts)
+        self.device = torch.device(device)
+        self.hidden_size = hidden_size
+        self.hidden_dtype = hidden_dtype
+        self.max_expanded_rows = self.max_num_tokens * self.topk
+        rows = self.max_expanded_rows
+        self.expert_first_token_offset = torch.empty(self.num_experts + 1, dtype=torch.int64, device=self.device)
+        self.permuted_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
+        self.inv_permuted_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
+        self.permuted_hidden_states = None
+        if hidden_size is not None:
+            self.permuted_hidden_states = torch.empty(rows * hidden_size, dtype=hidden_dtype, device=self.device)
+        self.permuted_scale = torch.empty(rows, dtype=torch.float32, device=self.device) if with_scale else None
+        ws = moe_permute_workspace_size(self.max_num_tokens, self.topk, self.num_experts)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
+
+    def validate(self, hidden_states, topk_ids) -> None:
+        n = topk_ids.shape[0]
+        if topk_ids.device != self.device or (hidden_states is not None and hidden_states.device != self.device):
+            raise ValueError("inputs are not on the scratch device")
+        if n > self.max_num_tokens:
+            raise ValueError("num_tokens %d exceeds max_num_tokens %d" % (n, self.max_num_tokens))
+        if topk_ids.dim() != 2 or topk_ids.shape[1] != self.topk:
+            raise ValueError("topk_ids must be [num_tokens, %d]" % self.topk)
+        if hidden_states is not None:
+            if hidden_states.shape[0] != n:
+                raise ValueError("hidden_states and topk_ids disagree on num_tokens")
+            if self.hidden_size is not None and (hidden_states.shape[-1] != self.hidden_size
+                                                 or hidden_states.dtype != self.hidden_dtype):
+                raise ValueError("hidden_states does not match the scratch hidden size / type")
+
+    def permute(self, hidden_states, topk_ids, token_scale=None, stream=None) -> dict:
+        """Run moe_permute into the scratch buffers; returns views sized for this call."""
+        self.validate(hidden_states, topk_ids)
+        n = topk_ids.shape[0]
+        rows = n * self.topk
+        out_hidden = None
+        if hidden_states is not None:
+            if self.permuted_hidden_states is None:
+                raise ValueError("scratch was created without hidden_size")
+            out_hidden = self.permuted_hidden_states[: rows * self.hidden_size].view(rows, self.hidden_size)
+        out_scale = None
+        if token_scale is not None:
+            if self.permuted_scale is None:
+                raise ValueError("scratch was created without with_scale=True")
+            out_scale = self.permuted_scale[:rows]
+        moe_permute(hidden_states, topk_ids, self.num_experts, out_hidden, self.expert_first_token_offset,
+                    self.permuted_idx[:rows], self.inv_permuted_idx[:rows], self.workspace,
+                    token_scale=token_scale, permuted_scale=out_scale, stream=stream)
+        return {
+            "permuted_hidden_states": out_hidden,
+            "permuted_scale": out_scale,
+            "expert_first_token_offset": self.expert_first_token_offset,
+            "permuted_idx": self.permuted_idx[:rows],
+            "inv_permuted_idx": self.inv_permuted_idx[:rows],
+        }

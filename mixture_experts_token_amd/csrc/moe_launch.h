@@ -1,0 +1,41 @@
+// moe_launch.h -- internal interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "moe_plan.h"
+
+namespace moe {
+
+struct PermuteArgs {
+    const void* hidden_states;      // [N, row_vecs * 16 bytes] or null when row_vecs == 0
+    const float* token_scale;       // [N] or null
+    const int32_t* topk_ids;        // [N, topk]
+    int64_t num_tokens;
+    int64_t row_vecs;               // row length in 16-byte vectors (0: indices only)
+    int32_t topk;
+    int32_t num_experts;
+    void* permuted_hidden_states;   // [N*topk, row_vecs * 16 bytes]
+    float* permuted_scale;          // [N*topk] or null
+    int64_t* expert_first_token_offset;  // [E+1]
+    int32_t* permuted_idx;          // [N*topk]
+    int32_t* inv_permuted_idx;      // [N*topk]
+};
+
+struct UnpermuteArgs {
+    const void* expanded_output;    // [N*topk, row_vecs * 16 bytes]
+    const float* topk_weights;      // [N, topk]
+    const int32_t* inv_permuted_idx;  // [N*topk]
+    int64_t num_tokens;
+    int64_t row_vecs;
+    int32_t topk;
+    void* output;                   // [N, row_vecs * 16 bytes]
+};
+
+hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t value, hipStream_t stream);
+hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream);
+hipError_t launch_unpermute(const UnpermuteArgs& a, bool bf16, hipStream_t stream);
+
+}  // namespace moe

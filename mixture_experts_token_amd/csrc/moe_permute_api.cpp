@@ -1,0 +1,200 @@
+// moe_permute_api.cpp -- the C ABI declared in include/moe_permute.h.
+//
+// Every argument check runs on the host before anything touches HIP, so a
+// rejected call has no side effect and the checks work on a host with no GPU.
+// The only HIP calls are the kernel launches (and, in moe_permute_supported,
+// the device queries).
+
+#include "moe_permute.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "moe_launch.h"
+#include "moe_plan.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;  // int32 indices
+constexpr int64_t kMaxRowBytes = int64_t(1) << 40;
+
+int64_t element_bytes(int32_t dtype) {
+    switch (dtype) {
+        case MOE_DTYPE_F32: return 4;
+        case MOE_DTYPE_BF16: return 2;
+        case MOE_DTYPE_FP8_E4M3: return 1;
+        default: return 0;
+    }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Span {
+    const void* p;
+    uint64_t bytes;
+};
+
+bool overlap(const Span& a, const Span& b) {
+    if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// True if any output overlaps any other output or any input.
+bool any_overlap(const Span* outs, int nouts, const Span* ins, int nins) {
+    for (int i = 0; i < nouts; ++i) {
+        for (int j = i + 1; j < nouts; ++j)
+            if (overlap(outs[i], outs[j])) return true;
+        for (int j = 0; j < nins; ++j)
+            if (overlap(outs[i], ins[j])) return true;
+    }
+    return false;
+}
+
+bool sizes_ok(int64_t num_tokens, int32_t topk, int32_t num_experts) {
+    if (num_tokens < 0 || topk < 1 || num_experts < 1 || num_experts > MOE_MAX_EXPERTS || topk > num_experts)
+        return false;
+    return num_tokens <= kMaxRows / topk;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+int moe_permute_supported(int device) {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess) return 0;
+    if (device < 0 || device >= count) return 0;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return 0;
+    return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+size_t moe_permute_workspace_size(int64_t max_num_tokens, int32_t topk, int32_t num_experts) {
+    if (!sizes_ok(max_num_tokens, topk, num_experts)) return 0;
+    return moe::workspace_bound(max_num_tokens, topk, num_experts);
+}
+
+moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* token_scale,
+                         const int32_t* topk_ids, int64_t num_tokens, int64_t hidden_size, int32_t topk,
+                         int32_t num_experts, void* permuted_hidden_states, float* permuted_scale,
+                         int64_t* expert_first_token_offset, int32_t* permuted_idx, int32_t* inv_permuted_idx,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    const int64_t eb = element_bytes(dtype);
+    if (eb == 0) return MOE_ERR_INVALID_ARG;
+    if (!sizes_ok(num_tokens, topk, num_experts)) return MOE_ERR_INVALID_ARG;
+    if (hidden_size < 0 || hidden_size > kMaxRowBytes / eb) return MOE_ERR_INVALID_ARG;
+    if (expert_first_token_offset == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!aligned(expert_first_token_offset, 8)) return MOE_ERR_MISALIGNED;
+    if ((token_scale == nullptr) != (permuted_scale == nullptr)) return MOE_ERR_INVALID_ARG;
+    const int64_t row_bytes = hidden_size * eb;
+    if (row_bytes % 16 != 0) return MOE_ERR_MISALIGNED;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (num_tokens == 0) {
+        return moe::launch_fill_offsets(expert_first_token_offset, num_experts, 0, s) == hipSuccess ? MOE_OK
+                                                                                                    : MOE_ERR_HIP;
+    }
+    if (topk_ids == nullptr || permuted_idx == nullptr || inv_permuted_idx == nullptr) return MOE_ERR_INVALID_ARG;
+    if (hidden_size > 0 && (hidden_states == nullptr || permuted_hidden_states == nullptr))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(topk_ids, 4) || !aligned(permuted_idx, 4) || !aligned(inv_permuted_idx, 4))
+        return MOE_ERR_MISALIGNED;
+    if (token_scale != nullptr && (!aligned(token_scale, 4) || !aligned(permuted_scale, 4))) return MOE_ERR_MISALIGNED;
+    if (hidden_size > 0 && (!aligned(hidden_states, 16) || !aligned(permuted_hidden_states, 16)))
+        return MOE_ERR_MISALIGNED;
+
+    const moe::PermutePlan plan = moe::plan_permute(num_tokens, topk, num_experts);
+    if (workspace_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (plan.ws_bytes > 0) {
+        if (workspace == nullptr) return MOE_ERR_INVALID_ARG;
+        if (!aligned(workspace, 16)) return MOE_ERR_MISALIGNED;
+    }
+
+    const uint64_t rows = (uint64_t)plan.rows;
+    const bool copy_rows = hidden_size > 0;
+    const Span outs[] = {
+        {copy_rows ? permuted_hidden_states : nullptr, rows * (uint64_t)row_bytes},
+        {permuted_scale, rows * 4},
+        {expert_first_token_offset, 8ull * (uint64_t)(num_experts + 1)},
+        {permuted_idx, rows * 4},
+        {inv_permuted_idx, rows * 4},
+        {workspace, (uint64_t)plan.ws_bytes},
+    };
+    const Span ins[] = {
+        {copy_rows ? hidden_states : nullptr, (uint64_t)num_tokens * (uint64_t)row_bytes},
+        {token_scale, (uint64_t)num_tokens * 4},
+        {topk_ids, rows * 4},
+    };
+    if (any_overlap(outs, 6, ins, 3)) return MOE_ERR_INVALID_ARG;
+
+    moe::PermuteArgs a;
+    a.hidden_states = copy_rows ? hidden_states : nullptr;
+    a.token_scale = token_scale;
+    a.topk_ids = topk_ids;
+    a.num_tokens = num_tokens;
+    a.row_vecs = row_bytes / 16;
+    a.topk = topk;
+    a.num_experts = num_experts;
+    a.permuted_hidden_states = copy_rows ? permuted_hidden_states : nullptr;
+    a.permuted_scale = permuted_scale;
+    a.expert_first_token_offset = expert_first_token_offset;
+    a.permuted_idx = permuted_idx;
+    a.inv_permuted_idx = inv_permuted_idx;
+    return moe::launch_permute(a, plan, workspace, s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t moe_unpermute(const void* expanded_output, int32_t dtype, const float* topk_weights,
+                           const int32_t* inv_permuted_idx, int64_t num_tokens, int64_t hidden_size, int32_t topk,
+                           void* output, void* stream) {
+    const int64_t eb = element_bytes(dtype);
+    if (eb == 0) return MOE_ERR_INVALID_ARG;
+    if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || topk < 1 || topk > MOE_MAX_EXPERTS || num_tokens > kMaxRows / topk)
+        return MOE_ERR_INVALID_ARG;
+    if (hidden_size < 1 || hidden_size > kMaxRowBytes / eb) return MOE_ERR_INVALID_ARG;
+    const int64_t row_bytes = hidden_size * eb;
+    if (row_bytes % 16 != 0) return MOE_ERR_MISALIGNED;
+    if (num_tokens == 0) return MOE_OK;
+    if (expanded_output == nullptr || topk_weights == nullptr || inv_permuted_idx == nullptr || output == nullptr)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(expanded_output, 16) || !aligned(output, 16) || !aligned(topk_weights, 4) ||
+        !aligned(inv_permuted_idx, 4))
+        return MOE_ERR_MISALIGNED;
+    const uint64_t rows = (uint64_t)num_tokens * (uint64_t)topk;
+    const Span outs[] = {{output, (uint64_t)num_tokens * (uint64_t)row_bytes}};
+    const Span ins[] = {
+        {expanded_output, rows * (uint64_t)row_bytes},
+        {topk_weights, rows * 4},
+        {inv_permuted_idx, rows * 4},
+    };
+    if (any_overlap(outs, 1, ins, 3)) return MOE_ERR_INVALID_ARG;
+
+    moe::UnpermuteArgs a;
+    a.expanded_output = expanded_output;
+    a.topk_weights = topk_weights;
+    a.inv_permuted_idx = inv_permuted_idx;
+    a.num_tokens = num_tokens;
+    a.row_vecs = row_bytes / 16;
+    a.topk = topk;
+    a.output = output;
+    return moe::launch_unpermute(a, dtype == MOE_DTYPE_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+}
+
+}  // extern "C"

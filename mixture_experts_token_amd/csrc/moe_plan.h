@@ -1,0 +1,114 @@
+// moe_plan.h -- host-side launch planning for the permute / unpermute kernels.
+//
+// Pure C++ with no HIP call, so the size query and the argument checks work on
+// a host without a GPU.  The plan fixes, for one call:
+//   * which permute schedule runs:
+//       fused  -- one kernel; every workgroup counts all expert ids itself
+//                 (cheap while N*topk is small, and it avoids two launches);
+//       staged -- three kernels: per-tile stable ranks and histograms, a
+//                 per-expert scan over tiles, then scatter + row copy;
+//   * how expanded rows are cut into tiles (whole tokens per tile);
+//   * where each piece of the workspace lives.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace moe {
+
+constexpr int kWaveSize = 64;
+constexpr int kBlockThreads = 256;                 // 4 waves per workgroup
+constexpr int kBlockWaves = kBlockThreads / kWaveSize;
+constexpr int kMaxExperts = 1024;
+constexpr int64_t kFusedMaxRows = 16384;           // fused schedule up to this many expanded rows
+constexpr int kStagedTileRows = 128;               // target expanded rows per staged tile
+constexpr int kFusedTargetBlocks = 512;
+constexpr int kMaxTileRows = 1024;                 // LDS staging bound for one tile
+constexpr size_t kWorkspaceAlign = 256;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline int key_bits(int num_experts) {
+    int b = 0;
+    while ((1 << b) < num_experts) ++b;
+    return b;
+}
+
+struct PermutePlan {
+    bool fused = false;
+    int64_t rows = 0;             // N * topk
+    int tokens_per_tile = 1;
+    int tile_rows = 0;            // tokens_per_tile * topk
+    int64_t num_tiles = 0;
+    int nbits = 0;
+    // staged-schedule workspace layout (bytes from the workspace base)
+    size_t ws_rank = 0;           // int32 [rows]           rank of each row within its tile
+    size_t ws_tile_hist = 0;      // int32 [E+1][num_tiles] per-tile counts, then per-tile bases
+    size_t ws_total = 0;          // int32 [E+1]            rows per expert (+ bad-id count)
+    size_t ws_bytes = 0;          // bytes this call needs
+};
+
+// Tokens per staged tile: about kStagedTileRows expanded rows, whole tokens.
+inline int staged_tokens_per_tile(int topk) {
+    int t = kStagedTileRows / topk;
+    return t < 1 ? 1 : t;
+}
+
+inline size_t staged_workspace_bytes(int64_t rows, int64_t num_tiles, int num_experts) {
+    size_t b = align_up(sizeof(int32_t) * (size_t)rows, kWorkspaceAlign);
+    b += align_up(sizeof(int32_t) * (size_t)(num_experts + 1) * (size_t)num_tiles, kWorkspaceAlign);
+    b += align_up(sizeof(int32_t) * (size_t)(num_experts + 1), kWorkspaceAlign);
+    return b;
+}
+
+// Workspace of a call with max_num_tokens tokens; every call with fewer tokens
+// needs no more (the tile size depends on topk only, and the size grows with
+// the row and tile counts).
+inline size_t workspace_bound(int64_t max_num_tokens, int topk, int num_experts) {
+    const int64_t rows = max_num_tokens * topk;
+    if (rows <= kFusedMaxRows) return 0;
+    const int tpt = staged_tokens_per_tile(topk);
+    const int64_t tiles = (max_num_tokens + tpt - 1) / tpt;
+    return staged_workspace_bytes(rows, tiles, num_experts);
+}
+
+inline PermutePlan plan_permute(int64_t num_tokens, int topk, int num_experts) {
+    PermutePlan p;
+    p.rows = num_tokens * topk;
+    p.nbits = key_bits(num_experts);
+    if (p.rows <= kFusedMaxRows) {
+        p.fused = true;
+        // Enough workgroups to spread the row copy, at most kBlockThreads rows per tile.
+        int64_t tpt = (num_tokens + kFusedTargetBlocks - 1) / kFusedTargetBlocks;
+        const int64_t cap = (kBlockThreads / topk) < 1 ? 1 : (kBlockThreads / topk);
+        if (tpt < 1) tpt = 1;
+        if (tpt > cap) tpt = cap;
+        p.tokens_per_tile = (int)tpt;
+    } else {
+        p.fused = false;
+        p.tokens_per_tile = staged_tokens_per_tile(topk);
+    }
+    p.tile_rows = p.tokens_per_tile * topk;
+    p.num_tiles = num_tokens == 0 ? 0 : (num_tokens + p.tokens_per_tile - 1) / p.tokens_per_tile;
+    if (!p.fused) {
+        p.ws_rank = 0;
+        p.ws_tile_hist = align_up(sizeof(int32_t) * (size_t)p.rows, kWorkspaceAlign);
+        p.ws_total = p.ws_tile_hist +
+                     align_up(sizeof(int32_t) * (size_t)(num_experts + 1) * (size_t)p.num_tiles, kWorkspaceAlign);
+        p.ws_bytes = staged_workspace_bytes(p.rows, p.num_tiles, num_experts);
+    }
+    return p;
+}
+
+// Dynamic LDS bytes of the fused and staged kernels for one tile shape.
+inline size_t fused_lds_bytes(int num_experts, int tile_rows) {
+    return sizeof(int) * ((size_t)(3 + kBlockWaves) * num_experts + 2 * (size_t)tile_rows + 16);
+}
+inline size_t rank_lds_bytes(int num_experts, int tile_rows) {
+    return sizeof(int) * ((size_t)(1 + kBlockWaves) * num_experts + 2 * (size_t)tile_rows + 16);
+}
+inline size_t scatter_lds_bytes(int num_experts, int tile_rows) {
+    return sizeof(int) * ((size_t)(num_experts + 1) + (size_t)tile_rows + 16);
+}
+
+}  // namespace moe

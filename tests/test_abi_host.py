@@ -1,0 +1,206 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry
+point the header declares, and rejects bad arguments before touching HIP.
+
+No call here launches a kernel: every case fails a host-side check, which
+returns before any HIP call.  Pointers are fake addresses that are never
+dereferenced.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mixture_experts_token_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_permute.h")
+
+OK, INVALID, TOO_SMALL, MISALIGNED, UNSUPPORTED = 0, 1, 2, 3, 4
+BF16, F32, FP8 = binding.MOE_DTYPE_BF16, binding.MOE_DTYPE_F32, binding.MOE_DTYPE_FP8_E4M3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def _no_gpu():
+    import torch
+
+    return not torch.cuda.is_available()
+
+
+# Cases below pass fake addresses; each must fail a host check before any
+# launch.  Where a GPU is visible they are skipped, so that a check that
+# wrongly passes can never launch a kernel on fake pointers.
+host_only = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer checks run only on a host without a GPU")
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["moe_permute", "moe_permute_supported", "moe_permute_workspace_size",
+                                    "moe_status_string", "moe_unpermute"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_header_compiles_as_c():
+    src = '#include "moe_permute.h"\nint main(void) { return (int)moe_permute_workspace_size(1, 1, 1); }\n'
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.dirname(HEADER),
+                          "-x", "c", "-"], input=src, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_supported_is_safe_without_gpu(lib):
+    import torch
+
+    expected = None if torch.cuda.is_available() else 0
+    for dev in (0, 1, -1, 1000):
+        v = lib.moe_permute_supported(dev)
+        assert v in (0, 1)
+        if expected is not None:
+            assert v == expected
+    assert lib.moe_permute_supported(-1) == 0
+
+
+def test_workspace_size_pure_and_monotone(lib):
+    for k, e in [(1, 1), (2, 8), (8, 128), (8, 256), (16, 1024), (600, 1000)]:
+        prev = 0
+        for n in [0, 1, 7, 100, 2048, 2049, 4096, 16384, 100000, 1 << 20]:
+            if n * k >= 2**31:
+                continue
+            s = lib.moe_permute_workspace_size(n, k, e)
+            assert s == lib.moe_permute_workspace_size(n, k, e)
+            assert s >= prev
+            prev = s
+    assert lib.moe_permute_workspace_size(-1, 2, 8) == 0
+    assert lib.moe_permute_workspace_size(10, 0, 8) == 0
+    assert lib.moe_permute_workspace_size(10, 9, 8) == 0  # topk > experts
+    assert lib.moe_permute_workspace_size(10, 2, 1025) == 0
+    assert lib.moe_permute_workspace_size(2**31 // 8, 8, 256) == 0  # N*topk reaches 2^31
+
+
+def test_small_calls_need_no_workspace(lib):
+    assert lib.moe_permute_workspace_size(2048, 8, 256) == 0
+    assert lib.moe_permute_workspace_size(4096, 2, 8) == 0
+    assert lib.moe_permute_workspace_size(16384, 8, 256) > 0
+
+
+A = 0x10000  # fake, 256-aligned device addresses spaced far apart
+
+
+def addr(i, extra=0):
+    return ctypes.c_void_p(A * (1 << 20) * (i + 1) + extra)
+
+
+def permute_call(lib, **kw):
+    args = dict(hidden=addr(0), dtype=BF16, scale=None, ids=addr(1), n=4096, h=4096, k=2, e=8, out=addr(2),
+                pscale=None, off=addr(3), perm=addr(4), inv=addr(5), ws=addr(6), ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.moe_permute(args["hidden"], args["dtype"], args["scale"], args["ids"], args["n"], args["h"],
+                           args["k"], args["e"], args["out"], args["pscale"], args["off"], args["perm"], args["inv"],
+                           args["ws"], args["ws_bytes"], args["stream"])
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), INVALID),
+    (dict(dtype=-1), INVALID),
+    (dict(n=-1), INVALID),
+    (dict(k=0), INVALID),
+    (dict(k=9), INVALID),               # topk > num_experts
+    (dict(e=0), INVALID),
+    (dict(e=1025), INVALID),
+    (dict(n=2**31 // 2), INVALID),      # N*topk reaches 2^31
+    (dict(h=-4), INVALID),
+    (dict(off=None), INVALID),
+    (dict(ids=None), INVALID),
+    (dict(perm=None), INVALID),
+    (dict(inv=None), INVALID),
+    (dict(hidden=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(scale=addr(7)), INVALID),     # scale without permuted_scale
+    (dict(pscale=addr(7)), INVALID),    # permuted_scale without scale
+    (dict(h=4095), MISALIGNED),         # 8190-byte rows
+    (dict(dtype=FP8, h=4100), MISALIGNED),
+    (dict(hidden=addr(0, 8)), MISALIGNED),
+    (dict(out=addr(2, 4)), MISALIGNED),
+    (dict(ids=addr(1, 2)), MISALIGNED),
+    (dict(off=addr(3, 4)), MISALIGNED),
+    (dict(perm=addr(4, 1)), MISALIGNED),
+    (dict(out=addr(0)), INVALID),                          # output aliases the input rows
+    (dict(perm=addr(5)), INVALID),                         # two outputs alias
+    (dict(inv=addr(1)), INVALID),                          # output aliases topk_ids
+    (dict(n=20000, k=8, e=256, ws_bytes=0), TOO_SMALL),    # staged schedule needs a workspace
+    (dict(n=20000, k=8, e=256, ws=None), INVALID),
+    (dict(n=20000, k=8, e=256, ws=addr(6, 8)), MISALIGNED),
+])
+def test_permute_rejects(lib, kw, status):
+    assert permute_call(lib, **kw) == status
+
+
+@host_only
+def test_permute_workspace_boundary(lib):
+    need = lib.moe_permute_workspace_size(20000, 8, 256)
+    assert permute_call(lib, n=20000, k=8, e=256, ws_bytes=need - 1) == TOO_SMALL
+
+
+def unpermute_call(lib, **kw):
+    args = dict(y=addr(0), dtype=BF16, w=addr(1), inv=addr(2), n=4096, h=4096, k=2, out=addr(3), stream=None)
+    args.update(kw)
+    return lib.moe_unpermute(args["y"], args["dtype"], args["w"], args["inv"], args["n"], args["h"], args["k"],
+                             args["out"], args["stream"])
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=FP8), UNSUPPORTED),
+    (dict(dtype=9), INVALID),
+    (dict(n=-1), INVALID),
+    (dict(k=0), INVALID),
+    (dict(k=1025), INVALID),
+    (dict(h=0), INVALID),
+    (dict(y=None), INVALID),
+    (dict(w=None), INVALID),
+    (dict(inv=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(h=4), MISALIGNED),            # 8-byte bf16 rows
+    (dict(y=addr(0, 4)), MISALIGNED),
+    (dict(out=addr(3, 8)), MISALIGNED),
+    (dict(w=addr(1, 2)), MISALIGNED),
+    (dict(out=addr(0)), INVALID),       # output aliases the input
+])
+def test_unpermute_rejects(lib, kw, status):
+    assert unpermute_call(lib, **kw) == status
+
+
+def test_unpermute_zero_tokens_is_a_no_op(lib):
+    assert unpermute_call(lib, n=0, y=None, w=None, inv=None, out=None) == OK
+
+
+def test_status_strings(lib):
+    for code, name in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_WORKSPACE_TOO_SMALL"),
+                       (3, b"MOE_ERR_MISALIGNED"), (4, b"MOE_ERR_UNSUPPORTED"), (5, b"MOE_ERR_HIP")]:
+        assert lib.moe_status_string(code) == name
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(FileNotFoundError):
+        binding.load_library()

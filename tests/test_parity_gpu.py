@@ -1,0 +1,334 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: expert_first_token_offset, permuted_idx, inv_permuted_idx, permuted rows
+and permuted scales bit-exact; unpermute within 2^-7 * max(1, |ref|) for
+bf16 and 1e-5 * max(1, |ref|) for fp32.  Every output buffer and the
+workspace are filled with 0xFF before each call, so a result that leans on
+earlier memory contents fails.
+"""
+
+import hashlib
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _parity import (POISON, assert_permute_equal, assert_unpermute_close, gpu_permute, gpu_unpermute,
+                     oracle_permute, poisoned, to_np)
+from mixture_experts_token_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _say(msg):
+    print("[case] " + msg, flush=True)
+
+
+def _inputs(name, dev, seed=0, n=None):
+    w = W.WORKLOADS[name]
+    if n is not None:
+        w = w.with_tokens(n)
+    gen_dev = "cpu" if w.num_rows * w.hidden_size <= (1 << 22) else dev
+    inp = W.make_all(w, seed=seed, device=gen_dev)
+    for key in ("topk_ids", "topk_weights", "hidden_states", "token_scale", "expert_output"):
+        if inp[key] is not None:
+            inp[key] = inp[key].to(dev)
+    return w, inp
+
+
+def _run_and_check(w, inp, sample_tokens=None):
+    _say("%s N=%d H=%d E=%d topk=%d %s" % (w.name, w.num_tokens, w.hidden_size, w.num_experts, w.topk,
+                                           w.hidden_dtype))
+    outs = gpu_permute(inp["hidden_states"], inp["topk_ids"], w.num_experts, token_scale=inp["token_scale"])
+    out = gpu_unpermute(inp["expert_output"], inp["topk_weights"], outs["inv_permuted_idx"])
+    torch.cuda.synchronize()
+    ref = oracle_permute(inp["hidden_states"], inp["topk_ids"], w.num_experts, inp["token_scale"])
+    assert_permute_equal(outs, ref)
+    y = to_np(inp["expert_output"])
+    wts = to_np(inp["topk_weights"])
+    inv = ref["inv_permuted_idx"]
+    got = to_np(out)
+    if sample_tokens is not None:
+        # oracle computes the sampled tokens one by one: gather their rows into a sub-problem
+        k = w.topk
+        rows = inv.reshape(-1, k)[sample_tokens].reshape(-1)
+        ref_out = oracle.unpermute(y[rows], wts[sample_tokens], np.arange(rows.size, dtype=np.int32),
+                                   w.output_dtype)
+        got = got[sample_tokens]
+    else:
+        ref_out = oracle.unpermute(y, wts, inv, w.output_dtype)
+    return assert_unpermute_close(got, ref_out, w.output_dtype)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "qwen3"])
+def test_workload_parity(name, hip_device):
+    w, inp = _inputs(name, hip_device)
+    _run_and_check(w, inp)
+
+
+def test_dsv3_parity_full_indices_and_rows_sampled_unpermute(hip_device):
+    w, inp = _inputs("dsv3", hip_device)
+    rng = np.random.default_rng(11)
+    sample = np.unique(np.concatenate([[0, 1, w.num_tokens - 1], rng.choice(w.num_tokens, 3000, replace=False)]))
+    _run_and_check(w, inp, sample_tokens=sample)
+
+
+def test_tiny_matches_stored_golden(hip_device):
+    g = json.load(open(os.path.join(HERE, "golden", "tiny_seed0.json")))
+    w, inp = _inputs("tiny", hip_device)
+    _say("tiny golden")
+    outs = gpu_permute(inp["hidden_states"], inp["topk_ids"], w.num_experts)
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == g["expected"]["expert_first_token_offset"]
+    assert to_np(outs["permuted_idx"]).tolist() == g["expected"]["permuted_idx"]
+    assert to_np(outs["inv_permuted_idx"]).tolist() == g["expected"]["inv_permuted_idx"]
+    sha = hashlib.sha256(to_np(outs["permuted_hidden_states"]).tobytes()).hexdigest()
+    assert sha == g["expected"]["permuted_hidden_states_sha256"]
+
+
+def test_decode_sweep_with_one_reused_scratch(hip_device):
+    """Scratch sized once for N=256 and reused for N = 1, 4, 16, 64, 256 in that order."""
+    w, inp = _inputs("decode", hip_device)
+    dev = hip_device
+    scratch = binding.MoEPermuteScratch(256, w.topk, w.num_experts, dev, hidden_size=w.hidden_size,
+                                        hidden_dtype=torch.uint8, with_scale=True)
+    scratch.workspace.fill_(POISON)
+    scratch.permuted_hidden_states.fill_(POISON)
+    for n in W.DECODE_SWEEP:
+        _say("decode sweep N=%d (reused scratch)" % n)
+        x = inp["hidden_states"][:n]
+        s = inp["token_scale"][:n]
+        ids = inp["topk_ids"][:n]
+        res = scratch.permute(x, ids, token_scale=s)
+        out = gpu_unpermute(inp["expert_output"][: n * w.topk], inp["topk_weights"][:n], res["inv_permuted_idx"])
+        fresh = gpu_permute(x, ids, w.num_experts, token_scale=s)
+        torch.cuda.synchronize()
+        ref = oracle_permute(x, ids, w.num_experts, s)
+        assert_permute_equal(res, ref)
+        assert_permute_equal(fresh, ref)
+        ref_out = oracle.unpermute(to_np(inp["expert_output"][: n * w.topk]), to_np(inp["topk_weights"][:n]),
+                                   ref["inv_permuted_idx"], "bf16")
+        assert_unpermute_close(to_np(out), ref_out, "bf16")
+
+
+# ----------------------------------------------------------------------------
+# Edge cases: several tiles with ragged tails, both permute schedules.
+# ----------------------------------------------------------------------------
+def _edge_ids(rng, n, k, e, mode):
+    if mode == "distinct":
+        return np.stack([rng.permutation(e)[:k] for _ in range(n)]) if n else np.zeros((0, k))
+    if mode == "one_expert":
+        return np.full((n, k), e - 1)
+    if mode == "first_expert":
+        return np.zeros((n, k))
+    if mode == "dups":
+        return rng.integers(0, e, size=(n, k))
+    if mode == "empties":  # experts 0, E-1 and every third one never chosen
+        allowed = np.array([x for x in range(1, e - 1) if x % 3])
+        return np.stack([rng.choice(allowed, k, replace=False) for _ in range(n)])
+    raise ValueError(mode)
+
+
+EDGE = [
+    # (N, topk, E, H, dtype, ids mode)
+    (1, 1, 1, 8, "f32", "distinct"),
+    (5, 4, 4, 64, "bf16", "distinct"),
+    (3000, 2, 64, 136, "bf16", "one_expert"),
+    (5000, 4, 16, 72, "bf16", "first_expert"),
+    (1000, 4, 3, 4, "f32", "dups"),
+    (9000, 3, 5, 40, "bf16", "dups"),
+    (4099, 8, 1024, 64, "bf16", "distinct"),
+    (100, 16, 1024, 128, "f32", "distinct"),
+    (2500, 8, 1000, 96, "bf16", "empties"),
+    (2048, 8, 256, 264, "bf16", "distinct"),   # exactly the largest fused row count
+    (2049, 8, 256, 264, "bf16", "distinct"),   # first staged row count
+    (777, 3, 37, 328, "f32", "distinct"),
+    (300, 64, 512, 16, "bf16", "distinct"),
+    (40, 512, 1024, 8, "f32", "distinct"),
+    (20, 600, 1000, 24, "bf16", "distinct"),
+    (3001, 8, 160, 7168, "bf16", "empties"),
+    (513, 8, 256, 16, "fp8_e4m3", "distinct"),
+    (2600, 8, 256, 7168, "fp8_e4m3", "distinct"),
+]
+
+
+@pytest.mark.parametrize("n,k,e,h,dtype,mode", EDGE, ids=["-".join(map(str, c)) for c in EDGE])
+def test_edge_case_parity(hip_device, n, k, e, h, dtype, mode):
+    dev = hip_device
+    rng = np.random.default_rng(n * 31 + k * 7 + e)
+    ids = torch.from_numpy(_edge_ids(rng, n, k, e, mode).astype(np.int32)).to(dev)
+    g = torch.Generator(device="cpu").manual_seed(n + k + e)
+    xf = torch.randn((n, h), generator=g)
+    scale = None
+    if dtype == "f32":
+        x = xf
+    elif dtype == "bf16":
+        x = xf.to(torch.bfloat16)
+    else:
+        x, scale = W.quantize_fp8_per_token(xf)
+        scale = scale.to(dev)
+    x = x.to(dev)
+    out_dtype = "f32" if dtype == "f32" else "bf16"
+    y = torch.randn((n * k, h), generator=g)
+    y = (y if out_dtype == "f32" else y.to(torch.bfloat16)).to(dev)
+    wts = torch.softmax(torch.randn((n, k), generator=g, dtype=torch.float64), dim=1).to(torch.float32).to(dev)
+    _say("edge N=%d topk=%d E=%d H=%d %s %s" % (n, k, e, h, dtype, mode))
+    outs = gpu_permute(x, ids, e, token_scale=scale)
+    out = gpu_unpermute(y, wts, outs["inv_permuted_idx"])
+    torch.cuda.synchronize()
+    ref = oracle_permute(x, ids, e, scale)
+    assert_permute_equal(outs, ref)
+    ref_out = oracle.unpermute(to_np(y), to_np(wts), ref["inv_permuted_idx"], out_dtype)
+    assert_unpermute_close(to_np(out), ref_out, out_dtype)
+
+
+@pytest.mark.parametrize("n,k,e", [(700, 4, 32), (6000, 4, 32)])
+def test_index_only_permute(hip_device, n, k, e):
+    rng = np.random.default_rng(5)
+    ids = torch.from_numpy(_edge_ids(rng, n, k, e, "distinct").astype(np.int32)).to(hip_device)
+    _say("index-only N=%d topk=%d E=%d" % (n, k, e))
+    outs = gpu_permute(None, ids, e)
+    torch.cuda.synchronize()
+    assert_permute_equal(outs, oracle_permute(None, ids, e), check_rows=False)
+
+
+def test_zero_tokens(hip_device):
+    ids = torch.zeros((0, 2), dtype=torch.int32, device=hip_device)
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=hip_device)
+    _say("zero tokens")
+    outs = gpu_permute(x, ids, 8)
+    out = gpu_unpermute(torch.zeros((0, 64), dtype=torch.bfloat16, device=hip_device),
+                        torch.zeros((0, 2), dtype=torch.float32, device=hip_device), outs["inv_permuted_idx"])
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == [0] * 9
+    assert out.shape == (0, 64)
+
+
+@pytest.mark.parametrize("n,k,e,bad", [(50, 2, 8, 8), (50, 2, 8, -1), (4000, 8, 64, 64), (4000, 8, 64, -7)])
+def test_out_of_range_expert_id_is_reported(hip_device, n, k, e, bad):
+    """The kernels' own check: offsets become -1 and nothing else is written."""
+    rng = np.random.default_rng(3)
+    ids_np = _edge_ids(rng, n, k, e, "distinct").astype(np.int32)
+    ids_np[n // 2, k - 1] = bad
+    ids = torch.from_numpy(ids_np).to(hip_device)
+    x = torch.randn((n, 32), device=hip_device).to(torch.bfloat16)
+    _say("bad id %d N=%d topk=%d E=%d" % (bad, n, k, e))
+    outs = gpu_permute(x, ids, e)
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == [-1] * (e + 1)
+    for key in ("permuted_idx", "inv_permuted_idx", "permuted_hidden_states"):
+        assert np.all(to_np(outs[key]).view(np.uint8) == POISON), key
+
+
+def test_out_of_range_inverse_index_gives_nan_row(hip_device):
+    n, k, h = 64, 4, 128
+    inv = torch.randperm(n * k, dtype=torch.int32).to(hip_device)
+    inv[10 * k + 2] = n * k  # token 10 points past the end
+    y = torch.randn((n * k, h), device=hip_device).to(torch.bfloat16)
+    wts = torch.full((n, k), 0.25, device=hip_device)
+    _say("bad inverse index")
+    out = gpu_unpermute(y, wts, inv)
+    torch.cuda.synchronize()
+    o = out.float().cpu()
+    assert torch.isnan(o[10]).all()
+    keep = [t for t in range(n) if t != 10]
+    inv_np = to_np(inv).reshape(n, k)
+    y_np = to_np(y)
+    rows = inv_np[keep].reshape(-1)
+    ref = oracle.unpermute(y_np[rows], to_np(wts)[keep], np.arange(rows.size, dtype=np.int32), "bf16")
+    assert_unpermute_close(to_np(out)[keep], ref, "bf16")
+
+
+# ----------------------------------------------------------------------------
+# Reuse, determinism, streams, round trip.
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["mixtral", "qwen3"])
+def test_scratch_reuse_same_pointers_identical_results(hip_device, name):
+    """Two calls with one scratch: same output pointers, identical bits (as the
+    pages' reuse test asserts), also after the scratch is poisoned in between."""
+    w, inp = _inputs(name, hip_device, n=W.WORKLOADS[name].num_tokens // 2)
+    scratch = binding.MoEPermuteScratch(w.num_tokens, w.topk, w.num_experts, hip_device,
+                                        hidden_size=w.hidden_size, hidden_dtype=torch.bfloat16)
+    _say("reuse %s" % name)
+    r1 = scratch.permute(inp["hidden_states"], inp["topk_ids"])
+    snap1 = {k: v.clone() for k, v in r1.items() if v is not None}
+    ptrs1 = {k: v.data_ptr() for k, v in r1.items() if v is not None}
+    scratch.workspace.fill_(POISON)
+    scratch.permuted_hidden_states.fill_(POISON)
+    scratch.permuted_idx.fill_(-1)
+    r2 = scratch.permute(inp["hidden_states"], inp["topk_ids"])
+    torch.cuda.synchronize()
+    for k, v in r2.items():
+        if v is None:
+            continue
+        assert v.data_ptr() == ptrs1[k], k
+        assert torch.equal(v.view(torch.uint8) if v.dtype == torch.bfloat16 else v,
+                           snap1[k].view(torch.uint8) if v.dtype == torch.bfloat16 else snap1[k]), k
+
+
+def test_smaller_call_after_larger_one(hip_device):
+    """Leftovers of a larger call in the scratch must not leak into a smaller one."""
+    w, inp = _inputs("qwen3", hip_device)
+    scratch = binding.MoEPermuteScratch(w.num_tokens, w.topk, w.num_experts, hip_device,
+                                        hidden_size=w.hidden_size, hidden_dtype=torch.bfloat16)
+    scratch.permute(inp["hidden_states"], inp["topk_ids"])
+    for n in (3000, 2049, 2048, 100, 1):
+        _say("qwen3 prefix N=%d after full call" % n)
+        res = scratch.permute(inp["hidden_states"][:n], inp["topk_ids"][:n])
+        torch.cuda.synchronize()
+        assert_permute_equal(res, oracle_permute(inp["hidden_states"][:n], inp["topk_ids"][:n], w.num_experts))
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3", "dsv3"])
+def test_repeat_is_bit_identical(hip_device, name):
+    w, inp = _inputs(name, hip_device, n=min(W.WORKLOADS[name].num_tokens, 4096))
+    _say("repeat %s" % name)
+    a = gpu_permute(inp["hidden_states"], inp["topk_ids"], w.num_experts)
+    oa = gpu_unpermute(inp["expert_output"], inp["topk_weights"], a["inv_permuted_idx"])
+    b = gpu_permute(inp["hidden_states"], inp["topk_ids"], w.num_experts)
+    ob = gpu_unpermute(inp["expert_output"], inp["topk_weights"], b["inv_permuted_idx"])
+    torch.cuda.synchronize()
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(to_np(a[k]).view(np.uint8), to_np(b[k]).view(np.uint8)), k
+    assert np.array_equal(to_np(oa).view(np.uint8), to_np(ob).view(np.uint8))
+
+
+def test_non_default_stream_with_queued_work(hip_device):
+    w, inp = _inputs("qwen3", hip_device)
+    s = torch.cuda.Stream(device=hip_device)
+    big = torch.randn((4096, 4096), device=hip_device)
+    ref = oracle_permute(inp["hidden_states"], inp["topk_ids"], w.num_experts)
+    _say("side stream")
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(4):
+            big = big * 1.0001  # queue work ahead of the permute on the same stream
+        outs = gpu_permute(inp["hidden_states"], inp["topk_ids"], w.num_experts, stream=s)
+        out = gpu_unpermute(inp["expert_output"], inp["topk_weights"], outs["inv_permuted_idx"], stream=s)
+    s.synchronize()
+    assert_permute_equal(outs, ref)
+    ref_out = oracle.unpermute(to_np(inp["expert_output"]), to_np(inp["topk_weights"]), ref["inv_permuted_idx"],
+                               "bf16")
+    assert_unpermute_close(to_np(out), ref_out, "bf16")
+
+
+@pytest.mark.parametrize("k,e", [(1, 8), (2, 8), (4, 64), (8, 256)])
+def test_round_trip_identity_experts_bf16_exact(hip_device, k, e):
+    """unpermute(permute(x)) with Y = permuted x and weights 1/topk gives x back bit for bit."""
+    n, h = 3000, 256
+    rng = np.random.default_rng(k)
+    ids = torch.from_numpy(_edge_ids(rng, n, k, e, "distinct").astype(np.int32)).to(hip_device)
+    x = torch.randn((n, h), device=hip_device).to(torch.bfloat16)
+    _say("round trip topk=%d" % k)
+    outs = gpu_permute(x, ids, e)
+    wts = torch.full((n, k), 1.0 / k, device=hip_device)
+    out = gpu_unpermute(outs["permuted_hidden_states"], wts, outs["inv_permuted_idx"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))
