@@ -103,6 +103,9 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate (default: enough to beat the LLC)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before timing, copy a fresh MIB-MiB buffer 5 times (a plain copy kernel of known "
+                         "size, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -131,7 +134,7 @@ def main() -> int:
     y0 = W.make_expert_output(w, seed=0, device=dev)
     hdt = x0.dtype
     step_footprint = nb["total"]
-    nsets = args.sets or max(1, math.ceil(3 * LLC_BYTES / step_footprint))
+    nsets = args.sets or min(64, max(1, math.ceil(3 * LLC_BYTES / step_footprint)))
     sets = []
     for i in range(nsets):
         sets.append({
@@ -156,6 +159,14 @@ def main() -> int:
     def unpermute(s):
         binding.moe_unpermute(s["y"], wts, s["inv"], s["out"], stream=stream)
 
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
+
     for i in range(args.warmup):
         s = sets[i % nsets]
         permute(s)
@@ -163,31 +174,41 @@ def main() -> int:
     torch.cuda.synchronize(dev)
 
     k = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(k)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+
+    # Timed region: exactly K steps, nothing else enqueued between the kernels.
     torch.cuda.synchronize(dev)
     wall0 = time.perf_counter()
     start.record(stream)
     for i in range(k):
         s = sets[i % nsets]
-        ev[i][0].record(stream)
         permute(s)
-        ev[i][1].record(stream)
         unpermute(s)
-        ev[i][2].record(stream)
     end.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(end) / k
-    perm_us = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(k)]
-    unperm_us = [ev[i][1].elapsed_time(ev[i][2]) * 1e3 for i in range(k)]
-    perm_avg = sum(perm_us) / k
-    unperm_avg = sum(unperm_us) / k
     value = nb["total"] / (ms_step * 1e-3) / 1e9
 
+    # Per-kernel durations: K back-to-back calls of one operation (same buffer
+    # rotation) between one pair of HIP events on the kernels' stream.
+    def batch_us(fn):
+        torch.cuda.synchronize(dev)
+        start.record(stream)
+        for i in range(k):
+            fn(sets[i % nsets])
+        end.record(stream)
+        torch.cuda.synchronize(dev)
+        return start.elapsed_time(end) * 1e3 / k
+
+    perm_avg = batch_us(permute)
+    unperm_avg = batch_us(unpermute)
+    tiny = torch.zeros(1, device=dev)
+    launch_floor_us = batch_us(lambda _s: tiny.add_(1.0))
+
     plan_fused = w.num_rows <= 16384
-    perm_kernel = "permute_fused_kernel" if plan_fused else "permute (rank + scan + scatter kernels)"
+    perm_kernel = "permute_fused_kernel" if plan_fused else "moe_permute (rank + scan + scatter kernels)"
     if unperm_avg >= perm_avg:
         dom, dom_us, dom_bytes = "unpermute_kernel", unperm_avg, nb["unpermute"]
     else:
@@ -223,6 +244,7 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "us_per_step": round(ms_step * 1e3, 3),
         "permute_us": round(perm_avg, 3),
+        "launch_floor_us": round(launch_floor_us, 3),
         "unpermute_us": round(unperm_avg, 3),
         "permute_GBps": round(nb["permute"] / (perm_avg * 1e-6) / 1e9, 1),
         "unpermute_GBps": round(nb["unpermute"] / (unperm_avg * 1e-6) / 1e9, 1),

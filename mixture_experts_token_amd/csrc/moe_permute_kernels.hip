@@ -19,7 +19,11 @@
 // an integer sum.  Every result is therefore deterministic.
 //
 // Row movement is token-major: each token row is read once and written to its
-// topk destinations, so HBM reads equal the algorithmic N*H bytes.
+// topk destinations, so HBM reads equal the algorithmic N*H bytes.  A wave
+// issues the loads of its first row chunk before the index work starts, and
+// barriers inside the kernels order LDS only, so those loads stay in flight
+// while the ranks are computed; the copy loop then double-buffers (loads of
+// the next chunk are in flight while the current chunk is stored).
 
 #include <hip/hip_runtime.h>
 
@@ -33,7 +37,7 @@ namespace moe {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ----------------------------------------------------------------------------
-// Wavefront helpers
+// Wavefront / workgroup helpers
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -56,11 +60,22 @@ __device__ __forceinline__ int wave_index() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWaveSize));
 }
 
+// Workgroup barrier that orders LDS only.  Global loads issued before it stay
+// in flight (no wait on the vector-memory counter); nothing in these kernels
+// communicates through global memory inside one launch.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Exclusive prefix sum of data[0..n) in LDS, in place; returns the total.
-// Every thread of the workgroup must call it.  tmp: kBlockWaves ints of LDS.
+// Every thread of the workgroup must call it.  tmp: NT/64 ints of LDS.
+template <int NT>
 __device__ int block_exclusive_scan(int* data, int n, int* tmp) {
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid % kWaveSize, w = tid / kWaveSize;
-    const int per = (n + nt - 1) / nt;
+    constexpr int W = NT / kWaveSize;
+    const int tid = threadIdx.x, lane = tid % kWaveSize, w = tid / kWaveSize;
+    const int per = (n + NT - 1) / NT;
     const int beg = min(tid * per, n), end = min(beg + per, n);
     int s = 0;
     for (int i = beg; i < end; ++i) s += data[i];
@@ -71,9 +86,10 @@ __device__ int block_exclusive_scan(int* data, int n, int* tmp) {
         if (lane >= d) x += y;
     }
     if (lane == kWaveSize - 1) tmp[w] = x;
-    __syncthreads();
+    lds_barrier();
     int before = 0, total = 0;
-    for (int v = 0; v < nt / kWaveSize; ++v) {
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
         const int c = tmp[v];
         before += v < w ? c : 0;
         total += c;
@@ -84,115 +100,142 @@ __device__ int block_exclusive_scan(int* data, int n, int* tmp) {
         data[i] = run;
         run += c;
     }
-    __syncthreads();
+    lds_barrier();
     return total;
 }
 
 // ----------------------------------------------------------------------------
-// Stable ranks within one tile of expanded rows [row0, row0 + tile_rows).
+// Stable ranks within one tile of expanded rows, keys already in LDS.
 //
-// Wave w owns rows [w*span, (w+1)*span) of the tile and walks them 64 at a
-// time, so a row's rank is (rows of its expert in earlier waves) + (rows of
-// its expert earlier in its own wave).  On return, after a barrier:
-//   key_s[i]  expert of tile row i, or -1 if its id is out of range
+// key_s[i] is the expert of tile row i, or -1 for a row whose id is out of
+// range (such rows get no rank).  Wave w owns rows [w*span, (w+1)*span) and
+// walks them 64 at a time, so a row's rank is (rows of its expert in earlier
+// waves) + (rows of its expert earlier in its own wave).  On return, after a
+// barrier:
 //   rank_s[i] rank of row i among the tile's rows with the same expert
 //   cnt_s[e]  rows of the tile routed to expert e
-//   *bad_s    incremented by the tile's rows with an out-of-range id
-// wave_s (kBlockWaves * E ints) must be zero on entry; it is clobbered.
+// wave_s (NT/64 * E ints) must be zero on entry; it is clobbered.
 // ----------------------------------------------------------------------------
-__device__ void rank_tile(const int32_t* __restrict__ ids, int64_t row0, int tile_rows, int E, int nbits,
-                          int* key_s, int* rank_s, int* wave_s, int* cnt_s, int* bad_s) {
+template <int NT>
+__device__ void rank_tile(const int* key_s, int tile_rows, int E, int nbits, int* rank_s, int* wave_s, int* cnt_s) {
+    constexpr int W = NT / kWaveSize;
     const int w = wave_index();
     const int lane = threadIdx.x % kWaveSize;
-    const int span = (tile_rows + kBlockThreads - 1) / kBlockThreads * kWaveSize;
+    const int span = (tile_rows + NT - 1) / NT * kWaveSize;
     const int beg = w * span;
     const int end = min(beg + span, tile_rows);
     int* run = wave_s + w * E;
-    int nbad = 0;
     for (int base = beg; base < end; base += kWaveSize) {
         const int i = base + lane;
-        const bool in_tile = i < end;
-        const int key = in_tile ? ids[row0 + i] : 0;
-        const bool ok = in_tile && (unsigned)key < (unsigned)E;
-        nbad += (in_tile && !ok) ? 1 : 0;
+        const int key = i < end ? key_s[i] : -1;
+        const bool ok = key >= 0;
         const uint64_t same = lanes_with_same_key(key, ok, nbits);
         const int below = lanes_below(same);
         if (ok) {
             const int r = run[key];
             rank_s[i] = r + below;
-            key_s[i] = key;
             if (below == 0) run[key] = r + (int)__popcll(same);
-        } else if (in_tile) {
-            key_s[i] = -1;
+        } else if (i < end) {
             rank_s[i] = 0;
         }
     }
-    if (nbad) atomicAdd(bad_s, nbad);
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    lds_barrier();
+    for (int e = threadIdx.x; e < E; e += NT) {
         int s = 0;
-        for (int v = 0; v < kBlockWaves; ++v) {
+#pragma unroll
+        for (int v = 0; v < W; ++v) {
             const int c = wave_s[v * E + e];
             wave_s[v * E + e] = s;
             s += c;
         }
         cnt_s[e] = s;
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < tile_rows; i += blockDim.x) {
+    lds_barrier();
+    for (int i = threadIdx.x; i < tile_rows; i += NT) {
         const int key = key_s[i];
         if (key >= 0) rank_s[i] += wave_s[(i / span) * E + key];
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // ----------------------------------------------------------------------------
-// Row copy of one tile: token-major, each token row read once and written to
-// its topk destinations.  Work items are (token, chunk of U*64 16-byte
-// vectors); waves take items round-robin.  dest_s[tl*topk + k] is the
-// permuted row of the tile's token tl, slot k.
+// Token-major row copy of one tile.  Work items are (token of the tile, chunk
+// of U*64 16-byte vectors); wave w takes items w, w+W, ...  dest_s[tl*topk+k]
+// is the permuted row of the tile's token tl, slot k.
 // ----------------------------------------------------------------------------
 template <int U>
-__device__ __forceinline__ void copy_tile_rows(const PermuteArgs& a, int64_t t0, int ntok, const int* dest_s) {
-    const int w = wave_index();
-    const int lane = threadIdx.x % kWaveSize;
-    const int K = a.topk;
-    const int64_t rows_total = a.num_tokens * K;
-    if (a.row_vecs > 0) {
-        const int64_t rv = a.row_vecs;
-        const int chunk = U * kWaveSize;
-        const int nchunks = (int)((rv + chunk - 1) / chunk);
-        const int items = ntok * nchunks;
-        const u32x4* __restrict__ src_base = reinterpret_cast<const u32x4*>(a.hidden_states);
-        u32x4* __restrict__ dst_base = reinterpret_cast<u32x4*>(a.permuted_hidden_states);
-        for (int it = w; it < items; it += kBlockWaves) {
-            const int tl = it / nchunks;
-            const int c = it - tl * nchunks;
-            const u32x4* src = src_base + (t0 + tl) * rv;
-            u32x4 v[U];
+struct TileCopy {
+    const u32x4* __restrict__ src;  // first row of the tile
+    u32x4* __restrict__ dst;        // permuted_hidden_states
+    int64_t rv;                     // row length in vectors
+    int64_t rows_total;             // N * topk
+    int nchunks;
+    int items;
+    int K;
+    int lane;
+
+    __device__ TileCopy(const PermuteArgs& a, int64_t t0, int ntok)
+        : src(reinterpret_cast<const u32x4*>(a.hidden_states) + t0 * a.row_vecs),
+          dst(reinterpret_cast<u32x4*>(a.permuted_hidden_states)),
+          rv(a.row_vecs),
+          rows_total(a.num_tokens * a.topk),
+          nchunks((int)((a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize))),
+          items(ntok * (int)((a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize))),
+          K(a.topk),
+          lane((int)(threadIdx.x % kWaveSize)) {}
+
+    __device__ __forceinline__ void load(int it, u32x4 (&v)[U]) const {
+        const int tl = it / nchunks;
+        const int64_t base = (int64_t)(it - tl * nchunks) * (U * kWaveSize) + lane;
+        const u32x4* s = src + tl * rv;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t idx = base + u * kWaveSize;
+            v[u] = idx < rv ? __builtin_nontemporal_load(s + idx) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    __device__ __forceinline__ void store(int it, const u32x4 (&v)[U], const int* dest_s) const {
+        const int tl = it / nchunks;
+        const int64_t base = (int64_t)(it - tl * nchunks) * (U * kWaveSize) + lane;
+        for (int k = 0; k < K; ++k) {
+            const int d = dest_s[tl * K + k];
+            if ((uint32_t)d >= (uint64_t)rows_total) continue;  // never taken when the ranks are right
+            u32x4* o = dst + (int64_t)d * rv;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t idx = (int64_t)c * chunk + u * kWaveSize + lane;
-                if (idx < rv) v[u] = __builtin_nontemporal_load(src + idx);
-            }
-            for (int k = 0; k < K; ++k) {
-                const int d = dest_s[tl * K + k];
-                if ((uint32_t)d >= (uint64_t)rows_total) continue;  // never taken when the ranks are right
-                u32x4* dst = dst_base + (int64_t)d * rv;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int64_t idx = (int64_t)c * chunk + u * kWaveSize + lane;
-                    if (idx < rv) __builtin_nontemporal_store(v[u], dst + idx);
-                }
+                const int64_t idx = base + u * kWaveSize;
+                if (idx < rv) __builtin_nontemporal_store(v[u], o + idx);
             }
         }
     }
-    if (a.token_scale != nullptr) {
-        const int rows = ntok * K;
-        for (int i = threadIdx.x; i < rows; i += blockDim.x) {
-            const int d = dest_s[i];
-            if ((uint32_t)d < (uint64_t)rows_total) a.permuted_scale[d] = a.token_scale[t0 + i / K];
+};
+
+// Store every item of wave w, starting from `cur` (already loaded for item w),
+// loading item it+W while item it is stored.
+template <int U, int NT>
+__device__ __forceinline__ void copy_items_pipelined(const TileCopy<U>& tc, u32x4 (&cur)[U], const int* dest_s) {
+    constexpr int W = NT / kWaveSize;
+    for (int it = wave_index(); it < tc.items; it += W) {
+        u32x4 nxt[U];
+        const bool more = it + W < tc.items;
+        if (more) tc.load(it + W, nxt);
+        tc.store(it, cur, dest_s);
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
         }
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void copy_tile_scales(const PermuteArgs& a, int64_t t0, int ntok, const int* dest_s) {
+    if (a.token_scale == nullptr) return;
+    const int K = a.topk;
+    const int64_t rows_total = a.num_tokens * K;
+    for (int i = threadIdx.x; i < ntok * K; i += NT) {
+        const int d = dest_s[i];
+        if ((uint32_t)d < (uint64_t)rows_total) a.permuted_scale[d] = a.token_scale[t0 + i / K];
     }
 }
 
@@ -202,9 +245,11 @@ __device__ __forceinline__ void copy_tile_rows(const PermuteArgs& a, int64_t t0,
 // ranks its own rows, derives expert_first_token_offset and its own base per
 // expert, scatters permuted_idx / inv_permuted_idx and copies its rows.
 // ----------------------------------------------------------------------------
-template <int U>
-__global__ __launch_bounds__(kBlockThreads) void permute_fused_kernel(PermuteArgs a, int tokens_per_tile,
-                                                                      int nbits) {
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int tokens_per_tile, int nbits) {
+    constexpr int W = NT / kWaveSize;
+    constexpr int kIds = kFusedMaxRows / NT;  // expert ids held per thread
+    static_assert(kFusedMaxRows % NT == 0, "fused row bound must be a multiple of the workgroup size");
     extern __shared__ int smem[];
     const int E = a.num_experts;
     const int K = a.topk;
@@ -213,56 +258,74 @@ __global__ __launch_bounds__(kBlockThreads) void permute_fused_kernel(PermuteArg
     const int64_t row0 = t0 * K;
     const int T = ntok * K;
     const int tile_cap = tokens_per_tile * K;
-    const int64_t R = a.num_tokens * K;
+    const int R = (int)(a.num_tokens * K);  // <= kFusedMaxRows
 
-    int* before_s = smem;                       // [E] rows before the tile, then the tile's base
-    int* after_s = before_s + E;                // [E] rows after the tile, then offsets
-    int* cnt_s = after_s + E;                   // [E] rows inside the tile
-    int* wave_s = cnt_s + E;                    // [kBlockWaves * E]
-    int* key_s = wave_s + kBlockWaves * E;      // [tile_cap]
-    int* rank_s = key_s + tile_cap;             // [tile_cap] rank, then destination
-    int* misc_s = rank_s + tile_cap;            // [16]: [0] bad ids, [1..] scan scratch
+    // Every expert id of the problem goes into registers first, then the first
+    // row chunk of this wave: the vector-memory counter retires in issue
+    // order, so the row loads stay in flight while the ids are consumed.
+    int idv[kIds];
+#pragma unroll
+    for (int j = 0; j < kIds; ++j) {
+        const int r = (int)threadIdx.x + j * NT;
+        idv[j] = a.topk_ids[r < R ? r : R - 1];
+    }
+    const TileCopy<U> tc(a, t0, ntok);
+    u32x4 cur[U];
+    if (a.row_vecs > 0 && wave_index() < tc.items) tc.load(wave_index(), cur);
 
-    for (int i = threadIdx.x; i < (3 + kBlockWaves) * E; i += blockDim.x) smem[i] = 0;
+    int* before_s = smem;                 // [E] rows before the tile, then the tile's base
+    int* after_s = before_s + E;          // [E] rows after the tile, then offsets
+    int* cnt_s = after_s + E;             // [E] rows inside the tile
+    int* wave_s = cnt_s + E;              // [W * E]
+    int* key_s = wave_s + W * E;          // [tile_cap]
+    int* rank_s = key_s + tile_cap;       // [tile_cap] rank, then destination
+    int* misc_s = rank_s + tile_cap;      // [16]: [0] bad ids, [1..] scan scratch
+
+    for (int i = threadIdx.x; i < (3 + W) * E; i += NT) smem[i] = 0;
     if (threadIdx.x < 16) misc_s[threadIdx.x] = 0;
-    __syncthreads();
+    lds_barrier();
 
     int nbad = 0;
-    for (int64_t r = threadIdx.x; r < R; r += blockDim.x) {
-        if (r >= row0 && r < row0 + T) continue;
-        const int key = a.topk_ids[r];
-        if ((unsigned)key >= (unsigned)E) {
-            ++nbad;
-            continue;
-        }
-        atomicAdd(r < row0 ? &before_s[key] : &after_s[key], 1);
+#pragma unroll
+    for (int j = 0; j < kIds; ++j) {
+        const int r = (int)threadIdx.x + j * NT;
+        if (r >= R) continue;
+        const int key = idv[j];
+        const bool ok = (unsigned)key < (unsigned)E;
+        nbad += ok ? 0 : 1;
+        if (r >= row0 && r < row0 + T)
+            key_s[r - row0] = ok ? key : -1;
+        else if (ok)
+            atomicAdd(r < row0 ? &before_s[key] : &after_s[key], 1);
     }
     if (nbad) atomicAdd(&misc_s[0], nbad);
+    lds_barrier();
 
-    rank_tile(a.topk_ids, row0, T, E, nbits, key_s, rank_s, wave_s, cnt_s, &misc_s[0]);
+    rank_tile<NT>(key_s, T, E, nbits, rank_s, wave_s, cnt_s);
 
     if (misc_s[0] != 0) {  // every workgroup saw every id, so all take this branch together
         if (blockIdx.x == 0)
-            for (int e = threadIdx.x; e <= E; e += blockDim.x) a.expert_first_token_offset[e] = -1;
+            for (int e = threadIdx.x; e <= E; e += NT) a.expert_first_token_offset[e] = -1;
         return;
     }
-    for (int e = threadIdx.x; e < E; e += blockDim.x) after_s[e] += before_s[e] + cnt_s[e];
-    __syncthreads();
-    const int total = block_exclusive_scan(after_s, E, misc_s + 1);
+    for (int e = threadIdx.x; e < E; e += NT) after_s[e] += before_s[e] + cnt_s[e];
+    lds_barrier();
+    const int total = block_exclusive_scan<NT>(after_s, E, misc_s + 1);
     if (blockIdx.x == 0) {
-        for (int e = threadIdx.x; e < E; e += blockDim.x) a.expert_first_token_offset[e] = after_s[e];
+        for (int e = threadIdx.x; e < E; e += NT) a.expert_first_token_offset[e] = after_s[e];
         if (threadIdx.x == 0) a.expert_first_token_offset[E] = total;
     }
-    for (int e = threadIdx.x; e < E; e += blockDim.x) before_s[e] += after_s[e];
-    __syncthreads();
-    for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    for (int e = threadIdx.x; e < E; e += NT) before_s[e] += after_s[e];
+    lds_barrier();
+    for (int i = threadIdx.x; i < T; i += NT) {
         const int dest = before_s[key_s[i]] + rank_s[i];
         rank_s[i] = dest;
         a.inv_permuted_idx[row0 + i] = dest;
-        if ((uint32_t)dest < (uint64_t)R) a.permuted_idx[dest] = (int32_t)(row0 + i);
+        if ((uint32_t)dest < (uint32_t)R) a.permuted_idx[dest] = (int32_t)(row0 + i);
     }
-    __syncthreads();
-    copy_tile_rows<U>(a, t0, ntok, rank_s);
+    lds_barrier();
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT>(tc, cur, rank_s);
+    copy_tile_scales<NT>(a, t0, ntok, rank_s);
 }
 
 // ----------------------------------------------------------------------------
@@ -270,9 +333,11 @@ __global__ __launch_bounds__(kBlockThreads) void permute_fused_kernel(PermuteArg
 // rank_ws[r] = rank of row r within its tile; tile_hist[e][tile] = count,
 // tile_hist[E][tile] = rows with an out-of-range id.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlockThreads) void permute_rank_tiles_kernel(PermuteArgs a, int tokens_per_tile,
-                                                                           int nbits, int64_t num_tiles,
-                                                                           int32_t* rank_ws, int32_t* tile_hist) {
+template <int NT>
+__global__ __launch_bounds__(NT) void permute_rank_tiles_kernel(PermuteArgs a, int tokens_per_tile, int nbits,
+                                                                int64_t num_tiles, int32_t* rank_ws,
+                                                                int32_t* tile_hist) {
+    constexpr int W = NT / kWaveSize;
     extern __shared__ int smem[];
     const int E = a.num_experts;
     const int K = a.topk;
@@ -283,18 +348,27 @@ __global__ __launch_bounds__(kBlockThreads) void permute_rank_tiles_kernel(Permu
     const int T = ntok * K;
     const int tile_cap = tokens_per_tile * K;
 
-    int* cnt_s = smem;                          // [E]
-    int* wave_s = cnt_s + E;                    // [kBlockWaves * E]
-    int* key_s = wave_s + kBlockWaves * E;      // [tile_cap]
-    int* rank_s = key_s + tile_cap;             // [tile_cap]
-    int* misc_s = rank_s + tile_cap;            // [16]
+    int* cnt_s = smem;                    // [E]
+    int* wave_s = cnt_s + E;              // [W * E]
+    int* key_s = wave_s + W * E;          // [tile_cap]
+    int* rank_s = key_s + tile_cap;       // [tile_cap]
+    int* misc_s = rank_s + tile_cap;      // [16]
 
-    for (int i = threadIdx.x; i < (1 + kBlockWaves) * E; i += blockDim.x) smem[i] = 0;
+    for (int i = threadIdx.x; i < (1 + W) * E; i += NT) smem[i] = 0;
     if (threadIdx.x < 16) misc_s[threadIdx.x] = 0;
-    __syncthreads();
-    rank_tile(a.topk_ids, row0, T, E, nbits, key_s, rank_s, wave_s, cnt_s, &misc_s[0]);
-    for (int i = threadIdx.x; i < T; i += blockDim.x) rank_ws[row0 + i] = rank_s[i];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) tile_hist[(int64_t)e * num_tiles + tile] = cnt_s[e];
+    lds_barrier();
+    int nbad = 0;
+    for (int i = threadIdx.x; i < T; i += NT) {
+        const int key = a.topk_ids[row0 + i];
+        const bool ok = (unsigned)key < (unsigned)E;
+        nbad += ok ? 0 : 1;
+        key_s[i] = ok ? key : -1;
+    }
+    if (nbad) atomicAdd(&misc_s[0], nbad);
+    lds_barrier();
+    rank_tile<NT>(key_s, T, E, nbits, rank_s, wave_s, cnt_s);
+    for (int i = threadIdx.x; i < T; i += NT) rank_ws[row0 + i] = rank_s[i];
+    for (int e = threadIdx.x; e < E; e += NT) tile_hist[(int64_t)e * num_tiles + tile] = cnt_s[e];
     if (threadIdx.x == 0) tile_hist[(int64_t)E * num_tiles + tile] = misc_s[0];
 }
 
@@ -302,10 +376,12 @@ __global__ __launch_bounds__(kBlockThreads) void permute_rank_tiles_kernel(Permu
 // Staged permute, kernel 2: one wave per histogram row (expert, or the
 // bad-id row E).  Exclusive scan over tiles in place, row total to total[e].
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlockThreads) void permute_scan_tiles_kernel(int32_t* tile_hist, int64_t num_tiles,
-                                                                           int num_rows_hist, int32_t* total) {
+template <int NT>
+__global__ __launch_bounds__(NT) void permute_scan_tiles_kernel(int32_t* tile_hist, int64_t num_tiles,
+                                                                int num_rows_hist, int32_t* total) {
+    constexpr int W = NT / kWaveSize;
     const int lane = threadIdx.x % kWaveSize;
-    const int e = blockIdx.x * kBlockWaves + wave_index();
+    const int e = blockIdx.x * W + wave_index();
     if (e >= num_rows_hist) return;
     int32_t* row = tile_hist + (int64_t)e * num_tiles;
     int carry = 0;
@@ -328,11 +404,12 @@ __global__ __launch_bounds__(kBlockThreads) void permute_scan_tiles_kernel(int32
 // Staged permute, kernel 3: offsets from the per-expert totals, destinations
 // from offset + tile base + rank, index scatter, and the row copy.
 // ----------------------------------------------------------------------------
-template <int U>
-__global__ __launch_bounds__(kBlockThreads) void permute_scatter_kernel(PermuteArgs a, int tokens_per_tile,
-                                                                        int64_t num_tiles, const int32_t* rank_ws,
-                                                                        const int32_t* tile_base,
-                                                                        const int32_t* total) {
+template <int NT, int U>
+__global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int tokens_per_tile, int64_t num_tiles,
+                                                             const int32_t* rank_ws, const int32_t* tile_base,
+                                                             const int32_t* total) {
+    constexpr int kE = (kMaxExperts + 1 + NT - 1) / NT;  // per-expert values held per thread
+    constexpr int kT = (kMaxTileRows + NT - 1) / NT;     // tile rows held per thread
     extern __shared__ int smem[];
     const int E = a.num_experts;
     const int K = a.topk;
@@ -342,34 +419,63 @@ __global__ __launch_bounds__(kBlockThreads) void permute_scatter_kernel(PermuteA
     const int64_t row0 = t0 * K;
     const int T = ntok * K;
     const int tile_cap = tokens_per_tile * K;
+    const int64_t R = a.num_tokens * K;
 
-    int* off_s = smem;                // [E + 1]
-    int* dest_s = off_s + (E + 1);    // [tile_cap]
+    // Independent index loads first, then the first row chunk of this wave
+    // (the vector-memory counter retires in issue order).
+    int tot[kE], tb[kE], key[kT], rk[kT];
+#pragma unroll
+    for (int j = 0; j < kE; ++j) {
+        const int e = (int)threadIdx.x + j * NT;
+        tot[j] = total[e <= E ? e : E];
+        tb[j] = tile_base[(int64_t)(e < E ? e : E - 1) * num_tiles + tile];
+    }
+#pragma unroll
+    for (int j = 0; j < kT; ++j) {
+        const int i = (int)threadIdx.x + j * NT;
+        const int64_t r = row0 + (i < T ? i : T - 1);
+        key[j] = a.topk_ids[r];
+        rk[j] = rank_ws[r];
+    }
+    const TileCopy<U> tc(a, t0, ntok);
+    u32x4 cur[U];
+    if (a.row_vecs > 0 && wave_index() < tc.items) tc.load(wave_index(), cur);
+
+    int* off_s = smem;                // [E + 1] totals, then offsets
+    int* base_s = off_s + (E + 1);    // [E]     this tile's base within each expert
+    int* dest_s = base_s + E;         // [tile_cap]
     int* misc_s = dest_s + tile_cap;  // [16]
 
-    for (int e = threadIdx.x; e < E; e += blockDim.x) off_s[e] = total[e];
-    __syncthreads();
-    if (total[E] != 0) {  // some id was out of range: report through the offsets, write nothing else
+#pragma unroll
+    for (int j = 0; j < kE; ++j) {
+        const int e = (int)threadIdx.x + j * NT;
+        if (e <= E) off_s[e] = tot[j];
+        if (e < E) base_s[e] = tb[j];
+    }
+    lds_barrier();
+    if (off_s[E] != 0) {  // some id was out of range: report through the offsets, write nothing else
         if (tile == 0)
-            for (int e = threadIdx.x; e <= E; e += blockDim.x) a.expert_first_token_offset[e] = -1;
+            for (int e = threadIdx.x; e <= E; e += NT) a.expert_first_token_offset[e] = -1;
         return;
     }
-    const int rows_total = block_exclusive_scan(off_s, E, misc_s);
+    const int rows_total = block_exclusive_scan<NT>(off_s, E, misc_s);
     if (tile == 0) {
-        for (int e = threadIdx.x; e < E; e += blockDim.x) a.expert_first_token_offset[e] = off_s[e];
+        for (int e = threadIdx.x; e < E; e += NT) a.expert_first_token_offset[e] = off_s[e];
         if (threadIdx.x == 0) a.expert_first_token_offset[E] = rows_total;
     }
-    const int64_t R = a.num_tokens * K;
-    for (int i = threadIdx.x; i < T; i += blockDim.x) {
-        const int64_t r = row0 + i;
-        const int key = min(max(a.topk_ids[r], 0), E - 1);  // all ids are in range here (total[E] == 0)
-        const int dest = off_s[key] + tile_base[(int64_t)key * num_tiles + tile] + rank_ws[r];
+#pragma unroll
+    for (int j = 0; j < kT; ++j) {
+        const int i = (int)threadIdx.x + j * NT;
+        if (i >= T) continue;
+        const int e = min(max(key[j], 0), E - 1);  // all ids are in range here (no bad-id count)
+        const int dest = off_s[e] + base_s[e] + rk[j];
         dest_s[i] = dest;
-        a.inv_permuted_idx[r] = dest;
-        if ((uint32_t)dest < (uint64_t)R) a.permuted_idx[dest] = (int32_t)r;
+        a.inv_permuted_idx[row0 + i] = dest;
+        if ((uint32_t)dest < (uint64_t)R) a.permuted_idx[dest] = (int32_t)(row0 + i);
     }
-    __syncthreads();
-    copy_tile_rows<U>(a, t0, ntok, dest_s);
+    lds_barrier();
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT>(tc, cur, dest_s);
+    copy_tile_scales<NT>(a, t0, ntok, dest_s);
 }
 
 __global__ void fill_offsets_kernel(int64_t* off, int n, int64_t value) {
@@ -377,9 +483,10 @@ __global__ void fill_offsets_kernel(int64_t* off, int n, int64_t value) {
 }
 
 // ----------------------------------------------------------------------------
-// Unpermute: one wave per (token, chunk of U*64 16-byte vectors).  The topk
-// rows of the token are read, weighted and summed in fp32 in ascending k,
-// then rounded once to the element type.
+// Unpermute: one wave per (token, chunk of U*64 16-byte vectors).  The loads
+// of all topk rows of the chunk are issued before any arithmetic (G rows at a
+// time when topk is not a compile-time constant), then summed in fp32 in
+// ascending k and rounded once to the element type.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -392,19 +499,38 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
 }
 
 template <bool kBF16, int U>
-__global__ __launch_bounds__(kBlockThreads) void unpermute_kernel(UnpermuteArgs a) {
+__device__ __forceinline__ void accumulate(float (&acc)[U][kBF16 ? 8 : 4], const u32x4 (&v)[U], float wk) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (kBF16) {
+                acc[u][2 * q] = __builtin_fmaf(wk, bf16_lo(v[u][q]), acc[u][2 * q]);
+                acc[u][2 * q + 1] = __builtin_fmaf(wk, bf16_hi(v[u][q]), acc[u][2 * q + 1]);
+            } else {
+                acc[u][q] = __builtin_fmaf(wk, __uint_as_float(v[u][q]), acc[u][q]);
+            }
+        }
+    }
+}
+
+// KC > 0: topk is exactly KC.  KC == 0: runtime topk, rows taken G at a time.
+template <bool kBF16, int KC, int U, int G>
+__global__ __launch_bounds__(256) void unpermute_kernel(UnpermuteArgs a) {
     constexpr int kEl = kBF16 ? 8 : 4;  // elements per 16-byte vector
+    constexpr int kGroup = KC > 0 ? KC : G;
     const int lane = threadIdx.x % kWaveSize;
     const int64_t rv = a.row_vecs;
-    const int chunk = U * kWaveSize;
-    const int64_t nchunks = (rv + chunk - 1) / chunk;
-    const int64_t item = (int64_t)blockIdx.x * kBlockWaves + wave_index();
+    const int64_t nchunks = (rv + U * kWaveSize - 1) / (U * kWaveSize);
+    const int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index();
     if (item >= a.num_tokens * nchunks) return;
     const int64_t t = item / nchunks;
-    const int64_t c = item - t * nchunks;
-    const int K = a.topk;
+    const int64_t base = (item - t * nchunks) * (U * kWaveSize) + lane;
+    const int K = KC > 0 ? KC : a.topk;
     const int64_t R = a.num_tokens * K;
     const u32x4* __restrict__ y = reinterpret_cast<const u32x4*>(a.expanded_output);
+    const int32_t* inv = a.inv_permuted_idx + t * K;
+    const float* wt = a.topk_weights + t * K;
 
     float acc[U][kEl];
 #pragma unroll
@@ -412,37 +538,31 @@ __global__ __launch_bounds__(kBlockThreads) void unpermute_kernel(UnpermuteArgs 
 #pragma unroll
         for (int e = 0; e < kEl; ++e) acc[u][e] = 0.0f;
     bool bad = false;
-    for (int k = 0; k < K; ++k) {
-        const int32_t j = a.inv_permuted_idx[t * K + k];
-        const float wk = a.topk_weights[t * K + k];
-        if (j < 0 || (int64_t)j >= R) {
-            bad = true;
-            continue;
-        }
-        const u32x4* src = y + (int64_t)j * rv;
-        u32x4 v[U];
+    for (int k0 = 0; k0 < K; k0 += kGroup) {
+        u32x4 v[kGroup][U];
+        float wk[kGroup];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t idx = c * chunk + u * kWaveSize + lane;
-            v[u] = idx < rv ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int g = 0; g < kGroup; ++g) {
+            const bool live = KC > 0 || k0 + g < K;
+            const int32_t j = live ? inv[k0 + g] : 0;
+            const bool ok = live && j >= 0 && (int64_t)j < R;
+            bad |= live && !ok;
+            wk[g] = live ? wt[k0 + g] : 0.0f;
+            const u32x4* src = y + (int64_t)(ok ? j : 0) * rv;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if constexpr (kBF16) {
-                    acc[u][2 * q] = __builtin_fmaf(wk, bf16_lo(v[u][q]), acc[u][2 * q]);
-                    acc[u][2 * q + 1] = __builtin_fmaf(wk, bf16_hi(v[u][q]), acc[u][2 * q + 1]);
-                } else {
-                    acc[u][q] = __builtin_fmaf(wk, __uint_as_float(v[u][q]), acc[u][q]);
-                }
+            for (int u = 0; u < U; ++u) {
+                const int64_t idx = base + u * kWaveSize;
+                v[g][u] = (ok && idx < rv) ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
             }
         }
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g)
+            if (KC > 0 || k0 + g < K) accumulate<kBF16, U>(acc, v[g], wk[g]);
     }
     u32x4* __restrict__ out = reinterpret_cast<u32x4*>(a.output) + t * rv;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t idx = c * chunk + u * kWaveSize + lane;
+        const int64_t idx = base + u * kWaveSize;
         if (idx >= rv) continue;
         u32x4 o;
 #pragma unroll
@@ -461,10 +581,9 @@ __global__ __launch_bounds__(kBlockThreads) void unpermute_kernel(UnpermuteArgs 
 // Launchers
 // ----------------------------------------------------------------------------
 static constexpr int kCopyUnroll = 4;
-static constexpr int kUnpermuteUnroll = 4;
 
 hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t value, hipStream_t stream) {
-    hipLaunchKernelGGL(fill_offsets_kernel, dim3(1), dim3(kBlockThreads), 0, stream, off, num_experts + 1, value);
+    hipLaunchKernelGGL(fill_offsets_kernel, dim3(1), dim3(256), 0, stream, off, num_experts + 1, value);
     return hipGetLastError();
 }
 
@@ -472,42 +591,53 @@ hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* work
     const int E = a.num_experts;
     if (p.fused) {
         const size_t lds = fused_lds_bytes(E, p.tile_rows);
-        hipLaunchKernelGGL(permute_fused_kernel<kCopyUnroll>, dim3((unsigned)p.num_tiles), dim3(kBlockThreads),
-                           lds, stream, a, p.tokens_per_tile, p.nbits);
+        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, kCopyUnroll>), dim3((unsigned)p.num_tiles),
+                           dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile, p.nbits);
         return hipGetLastError();
     }
     char* ws = static_cast<char*>(workspace);
     int32_t* rank_ws = reinterpret_cast<int32_t*>(ws + p.ws_rank);
     int32_t* tile_hist = reinterpret_cast<int32_t*>(ws + p.ws_tile_hist);
     int32_t* total = reinterpret_cast<int32_t*>(ws + p.ws_total);
-    hipLaunchKernelGGL(permute_rank_tiles_kernel, dim3((unsigned)p.num_tiles), dim3(kBlockThreads),
+    hipLaunchKernelGGL((permute_rank_tiles_kernel<kRankThreads>), dim3((unsigned)p.num_tiles), dim3(kRankThreads),
                        rank_lds_bytes(E, p.tile_rows), stream, a, p.tokens_per_tile, p.nbits, p.num_tiles, rank_ws,
                        tile_hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int hist_rows = E + 1;
-    hipLaunchKernelGGL(permute_scan_tiles_kernel, dim3((unsigned)((hist_rows + kBlockWaves - 1) / kBlockWaves)),
-                       dim3(kBlockThreads), 0, stream, tile_hist, p.num_tiles, hist_rows, total);
+    constexpr int kScanWaves = kScanThreads / kWaveSize;
+    hipLaunchKernelGGL((permute_scan_tiles_kernel<kScanThreads>), dim3((unsigned)((hist_rows + kScanWaves - 1) / kScanWaves)),
+                       dim3(kScanThreads), 0, stream, tile_hist, p.num_tiles, hist_rows, total);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(permute_scatter_kernel<kCopyUnroll>, dim3((unsigned)p.num_tiles), dim3(kBlockThreads),
-                       scatter_lds_bytes(E, p.tile_rows), stream, a, p.tokens_per_tile, p.num_tiles, rank_ws,
-                       tile_hist, total);
+    hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, kCopyUnroll>), dim3((unsigned)p.num_tiles),
+                       dim3(kScatterThreads), scatter_lds_bytes(E, p.tile_rows), stream, a, p.tokens_per_tile,
+                       p.num_tiles, rank_ws, tile_hist, total);
     return hipGetLastError();
 }
 
-hipError_t launch_unpermute(const UnpermuteArgs& a, bool bf16, hipStream_t stream) {
-    const int64_t chunk = kUnpermuteUnroll * kWaveSize;
-    const int64_t nchunks = (a.row_vecs + chunk - 1) / chunk;
+template <bool kBF16, int KC, int U, int G>
+static hipError_t launch_unpermute_t(const UnpermuteArgs& a, hipStream_t stream) {
+    const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
     const int64_t items = a.num_tokens * nchunks;
-    const int64_t blocks = (items + kBlockWaves - 1) / kBlockWaves;
-    if (bf16)
-        hipLaunchKernelGGL((unpermute_kernel<true, kUnpermuteUnroll>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((unpermute_kernel<false, kUnpermuteUnroll>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
-                           stream, a);
+    const int64_t blocks = (items + 3) / 4;
+    hipLaunchKernelGGL((unpermute_kernel<kBF16, KC, U, G>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+template <bool kBF16>
+static hipError_t launch_unpermute_dtype(const UnpermuteArgs& a, hipStream_t stream) {
+    switch (a.topk) {
+        case 1: return launch_unpermute_t<kBF16, 1, 8, 1>(a, stream);
+        case 2: return launch_unpermute_t<kBF16, 2, 4, 2>(a, stream);
+        case 4: return launch_unpermute_t<kBF16, 4, 4, 4>(a, stream);
+        case 8: return launch_unpermute_t<kBF16, 8, 2, 8>(a, stream);
+        default: return launch_unpermute_t<kBF16, 0, 4, 4>(a, stream);
+    }
+}
+
+hipError_t launch_unpermute(const UnpermuteArgs& a, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_unpermute_dtype<true>(a, stream) : launch_unpermute_dtype<false>(a, stream);
 }
 
 }  // namespace moe

@@ -17,8 +17,10 @@
 namespace moe {
 
 constexpr int kWaveSize = 64;
-constexpr int kBlockThreads = 256;                 // 4 waves per workgroup
-constexpr int kBlockWaves = kBlockThreads / kWaveSize;
+constexpr int kFusedThreads = 512;                 // fused permute workgroup (8 waves)
+constexpr int kRankThreads = 256;                  // staged kernel 1
+constexpr int kScanThreads = 256;                  // staged kernel 2 (one wave per expert row)
+constexpr int kScatterThreads = 256;               // staged kernel 3
 constexpr int kMaxExperts = 1024;
 constexpr int64_t kFusedMaxRows = 16384;           // fused schedule up to this many expanded rows
 constexpr int kStagedTileRows = 128;               // target expanded rows per staged tile
@@ -78,9 +80,9 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int num_experts) {
     p.nbits = key_bits(num_experts);
     if (p.rows <= kFusedMaxRows) {
         p.fused = true;
-        // Enough workgroups to spread the row copy, at most kBlockThreads rows per tile.
+        // Enough workgroups to spread the row copy, at most kFusedThreads rows per tile.
         int64_t tpt = (num_tokens + kFusedTargetBlocks - 1) / kFusedTargetBlocks;
-        const int64_t cap = (kBlockThreads / topk) < 1 ? 1 : (kBlockThreads / topk);
+        const int64_t cap = (kFusedThreads / topk) < 1 ? 1 : (kFusedThreads / topk);
         if (tpt < 1) tpt = 1;
         if (tpt > cap) tpt = cap;
         p.tokens_per_tile = (int)tpt;
@@ -102,13 +104,13 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int num_experts) {
 
 // Dynamic LDS bytes of the fused and staged kernels for one tile shape.
 inline size_t fused_lds_bytes(int num_experts, int tile_rows) {
-    return sizeof(int) * ((size_t)(3 + kBlockWaves) * num_experts + 2 * (size_t)tile_rows + 16);
+    return sizeof(int) * ((size_t)(3 + kFusedThreads / kWaveSize) * num_experts + 2 * (size_t)tile_rows + 16);
 }
 inline size_t rank_lds_bytes(int num_experts, int tile_rows) {
-    return sizeof(int) * ((size_t)(1 + kBlockWaves) * num_experts + 2 * (size_t)tile_rows + 16);
+    return sizeof(int) * ((size_t)(1 + kRankThreads / kWaveSize) * num_experts + 2 * (size_t)tile_rows + 16);
 }
 inline size_t scatter_lds_bytes(int num_experts, int tile_rows) {
-    return sizeof(int) * ((size_t)(num_experts + 1) + (size_t)tile_rows + 16);
+    return sizeof(int) * ((size_t)(2 * num_experts + 1) + (size_t)tile_rows + 16);
 }
 
 }  // namespace moe

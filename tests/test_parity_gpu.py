@@ -141,7 +141,7 @@ EDGE = [
     (5, 4, 4, 64, "bf16", "distinct"),
     (3000, 2, 64, 136, "bf16", "one_expert"),
     (5000, 4, 16, 72, "bf16", "first_expert"),
-    (1000, 4, 3, 4, "f32", "dups"),
+    (1000, 3, 3, 4, "f32", "dups"),
     (9000, 3, 5, 40, "bf16", "dups"),
     (4099, 8, 1024, 64, "bf16", "distinct"),
     (100, 16, 1024, 128, "f32", "distinct"),
