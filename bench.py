@@ -104,8 +104,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate (default: enough to beat the LLC)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="before timing, copy a fresh MIB-MiB buffer 5 times (a plain copy kernel of known "
-                         "size, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
+                    help="before timing, run a plain elementwise copy kernel (negation) over a fresh MIB-MiB "
+                         "float32 buffer 5 times; its known traffic scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K steps (and each per-operation batch) in a HIP graph and time its replay")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -150,20 +152,47 @@ def main() -> int:
         })
     ws = torch.empty(max(16, binding.moe_permute_workspace_size(w.num_tokens, w.topk, w.num_experts)),
                      dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
+    # Kernels go to torch's current stream (the capture stream while a graph is recorded).
     def permute(s):
         binding.moe_permute(s["x"], ids, w.num_experts, s["xp"], s["off"], s["perm"], s["inv"], ws,
-                            token_scale=s["scale"], permuted_scale=s["sp"], stream=stream)
+                            token_scale=s["scale"], permuted_scale=s["sp"])
 
     def unpermute(s):
-        binding.moe_unpermute(s["y"], wts, s["inv"], s["out"], stream=stream)
+        binding.moe_unpermute(s["y"], wts, s["inv"], s["out"])
+
+    def step(i):
+        permute(sets[i % nsets])
+        unpermute(sets[i % nsets])
+
+    def timed(body, k):
+        """Time k calls of body(i) between HIP events on the current stream; returns us per call."""
+        if args.graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(k):
+                    body(i)
+            g.replay()
+            torch.cuda.synchronize(dev)
+            run = g.replay
+        else:
+            def run():
+                for i in range(k):
+                    body(i)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        start.record()
+        run()
+        end.record()
+        torch.cuda.synchronize(dev)
+        return start.elapsed_time(end) * 1e3 / k, time.perf_counter() - t0
 
     if args.copy_calibration:
-        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev).fill_(1)
+        src = torch.ones((args.copy_calibration << 20) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize(dev)
         del src, dst
 
@@ -174,38 +203,18 @@ def main() -> int:
     torch.cuda.synchronize(dev)
 
     k = args.steps
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-
-    # Timed region: exactly K steps, nothing else enqueued between the kernels.
-    torch.cuda.synchronize(dev)
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(k):
-        s = sets[i % nsets]
-        permute(s)
-        unpermute(s)
-    end.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - wall0
-    ms_step = start.elapsed_time(end) / k
+    # Timed region: exactly K steps (permute + unpermute), nothing else between the kernels.
+    us_step, wall = timed(step, k)
+    ms_step = us_step / 1e3
     value = nb["total"] / (ms_step * 1e-3) / 1e9
 
-    # Per-kernel durations: K back-to-back calls of one operation (same buffer
+    # Per-operation durations: K back-to-back calls of one operation (same buffer
     # rotation) between one pair of HIP events on the kernels' stream.
-    def batch_us(fn):
-        torch.cuda.synchronize(dev)
-        start.record(stream)
-        for i in range(k):
-            fn(sets[i % nsets])
-        end.record(stream)
-        torch.cuda.synchronize(dev)
-        return start.elapsed_time(end) * 1e3 / k
-
-    perm_avg = batch_us(permute)
-    unperm_avg = batch_us(unpermute)
+    perm_avg, _ = timed(lambda i: permute(sets[i % nsets]), k)
+    unperm_avg, _ = timed(lambda i: unpermute(sets[i % nsets]), k)
     tiny = torch.zeros(1, device=dev)
-    launch_floor_us = batch_us(lambda _s: tiny.add_(1.0))
+    floor_args = args.graph
+    launch_floor_us = timed(lambda i: tiny.add_(1.0), k)[0] if floor_args else None
 
     plan_fused = w.num_rows <= 16384
     perm_kernel = "permute_fused_kernel" if plan_fused else "moe_permute (rank + scan + scatter kernels)"
@@ -244,7 +253,8 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "us_per_step": round(ms_step * 1e3, 3),
         "permute_us": round(perm_avg, 3),
-        "launch_floor_us": round(launch_floor_us, 3),
+        "launch_floor_us": None if launch_floor_us is None else round(launch_floor_us, 3),
+        "timing": "hip_graph_replay" if args.graph else "eager_launches",
         "unpermute_us": round(unperm_avg, 3),
         "permute_GBps": round(nb["permute"] / (perm_avg * 1e-6) / 1e9, 1),
         "unpermute_GBps": round(nb["unpermute"] / (unperm_avg * 1e-6) / 1e9, 1),

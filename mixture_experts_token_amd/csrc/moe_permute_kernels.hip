@@ -373,31 +373,54 @@ __global__ __launch_bounds__(NT) void permute_rank_tiles_kernel(PermuteArgs a, i
 }
 
 // ----------------------------------------------------------------------------
-// Staged permute, kernel 2: one wave per histogram row (expert, or the
-// bad-id row E).  Exclusive scan over tiles in place, row total to total[e].
+// Staged permute, kernel 2: one workgroup per histogram row (an expert, or the
+// bad-id row E).  The row's tile counts are loaded at once (P per thread,
+// thread-contiguous), scanned in registers, then across the workgroup; the
+// exclusive prefix goes back in place and the row total to total[e].
 // ----------------------------------------------------------------------------
-template <int NT>
+template <int NT, int P>
 __global__ __launch_bounds__(NT) void permute_scan_tiles_kernel(int32_t* tile_hist, int64_t num_tiles,
-                                                                int num_rows_hist, int32_t* total) {
-    constexpr int W = NT / kWaveSize;
-    const int lane = threadIdx.x % kWaveSize;
-    const int e = blockIdx.x * W + wave_index();
-    if (e >= num_rows_hist) return;
-    int32_t* row = tile_hist + (int64_t)e * num_tiles;
+                                                                int32_t* total) {
+    __shared__ int tmp[NT / kWaveSize];
+    const int tid = threadIdx.x;
+    const int lane = tid % kWaveSize, w = tid / kWaveSize;
+    int32_t* row = tile_hist + (int64_t)blockIdx.x * num_tiles;
     int carry = 0;
-    for (int64_t base = 0; base < num_tiles; base += kWaveSize) {
-        const int64_t i = base + lane;
-        const int v = i < num_tiles ? row[i] : 0;
-        int x = v;
+    for (int64_t base = 0; base < num_tiles; base += (int64_t)NT * P) {
+        const int64_t first = base + (int64_t)tid * P;
+        int v[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) v[p] = first + p < num_tiles ? row[first + p] : 0;
+        int s = 0;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int c = v[p];
+            v[p] = s;  // exclusive within the thread
+            s += c;
+        }
+        int x = s;
 #pragma unroll
         for (int d = 1; d < kWaveSize; d <<= 1) {
             const int y = __shfl_up(x, d, kWaveSize);
             if (lane >= d) x += y;
         }
-        if (i < num_tiles) row[i] = carry + x - v;
-        carry += __shfl(x, kWaveSize - 1, kWaveSize);
+        if (lane == kWaveSize - 1) tmp[w] = x;
+        lds_barrier();
+        int before = carry, pass_total = 0;
+#pragma unroll
+        for (int q = 0; q < NT / kWaveSize; ++q) {
+            const int c = tmp[q];
+            before += q < w ? c : 0;
+            pass_total += c;
+        }
+        before += x - s;
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            if (first + p < num_tiles) row[first + p] = before + v[p];
+        carry += pass_total;
+        lds_barrier();  // tmp is reused by the next pass
     }
-    if (lane == 0) total[e] = carry;
+    if (tid == 0) total[blockIdx.x] = carry;
 }
 
 // ----------------------------------------------------------------------------
@@ -515,84 +538,116 @@ __device__ __forceinline__ void accumulate(float (&acc)[U][kBF16 ? 8 : 4], const
 }
 
 // KC > 0: topk is exactly KC.  KC == 0: runtime topk, rows taken G at a time.
+// One item per wave; only when the grid would exceed kMaxGridBlocks does a
+// wave loop over items g, g + total_waves, ...
 template <bool kBF16, int KC, int U, int G>
-__global__ __launch_bounds__(256) void unpermute_kernel(UnpermuteArgs a) {
+__global__ __launch_bounds__(256) void unpermute_kernel(UnpermuteArgs a, int64_t total_waves) {
     constexpr int kEl = kBF16 ? 8 : 4;  // elements per 16-byte vector
     constexpr int kGroup = KC > 0 ? KC : G;
     const int lane = threadIdx.x % kWaveSize;
     const int64_t rv = a.row_vecs;
     const int64_t nchunks = (rv + U * kWaveSize - 1) / (U * kWaveSize);
-    const int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index();
-    if (item >= a.num_tokens * nchunks) return;
-    const int64_t t = item / nchunks;
-    const int64_t base = (item - t * nchunks) * (U * kWaveSize) + lane;
+    const int64_t items = a.num_tokens * nchunks;
     const int K = KC > 0 ? KC : a.topk;
     const int64_t R = a.num_tokens * K;
     const u32x4* __restrict__ y = reinterpret_cast<const u32x4*>(a.expanded_output);
-    const int32_t* inv = a.inv_permuted_idx + t * K;
-    const float* wt = a.topk_weights + t * K;
+    u32x4* __restrict__ out_base = reinterpret_cast<u32x4*>(a.output);
 
-    float acc[U][kEl];
+    for (int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index(); item < items; item += total_waves) {
+        const int64_t t = item / nchunks;
+        const int64_t base = (item - t * nchunks) * (U * kWaveSize) + lane;
+        const int32_t* inv = a.inv_permuted_idx + t * K;
+        const float* wt = a.topk_weights + t * K;
+
+        float acc[U][kEl];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int e = 0; e < kEl; ++e) acc[u][e] = 0.0f;
-    bool bad = false;
-    for (int k0 = 0; k0 < K; k0 += kGroup) {
-        u32x4 v[kGroup][U];
-        float wk[kGroup];
+            for (int e = 0; e < kEl; ++e) acc[u][e] = 0.0f;
+        bool bad = false;
+        for (int k0 = 0; k0 < K; k0 += kGroup) {
+            u32x4 v[kGroup][U];
+            float wk[kGroup];
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g) {
-            const bool live = KC > 0 || k0 + g < K;
-            const int32_t j = live ? inv[k0 + g] : 0;
-            const bool ok = live && j >= 0 && (int64_t)j < R;
-            bad |= live && !ok;
-            wk[g] = live ? wt[k0 + g] : 0.0f;
-            const u32x4* src = y + (int64_t)(ok ? j : 0) * rv;
+            for (int g = 0; g < kGroup; ++g) {
+                const bool live = KC > 0 || k0 + g < K;
+                const int32_t j = live ? inv[k0 + g] : 0;
+                const bool ok = live && j >= 0 && (int64_t)j < R;
+                bad |= live && !ok;
+                wk[g] = live ? wt[k0 + g] : 0.0f;
+                const u32x4* src = y + (int64_t)(ok ? j : 0) * rv;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t idx = base + u * kWaveSize;
-                v[g][u] = (ok && idx < rv) ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+                for (int u = 0; u < U; ++u) {
+                    const int64_t idx = base + u * kWaveSize;
+                    v[g][u] = (ok && idx < rv) ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+                }
             }
+#pragma unroll
+            for (int g = 0; g < kGroup; ++g)
+                if (KC > 0 || k0 + g < K) accumulate<kBF16, U>(acc, v[g], wk[g]);
         }
+        u32x4* __restrict__ out = out_base + t * rv;
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g)
-            if (KC > 0 || k0 + g < K) accumulate<kBF16, U>(acc, v[g], wk[g]);
-    }
-    u32x4* __restrict__ out = reinterpret_cast<u32x4*>(a.output) + t * rv;
+        for (int u = 0; u < U; ++u) {
+            const int64_t idx = base + u * kWaveSize;
+            if (idx >= rv) continue;
+            u32x4 o;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t idx = base + u * kWaveSize;
-        if (idx >= rv) continue;
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if constexpr (kBF16) {
-                o[q] = bad ? 0x7FC07FC0u : (bf16_bits(acc[u][2 * q]) | (bf16_bits(acc[u][2 * q + 1]) << 16));
-            } else {
-                o[q] = bad ? 0x7FC00000u : __float_as_uint(acc[u][q]);
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (kBF16) {
+                    o[q] = bad ? 0x7FC07FC0u : (bf16_bits(acc[u][2 * q]) | (bf16_bits(acc[u][2 * q + 1]) << 16));
+                } else {
+                    o[q] = bad ? 0x7FC00000u : __float_as_uint(acc[u][q]);
+                }
             }
+            __builtin_nontemporal_store(o, out + idx);
         }
-        __builtin_nontemporal_store(o, out + idx);
     }
 }
 
 // ----------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------
-static constexpr int kCopyUnroll = 4;
+static constexpr int kCopyUnrolls[] = {8, 7, 6, 5, 4, 3, 2, 1};
 
 hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t value, hipStream_t stream) {
     hipLaunchKernelGGL(fill_offsets_kernel, dim3(1), dim3(256), 0, stream, off, num_experts + 1, value);
     return hipGetLastError();
 }
 
+template <int U>
+static void launch_fused_u(const PermuteArgs& a, const PermutePlan& p, hipStream_t stream) {
+    hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U>), dim3((unsigned)p.num_tiles), dim3(kFusedThreads),
+                       fused_lds_bytes(a.num_experts, p.tile_rows), stream, a, p.tokens_per_tile, p.nbits);
+}
+
+template <int U>
+static void launch_scatter_u(const PermuteArgs& a, const PermutePlan& p, const int32_t* rank_ws,
+                             const int32_t* tile_base, const int32_t* total, hipStream_t stream) {
+    hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U>), dim3((unsigned)p.num_tiles),
+                       dim3(kScatterThreads), scatter_lds_bytes(a.num_experts, p.tile_rows), stream, a,
+                       p.tokens_per_tile, p.num_tiles, rank_ws, tile_base, total);
+}
+
+#define MOE_DISPATCH_U(u, CALL) \
+    switch (u) {                \
+        case 8: CALL(8); break; \
+        case 7: CALL(7); break; \
+        case 6: CALL(6); break; \
+        case 5: CALL(5); break; \
+        case 4: CALL(4); break; \
+        case 3: CALL(3); break; \
+        case 2: CALL(2); break; \
+        default: CALL(1); break; \
+    }
+
 hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream) {
     const int E = a.num_experts;
+    const int u = choose_unroll(a.row_vecs, kCopyUnrolls, 8);
     if (p.fused) {
-        const size_t lds = fused_lds_bytes(E, p.tile_rows);
-        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, kCopyUnroll>), dim3((unsigned)p.num_tiles),
-                           dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile, p.nbits);
+#define MOE_FUSED(U) launch_fused_u<U>(a, p, stream)
+        MOE_DISPATCH_U(u, MOE_FUSED)
+#undef MOE_FUSED
         return hipGetLastError();
     }
     char* ws = static_cast<char*>(workspace);
@@ -604,15 +659,13 @@ hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* work
                        tile_hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int hist_rows = E + 1;
-    constexpr int kScanWaves = kScanThreads / kWaveSize;
-    hipLaunchKernelGGL((permute_scan_tiles_kernel<kScanThreads>), dim3((unsigned)((hist_rows + kScanWaves - 1) / kScanWaves)),
-                       dim3(kScanThreads), 0, stream, tile_hist, p.num_tiles, hist_rows, total);
+    hipLaunchKernelGGL((permute_scan_tiles_kernel<kScanThreads, kScanPerThread>), dim3((unsigned)(E + 1)),
+                       dim3(kScanThreads), 0, stream, tile_hist, p.num_tiles, total);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, kCopyUnroll>), dim3((unsigned)p.num_tiles),
-                       dim3(kScatterThreads), scatter_lds_bytes(E, p.tile_rows), stream, a, p.tokens_per_tile,
-                       p.num_tiles, rank_ws, tile_hist, total);
+#define MOE_SCATTER(U) launch_scatter_u<U>(a, p, rank_ws, tile_hist, total, stream)
+    MOE_DISPATCH_U(u, MOE_SCATTER)
+#undef MOE_SCATTER
     return hipGetLastError();
 }
 
@@ -620,19 +673,55 @@ template <bool kBF16, int KC, int U, int G>
 static hipError_t launch_unpermute_t(const UnpermuteArgs& a, hipStream_t stream) {
     const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
     const int64_t items = a.num_tokens * nchunks;
-    const int64_t blocks = (items + 3) / 4;
-    hipLaunchKernelGGL((unpermute_kernel<kBF16, KC, U, G>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    const int64_t blocks_needed = (items + 3) / 4;
+    const int64_t blocks = blocks_needed < kMaxGridBlocks ? blocks_needed : kMaxGridBlocks;
+    hipLaunchKernelGGL((unpermute_kernel<kBF16, KC, U, G>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
+                       blocks * 4);
     return hipGetLastError();
+}
+
+// Vectors per lane are bounded so that the topk rows of one chunk stay in
+// registers (topk * U <= 16 vectors).
+static constexpr int kUnrollsWide[] = {8, 7, 4, 2, 1};
+static constexpr int kUnrolls4[] = {4, 2, 1};
+static constexpr int kUnrolls2[] = {2, 1};
+
+template <bool kBF16, int KC, int G>
+static hipError_t launch_unpermute_k(const UnpermuteArgs& a, hipStream_t stream) {
+    int u;
+    if (KC == 1 || KC == 2)
+        u = choose_unroll(a.row_vecs, kUnrollsWide, 5);
+    else if (KC == 8)
+        u = choose_unroll(a.row_vecs, kUnrolls2, 2);
+    else
+        u = choose_unroll(a.row_vecs, kUnrolls4, 3);
+    if constexpr (KC == 1 || KC == 2) {
+        switch (u) {
+            case 8: return launch_unpermute_t<kBF16, KC, 8, G>(a, stream);
+            case 7: return launch_unpermute_t<kBF16, KC, 7, G>(a, stream);
+            case 4: return launch_unpermute_t<kBF16, KC, 4, G>(a, stream);
+            case 2: return launch_unpermute_t<kBF16, KC, 2, G>(a, stream);
+            default: return launch_unpermute_t<kBF16, KC, 1, G>(a, stream);
+        }
+    } else if constexpr (KC == 8) {
+        return u == 2 ? launch_unpermute_t<kBF16, KC, 2, G>(a, stream) : launch_unpermute_t<kBF16, KC, 1, G>(a, stream);
+    } else {
+        switch (u) {
+            case 4: return launch_unpermute_t<kBF16, KC, 4, G>(a, stream);
+            case 2: return launch_unpermute_t<kBF16, KC, 2, G>(a, stream);
+            default: return launch_unpermute_t<kBF16, KC, 1, G>(a, stream);
+        }
+    }
 }
 
 template <bool kBF16>
 static hipError_t launch_unpermute_dtype(const UnpermuteArgs& a, hipStream_t stream) {
     switch (a.topk) {
-        case 1: return launch_unpermute_t<kBF16, 1, 8, 1>(a, stream);
-        case 2: return launch_unpermute_t<kBF16, 2, 4, 2>(a, stream);
-        case 4: return launch_unpermute_t<kBF16, 4, 4, 4>(a, stream);
-        case 8: return launch_unpermute_t<kBF16, 8, 2, 8>(a, stream);
-        default: return launch_unpermute_t<kBF16, 0, 4, 4>(a, stream);
+        case 1: return launch_unpermute_k<kBF16, 1, 1>(a, stream);
+        case 2: return launch_unpermute_k<kBF16, 2, 2>(a, stream);
+        case 4: return launch_unpermute_k<kBF16, 4, 4>(a, stream);
+        case 8: return launch_unpermute_k<kBF16, 8, 8>(a, stream);
+        default: return launch_unpermute_k<kBF16, 0, 4>(a, stream);
     }
 }
 

@@ -19,8 +19,10 @@ namespace moe {
 constexpr int kWaveSize = 64;
 constexpr int kFusedThreads = 512;                 // fused permute workgroup (8 waves)
 constexpr int kRankThreads = 256;                  // staged kernel 1
-constexpr int kScanThreads = 256;                  // staged kernel 2 (one wave per expert row)
+constexpr int kScanThreads = 256;                  // staged kernel 2 (one workgroup per histogram row)
 constexpr int kScatterThreads = 256;               // staged kernel 3
+constexpr int64_t kMaxGridBlocks = int64_t(1) << 20;  // beyond this, waves loop over further items
+constexpr int kScanPerThread = 8;                  // tile counts one scan thread holds per pass
 constexpr int kMaxExperts = 1024;
 constexpr int64_t kFusedMaxRows = 16384;           // fused schedule up to this many expanded rows
 constexpr int kStagedTileRows = 128;               // target expanded rows per staged tile
@@ -29,6 +31,21 @@ constexpr int kMaxTileRows = 1024;                 // LDS staging bound for one 
 constexpr size_t kWorkspaceAlign = 256;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Vectors per lane per work item (a chunk is U*64 16-byte vectors of one row).
+// Picks the widest U from `allowed` (descending) whose chunks cover the row
+// with at most 10% idle lanes, so rows split evenly (e.g. 14 groups of 64
+// vectors -> U = 7, two full chunks).
+inline int choose_unroll(int64_t row_vecs, const int* allowed, int n_allowed) {
+    const int64_t groups = (row_vecs + kWaveSize - 1) / kWaveSize;
+    if (groups <= 0) return allowed[n_allowed - 1];
+    for (int i = 0; i < n_allowed; ++i) {
+        const int64_t u = allowed[i];
+        const int64_t lanes = (groups + u - 1) / u * u;
+        if (groups * 10 >= lanes * 9) return (int)u;
+    }
+    return allowed[n_allowed - 1];
+}
 
 inline int key_bits(int num_experts) {
     int b = 0;

@@ -155,6 +155,7 @@ EDGE = [
     (3001, 8, 160, 7168, "bf16", "empties"),
     (513, 8, 256, 16, "fp8_e4m3", "distinct"),
     (2600, 8, 256, 7168, "fp8_e4m3", "distinct"),
+    (140000, 2, 16, 8, "bf16", "dups"),        # > 2048 tiles: the tile scan takes several passes
 ]
 
 
@@ -186,6 +187,25 @@ def test_edge_case_parity(hip_device, n, k, e, h, dtype, mode):
     assert_permute_equal(outs, ref)
     ref_out = oracle.unpermute(to_np(y), to_np(wts), ref["inv_permuted_idx"], out_dtype)
     assert_unpermute_close(to_np(out), ref_out, out_dtype)
+
+
+def test_sizes_that_loop_inside_kernels(hip_device):
+    """4.3M tokens with topk 1: the tile scan runs many passes and unpermute waves
+    loop over items (more items than the capped grid has waves)."""
+    n, k, e, h = 4_300_000, 1, 4, 8
+    rng = np.random.default_rng(17)
+    ids = torch.from_numpy(rng.integers(0, e, size=(n, k)).astype(np.int32)).to(hip_device)
+    x = torch.randn((n, h), device=hip_device).to(torch.bfloat16)
+    y = torch.randn((n * k, h), device=hip_device).to(torch.bfloat16)
+    wts = torch.rand((n, k), device=hip_device) + 0.5
+    _say("looping sizes N=%d topk=%d E=%d H=%d" % (n, k, e, h))
+    outs = gpu_permute(x, ids, e)
+    out = gpu_unpermute(y, wts, outs["inv_permuted_idx"])
+    torch.cuda.synchronize()
+    ref = oracle_permute(x, ids, e)
+    assert_permute_equal(outs, ref)
+    ref_out = oracle.unpermute(to_np(y), to_np(wts), ref["inv_permuted_idx"], "bf16")
+    assert_unpermute_close(to_np(out), ref_out, "bf16")
 
 
 @pytest.mark.parametrize("n,k,e", [(700, 4, 32), (6000, 4, 32)])
@@ -332,3 +352,40 @@ def test_round_trip_identity_experts_bf16_exact(hip_device, k, e):
     out = gpu_unpermute(outs["permuted_hidden_states"], wts, outs["inv_permuted_idx"])
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,n", [("decode", 64), ("qwen3", 3000)])
+def test_graph_replay_matches_eager(hip_device, name, n):
+    """permute + unpermute captured in a HIP graph: every replay equals the eager result,
+    with eager work and a poisoning of the outputs between replays."""
+    w, inp = _inputs(name, hip_device, n=n)
+    _say("graph replay %s N=%d" % (name, n))
+    eager = gpu_permute(inp["hidden_states"], inp["topk_ids"], w.num_experts, token_scale=inp["token_scale"])
+    eager_out = gpu_unpermute(inp["expert_output"], inp["topk_weights"], eager["inv_permuted_idx"])
+    torch.cuda.synchronize()
+    ref_bytes = {k: to_np(v).view(np.uint8).copy() for k, v in eager.items() if v is not None}
+    ref_out = to_np(eager_out).view(np.uint8).copy()
+
+    outs = {k: (None if v is None else torch.empty_like(v)) for k, v in eager.items()}
+    ws = poisoned((max(16, binding.moe_permute_workspace_size(w.num_tokens, w.topk, w.num_experts)),),
+                  torch.uint8, hip_device)
+    out = torch.empty_like(eager_out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.moe_permute(inp["hidden_states"], inp["topk_ids"], w.num_experts, outs["permuted_hidden_states"],
+                            outs["expert_first_token_offset"], outs["permuted_idx"], outs["inv_permuted_idx"], ws,
+                            token_scale=inp["token_scale"], permuted_scale=outs["permuted_scale"])
+        binding.moe_unpermute(inp["expert_output"], inp["topk_weights"], outs["inv_permuted_idx"], out)
+    scratch = torch.randn((2048, 2048), device=hip_device)
+    for rep in range(3):
+        for v in list(outs.values()) + [out, ws]:
+            if v is not None:
+                v.view(torch.uint8).fill_(POISON)
+        scratch = scratch @ scratch.T * 1e-3  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            if v is not None:
+                assert np.array_equal(to_np(v).view(np.uint8), ref_bytes[k]), (rep, k)
+        assert np.array_equal(to_np(out).view(np.uint8), ref_out), rep
