@@ -248,84 +248,158 @@ __device__ __forceinline__ void copy_tile_scales(const PermuteArgs& a, int64_t t
 template <int NT, int U>
 __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int tokens_per_tile, int nbits) {
     constexpr int W = NT / kWaveSize;
-    constexpr int kIds = kFusedMaxRows / NT;  // expert ids held per thread
+    constexpr int kIds = kFusedMaxRows / NT;                       // expert ids held per thread
+    constexpr int kBatches = (kMaxTileRows + NT - 1) / NT;         // tile batches of 64 per wave
+    constexpr int kPer = (kMaxExperts + NT - 1) / NT;              // experts per thread in the scan
     static_assert(kFusedMaxRows % NT == 0, "fused row bound must be a multiple of the workgroup size");
     extern __shared__ int smem[];
     const int E = a.num_experts;
     const int K = a.topk;
+    const int w = wave_index();
+    const int lane = threadIdx.x % kWaveSize;
     const int64_t t0 = (int64_t)blockIdx.x * tokens_per_tile;
     const int ntok = (int)min((int64_t)tokens_per_tile, a.num_tokens - t0);
-    const int64_t row0 = t0 * K;
+    const int row0 = (int)(t0 * K);
     const int T = ntok * K;
     const int tile_cap = tokens_per_tile * K;
     const int R = (int)(a.num_tokens * K);  // <= kFusedMaxRows
+    const int span = (T + NT - 1) / NT * kWaveSize;  // tile rows ranked by each wave
 
-    // Every expert id of the problem goes into registers first, then the first
-    // row chunk of this wave: the vector-memory counter retires in issue
-    // order, so the row loads stay in flight while the ids are consumed.
+    // Loads, all independent: every expert id of the problem, this wave's own
+    // tile rows, then the first row chunk(s) of this wave.  The vector-memory
+    // counter retires in issue order, so the row loads stay in flight while
+    // the ids are consumed.
     int idv[kIds];
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
         const int r = (int)threadIdx.x + j * NT;
         idv[j] = a.topk_ids[r < R ? r : R - 1];
     }
+    int tkey[kBatches];
+#pragma unroll
+    for (int b = 0; b < kBatches; ++b) {
+        const int i = w * span + b * kWaveSize + lane;
+        tkey[b] = a.topk_ids[row0 + (i < T ? i : T - 1)];
+    }
     const TileCopy<U> tc(a, t0, ntok);
     u32x4 cur[U];
-    if (a.row_vecs > 0 && wave_index() < tc.items) tc.load(wave_index(), cur);
+    if (a.row_vecs > 0 && w < tc.items) tc.load(w, cur);
 
-    int* before_s = smem;                 // [E] rows before the tile, then the tile's base
-    int* after_s = before_s + E;          // [E] rows after the tile, then offsets
-    int* cnt_s = after_s + E;             // [E] rows inside the tile
-    int* wave_s = cnt_s + E;              // [W * E]
-    int* key_s = wave_s + W * E;          // [tile_cap]
-    int* rank_s = key_s + tile_cap;       // [tile_cap] rank, then destination
-    int* misc_s = rank_s + tile_cap;      // [16]: [0] bad ids, [1..] scan scratch
+    int* before_s = smem;                 // [E] rows before the tile, then the tile's base per expert
+    int* after_s = before_s + E;          // [E] rows after the tile
+    int* wave_s = after_s + E;            // [W * E] per-wave counts inside the tile, then prefixes
+    int* dest_s = wave_s + W * E;         // [tile_cap] destination of each tile row
+    int* misc_s = dest_s + tile_cap;      // [16]: [0] bad ids, [1..W] scan scratch
 
-    for (int i = threadIdx.x; i < (3 + W) * E; i += NT) smem[i] = 0;
+    for (int i = threadIdx.x; i < (2 + W) * E; i += NT) smem[i] = 0;
     if (threadIdx.x < 16) misc_s[threadIdx.x] = 0;
     lds_barrier();
 
+    // Phase 1: counts outside the tile (LDS atomics, order-free) and stable
+    // ranks inside each wave's span of the tile (ballot match + mbcnt).
     int nbad = 0;
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
         const int r = (int)threadIdx.x + j * NT;
-        if (r >= R) continue;
         const int key = idv[j];
         const bool ok = (unsigned)key < (unsigned)E;
-        nbad += ok ? 0 : 1;
-        if (r >= row0 && r < row0 + T)
-            key_s[r - row0] = ok ? key : -1;
-        else if (ok)
-            atomicAdd(r < row0 ? &before_s[key] : &after_s[key], 1);
+        if (r < R && (r < row0 || r >= row0 + T)) {
+            nbad += ok ? 0 : 1;
+            if (ok) atomicAdd(r < row0 ? &before_s[key] : &after_s[key], 1);
+        }
+    }
+    int trank[kBatches];
+    int* run = wave_s + w * E;
+#pragma unroll
+    for (int b = 0; b < kBatches; ++b) {
+        const int base = w * span + b * kWaveSize;
+        trank[b] = 0;
+        if (b * kWaveSize < span && base < T) {  // wave-uniform
+            const int i = base + lane;
+            const bool in_tile = i < T && i < w * span + span;
+            const bool ok = in_tile && (unsigned)tkey[b] < (unsigned)E;
+            nbad += (in_tile && !ok) ? 1 : 0;
+            const uint64_t same = lanes_with_same_key(tkey[b], ok, nbits);
+            const int below = lanes_below(same);
+            if (ok) {
+                const int c = run[tkey[b]];
+                trank[b] = c + below;
+                if (below == 0) run[tkey[b]] = c + (int)__popcll(same);
+            }
+        }
     }
     if (nbad) atomicAdd(&misc_s[0], nbad);
     lds_barrier();
-
-    rank_tile<NT>(key_s, T, E, nbits, rank_s, wave_s, cnt_s);
-
     if (misc_s[0] != 0) {  // every workgroup saw every id, so all take this branch together
         if (blockIdx.x == 0)
             for (int e = threadIdx.x; e <= E; e += NT) a.expert_first_token_offset[e] = -1;
         return;
     }
-    for (int e = threadIdx.x; e < E; e += NT) after_s[e] += before_s[e] + cnt_s[e];
-    lds_barrier();
-    const int total = block_exclusive_scan<NT>(after_s, E, misc_s + 1);
-    if (blockIdx.x == 0) {
-        for (int e = threadIdx.x; e < E; e += NT) a.expert_first_token_offset[e] = after_s[e];
-        if (threadIdx.x == 0) a.expert_first_token_offset[E] = total;
+
+    // Phase 2: per expert, prefix over waves (in place) and the total count;
+    // exclusive scan over experts gives expert_first_token_offset, and the
+    // tile's base in each expert is offset + rows before the tile.
+    int tot[kPer];
+    int s = 0;
+    const int e0 = (int)threadIdx.x * kPer;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int e = e0 + q;
+        tot[q] = 0;
+        if (e < E) {
+            int c = 0;
+#pragma unroll
+            for (int v = 0; v < W; ++v) {
+                const int x = wave_s[v * E + e];
+                wave_s[v * E + e] = c;
+                c += x;
+            }
+            tot[q] = before_s[e] + c + after_s[e];
+        }
+        s += tot[q];
     }
-    for (int e = threadIdx.x; e < E; e += NT) before_s[e] += after_s[e];
+    int x = s;
+#pragma unroll
+    for (int d = 1; d < kWaveSize; d <<= 1) {
+        const int y = __shfl_up(x, d, kWaveSize);
+        if (lane >= d) x += y;
+    }
+    if (lane == kWaveSize - 1) misc_s[1 + w] = x;
     lds_barrier();
-    for (int i = threadIdx.x; i < T; i += NT) {
-        const int dest = before_s[key_s[i]] + rank_s[i];
-        rank_s[i] = dest;
-        a.inv_permuted_idx[row0 + i] = dest;
-        if ((uint32_t)dest < (uint32_t)R) a.permuted_idx[dest] = (int32_t)(row0 + i);
+    int excl = x - s, total = 0;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+        const int c = misc_s[1 + v];
+        excl += v < w ? c : 0;
+        total += c;
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int e = e0 + q;
+        if (e < E) {
+            if (blockIdx.x == 0) a.expert_first_token_offset[e] = excl;
+            before_s[e] += excl;
+            excl += tot[q];
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.expert_first_token_offset[E] = total;
+    lds_barrier();
+
+    // Phase 3: destinations of this wave's tile rows.
+#pragma unroll
+    for (int b = 0; b < kBatches; ++b) {
+        const int i = w * span + b * kWaveSize + lane;
+        if (b * kWaveSize < span && i < T && i < w * span + span) {
+            const int key = tkey[b];
+            const int dest = before_s[key] + wave_s[w * E + key] + trank[b];
+            dest_s[i] = dest;
+            a.inv_permuted_idx[row0 + i] = dest;
+            if ((uint32_t)dest < (uint32_t)R) a.permuted_idx[dest] = row0 + i;
+        }
     }
     lds_barrier();
-    if (a.row_vecs > 0) copy_items_pipelined<U, NT>(tc, cur, rank_s);
-    copy_tile_scales<NT>(a, t0, ntok, rank_s);
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT>(tc, cur, dest_s);
+    copy_tile_scales<NT>(a, t0, ntok, dest_s);
 }
 
 // ----------------------------------------------------------------------------
@@ -537,11 +611,96 @@ __device__ __forceinline__ void accumulate(float (&acc)[U][kBF16 ? 8 : 4], const
     }
 }
 
+// One work item of a compile-time topk: all topk indices and weights are
+// read first (scalar loads, independent of each other), then every row load
+// of the chunk is issued; `finish` weights, sums, rounds and stores.
+template <bool kBF16, int K, int U>
+struct UnpermuteItem {
+    int32_t j[K];
+    float wk[K];
+    u32x4 v[K][U];
+};
+
+template <bool kBF16, int K, int U>
+__device__ __forceinline__ void unpermute_issue(const UnpermuteArgs& a, int64_t item, int64_t nchunks,
+                                                UnpermuteItem<kBF16, K, U>& it) {
+    const int lane = threadIdx.x % kWaveSize;
+    const int64_t rv = a.row_vecs;
+    const int64_t t = item / nchunks;
+    const int64_t base = (item - t * nchunks) * (U * kWaveSize) + lane;
+    const int64_t R = a.num_tokens * K;
+    const u32x4* __restrict__ y = reinterpret_cast<const u32x4*>(a.expanded_output);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        it.j[k] = a.inv_permuted_idx[t * K + k];
+        it.wk[k] = a.topk_weights[t * K + k];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const bool ok = it.j[k] >= 0 && (int64_t)it.j[k] < R;
+        const u32x4* src = y + (int64_t)(ok ? it.j[k] : 0) * rv;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t idx = base + u * kWaveSize;
+            it.v[k][u] = (ok && idx < rv) ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+template <bool kBF16, int K, int U>
+__device__ __forceinline__ void unpermute_finish(const UnpermuteArgs& a, int64_t item, int64_t nchunks,
+                                                 const UnpermuteItem<kBF16, K, U>& it) {
+    constexpr int kEl = kBF16 ? 8 : 4;
+    const int lane = threadIdx.x % kWaveSize;
+    const int64_t rv = a.row_vecs;
+    const int64_t t = item / nchunks;
+    const int64_t base = (item - t * nchunks) * (U * kWaveSize) + lane;
+    const int64_t R = a.num_tokens * K;
+    float acc[U][kEl];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kEl; ++e) acc[u][e] = 0.0f;
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        bad |= !(it.j[k] >= 0 && (int64_t)it.j[k] < R);
+        accumulate<kBF16, U>(acc, it.v[k], it.wk[k]);
+    }
+    u32x4* __restrict__ out = reinterpret_cast<u32x4*>(a.output) + t * rv;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t idx = base + u * kWaveSize;
+        if (idx >= rv) continue;
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (kBF16) {
+                o[q] = bad ? 0x7FC07FC0u : (bf16_bits(acc[u][2 * q]) | (bf16_bits(acc[u][2 * q + 1]) << 16));
+            } else {
+                o[q] = bad ? 0x7FC00000u : __float_as_uint(acc[u][q]);
+            }
+        }
+        __builtin_nontemporal_store(o, out + idx);
+    }
+}
+
 // KC > 0: topk is exactly KC.  KC == 0: runtime topk, rows taken G at a time.
 // One item per wave; only when the grid would exceed kMaxGridBlocks does a
 // wave loop over items g, g + total_waves, ...
 template <bool kBF16, int KC, int U, int G>
 __global__ __launch_bounds__(256) void unpermute_kernel(UnpermuteArgs a, int64_t total_waves) {
+    if constexpr (KC > 0) {
+        const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
+        const int64_t items = a.num_tokens * nchunks;
+        for (int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index(); item < items;
+             item += total_waves) {
+            UnpermuteItem<kBF16, KC, U> it;
+            unpermute_issue<kBF16, KC, U>(a, item, nchunks, it);
+            unpermute_finish<kBF16, KC, U>(a, item, nchunks, it);
+        }
+        return;
+    }
     constexpr int kEl = kBF16 ? 8 : 4;  // elements per 16-byte vector
     constexpr int kGroup = KC > 0 ? KC : G;
     const int lane = threadIdx.x % kWaveSize;
@@ -601,6 +760,33 @@ __global__ __launch_bounds__(256) void unpermute_kernel(UnpermuteArgs a, int64_t
                 }
             }
             __builtin_nontemporal_store(o, out + idx);
+        }
+    }
+}
+
+// Pipelined variant: persistent waves; the loads of a wave's next item are
+// issued before the current item is weighted and stored, so the wave always
+// has reads in flight while it writes, and the in-order vector-memory counter
+// never waits on the wave's own stores.
+template <bool kBF16, int K, int U>
+__global__ __launch_bounds__(256) void unpermute_pipelined_kernel(UnpermuteArgs a, int64_t total_waves) {
+    const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
+    const int64_t items = a.num_tokens * nchunks;
+    int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index();
+    if (item >= items) return;
+    UnpermuteItem<kBF16, K, U> cur;
+    unpermute_issue<kBF16, K, U>(a, item, nchunks, cur);
+    for (;;) {
+        const int64_t nxt = item + total_waves;
+        if (nxt < items) {
+            UnpermuteItem<kBF16, K, U> next;
+            unpermute_issue<kBF16, K, U>(a, nxt, nchunks, next);
+            unpermute_finish<kBF16, K, U>(a, item, nchunks, cur);
+            cur = next;
+            item = nxt;
+        } else {
+            unpermute_finish<kBF16, K, U>(a, item, nchunks, cur);
+            break;
         }
     }
 }
@@ -680,33 +866,55 @@ static hipError_t launch_unpermute_t(const UnpermuteArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Vectors per lane are bounded so that the topk rows of one chunk stay in
-// registers (topk * U <= 16 vectors).
-static constexpr int kUnrollsWide[] = {8, 7, 4, 2, 1};
+
+// Unpermute dispatch.  Measured on MI355X:
+//  * topk <= 2: pipelined persistent waves, 2 vectors per lane, 32 waves per
+//    compute unit (reads of the next chunk overlap the writes of this one);
+//  * larger topk: one item per wave; 2 vectors per lane (4 for topk 4) when
+//    that still gives every compute unit at least kFillWavesPerCU waves,
+//    else 1 vector per lane so that small (decode) batches spread wider.
+static constexpr int kComputeUnits = 256;
+static constexpr int kPipeWavesPerCU = 32;
+static constexpr int kFillWavesPerCU = 16;
+static constexpr int kPipeUnrolls[] = {2, 1};
+
+template <bool kBF16, int K, int U>
+static hipError_t launch_unpermute_pipe_t(const UnpermuteArgs& a, hipStream_t stream) {
+    const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
+    const int64_t items = a.num_tokens * nchunks;
+    const int64_t cap = (int64_t)kComputeUnits * kPipeWavesPerCU;
+    const int64_t waves = items < cap ? items : cap;
+    const int64_t blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((unpermute_pipelined_kernel<kBF16, K, U>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
+                       blocks * 4);
+    return hipGetLastError();
+}
+
+// Widest U in `allowed` (descending) that still fills the machine, else the narrowest.
+static int fill_unroll(const UnpermuteArgs& a, const int* allowed, int n_allowed) {
+    const int64_t groups = (a.row_vecs + kWaveSize - 1) / kWaveSize;
+    for (int i = 0; i < n_allowed; ++i) {
+        const int64_t u = allowed[i];
+        const int64_t items = a.num_tokens * ((groups + u - 1) / u);
+        const bool even = groups * 10 >= (groups + u - 1) / u * u * 9;
+        if (even && items >= (int64_t)kComputeUnits * kFillWavesPerCU) return (int)u;
+    }
+    return allowed[n_allowed - 1];
+}
+
 static constexpr int kUnrolls4[] = {4, 2, 1};
 static constexpr int kUnrolls2[] = {2, 1};
 
 template <bool kBF16, int KC, int G>
 static hipError_t launch_unpermute_k(const UnpermuteArgs& a, hipStream_t stream) {
-    int u;
-    if (KC == 1 || KC == 2)
-        u = choose_unroll(a.row_vecs, kUnrollsWide, 5);
-    else if (KC == 8)
-        u = choose_unroll(a.row_vecs, kUnrolls2, 2);
-    else
-        u = choose_unroll(a.row_vecs, kUnrolls4, 3);
     if constexpr (KC == 1 || KC == 2) {
-        switch (u) {
-            case 8: return launch_unpermute_t<kBF16, KC, 8, G>(a, stream);
-            case 7: return launch_unpermute_t<kBF16, KC, 7, G>(a, stream);
-            case 4: return launch_unpermute_t<kBF16, KC, 4, G>(a, stream);
-            case 2: return launch_unpermute_t<kBF16, KC, 2, G>(a, stream);
-            default: return launch_unpermute_t<kBF16, KC, 1, G>(a, stream);
-        }
+        return choose_unroll(a.row_vecs, kPipeUnrolls, 2) == 2 ? launch_unpermute_pipe_t<kBF16, KC, 2>(a, stream)
+                                                               : launch_unpermute_pipe_t<kBF16, KC, 1>(a, stream);
     } else if constexpr (KC == 8) {
-        return u == 2 ? launch_unpermute_t<kBF16, KC, 2, G>(a, stream) : launch_unpermute_t<kBF16, KC, 1, G>(a, stream);
+        return fill_unroll(a, kUnrolls2, 2) == 2 ? launch_unpermute_t<kBF16, KC, 2, G>(a, stream)
+                                                 : launch_unpermute_t<kBF16, KC, 1, G>(a, stream);
     } else {
-        switch (u) {
+        switch (fill_unroll(a, kUnrolls4, 3)) {
             case 4: return launch_unpermute_t<kBF16, KC, 4, G>(a, stream);
             case 2: return launch_unpermute_t<kBF16, KC, 2, G>(a, stream);
             default: return launch_unpermute_t<kBF16, KC, 1, G>(a, stream);

@@ -121,7 +121,7 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int num_experts) {
 
 // Dynamic LDS bytes of the fused and staged kernels for one tile shape.
 inline size_t fused_lds_bytes(int num_experts, int tile_rows) {
-    return sizeof(int) * ((size_t)(3 + kFusedThreads / kWaveSize) * num_experts + 2 * (size_t)tile_rows + 16);
+    return sizeof(int) * ((size_t)(2 + kFusedThreads / kWaveSize) * num_experts + (size_t)tile_rows + 16);
 }
 inline size_t rank_lds_bytes(int num_experts, int tile_rows) {
     return sizeof(int) * ((size_t)(1 + kRankThreads / kWaveSize) * num_experts + 2 * (size_t)tile_rows + 16);

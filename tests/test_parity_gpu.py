@@ -246,13 +246,14 @@ def test_out_of_range_expert_id_is_reported(hip_device, n, k, e, bad):
         assert np.all(to_np(outs[key]).view(np.uint8) == POISON), key
 
 
-def test_out_of_range_inverse_index_gives_nan_row(hip_device):
-    n, k, h = 64, 4, 128
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 8])
+def test_out_of_range_inverse_index_gives_nan_row(hip_device, k):
+    n, h = 64, 128
     inv = torch.randperm(n * k, dtype=torch.int32).to(hip_device)
-    inv[10 * k + 2] = n * k  # token 10 points past the end
+    inv[10 * k + (k - 1)] = n * k  # token 10 points past the end
     y = torch.randn((n * k, h), device=hip_device).to(torch.bfloat16)
-    wts = torch.full((n, k), 0.25, device=hip_device)
-    _say("bad inverse index")
+    wts = torch.full((n, k), 1.0 / k, device=hip_device)
+    _say("bad inverse index topk=%d" % k)
     out = gpu_unpermute(y, wts, inv)
     torch.cuda.synchronize()
     o = out.float().cpu()
