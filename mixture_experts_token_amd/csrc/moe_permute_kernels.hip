@@ -163,7 +163,7 @@ __device__ void rank_tile(const int* key_s, int tile_rows, int E, int nbits, int
 // of U*64 16-byte vectors); wave w takes items w, w+W, ...  dest_s[tl*topk+k]
 // is the permuted row of the tile's token tl, slot k.
 // ----------------------------------------------------------------------------
-template <int U>
+template <int U, bool kNTStore>
 struct TileCopy {
     const u32x4* __restrict__ src;  // first row of the tile
     u32x4* __restrict__ dst;        // permuted_hidden_states
@@ -205,7 +205,12 @@ struct TileCopy {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t idx = base + u * kWaveSize;
-                if (idx < rv) __builtin_nontemporal_store(v[u], o + idx);
+                if (idx < rv) {
+                    if constexpr (kNTStore)
+                        __builtin_nontemporal_store(v[u], o + idx);
+                    else
+                        o[idx] = v[u];
+                }
             }
         }
     }
@@ -213,8 +218,9 @@ struct TileCopy {
 
 // Store every item of wave w, starting from `cur` (already loaded for item w),
 // loading item it+W while item it is stored.
-template <int U, int NT>
-__device__ __forceinline__ void copy_items_pipelined(const TileCopy<U>& tc, u32x4 (&cur)[U], const int* dest_s) {
+template <int U, int NT, bool kNTStore>
+__device__ __forceinline__ void copy_items_pipelined(const TileCopy<U, kNTStore>& tc, u32x4 (&cur)[U],
+                                                     const int* dest_s) {
     constexpr int W = NT / kWaveSize;
     for (int it = wave_index(); it < tc.items; it += W) {
         u32x4 nxt[U];
@@ -245,7 +251,7 @@ __device__ __forceinline__ void copy_tile_scales(const PermuteArgs& a, int64_t t
 // ranks its own rows, derives expert_first_token_offset and its own base per
 // expert, scatters permuted_idx / inv_permuted_idx and copies its rows.
 // ----------------------------------------------------------------------------
-template <int NT, int U>
+template <int NT, int U, bool kNTStore>
 __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int tokens_per_tile, int nbits) {
     constexpr int W = NT / kWaveSize;
     constexpr int kIds = kFusedMaxRows / NT;                       // expert ids held per thread
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
         const int i = w * span + b * kWaveSize + lane;
         tkey[b] = a.topk_ids[row0 + (i < T ? i : T - 1)];
     }
-    const TileCopy<U> tc(a, t0, ntok);
+    const TileCopy<U, kNTStore> tc(a, t0, ntok);
     u32x4 cur[U];
     if (a.row_vecs > 0 && w < tc.items) tc.load(w, cur);
 
@@ -398,7 +404,7 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
         }
     }
     lds_barrier();
-    if (a.row_vecs > 0) copy_items_pipelined<U, NT>(tc, cur, dest_s);
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore>(tc, cur, dest_s);
     copy_tile_scales<NT>(a, t0, ntok, dest_s);
 }
 
@@ -501,7 +507,7 @@ __global__ __launch_bounds__(NT) void permute_scan_tiles_kernel(int32_t* tile_hi
 // Staged permute, kernel 3: offsets from the per-expert totals, destinations
 // from offset + tile base + rank, index scatter, and the row copy.
 // ----------------------------------------------------------------------------
-template <int NT, int U>
+template <int NT, int U, bool kNTStore>
 __global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int tokens_per_tile, int64_t num_tiles,
                                                              const int32_t* rank_ws, const int32_t* tile_base,
                                                              const int32_t* total) {
@@ -534,7 +540,7 @@ __global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int 
         key[j] = a.topk_ids[r];
         rk[j] = rank_ws[r];
     }
-    const TileCopy<U> tc(a, t0, ntok);
+    const TileCopy<U, kNTStore> tc(a, t0, ntok);
     u32x4 cur[U];
     if (a.row_vecs > 0 && wave_index() < tc.items) tc.load(wave_index(), cur);
 
@@ -571,7 +577,7 @@ __global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int 
         if ((uint32_t)dest < (uint64_t)R) a.permuted_idx[dest] = (int32_t)(row0 + i);
     }
     lds_barrier();
-    if (a.row_vecs > 0) copy_items_pipelined<U, NT>(tc, cur, dest_s);
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore>(tc, cur, dest_s);
     copy_tile_scales<NT>(a, t0, ntok, dest_s);
 }
 
@@ -801,18 +807,40 @@ hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t value, hip
     return hipGetLastError();
 }
 
+// Row stores: plain stores when each row fans out to many destinations and
+// the permuted output is large (measured faster for 8-way fan-out at 256 MiB
+// and above); non-temporal otherwise (faster for 2-way fan-out and for small
+// outputs).  Measured with buffer rotation well beyond the last-level cache.
+static constexpr int kPlainStoreMinTopk = 4;
+static constexpr int64_t kPlainStoreMinBytes = int64_t(32) << 20;
+
+static bool plain_row_stores(const PermuteArgs& a) {
+    return a.topk >= kPlainStoreMinTopk && a.num_tokens * a.topk * a.row_vecs * 16 >= kPlainStoreMinBytes;
+}
+
 template <int U>
 static void launch_fused_u(const PermuteArgs& a, const PermutePlan& p, hipStream_t stream) {
-    hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U>), dim3((unsigned)p.num_tiles), dim3(kFusedThreads),
-                       fused_lds_bytes(a.num_experts, p.tile_rows), stream, a, p.tokens_per_tile, p.nbits);
+    const size_t lds = fused_lds_bytes(a.num_experts, p.tile_rows);
+    if (plain_row_stores(a))
+        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, false>), dim3((unsigned)p.num_tiles),
+                           dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile, p.nbits);
+    else
+        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, true>), dim3((unsigned)p.num_tiles),
+                           dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile, p.nbits);
 }
 
 template <int U>
 static void launch_scatter_u(const PermuteArgs& a, const PermutePlan& p, const int32_t* rank_ws,
                              const int32_t* tile_base, const int32_t* total, hipStream_t stream) {
-    hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U>), dim3((unsigned)p.num_tiles),
-                       dim3(kScatterThreads), scatter_lds_bytes(a.num_experts, p.tile_rows), stream, a,
-                       p.tokens_per_tile, p.num_tiles, rank_ws, tile_base, total);
+    const size_t lds = scatter_lds_bytes(a.num_experts, p.tile_rows);
+    if (plain_row_stores(a))
+        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, false>), dim3((unsigned)p.num_tiles),
+                           dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
+                           total);
+    else
+        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, true>), dim3((unsigned)p.num_tiles),
+                           dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
+                           total);
 }
 
 #define MOE_DISPATCH_U(u, CALL) \
