@@ -85,19 +85,21 @@ def _dtype_code(t) -> int:
 
 
 def _ptr(t):
+    """Raw device address of a contiguous tensor (None stays None)."""
     if t is None:
         return None
     if not t.is_contiguous():
         raise ValueError("tensors passed to the MoE library must be contiguous")
-    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else None
+    return t.data_ptr()
 
 
-def _stream(stream, device):
+def _stream(stream, t):
+    """hipStream_t handle: the given torch stream, else torch's current stream on t's device."""
+    if stream is not None:
+        return stream.cuda_stream
     import torch
 
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+    return torch._C._cuda_getCurrentRawStream(t.get_device())
 
 
 def moe_permute_supported(device: int = 0) -> bool:
@@ -131,7 +133,7 @@ def moe_permute(hidden_states, topk_ids, num_experts: int, permuted_hidden_state
         _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), n, hsize, topk, int(num_experts),
         _ptr(permuted_hidden_states) if hsize else None, _ptr(permuted_scale),
         _ptr(expert_first_token_offset), _ptr(permuted_idx), _ptr(inv_permuted_idx),
-        _ptr(workspace), ws_bytes, _stream(stream, topk_ids.device))
+        _ptr(workspace), ws_bytes, _stream(stream, topk_ids))
     if status != MOE_OK:
         raise MoEError(status, "moe_permute")
 
@@ -146,7 +148,7 @@ def moe_unpermute(expanded_output, topk_weights, inv_permuted_idx, output, strea
     n, topk = topk_weights.shape
     status = load_library().moe_unpermute(
         _ptr(expanded_output), _dtype_code(expanded_output), _ptr(topk_weights), _ptr(inv_permuted_idx),
-        n, expanded_output.shape[-1], topk, _ptr(output), _stream(stream, output.device))
+        n, expanded_output.shape[-1], topk, _ptr(output), _stream(stream, output))
     if status != MOE_OK:
         raise MoEError(status, "moe_unpermute")
 

@@ -617,9 +617,14 @@ __device__ __forceinline__ void accumulate(float (&acc)[U][kBF16 ? 8 : 4], const
     }
 }
 
+// Unpermute kernels take separate __restrict__ pointers (not a struct) so the
+// compiler can prove the index / weight reads are never clobbered by the
+// output stores, which keeps those wave-uniform reads on the scalar path,
+// off the in-order vector-memory counter that the row loads use.
+
 // One work item of a compile-time topk: all topk indices and weights are
-// read first (scalar loads, independent of each other), then every row load
-// of the chunk is issued; `finish` weights, sums, rounds and stores.
+// read first (independent of each other), then every row load of the chunk
+// is issued; `finish` weights, sums, rounds and stores.
 template <bool kBF16, int K, int U>
 struct UnpermuteItem {
     int32_t j[K];
@@ -628,18 +633,13 @@ struct UnpermuteItem {
 };
 
 template <bool kBF16, int K, int U>
-__device__ __forceinline__ void unpermute_issue(const UnpermuteArgs& a, int64_t item, int64_t nchunks,
-                                                UnpermuteItem<kBF16, K, U>& it) {
-    const int lane = threadIdx.x % kWaveSize;
-    const int64_t rv = a.row_vecs;
-    const int64_t t = item / nchunks;
-    const int64_t base = (item - t * nchunks) * (U * kWaveSize) + lane;
-    const int64_t R = a.num_tokens * K;
-    const u32x4* __restrict__ y = reinterpret_cast<const u32x4*>(a.expanded_output);
+__device__ __forceinline__ void unpermute_issue(const u32x4* __restrict__ y, const float* __restrict__ wts,
+                                                const int32_t* __restrict__ inv, int64_t R, int64_t rv, int64_t t,
+                                                int64_t base, UnpermuteItem<kBF16, K, U>& it) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        it.j[k] = a.inv_permuted_idx[t * K + k];
-        it.wk[k] = a.topk_weights[t * K + k];
+        it.j[k] = inv[t * K + k];
+        it.wk[k] = wts[t * K + k];
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -653,27 +653,9 @@ __device__ __forceinline__ void unpermute_issue(const UnpermuteArgs& a, int64_t 
     }
 }
 
-template <bool kBF16, int K, int U>
-__device__ __forceinline__ void unpermute_finish(const UnpermuteArgs& a, int64_t item, int64_t nchunks,
-                                                 const UnpermuteItem<kBF16, K, U>& it) {
-    constexpr int kEl = kBF16 ? 8 : 4;
-    const int lane = threadIdx.x % kWaveSize;
-    const int64_t rv = a.row_vecs;
-    const int64_t t = item / nchunks;
-    const int64_t base = (item - t * nchunks) * (U * kWaveSize) + lane;
-    const int64_t R = a.num_tokens * K;
-    float acc[U][kEl];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int e = 0; e < kEl; ++e) acc[u][e] = 0.0f;
-    bool bad = false;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        bad |= !(it.j[k] >= 0 && (int64_t)it.j[k] < R);
-        accumulate<kBF16, U>(acc, it.v[k], it.wk[k]);
-    }
-    u32x4* __restrict__ out = reinterpret_cast<u32x4*>(a.output) + t * rv;
+template <bool kBF16, int U>
+__device__ __forceinline__ void store_outputs(u32x4* __restrict__ out, int64_t rv, int64_t base,
+                                              const float (&acc)[U][kBF16 ? 8 : 4], bool bad) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t idx = base + u * kWaveSize;
@@ -691,108 +673,87 @@ __device__ __forceinline__ void unpermute_finish(const UnpermuteArgs& a, int64_t
     }
 }
 
-// KC > 0: topk is exactly KC.  KC == 0: runtime topk, rows taken G at a time.
-// One item per wave; only when the grid would exceed kMaxGridBlocks does a
-// wave loop over items g, g + total_waves, ...
-template <bool kBF16, int KC, int U, int G>
-__global__ __launch_bounds__(256) void unpermute_kernel(UnpermuteArgs a, int64_t total_waves) {
-    if constexpr (KC > 0) {
-        const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
-        const int64_t items = a.num_tokens * nchunks;
-        for (int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index(); item < items;
-             item += total_waves) {
-            UnpermuteItem<kBF16, KC, U> it;
-            unpermute_issue<kBF16, KC, U>(a, item, nchunks, it);
-            unpermute_finish<kBF16, KC, U>(a, item, nchunks, it);
-        }
-        return;
+template <bool kBF16, int K, int U>
+__device__ __forceinline__ void unpermute_finish(u32x4* __restrict__ out, int64_t R, int64_t rv, int64_t t,
+                                                 int64_t base, const UnpermuteItem<kBF16, K, U>& it) {
+    constexpr int kEl = kBF16 ? 8 : 4;
+    float acc[U][kEl];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kEl; ++e) acc[u][e] = 0.0f;
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        bad |= !(it.j[k] >= 0 && (int64_t)it.j[k] < R);
+        accumulate<kBF16, U>(acc, it.v[k], it.wk[k]);
     }
-    constexpr int kEl = kBF16 ? 8 : 4;  // elements per 16-byte vector
-    constexpr int kGroup = KC > 0 ? KC : G;
-    const int lane = threadIdx.x % kWaveSize;
-    const int64_t rv = a.row_vecs;
-    const int64_t nchunks = (rv + U * kWaveSize - 1) / (U * kWaveSize);
-    const int64_t items = a.num_tokens * nchunks;
-    const int K = KC > 0 ? KC : a.topk;
-    const int64_t R = a.num_tokens * K;
-    const u32x4* __restrict__ y = reinterpret_cast<const u32x4*>(a.expanded_output);
-    u32x4* __restrict__ out_base = reinterpret_cast<u32x4*>(a.output);
-
-    for (int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index(); item < items; item += total_waves) {
-        const int64_t t = item / nchunks;
-        const int64_t base = (item - t * nchunks) * (U * kWaveSize) + lane;
-        const int32_t* inv = a.inv_permuted_idx + t * K;
-        const float* wt = a.topk_weights + t * K;
-
-        float acc[U][kEl];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < kEl; ++e) acc[u][e] = 0.0f;
-        bool bad = false;
-        for (int k0 = 0; k0 < K; k0 += kGroup) {
-            u32x4 v[kGroup][U];
-            float wk[kGroup];
-#pragma unroll
-            for (int g = 0; g < kGroup; ++g) {
-                const bool live = KC > 0 || k0 + g < K;
-                const int32_t j = live ? inv[k0 + g] : 0;
-                const bool ok = live && j >= 0 && (int64_t)j < R;
-                bad |= live && !ok;
-                wk[g] = live ? wt[k0 + g] : 0.0f;
-                const u32x4* src = y + (int64_t)(ok ? j : 0) * rv;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int64_t idx = base + u * kWaveSize;
-                    v[g][u] = (ok && idx < rv) ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-#pragma unroll
-            for (int g = 0; g < kGroup; ++g)
-                if (KC > 0 || k0 + g < K) accumulate<kBF16, U>(acc, v[g], wk[g]);
-        }
-        u32x4* __restrict__ out = out_base + t * rv;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t idx = base + u * kWaveSize;
-            if (idx >= rv) continue;
-            u32x4 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if constexpr (kBF16) {
-                    o[q] = bad ? 0x7FC07FC0u : (bf16_bits(acc[u][2 * q]) | (bf16_bits(acc[u][2 * q + 1]) << 16));
-                } else {
-                    o[q] = bad ? 0x7FC00000u : __float_as_uint(acc[u][q]);
-                }
-            }
-            __builtin_nontemporal_store(o, out + idx);
-        }
-    }
+    store_outputs<kBF16, U>(out + t * rv, rv, base, acc, bad);
 }
 
-// Pipelined variant: persistent waves; the loads of a wave's next item are
-// issued before the current item is weighted and stored, so the wave always
-// has reads in flight while it writes, and the in-order vector-memory counter
-// never waits on the wave's own stores.
-template <bool kBF16, int K, int U>
-__global__ __launch_bounds__(256) void unpermute_pipelined_kernel(UnpermuteArgs a, int64_t total_waves) {
-    const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
-    const int64_t items = a.num_tokens * nchunks;
-    int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index();
-    if (item >= items) return;
-    UnpermuteItem<kBF16, K, U> cur;
-    unpermute_issue<kBF16, K, U>(a, item, nchunks, cur);
-    for (;;) {
-        const int64_t nxt = item + total_waves;
-        if (nxt < items) {
-            UnpermuteItem<kBF16, K, U> next;
-            unpermute_issue<kBF16, K, U>(a, nxt, nchunks, next);
-            unpermute_finish<kBF16, K, U>(a, item, nchunks, cur);
-            cur = next;
-            item = nxt;
+// Item -> (token, first vector of this lane).  The token is the same for the
+// whole wave, which readfirstlane makes explicit.
+__device__ __forceinline__ void item_position(int64_t item, int64_t nchunks, int chunk_vecs, int64_t& t,
+                                              int64_t& base) {
+    t = __builtin_amdgcn_readfirstlane((int)(item / nchunks));
+    base = (item - t * nchunks) * chunk_vecs + (int)(threadIdx.x % kWaveSize);
+}
+
+// KC > 0: topk is exactly KC.  KC == 0: runtime topk, rows taken G at a time.
+// One item (token, chunk of U*64 vectors) per wave; only when the grid would
+// exceed kMaxGridBlocks does a wave loop over items g, g + total_waves, ...
+template <bool kBF16, int KC, int U, int G>
+__global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict__ y, const float* __restrict__ wts,
+                                                        const int32_t* __restrict__ inv, u32x4* __restrict__ out,
+                                                        int64_t num_tokens, int64_t rv, int topk,
+                                                        int64_t total_waves) {
+    constexpr int kEl = kBF16 ? 8 : 4;  // elements per 16-byte vector
+    constexpr int kGroup = KC > 0 ? KC : G;
+    const int64_t nchunks = (rv + U * kWaveSize - 1) / (U * kWaveSize);
+    const int64_t items = num_tokens * nchunks;
+    const int K = KC > 0 ? KC : topk;
+    const int64_t R = num_tokens * K;
+    for (int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index(); item < items; item += total_waves) {
+        int64_t t, base;
+        item_position(item, nchunks, U * kWaveSize, t, base);
+        if constexpr (KC > 0) {
+            UnpermuteItem<kBF16, KC, U> it;
+            unpermute_issue<kBF16, KC, U>(y, wts, inv, R, rv, t, base, it);
+            unpermute_finish<kBF16, KC, U>(out, R, rv, t, base, it);
         } else {
-            unpermute_finish<kBF16, K, U>(a, item, nchunks, cur);
-            break;
+            float acc[U][kEl];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < kEl; ++e) acc[u][e] = 0.0f;
+            bool bad = false;
+            for (int k0 = 0; k0 < K; k0 += kGroup) {
+                int32_t j[kGroup];
+                float wk[kGroup];
+#pragma unroll
+                for (int g = 0; g < kGroup; ++g) {
+                    const bool live = k0 + g < K;
+                    j[g] = live ? inv[t * K + k0 + g] : 0;
+                    wk[g] = live ? wts[t * K + k0 + g] : 0.0f;
+                }
+                u32x4 v[kGroup][U];
+#pragma unroll
+                for (int g = 0; g < kGroup; ++g) {
+                    const bool live = k0 + g < K;
+                    const bool ok = live && j[g] >= 0 && (int64_t)j[g] < R;
+                    bad |= live && !ok;
+                    const u32x4* src = y + (int64_t)(ok ? j[g] : 0) * rv;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int64_t idx = base + u * kWaveSize;
+                        v[g][u] = (ok && idx < rv) ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < kGroup; ++g)
+                    if (k0 + g < K) accumulate<kBF16, U>(acc, v[g], wk[g]);
+            }
+            store_outputs<kBF16, U>(out + t * rv, rv, base, acc, bad);
         }
     }
 }
@@ -800,7 +761,11 @@ __global__ __launch_bounds__(256) void unpermute_pipelined_kernel(UnpermuteArgs 
 // ----------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------
+// Vectors per lane in the permute row copy: up to 8 while a row has few
+// copies (2-way fan-out measured best with full-row chunks), up to 4 for
+// 4-way and wider fan-out (measured slightly faster: more waves in flight).
 static constexpr int kCopyUnrolls[] = {8, 7, 6, 5, 4, 3, 2, 1};
+static constexpr int kCopyUnrollsWideFanout[] = {4, 3, 2, 1};
 
 hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t value, hipStream_t stream) {
     hipLaunchKernelGGL(fill_offsets_kernel, dim3(1), dim3(256), 0, stream, off, num_experts + 1, value);
@@ -857,7 +822,8 @@ static void launch_scatter_u(const PermuteArgs& a, const PermutePlan& p, const i
 
 hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream) {
     const int E = a.num_experts;
-    const int u = choose_unroll(a.row_vecs, kCopyUnrolls, 8);
+    const int u = a.topk >= 4 ? choose_unroll(a.row_vecs, kCopyUnrollsWideFanout, 4)
+                              : choose_unroll(a.row_vecs, kCopyUnrolls, 8);
     if (p.fused) {
 #define MOE_FUSED(U) launch_fused_u<U>(a, p, stream)
         MOE_DISPATCH_U(u, MOE_FUSED)
@@ -889,65 +855,21 @@ static hipError_t launch_unpermute_t(const UnpermuteArgs& a, hipStream_t stream)
     const int64_t items = a.num_tokens * nchunks;
     const int64_t blocks_needed = (items + 3) / 4;
     const int64_t blocks = blocks_needed < kMaxGridBlocks ? blocks_needed : kMaxGridBlocks;
-    hipLaunchKernelGGL((unpermute_kernel<kBF16, KC, U, G>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
-                       blocks * 4);
+    hipLaunchKernelGGL((unpermute_kernel<kBF16, KC, U, G>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const u32x4*>(a.expanded_output), a.topk_weights, a.inv_permuted_idx,
+                       reinterpret_cast<u32x4*>(a.output), a.num_tokens, a.row_vecs, a.topk, blocks * 4);
     return hipGetLastError();
 }
 
 
-// Unpermute dispatch.  Measured on MI355X:
-//  * topk <= 2: pipelined persistent waves, 2 vectors per lane, 32 waves per
-//    compute unit (reads of the next chunk overlap the writes of this one);
-//  * larger topk: one item per wave; 2 vectors per lane (4 for topk 4) when
-//    that still gives every compute unit at least kFillWavesPerCU waves,
-//    else 1 vector per lane so that small (decode) batches spread wider.
-static constexpr int kComputeUnits = 256;
-static constexpr int kPipeWavesPerCU = 32;
-static constexpr int kFillWavesPerCU = 16;
-static constexpr int kPipeUnrolls[] = {2, 1};
-
-template <bool kBF16, int K, int U>
-static hipError_t launch_unpermute_pipe_t(const UnpermuteArgs& a, hipStream_t stream) {
-    const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
-    const int64_t items = a.num_tokens * nchunks;
-    const int64_t cap = (int64_t)kComputeUnits * kPipeWavesPerCU;
-    const int64_t waves = items < cap ? items : cap;
-    const int64_t blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((unpermute_pipelined_kernel<kBF16, K, U>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
-                       blocks * 4);
-    return hipGetLastError();
-}
-
-// Widest U in `allowed` (descending) that still fills the machine, else the narrowest.
-static int fill_unroll(const UnpermuteArgs& a, const int* allowed, int n_allowed) {
-    const int64_t groups = (a.row_vecs + kWaveSize - 1) / kWaveSize;
-    for (int i = 0; i < n_allowed; ++i) {
-        const int64_t u = allowed[i];
-        const int64_t items = a.num_tokens * ((groups + u - 1) / u);
-        const bool even = groups * 10 >= (groups + u - 1) / u * u * 9;
-        if (even && items >= (int64_t)kComputeUnits * kFillWavesPerCU) return (int)u;
-    }
-    return allowed[n_allowed - 1];
-}
-
-static constexpr int kUnrolls4[] = {4, 2, 1};
-static constexpr int kUnrolls2[] = {2, 1};
-
+// Unpermute dispatch: one item per wave, one 16-byte vector per lane (a
+// chunk is 64 vectors = 1 KiB of each of the topk rows).  Measured on MI355X
+// against 2, 4 and 7-8 vectors per lane and against persistent pipelined
+// waves: the narrowest chunks, i.e. the most waves in flight, were fastest for
+// every workload once the index reads stayed on the scalar path.
 template <bool kBF16, int KC, int G>
 static hipError_t launch_unpermute_k(const UnpermuteArgs& a, hipStream_t stream) {
-    if constexpr (KC == 1 || KC == 2) {
-        return choose_unroll(a.row_vecs, kPipeUnrolls, 2) == 2 ? launch_unpermute_pipe_t<kBF16, KC, 2>(a, stream)
-                                                               : launch_unpermute_pipe_t<kBF16, KC, 1>(a, stream);
-    } else if constexpr (KC == 8) {
-        return fill_unroll(a, kUnrolls2, 2) == 2 ? launch_unpermute_t<kBF16, KC, 2, G>(a, stream)
-                                                 : launch_unpermute_t<kBF16, KC, 1, G>(a, stream);
-    } else {
-        switch (fill_unroll(a, kUnrolls4, 3)) {
-            case 4: return launch_unpermute_t<kBF16, KC, 4, G>(a, stream);
-            case 2: return launch_unpermute_t<kBF16, KC, 2, G>(a, stream);
-            default: return launch_unpermute_t<kBF16, KC, 1, G>(a, stream);
-        }
-    }
+    return launch_unpermute_t<kBF16, KC, 1, G>(a, stream);
 }
 
 template <bool kBF16>
