@@ -53,8 +53,11 @@ def algorithmic_bytes(w) -> dict:
 
 
 def kernel_source_digest() -> str:
+    """SHA-256 over the permute library's sources (what the counters were taken on)."""
+    from mixture_experts_token_amd import build_lib
+
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(build_lib.SOURCES + build_lib.HEADERS):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -77,6 +80,21 @@ def load_traffic(workload: str, op: str):
     if rec.get("kernel_source_sha256") != kernel_source_digest():
         return None, kernels
     return entry.get("hbm_bytes_per_call"), kernels
+
+
+def load_probe():
+    """libhbm_probe.so (streaming-ceiling kernels built beside the library), or None."""
+    import ctypes
+
+    path = os.path.join(ROOT, "mixture_experts_token_amd", "libhbm_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    for fn in (lib.hbm_probe_fanout, lib.hbm_probe_reduce):
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                       ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    return lib
 
 
 def cpu_baseline(inputs_host, w, budget_s: float = 10.0, max_reps: int = 50) -> dict:
@@ -216,6 +234,41 @@ def main() -> int:
     # rotation) between one pair of HIP events on the kernels' stream.
     perm_avg, _ = timed(lambda i: permute(sets[i % nsets]), k)
     unperm_avg, _ = timed(lambda i: unpermute(sets[i % nsets]), k)
+    # Same-run streaming ceiling for each operation's byte mix: plain fan-out and
+    # reduce kernels (no index work, contiguous destinations) over the same
+    # rotating buffers; the fastest of 1/2/4/8 vectors per lane with
+    # non-temporal or plain stores counts.
+    ceiling = None
+    probe = load_probe()
+    if probe is not None:
+        dev_index = dev.index if dev.index is not None else 0
+        xrow = w.hidden_size * W.ELEMENT_BYTES[w.hidden_dtype]
+        yrow = w.hidden_size * W.ELEMENT_BYTES[w.output_dtype]
+
+        def probe_fan(i, variant):
+            s = sets[i % nsets]
+            rc = probe.hbm_probe_fanout(s["x"].data_ptr(), s["xp"].data_ptr(), w.num_tokens, xrow, w.topk, variant,
+                                        torch._C._cuda_getCurrentRawStream(dev_index))
+            assert rc == 0, rc
+
+        def probe_red(i, variant):
+            s = sets[i % nsets]
+            rc = probe.hbm_probe_reduce(s["y"].data_ptr(), s["out"].data_ptr(), w.num_tokens, yrow, w.topk, variant,
+                                        torch._C._cuda_getCurrentRawStream(dev_index))
+            assert rc == 0, rc
+
+        fan_us = min(timed(lambda i: probe_fan(i, v), k)[0] for v in range(8))
+        red_us = min(timed(lambda i: probe_red(i, v), k)[0] for v in range(8))
+        fan_bytes = (1 + w.topk) * w.num_tokens * xrow
+        red_bytes = (1 + w.topk) * w.num_tokens * yrow
+        step_ceiling = (fan_bytes + red_bytes) / ((fan_us + red_us) * 1e-6) / 1e9
+        ceiling = {"kind": "same-run streaming probe: same byte mix, no index work, contiguous destinations",
+                   "permute_GBps": round(fan_bytes / (fan_us * 1e-6) / 1e9, 1),
+                   "unpermute_GBps": round(red_bytes / (red_us * 1e-6) / 1e9, 1),
+                   "step_GBps": round(step_ceiling, 1),
+                   "pct_of_step_ceiling": round(100 * value / step_ceiling, 2)}
+        torch.cuda.synchronize(dev)
+
     tiny = torch.zeros(1, device=dev)
     floor_args = args.graph
     launch_floor_us = timed(lambda i: tiny.add_(1.0), k)[0] if floor_args else None
@@ -264,6 +317,7 @@ def main() -> int:
         "unpermute_GBps": round(nb["unpermute"] / (unperm_avg * 1e-6) / 1e9, 1),
         "algorithmic_bytes_per_step": nb["total"],
         "wall_s_timed_region": round(wall, 4),
+        "ceiling": ceiling,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

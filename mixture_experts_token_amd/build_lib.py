@@ -18,8 +18,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_permute.so")
+PROBE_LIB = os.path.join(PKG, "libhbm_probe.so")
 
 SOURCES = ["moe_permute_kernels.hip", "moe_permute_api.cpp"]
+HEADERS = ["moe_launch.h", "moe_plan.h"]
+PROBE_SOURCES = ["hbm_probe.hip"]  # streaming-ceiling kernels used by bench.py only
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -38,9 +41,14 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
+    _build_one(PROBE_LIB, PROBE_SOURCES, verbose)
+    return _build_one(LIB, SOURCES, verbose)
+
+
+def _build_one(target: str, sources, verbose: bool) -> str:
+    tmp = target + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
+           *[os.path.join(CSRC, s) for s in sources]]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,8 +58,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":

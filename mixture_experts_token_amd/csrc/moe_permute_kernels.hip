@@ -246,6 +246,133 @@ __device__ __forceinline__ void copy_tile_scales(const PermuteArgs& a, int64_t t
 }
 
 // ----------------------------------------------------------------------------
+// Tile phases shared by the fused and coarse schedules.  A tile is a run of
+// whole tokens (T expanded rows from row0); wave w ranks tile rows
+// [w*span, w*span + span), span = ceil(T / NT) * 64, at most kB batches of 64.
+// ----------------------------------------------------------------------------
+
+// Expert ids of this wave's tile rows (issued early, independent loads).
+template <int kB>
+__device__ __forceinline__ void load_tile_keys(const int32_t* __restrict__ ids, int row0, int T, int span, int w,
+                                               int lane, int (&tkey)[kB]) {
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+        const int i = w * span + b * kWaveSize + lane;
+        tkey[b] = ids[row0 + (i < T ? i : T - 1)];
+    }
+}
+
+__device__ __forceinline__ bool own_row(int b, int i, int T, int span, int w) {
+    return b * kWaveSize < span && i < T && i < w * span + span;
+}
+
+// Stable ranks of this wave's tile rows among the wave's rows with the same
+// expert (ballot match + mbcnt); the lowest lane of each equal-key group adds
+// the group size to the wave's running count run[key].  Returns the number of
+// out-of-range ids among the wave's rows (this lane's share).
+template <int kB>
+__device__ __forceinline__ int rank_own_rows(const int (&tkey)[kB], int T, int span, int E, int nbits, int w,
+                                             int lane, int* run, int (&trank)[kB]) {
+    int nbad = 0;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+        const int base = w * span + b * kWaveSize;
+        trank[b] = 0;
+        if (b * kWaveSize < span && base < T) {  // wave-uniform
+            const int i = base + lane;
+            const bool in_tile = own_row(b, i, T, span, w);
+            const bool ok = in_tile && (unsigned)tkey[b] < (unsigned)E;
+            nbad += (in_tile && !ok) ? 1 : 0;
+            const uint64_t same = lanes_with_same_key(tkey[b], ok, nbits);
+            const int below = lanes_below(same);
+            if (ok) {
+                const int c = run[tkey[b]];
+                trank[b] = c + below;
+                if (below == 0) run[tkey[b]] = c + (int)__popcll(same);
+            }
+        }
+    }
+    return nbad;
+}
+
+// Per expert e (kPer consecutive experts per thread): turn the per-wave counts
+// wave_s[v*E + e] into prefixes over waves, take the expert's total rows
+// total_of(e, rows_in_tile), scan the totals over experts (one barrier) into
+// expert_first_token_offset (written when write_off), and store the tile's
+// base in each expert, offset + before_of(e), into base_s[e].  Each expert is
+// read and written by one thread only, so base_s may alias before_of's data.
+template <int NT, int kPer, class TotalFn, class BeforeFn>
+__device__ __forceinline__ void expert_bases(int E, int* wave_s, int* base_s, int* scan_tmp, int64_t* off_out,
+                                             bool write_off, TotalFn total_of, BeforeFn before_of) {
+    constexpr int W = NT / kWaveSize;
+    const int w = threadIdx.x / kWaveSize, lane = threadIdx.x % kWaveSize;
+    int tot[kPer];
+    int s = 0;
+    const int e0 = (int)threadIdx.x * kPer;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int e = e0 + q;
+        tot[q] = 0;
+        if (e < E) {
+            int c = 0;
+#pragma unroll
+            for (int v = 0; v < W; ++v) {
+                const int x = wave_s[v * E + e];
+                wave_s[v * E + e] = c;
+                c += x;
+            }
+            tot[q] = total_of(e, c);
+        }
+        s += tot[q];
+    }
+    int x = s;
+#pragma unroll
+    for (int d = 1; d < kWaveSize; d <<= 1) {
+        const int y = __shfl_up(x, d, kWaveSize);
+        if (lane >= d) x += y;
+    }
+    if (lane == kWaveSize - 1) scan_tmp[w] = x;
+    lds_barrier();
+    int excl = x - s, total = 0;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+        const int c = scan_tmp[v];
+        excl += v < w ? c : 0;
+        total += c;
+    }
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int e = e0 + q;
+        if (e < E) {
+            if (write_off) off_out[e] = excl;
+            base_s[e] = excl + before_of(e);
+            excl += tot[q];
+        }
+    }
+    if (write_off && threadIdx.x == 0) off_out[E] = total;
+}
+
+// Destinations of this wave's tile rows: tile base + rows of the same expert
+// in earlier waves + rank within the wave.
+template <int kB>
+__device__ __forceinline__ void write_dests(const PermuteArgs& a, const int (&tkey)[kB], const int (&trank)[kB],
+                                            int row0, int T, int span, int E, int w, int lane, const int* base_s,
+                                            const int* wave_s, int* dest_s) {
+    const int64_t R = a.num_tokens * a.topk;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+        const int i = w * span + b * kWaveSize + lane;
+        if (own_row(b, i, T, span, w)) {
+            const int key = tkey[b];
+            const int dest = base_s[key] + wave_s[w * E + key] + trank[b];
+            dest_s[i] = dest;
+            a.inv_permuted_idx[row0 + i] = dest;
+            if ((uint32_t)dest < (uint64_t)R) a.permuted_idx[dest] = row0 + i;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
 // Fused permute: one workgroup per tile of whole tokens.  Every workgroup
 // counts the expert ids of all rows outside its tile (before / after it),
 // ranks its own rows, derives expert_first_token_offset and its own base per
@@ -269,10 +396,10 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
     const int T = ntok * K;
     const int tile_cap = tokens_per_tile * K;
     const int R = (int)(a.num_tokens * K);  // <= kFusedMaxRows
-    const int span = (T + NT - 1) / NT * kWaveSize;  // tile rows ranked by each wave
+    const int span = (T + NT - 1) / NT * kWaveSize;
 
     // Loads, all independent: every expert id of the problem, this wave's own
-    // tile rows, then the first row chunk(s) of this wave.  The vector-memory
+    // tile rows, then the first row chunk of this wave.  The vector-memory
     // counter retires in issue order, so the row loads stay in flight while
     // the ids are consumed.
     int idv[kIds];
@@ -282,11 +409,7 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
         idv[j] = a.topk_ids[r < R ? r : R - 1];
     }
     int tkey[kBatches];
-#pragma unroll
-    for (int b = 0; b < kBatches; ++b) {
-        const int i = w * span + b * kWaveSize + lane;
-        tkey[b] = a.topk_ids[row0 + (i < T ? i : T - 1)];
-    }
+    load_tile_keys<kBatches>(a.topk_ids, row0, T, span, w, lane, tkey);
     const TileCopy<U, kNTStore> tc(a, t0, ntok);
     u32x4 cur[U];
     if (a.row_vecs > 0 && w < tc.items) tc.load(w, cur);
@@ -302,7 +425,7 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
     lds_barrier();
 
     // Phase 1: counts outside the tile (LDS atomics, order-free) and stable
-    // ranks inside each wave's span of the tile (ballot match + mbcnt).
+    // ranks inside each wave's span of the tile.
     int nbad = 0;
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
@@ -315,25 +438,7 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
         }
     }
     int trank[kBatches];
-    int* run = wave_s + w * E;
-#pragma unroll
-    for (int b = 0; b < kBatches; ++b) {
-        const int base = w * span + b * kWaveSize;
-        trank[b] = 0;
-        if (b * kWaveSize < span && base < T) {  // wave-uniform
-            const int i = base + lane;
-            const bool in_tile = i < T && i < w * span + span;
-            const bool ok = in_tile && (unsigned)tkey[b] < (unsigned)E;
-            nbad += (in_tile && !ok) ? 1 : 0;
-            const uint64_t same = lanes_with_same_key(tkey[b], ok, nbits);
-            const int below = lanes_below(same);
-            if (ok) {
-                const int c = run[tkey[b]];
-                trank[b] = c + below;
-                if (below == 0) run[tkey[b]] = c + (int)__popcll(same);
-            }
-        }
-    }
+    nbad += rank_own_rows<kBatches>(tkey, T, span, E, nbits, w, lane, wave_s + w * E, trank);
     if (nbad) atomicAdd(&misc_s[0], nbad);
     lds_barrier();
     if (misc_s[0] != 0) {  // every workgroup saw every id, so all take this branch together
@@ -342,67 +447,145 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
         return;
     }
 
-    // Phase 2: per expert, prefix over waves (in place) and the total count;
-    // exclusive scan over experts gives expert_first_token_offset, and the
-    // tile's base in each expert is offset + rows before the tile.
-    int tot[kPer];
-    int s = 0;
-    const int e0 = (int)threadIdx.x * kPer;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int e = e0 + q;
-        tot[q] = 0;
-        if (e < E) {
-            int c = 0;
-#pragma unroll
-            for (int v = 0; v < W; ++v) {
-                const int x = wave_s[v * E + e];
-                wave_s[v * E + e] = c;
-                c += x;
-            }
-            tot[q] = before_s[e] + c + after_s[e];
-        }
-        s += tot[q];
-    }
-    int x = s;
-#pragma unroll
-    for (int d = 1; d < kWaveSize; d <<= 1) {
-        const int y = __shfl_up(x, d, kWaveSize);
-        if (lane >= d) x += y;
-    }
-    if (lane == kWaveSize - 1) misc_s[1 + w] = x;
-    lds_barrier();
-    int excl = x - s, total = 0;
-#pragma unroll
-    for (int v = 0; v < W; ++v) {
-        const int c = misc_s[1 + v];
-        excl += v < w ? c : 0;
-        total += c;
-    }
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int e = e0 + q;
-        if (e < E) {
-            if (blockIdx.x == 0) a.expert_first_token_offset[e] = excl;
-            before_s[e] += excl;
-            excl += tot[q];
-        }
-    }
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.expert_first_token_offset[E] = total;
+    // Phase 2: offsets and this tile's base per expert.
+    expert_bases<NT, kPer>(
+        E, wave_s, before_s, misc_s + 1, a.expert_first_token_offset, blockIdx.x == 0,
+        [&](int e, int in_tile) { return before_s[e] + in_tile + after_s[e]; }, [&](int e) { return before_s[e]; });
     lds_barrier();
 
-    // Phase 3: destinations of this wave's tile rows.
-#pragma unroll
-    for (int b = 0; b < kBatches; ++b) {
-        const int i = w * span + b * kWaveSize + lane;
-        if (b * kWaveSize < span && i < T && i < w * span + span) {
-            const int key = tkey[b];
-            const int dest = before_s[key] + wave_s[w * E + key] + trank[b];
-            dest_s[i] = dest;
-            a.inv_permuted_idx[row0 + i] = dest;
-            if ((uint32_t)dest < (uint32_t)R) a.permuted_idx[dest] = row0 + i;
-        }
+    // Phase 3: destinations of this wave's tile rows, then the row copy.
+    write_dests<kBatches>(a, tkey, trank, row0, T, span, E, w, lane, before_s, wave_s, dest_s);
+    lds_barrier();
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore>(tc, cur, dest_s);
+    copy_tile_scales<NT>(a, t0, ntok, dest_s);
+}
+
+// ----------------------------------------------------------------------------
+// Coarse permute, kernel 1 of 2: expert counts of each coarse tile of
+// coarse_rows expanded rows.  hist[c][e] = rows of coarse tile c with expert
+// e; hist[c][E] = rows with an out-of-range id.
+// ----------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(NT) void permute_coarse_hist_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                                 int coarse_rows, int32_t* __restrict__ hist) {
+    extern __shared__ int smem[];  // [E + 1]
+    for (int e = threadIdx.x; e <= E; e += NT) smem[e] = 0;
+    lds_barrier();
+    const int r0 = (int)blockIdx.x * coarse_rows;
+    const int r1 = min(r0 + coarse_rows, R);
+    for (int r = r0 + (int)threadIdx.x; r < r1; r += NT) {
+        const int key = ids[r];
+        atomicAdd(&smem[(unsigned)key < (unsigned)E ? key : E], 1);
     }
+    lds_barrier();
+    int32_t* row = hist + (int64_t)blockIdx.x * (E + 1);
+    for (int e = threadIdx.x; e <= E; e += NT) row[e] = smem[e];
+}
+
+// ----------------------------------------------------------------------------
+// Coarse permute, kernel 2 of 2: one workgroup per tile of whole tokens, like
+// the fused kernel, except that the counts outside the tile come from the
+// coarse histogram (held in LDS) plus a count of the rows that precede the
+// tile inside its own coarse tile.  Tiles never straddle coarse tiles.
+// ----------------------------------------------------------------------------
+template <int NT, int U, bool kNTStore>
+__global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs a, int tokens_per_tile, int nbits,
+                                                                    int coarse_rows, int num_coarse,
+                                                                    const int32_t* __restrict__ hist) {
+    constexpr int W = NT / kWaveSize;
+    constexpr int kHist = kCoarseMaxHist / NT;                     // histogram entries loaded per thread
+    constexpr int kPartial = kCoarseMaxRowsPerTile / NT;           // preceding rows counted per thread
+    constexpr int kBatches = (kMaxTileRows + NT - 1) / NT;
+    constexpr int kPer = (kMaxExperts + NT - 1) / NT;
+    static_assert(kCoarseMaxHist % NT == 0 && kCoarseMaxRowsPerTile % NT == 0, "coarse bounds vs workgroup size");
+    extern __shared__ int smem[];
+    const int E = a.num_experts;
+    const int K = a.topk;
+    const int w = wave_index();
+    const int lane = threadIdx.x % kWaveSize;
+    const int64_t t0 = (int64_t)blockIdx.x * tokens_per_tile;
+    const int ntok = (int)min((int64_t)tokens_per_tile, a.num_tokens - t0);
+    const int row0 = (int)(t0 * K);
+    const int T = ntok * K;
+    const int tile_cap = tokens_per_tile * K;
+    const int span = (T + NT - 1) / NT * kWaveSize;
+    const int cc = row0 / coarse_rows;  // this tile's coarse tile
+    const int c_start = cc * coarse_rows;
+    const int hist_n = num_coarse * (E + 1);
+
+    // Independent loads first: the coarse histogram, the rows that precede
+    // this tile in its coarse tile, this wave's tile keys; then row chunks.
+    int hv[kHist];
+#pragma unroll
+    for (int j = 0; j < kHist; ++j) {
+        const int i = (int)threadIdx.x + j * NT;
+        hv[j] = hist[i < hist_n ? i : hist_n - 1];
+    }
+    int pv[kPartial];
+#pragma unroll
+    for (int j = 0; j < kPartial; ++j) {
+        const int r = c_start + (int)threadIdx.x + j * NT;
+        pv[j] = a.topk_ids[r < row0 ? r : row0];  // row0 is a valid row (T >= 1)
+    }
+    int tkey[kBatches];
+    load_tile_keys<kBatches>(a.topk_ids, row0, T, span, w, lane, tkey);
+    const TileCopy<U, kNTStore> tc(a, t0, ntok);
+    u32x4 cur[U];
+    if (a.row_vecs > 0 && w < tc.items) tc.load(w, cur);
+
+    int* hist_s = smem;                   // [num_coarse * (E + 1)]
+    int* before_s = hist_s + hist_n;      // [E] preceding rows in the coarse tile, then the tile's base
+    int* wave_s = before_s + E;           // [W * E]
+    int* dest_s = wave_s + W * E;         // [tile_cap]
+    int* misc_s = dest_s + tile_cap;      // [16]: [0] bad ids, [1..W] scan scratch
+
+#pragma unroll
+    for (int j = 0; j < kHist; ++j) {
+        const int i = (int)threadIdx.x + j * NT;
+        if (i < hist_n) hist_s[i] = hv[j];
+    }
+    for (int i = threadIdx.x; i < (1 + W) * E; i += NT) before_s[i] = 0;
+    if (threadIdx.x < 16) misc_s[threadIdx.x] = 0;
+    lds_barrier();
+
+    // Phase 1: preceding rows of the coarse tile (LDS atomics), ranks inside
+    // each wave's span, and the bad-id total from the histogram.
+#pragma unroll
+    for (int j = 0; j < kPartial; ++j) {
+        const int r = c_start + (int)threadIdx.x + j * NT;
+        if (r < row0 && (unsigned)pv[j] < (unsigned)E) atomicAdd(&before_s[pv[j]], 1);
+    }
+    int trank[kBatches];
+    rank_own_rows<kBatches>(tkey, T, span, E, nbits, w, lane, wave_s + w * E, trank);
+    if (threadIdx.x == 0) {
+        int bad = 0;
+        for (int c = 0; c < num_coarse; ++c) bad += hist_s[c * (E + 1) + E];
+        misc_s[0] = bad;
+    }
+    lds_barrier();
+    if (misc_s[0] != 0) {  // the histogram covers every id, so all workgroups agree
+        if (blockIdx.x == 0)
+            for (int e = threadIdx.x; e <= E; e += NT) a.expert_first_token_offset[e] = -1;
+        return;
+    }
+
+    // Phase 2: offsets and this tile's base per expert.
+    expert_bases<NT, kPer>(
+        E, wave_s, before_s, misc_s + 1, a.expert_first_token_offset, blockIdx.x == 0,
+        [&](int e, int) {
+            int t = 0;
+            for (int c = 0; c < num_coarse; ++c) t += hist_s[c * (E + 1) + e];
+            return t;
+        },
+        [&](int e) {
+            int b = before_s[e];
+            for (int c = 0; c < cc; ++c) b += hist_s[c * (E + 1) + e];
+            return b;
+        });
+    lds_barrier();
+
+    // Phase 3: destinations, then the row copy.
+    write_dests<kBatches>(a, tkey, trank, row0, T, span, E, w, lane, before_s, wave_s, dest_s);
     lds_barrier();
     if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore>(tc, cur, dest_s);
     copy_tile_scales<NT>(a, t0, ntok, dest_s);
@@ -795,6 +978,19 @@ static void launch_fused_u(const PermuteArgs& a, const PermutePlan& p, hipStream
 }
 
 template <int U>
+static void launch_coarse_u(const PermuteArgs& a, const PermutePlan& p, const int32_t* hist, hipStream_t stream) {
+    const size_t lds = coarse_scatter_lds_bytes(a.num_experts, p.tile_rows, p.num_coarse);
+    if (plain_row_stores(a))
+        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, false>), dim3((unsigned)p.num_tiles),
+                           dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile, p.nbits, p.coarse_rows,
+                           p.num_coarse, hist);
+    else
+        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, true>), dim3((unsigned)p.num_tiles),
+                           dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile, p.nbits, p.coarse_rows,
+                           p.num_coarse, hist);
+}
+
+template <int U>
 static void launch_scatter_u(const PermuteArgs& a, const PermutePlan& p, const int32_t* rank_ws,
                              const int32_t* tile_base, const int32_t* total, hipStream_t stream) {
     const size_t lds = scatter_lds_bytes(a.num_experts, p.tile_rows);
@@ -831,6 +1027,18 @@ hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* work
         return hipGetLastError();
     }
     char* ws = static_cast<char*>(workspace);
+    if (p.coarse) {
+        int32_t* hist = reinterpret_cast<int32_t*>(ws);
+        hipLaunchKernelGGL((permute_coarse_hist_kernel<kCoarseThreads>), dim3((unsigned)p.num_coarse),
+                           dim3(kCoarseThreads), coarse_hist_lds_bytes(E), stream, a.topk_ids, (int)p.rows, E,
+                           p.coarse_rows, hist);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+#define MOE_COARSE(U) launch_coarse_u<U>(a, p, hist, stream)
+        MOE_DISPATCH_U(u, MOE_COARSE)
+#undef MOE_COARSE
+        return hipGetLastError();
+    }
     int32_t* rank_ws = reinterpret_cast<int32_t*>(ws + p.ws_rank);
     int32_t* tile_hist = reinterpret_cast<int32_t*>(ws + p.ws_tile_hist);
     int32_t* total = reinterpret_cast<int32_t*>(ws + p.ws_total);

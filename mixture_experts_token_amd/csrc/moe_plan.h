@@ -4,9 +4,14 @@
 // a host without a GPU.  The plan fixes, for one call:
 //   * which permute schedule runs:
 //       fused  -- one kernel; every workgroup counts all expert ids itself
-//                 (cheap while N*topk is small, and it avoids two launches);
+//                 (cheap while N*topk is small, and it avoids extra launches);
+//       coarse -- two kernels: expert counts per coarse tile (a few dozen),
+//                 then the fused-style kernel whose counts outside its tile
+//                 come from that histogram plus the rows that precede it in
+//                 its coarse tile;
 //       staged -- three kernels: per-tile stable ranks and histograms, a
-//                 per-expert scan over tiles, then scatter + row copy;
+//                 per-expert scan over tiles, then scatter + row copy (any
+//                 size);
 //   * how expanded rows are cut into tiles (whole tokens per tile);
 //   * where each piece of the workspace lives.
 #pragma once
@@ -21,6 +26,11 @@ constexpr int kFusedThreads = 512;                 // fused permute workgroup (8
 constexpr int kRankThreads = 256;                  // staged kernel 1
 constexpr int kScanThreads = 256;                  // staged kernel 2 (one workgroup per histogram row)
 constexpr int kScatterThreads = 256;               // staged kernel 3
+constexpr int kCoarseThreads = 512;                // coarse schedule, both kernels
+constexpr int kCoarseMaxHist = 8192;               // coarse histogram entries held in LDS
+constexpr int kCoarseMaxRowsPerTile = 8192;        // rows before a tile inside its coarse tile, at most
+constexpr int kMaxCoarseTiles = 32;
+constexpr int kMaxLdsInts = 16384;                 // 64 KiB of dynamic LDS per workgroup
 constexpr int64_t kMaxGridBlocks = int64_t(1) << 20;  // beyond this, waves loop over further items
 constexpr int kScanPerThread = 8;                  // tile counts one scan thread holds per pass
 constexpr int kMaxExperts = 1024;
@@ -55,6 +65,9 @@ inline int key_bits(int num_experts) {
 
 struct PermutePlan {
     bool fused = false;
+    bool coarse = false;          // two-kernel schedule (only when !fused)
+    int coarse_rows = 0;          // expanded rows per coarse tile (a multiple of tile_rows)
+    int num_coarse = 0;
     int64_t rows = 0;             // N * topk
     int tokens_per_tile = 1;
     int tile_rows = 0;            // tokens_per_tile * topk
@@ -65,6 +78,7 @@ struct PermutePlan {
     size_t ws_tile_hist = 0;      // int32 [E+1][num_tiles] per-tile counts, then per-tile bases
     size_t ws_total = 0;          // int32 [E+1]            rows per expert (+ bad-id count)
     size_t ws_bytes = 0;          // bytes this call needs
+    // coarse schedule workspace: int32 [num_coarse][E+1] counts per coarse tile (+ bad ids)
 };
 
 // Tokens per staged tile: about kStagedTileRows expanded rows, whole tokens.
@@ -80,15 +94,49 @@ inline size_t staged_workspace_bytes(int64_t rows, int64_t num_tiles, int num_ex
     return b;
 }
 
+// Coarse tiles a problem may use: bounded by kMaxCoarseTiles, by the LDS held
+// histogram (entries and the whole workgroup's LDS), for E experts and tiles
+// of tile_rows rows.
+inline int max_coarse_tiles(int num_experts, int tile_rows) {
+    int n = kMaxCoarseTiles;
+    const int by_hist = kCoarseMaxHist / (num_experts + 1);
+    const int by_lds = (kMaxLdsInts - 16 - (1 + kCoarseThreads / kWaveSize) * num_experts - tile_rows) / (num_experts + 1);
+    if (by_hist < n) n = by_hist;
+    if (by_lds < n) n = by_lds;
+    return n;
+}
+
+// Coarse tile length for R rows (a multiple of tile_rows), or 0 when the
+// coarse schedule does not apply (too many rows per coarse tile).
+inline int64_t coarse_rows_for(int64_t rows, int num_experts, int tile_rows) {
+    const int nmax = max_coarse_tiles(num_experts, tile_rows);
+    if (nmax < 1) return 0;
+    const int64_t per = (rows + nmax - 1) / nmax;
+    const int64_t m = (per + tile_rows - 1) / tile_rows;
+    const int64_t cr = m * tile_rows;
+    return cr - tile_rows <= kCoarseMaxRowsPerTile ? cr : 0;
+}
+
+inline size_t coarse_workspace_bytes(int num_coarse, int num_experts) {
+    return align_up(sizeof(int32_t) * (size_t)num_coarse * (size_t)(num_experts + 1), kWorkspaceAlign);
+}
+
 // Workspace of a call with max_num_tokens tokens; every call with fewer tokens
-// needs no more (the tile size depends on topk only, and the size grows with
-// the row and tile counts).
+// needs no more: the schedules go fused -> coarse -> staged as the row count
+// grows, a coarse call needs at most max_coarse_tiles(E) histogram rows, and
+// the staged size grows with the row and tile counts (the tile size depends
+// on topk only).
 inline size_t workspace_bound(int64_t max_num_tokens, int topk, int num_experts) {
     const int64_t rows = max_num_tokens * topk;
     if (rows <= kFusedMaxRows) return 0;
     const int tpt = staged_tokens_per_tile(topk);
+    const int tile_rows = tpt * topk;
+    const int nmax = max_coarse_tiles(num_experts, tile_rows);
+    const size_t coarse = nmax > 0 ? coarse_workspace_bytes(nmax, num_experts) : 0;
+    if (coarse_rows_for(rows, num_experts, tile_rows) > 0) return coarse;
     const int64_t tiles = (max_num_tokens + tpt - 1) / tpt;
-    return staged_workspace_bytes(rows, tiles, num_experts);
+    const size_t staged = staged_workspace_bytes(rows, tiles, num_experts);
+    return staged > coarse ? staged : coarse;
 }
 
 inline PermutePlan plan_permute(int64_t num_tokens, int topk, int num_experts) {
@@ -110,11 +158,19 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int num_experts) {
     p.tile_rows = p.tokens_per_tile * topk;
     p.num_tiles = num_tokens == 0 ? 0 : (num_tokens + p.tokens_per_tile - 1) / p.tokens_per_tile;
     if (!p.fused) {
-        p.ws_rank = 0;
-        p.ws_tile_hist = align_up(sizeof(int32_t) * (size_t)p.rows, kWorkspaceAlign);
-        p.ws_total = p.ws_tile_hist +
-                     align_up(sizeof(int32_t) * (size_t)(num_experts + 1) * (size_t)p.num_tiles, kWorkspaceAlign);
-        p.ws_bytes = staged_workspace_bytes(p.rows, p.num_tiles, num_experts);
+        const int64_t cr = coarse_rows_for(p.rows, num_experts, p.tile_rows);
+        if (cr > 0) {
+            p.coarse = true;
+            p.coarse_rows = (int)cr;
+            p.num_coarse = (int)((p.rows + cr - 1) / cr);
+            p.ws_bytes = coarse_workspace_bytes(p.num_coarse, num_experts);
+        } else {
+            p.ws_rank = 0;
+            p.ws_tile_hist = align_up(sizeof(int32_t) * (size_t)p.rows, kWorkspaceAlign);
+            p.ws_total = p.ws_tile_hist +
+                         align_up(sizeof(int32_t) * (size_t)(num_experts + 1) * (size_t)p.num_tiles, kWorkspaceAlign);
+            p.ws_bytes = staged_workspace_bytes(p.rows, p.num_tiles, num_experts);
+        }
     }
     return p;
 }
@@ -125,6 +181,11 @@ inline size_t fused_lds_bytes(int num_experts, int tile_rows) {
 }
 inline size_t rank_lds_bytes(int num_experts, int tile_rows) {
     return sizeof(int) * ((size_t)(1 + kRankThreads / kWaveSize) * num_experts + 2 * (size_t)tile_rows + 16);
+}
+inline size_t coarse_hist_lds_bytes(int num_experts) { return sizeof(int) * (size_t)(num_experts + 1); }
+inline size_t coarse_scatter_lds_bytes(int num_experts, int tile_rows, int num_coarse) {
+    return sizeof(int) * ((size_t)num_coarse * (num_experts + 1) + (size_t)(1 + kCoarseThreads / kWaveSize) * num_experts +
+                          (size_t)tile_rows + 16);
 }
 inline size_t scatter_lds_bytes(int num_experts, int tile_rows) {
     return sizeof(int) * ((size_t)(2 * num_experts + 1) + (size_t)tile_rows + 16);

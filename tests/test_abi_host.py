@@ -204,3 +204,20 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(FileNotFoundError):
         binding.load_library()
+
+
+def test_streaming_probe_library_checks_arguments():
+    """The bench's ceiling probe (libhbm_probe.so) loads and rejects bad sizes before any launch."""
+    import os
+
+    path = os.path.join(os.path.dirname(binding.LIB_PATH), "libhbm_probe.so")
+    probe = ctypes.CDLL(path)
+    for fn in (probe.hbm_probe_fanout, probe.hbm_probe_reduce):
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                       ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+        assert fn(None, addr(1), 10, 64, 2, 1, None) == 1
+        assert fn(addr(0), addr(1), 0, 64, 2, 1, None) == 1
+        assert fn(addr(0), addr(1), 10, 24, 2, 1, None) == 1
+        assert fn(addr(0), addr(1), 10, 64, 0, 1, None) == 1
+        assert fn(addr(0), addr(1), 10, 64, 2, 8, None) == 1  # variant out of range
