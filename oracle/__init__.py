@@ -80,6 +80,8 @@ def _load():
         lib.oracle_gather_rows.restype = None
         lib.oracle_moe_permute.argtypes = [p, i64, p, p, i64, i32, i32, p, p, p, p, p]
         lib.oracle_moe_permute.restype = ctypes.c_int
+        lib.oracle_moe_permute_local.argtypes = [p, i64, p, p, i64, i32, i32, p, i32, p, p, p, p, p]
+        lib.oracle_moe_permute_local.restype = ctypes.c_int
         lib.oracle_unpermute_f32.argtypes = [p, p, p, i64, i32, i64, p]
         lib.oracle_unpermute_f32.restype = ctypes.c_int
         lib.oracle_unpermute_bf16.argtypes = [p, p, p, i64, i32, i64, p]
@@ -195,11 +197,50 @@ def permute(hidden: np.ndarray, topk_ids, num_experts: int, token_scale=None) ->
     }
 
 
+def permute_local(hidden: np.ndarray, topk_ids, num_experts: int, expert_map, num_local_experts: int,
+                  token_scale=None) -> dict:
+    """Permute with a local-expert filter: expert_map[g] = local id of global expert g, or -1.
+
+    Returns the same keys as ``permute``; ``expert_first_token_offset`` has
+    num_local_experts + 1 entries, ``permuted_idx`` / ``permuted_hidden_states``
+    / ``permuted_scale`` hold only the local rows, and ``inv_permuted_idx`` is
+    -1 for rows of experts on other ranks.
+    """
+    ids = _ids2d(topk_ids)
+    n, topk = ids.shape
+    emap = np.ascontiguousarray(expert_map, dtype=np.int32)
+    if emap.shape != (num_experts,):
+        raise ValueError("expert_map must have num_experts entries")
+    h = np.ascontiguousarray(hidden)
+    hb = as_row_bytes(h) if h.size else np.zeros((n, 0), dtype=np.uint8)
+    rows = n * topk
+    off = np.zeros(num_local_experts + 1, dtype=np.int64)
+    perm = np.zeros(rows, dtype=np.int32)
+    inv = np.zeros(rows, dtype=np.int32)
+    out = np.zeros((rows, hb.shape[1]), dtype=np.uint8)
+    scale = None if token_scale is None else np.ascontiguousarray(token_scale, dtype=np.float32)
+    out_scale = None if scale is None else np.zeros(rows, dtype=np.float32)
+    _check(_load().oracle_moe_permute_local(_ptr(hb), hb.shape[1], _ptr(scale), _ptr(ids), n, topk, num_experts,
+                                            _ptr(emap), num_local_experts, _ptr(out), _ptr(out_scale), _ptr(off),
+                                            _ptr(perm), _ptr(inv)))
+    local_rows = int(off[-1])
+    return {
+        "expert_first_token_offset": off,
+        "permuted_idx": perm[:local_rows],
+        "inv_permuted_idx": inv,
+        "permuted_hidden_states": (out[:local_rows].view(h.dtype).reshape((local_rows,) + h.shape[1:])
+                                   if h.ndim == 2 else out[:local_rows]),
+        "permuted_scale": None if out_scale is None else out_scale[:local_rows],
+    }
+
+
 # --------------------------------------------------------------------------
 # Unpermute
 # --------------------------------------------------------------------------
 def unpermute(expanded_output: np.ndarray, topk_weights, inv_permuted_idx, dtype: str) -> np.ndarray:
     """out[t] = sum_k w[t,k] * Y[inv[t*topk+k]], double-precision sum rounded once.
+
+    Slots whose index is -1 (experts on another rank) contribute nothing.
 
     ``dtype`` is ``"f32"`` (Y float32) or ``"bf16"`` (Y as uint16 bit patterns);
     the output has the same representation as Y.

@@ -28,7 +28,9 @@
  *     inv_permuted_idx[r] = j, its inverse;
  *   - unpermute computes out[t] = sum_k w[t,k] * Y[inv[t*topk+k]]: here the
  *     sum is formed in double precision in ascending k and rounded once to the
- *     output type (round to nearest, ties to even).
+ *     output type (round to nearest, ties to even);
+ *   - with a local-expert filter, rows of experts on other ranks are left out
+ *     of the permute (inverse index -1) and add nothing in the unpermute.
  *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared -o libmoe_oracle.so moe_oracle.c -lm
  */
@@ -168,6 +170,83 @@ int oracle_moe_permute(const uint8_t *hidden_states, int64_t row_bytes,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Permute with a local-expert filter (expert parallelism).                   */
+/* [P1] PR description: expert parallelism through an expert_map was not yet  */
+/* supported.  [P3] key code snippets: the offsets have num_local_experts + 1 */
+/* entries.  Reading taken: expert_map[g] is the local id of global expert g, */
+/* or -1 when g lives elsewhere.  Only rows whose expert is local are         */
+/* counted, ordered (by local id, then ascending r) and copied; such a row's  */
+/* inv_permuted_idx is its slot, every other row's is -1.  permuted_idx and   */
+/* the permuted rows are written for the first (number of local rows) slots.  */
+/* An id outside [0, num_experts) or a map entry outside [-1, num_local)      */
+/* makes the call fail.                                                       */
+/* ------------------------------------------------------------------------ */
+int oracle_moe_permute_local(const uint8_t *hidden_states, int64_t row_bytes,
+                             const float *token_scale, const int32_t *topk_ids,
+                             int64_t num_tokens, int32_t topk, int32_t num_experts,
+                             const int32_t *expert_map, int32_t num_local_experts,
+                             uint8_t *permuted_hidden_states, float *permuted_scale,
+                             int64_t *expert_first_token_offset, int32_t *permuted_idx,
+                             int32_t *inv_permuted_idx)
+{
+    if (num_tokens < 0 || topk < 1 || num_experts < 1 || num_local_experts < 1)
+        return ORACLE_BAD_ARG;
+    int64_t num_rows = num_tokens * topk;
+    /* local expert of every expanded row, -1 for rows of other ranks */
+    int32_t *local = (int32_t *)malloc(sizeof(int32_t) * (size_t)(num_rows > 0 ? num_rows : 1));
+    int64_t *counts = (int64_t *)malloc(sizeof(int64_t) * (size_t)num_local_experts);
+    int64_t *next_slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)num_local_experts);
+    if (local == NULL || counts == NULL || next_slot == NULL) {
+        free(local);
+        free(counts);
+        free(next_slot);
+        return ORACLE_BAD_ARG;
+    }
+    int status = ORACLE_OK;
+    for (int32_t e = 0; e < num_local_experts; ++e)
+        counts[e] = 0;
+    for (int64_t r = 0; r < num_rows && status == ORACLE_OK; ++r) {
+        int32_t id = topk_ids[r];
+        if (id < 0 || id >= num_experts) {
+            status = ORACLE_BAD_ID;
+            break;
+        }
+        int32_t l = expert_map[id];
+        if (l < -1 || l >= num_local_experts) {
+            status = ORACLE_BAD_ID;
+            break;
+        }
+        local[r] = l;
+        if (l >= 0)
+            counts[l] += 1;
+    }
+    if (status == ORACLE_OK) {
+        expert_first_token_offset[0] = 0;
+        for (int32_t e = 0; e < num_local_experts; ++e)
+            expert_first_token_offset[e + 1] = expert_first_token_offset[e] + counts[e];
+        for (int32_t e = 0; e < num_local_experts; ++e)
+            next_slot[e] = expert_first_token_offset[e];
+        for (int64_t r = 0; r < num_rows; ++r) {
+            if (local[r] < 0) {
+                inv_permuted_idx[r] = -1;
+                continue;
+            }
+            int64_t j = next_slot[local[r]]++;
+            permuted_idx[j] = (int32_t)r;
+            inv_permuted_idx[r] = (int32_t)j;
+        }
+        if (row_bytes > 0)
+            oracle_gather_rows(hidden_states, row_bytes, token_scale, permuted_idx,
+                               expert_first_token_offset[num_local_experts], topk,
+                               permuted_hidden_states, permuted_scale);
+    }
+    free(local);
+    free(counts);
+    free(next_slot);
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
 /* bfloat16, written from the format: 1 sign bit, 8 exponent bits (bias 127), */
 /* 7 fraction bits.  Exponent field 0 holds zero and the subnormals          */
 /* (fraction * 2^-133); field 255 holds infinities (fraction 0) and NaNs.    */
@@ -225,7 +304,9 @@ uint16_t oracle_double_to_bf16(double x)
 /*     out[t, h] = sum_{k=0}^{topk-1} w[t, k] * Y[inv_permuted_idx[t*topk+k], h] */
 /* Y is in permuted order, so the row holding token t's slot k is             */
 /* inv_permuted_idx[t*topk+k].  The sum is formed in double precision in      */
-/* ascending k and rounded once to the output type.                          */
+/* ascending k and rounded once to the output type.  A slot whose index is -1 */
+/* (its expert lives on another rank, see the local-expert filter above)      */
+/* contributes nothing.                                                       */
 /* ------------------------------------------------------------------------ */
 int oracle_unpermute_f32(const float *expanded_output, const float *topk_weights,
                          const int32_t *inv_permuted_idx, int64_t num_tokens,
@@ -233,7 +314,7 @@ int oracle_unpermute_f32(const float *expanded_output, const float *topk_weights
 {
     int64_t num_rows = num_tokens * topk;
     for (int64_t r = 0; r < num_rows; ++r)
-        if (inv_permuted_idx[r] < 0 || inv_permuted_idx[r] >= num_rows)
+        if (inv_permuted_idx[r] < -1 || inv_permuted_idx[r] >= num_rows)
             return ORACLE_BAD_INV;
     for (int64_t t = 0; t < num_tokens; ++t) {
         for (int64_t h = 0; h < hidden_size; ++h) {
@@ -241,6 +322,8 @@ int oracle_unpermute_f32(const float *expanded_output, const float *topk_weights
             for (int32_t k = 0; k < topk; ++k) {
                 int64_t r = t * topk + k;
                 int64_t j = inv_permuted_idx[r];
+                if (j < 0)
+                    continue;
                 acc += (double)topk_weights[r] * (double)expanded_output[j * hidden_size + h];
             }
             output[t * hidden_size + h] = (float)acc;
@@ -255,7 +338,7 @@ int oracle_unpermute_bf16(const uint16_t *expanded_output, const float *topk_wei
 {
     int64_t num_rows = num_tokens * topk;
     for (int64_t r = 0; r < num_rows; ++r)
-        if (inv_permuted_idx[r] < 0 || inv_permuted_idx[r] >= num_rows)
+        if (inv_permuted_idx[r] < -1 || inv_permuted_idx[r] >= num_rows)
             return ORACLE_BAD_INV;
     for (int64_t t = 0; t < num_tokens; ++t) {
         for (int64_t h = 0; h < hidden_size; ++h) {
@@ -263,6 +346,8 @@ int oracle_unpermute_bf16(const uint16_t *expanded_output, const float *topk_wei
             for (int32_t k = 0; k < topk; ++k) {
                 int64_t r = t * topk + k;
                 int64_t j = inv_permuted_idx[r];
+                if (j < 0)
+                    continue;
                 acc += (double)topk_weights[r] *
                        oracle_bf16_to_double(expanded_output[j * hidden_size + h]);
             }

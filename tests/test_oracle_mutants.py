@@ -34,11 +34,33 @@ MUTANTS = {
         "acc += (double)topk_weights[r] * (double)expanded_output[j * hidden_size + h];",
         "acc += (double)topk_weights[k * num_tokens + t] * (double)expanded_output[j * hidden_size + h];"),
     "unpermute_ignores_inverse": (
-        "int64_t j = inv_permuted_idx[r];\n                acc += (double)topk_weights[r] *\n",
-        "int64_t j = r;\n                acc += (double)topk_weights[r] *\n"),
+        "int64_t j = inv_permuted_idx[r];\n                if (j < 0)\n                    continue;\n"
+        "                acc += (double)topk_weights[r] *\n",
+        "int64_t j = r;\n                if (j < 0)\n                    continue;\n"
+        "                acc += (double)topk_weights[r] *\n"),
     "unpermute_drops_last_slot": (
-        "for (int32_t k = 0; k < topk; ++k) {\n                int64_t r = t * topk + k;\n                int64_t j = inv_permuted_idx[r];\n                acc += (double)topk_weights[r] * (double)",
-        "for (int32_t k = 0; k < topk - 1; ++k) {\n                int64_t r = t * topk + k;\n                int64_t j = inv_permuted_idx[r];\n                acc += (double)topk_weights[r] * (double)"),
+        "for (int32_t k = 0; k < topk; ++k) {\n                int64_t r = t * topk + k;\n"
+        "                int64_t j = inv_permuted_idx[r];\n                if (j < 0)\n                    continue;\n"
+        "                acc += (double)topk_weights[r] * (double)",
+        "for (int32_t k = 0; k < topk - 1; ++k) {\n                int64_t r = t * topk + k;\n"
+        "                int64_t j = inv_permuted_idx[r];\n                if (j < 0)\n                    continue;\n"
+        "                acc += (double)topk_weights[r] * (double)"),
+    # local-expert filter
+    "local_remote_rows_get_slot_zero": (
+        "inv_permuted_idx[r] = -1;\n                continue;",
+        "inv_permuted_idx[r] = 0;\n                continue;"),
+    "local_map_assumed_prefix": (
+        "int32_t l = expert_map[id];",
+        "int32_t l = id < num_local_experts ? id : -1;"),
+    "local_order_not_stable": (
+        "for (int64_t r = 0; r < num_rows; ++r) {\n            if (local[r] < 0) {",
+        "for (int64_t r = num_rows - 1; r >= 0; --r) {\n            if (local[r] < 0) {"),
+    "local_gathers_with_expert_id": (
+        "expert_first_token_offset[num_local_experts], topk,",
+        "expert_first_token_offset[num_local_experts], 1,"),
+    "unpermute_minus_one_wraps_to_last_row": (
+        "if (j < 0)\n                    continue;",
+        "if (j < 0)\n                    j = num_rows - 1;"),
     "unpermute_wrong_sign": (
         "acc += (double)topk_weights[r] *\n                       oracle_bf16_to_double",
         "acc -= (double)topk_weights[r] *\n                       oracle_bf16_to_double"),

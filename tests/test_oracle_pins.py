@@ -348,3 +348,171 @@ def test_unpermute_weight_index_is_token_major():
     w = np.array([[1, 10], [100, 1000], [10000, 100000]], np.float32)
     out = oracle.unpermute(y, w, inv, "f32")
     assert out.reshape(-1).tolist() == [1 * 1 + 10 * 2, 100 * 3 + 1000 * 4, 10000 * 5 + 100000 * 6]
+
+
+# --------------------------------------------------------------------------
+# Local-expert filter (expert parallelism).  The reading pinned here: the
+# expert map sends a global expert id to its local id, or to -1 when the expert
+# lives on another rank; local rows are ordered by local id, then ascending
+# expanded row; other rows get inverse index -1 and add nothing when unpermuted.
+# --------------------------------------------------------------------------
+def brute_permute_local(ids2d, emap, num_local, hidden_rows):
+    flat = [int(v) for row in ids2d for v in row]
+    topk = len(ids2d[0]) if len(ids2d) else 1
+    keyed = sorted((emap[g], r) for r, g in enumerate(flat) if emap[g] >= 0)  # tuple sort, not a counting pass
+    perm = [r for _, r in keyed]
+    inv = [-1] * len(flat)
+    for j, r in enumerate(perm):
+        inv[r] = j
+    off = [0]
+    for l in range(num_local):
+        off.append(off[-1] + sum(1 for g in flat if emap[g] == l))
+    return off, perm, inv, [hidden_rows[r // topk] for r in perm]
+
+
+def _maps(rng, e):
+    """(name, expert_map, num_local) cases of several shapes for e global experts."""
+    out = [("identity", list(range(e)), e), ("none_local", [-1] * e, 1)]
+    if e >= 2:
+        half = e // 2
+        out.append(("upper_half", [-1] * half + list(range(e - half)), e - half))
+        out.append(("lower_half", list(range(half)) + [-1] * (e - half), half))
+        out.append(("even", [g // 2 if g % 2 == 0 else -1 for g in range(e)], (e + 1) // 2))
+    if e >= 3:  # local ids not monotone in the global id
+        chosen = rng.permutation(e)[: e - 1]
+        m = [-1] * e
+        for l, g in enumerate(chosen):
+            m[int(g)] = l
+        out.append(("shuffled", m, e - 1))
+        out.append(("one_local_unused_slot", [0 if g == e - 1 else -1 for g in range(e)], 2))
+    return out
+
+
+@pytest.mark.parametrize("n,k,e", list(itertools.product([0, 1, 3, 7, 16], [1, 2, 3, 8], [1, 2, 3, 8])))
+def test_oracle_permute_local_matches_brute_force(n, k, e):
+    rng = np.random.default_rng(2000 + 97 * n + 13 * k + e)
+    for mode in ("random", "one_expert", "distinct", "skip_first_last"):
+        ids = _grid_ids(rng, n, k, e, mode).astype(np.int32).reshape(n, k)
+        hidden = rng.standard_normal((n, 3)).astype(np.float32)
+        scale = rng.random(n).astype(np.float32)
+        for name, emap, nl in _maps(rng, e):
+            got = oracle.permute_local(hidden, ids, e, emap, nl, token_scale=scale)
+            off, perm, inv, gathered = brute_permute_local(ids.tolist(), emap, nl, [row.tobytes() for row in hidden])
+            assert got["expert_first_token_offset"].tolist() == off, name
+            assert got["permuted_idx"].tolist() == perm, name
+            assert got["inv_permuted_idx"].tolist() == inv, name
+            assert [row.tobytes() for row in got["permuted_hidden_states"]] == gathered, name
+            assert got["permuted_scale"].tolist() == [float(scale[r // k]) for r in perm], name
+
+
+def test_local_hand_worked_example():
+    # 3 tokens, topk 2, 4 global experts; this rank holds experts 3 and 1 as
+    # local 0 and 1 (map [-1, 1, -1, 0]).
+    # ids: t0 -> (1, 2), t1 -> (3, 1), t2 -> (0, 3); expanded rows r = 2t + k:
+    #   r0:1  r1:2  r2:3  r3:1  r4:0  r5:3
+    # local ids: r0:1  r1:-  r2:0  r3:1  r4:-  r5:0
+    # local 0 (expert 3) gets rows 2, 5; local 1 (expert 1) gets rows 0, 3.
+    # offsets [0, 2, 4]; permuted_idx [2, 5, 0, 3];
+    # inv: r0->2, r1->-1, r2->0, r3->3, r4->-1, r5->1.
+    # Gathered tokens r // 2: [1, 2, 0, 1].
+    ids = np.array([[1, 2], [3, 1], [0, 3]], np.int32)
+    hidden = np.array([[10.0], [20.0], [30.0]], np.float32)
+    got = oracle.permute_local(hidden, ids, 4, [-1, 1, -1, 0], 2)
+    assert got["expert_first_token_offset"].tolist() == [0, 2, 4]
+    assert got["permuted_idx"].tolist() == [2, 5, 0, 3]
+    assert got["inv_permuted_idx"].tolist() == [2, -1, 0, 3, -1, 1]
+    assert got["permuted_hidden_states"].reshape(-1).tolist() == [20.0, 30.0, 10.0, 20.0]
+    # unpermute with Y = the gathered rows times (slot + 1): token 0 gets
+    # w00 * Y[2] + (nothing for r1) = 0.5 * 30; token 1 gets w10*Y[0] + w11*Y[3]
+    # = 0.25*20 + 2*80; token 2 gets (nothing for r4) + w21*Y[1] = 4 * 60.
+    y = (got["permuted_hidden_states"].reshape(-1) * np.arange(1, 5, dtype=np.float32)).reshape(4, 1)
+    w = np.array([[0.5, 9.0], [0.25, 2.0], [9.0, 4.0]], np.float32)
+    out = oracle.unpermute(y, w, got["inv_permuted_idx"], "f32")
+    assert out.reshape(-1).tolist() == [15.0, 165.0, 240.0]
+
+
+@pytest.mark.parametrize("bad_map", [[0, 2, -1], [0, -2, 1], [3, 0, 1]])
+def test_local_bad_map_rejected(bad_map):
+    ids = np.array([[0, 1], [2, 1]], np.int32)
+    with pytest.raises(oracle.OracleError):
+        oracle.permute_local(np.zeros((2, 4), np.float32), ids, 3, bad_map, 2)
+
+
+def test_local_bad_id_rejected():
+    ids = np.array([[0, 3]], np.int32)
+    with pytest.raises(oracle.OracleError):
+        oracle.permute_local(np.zeros((1, 4), np.float32), ids, 3, [0, -1, 1], 2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ranks,layout", [(2, "contiguous"), (4, "contiguous"), (4, "round_robin"), (3, "contiguous")])
+def test_expert_parallel_ranks_sum_to_the_full_unpermute(dtype, ranks, layout):
+    # Split the experts over ranks; each rank permutes only its experts, runs
+    # its "experts" on its rows and unpermutes with -1 for remote slots.  The
+    # partial outputs summed over ranks must equal the single-rank result.  The
+    # values are small integers and the weights powers of two, so every sum is
+    # exact and the comparison is bit for bit.  For bfloat16 (8 significant
+    # bits) x is in {-1, 0, 1} and w in {1/2, 1}: every term is a multiple of
+    # 1/2 of size <= 12 and every sum of 4 terms at most 192 halves < 2^8.
+    rng = np.random.default_rng(11 + ranks)
+    n, e, k, h = 57, 12, 4, 6
+    ids = np.stack([rng.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    if dtype == "bf16":
+        x = _bf16_bits_from_f32(rng.integers(-1, 2, size=(n, h)).astype(np.float32))
+        w = (2.0 ** rng.integers(-1, 1, size=(n, k))).astype(np.float32)
+    else:
+        x = rng.integers(-8, 9, size=(n, h)).astype(np.float32)
+        w = (2.0 ** rng.integers(-3, 3, size=(n, k))).astype(np.float32)
+
+    def expert_fn(rows, expert_ids):  # a per-expert map of the row: x * (expert + 1)
+        xf = _f32_from_bf16_bits(rows) if dtype == "bf16" else rows
+        yf = xf * (expert_ids[:, None] + 1).astype(np.float32)
+        return _bf16_bits_from_f32(yf) if dtype == "bf16" else yf
+
+    full = oracle.permute(x, ids, e)
+    full_experts = ids.reshape(-1)[full["permuted_idx"]]
+    want = oracle.unpermute(expert_fn(full["permuted_hidden_states"], full_experts), w,
+                            full["inv_permuted_idx"], dtype)
+    total = np.zeros((n, h), np.float64)
+    covered = np.zeros(n * k, np.int64)
+    for rank in range(ranks):
+        if layout == "contiguous":
+            owned = [g for g in range(e) if g * ranks // e == rank]
+        else:
+            owned = [g for g in range(e) if g % ranks == rank]
+        emap = [-1] * e
+        for l, g in enumerate(owned):
+            emap[g] = l
+        part = oracle.permute_local(x, ids, e, emap, len(owned))
+        covered += part["inv_permuted_idx"] >= 0
+        experts = ids.reshape(-1)[part["permuted_idx"]]
+        y = expert_fn(part["permuted_hidden_states"], experts)
+        out = oracle.unpermute(y, w, part["inv_permuted_idx"], dtype)
+        total += (_f32_from_bf16_bits(out) if dtype == "bf16" else out).astype(np.float64)
+    assert covered.tolist() == [1] * (n * k)  # every slot is local on exactly one rank
+    wantf = (_f32_from_bf16_bits(want) if dtype == "bf16" else want).astype(np.float64)
+    np.testing.assert_array_equal(total, wantf)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unpermute_minus_one_slots_match_masked_einsum(dtype):
+    rng = np.random.default_rng(12)
+    n, k, h = 37, 3, 20
+    inv = rng.permutation(n * k).astype(np.int32)
+    drop = rng.random(n * k) < 0.4
+    inv[drop] = -1
+    inv[0:k] = -1  # token 0 has no local slot: its output is exactly zero
+    y32 = rng.standard_normal((n * k, h)).astype(np.float32)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    y = _bf16_bits_from_f32(y32) if dtype == "bf16" else y32
+    yv = (_f32_from_bf16_bits(y) if dtype == "bf16" else y).astype(np.float64)
+    mask = (inv >= 0).reshape(n, k).astype(np.float64)
+    gathered = yv[np.where(inv >= 0, inv, 0)].reshape(n, k, h)
+    ref = np.einsum("tk,tkh->th", w.astype(np.float64) * mask, gathered)
+    out = oracle.unpermute(y, w, inv, dtype)
+    of = (_f32_from_bf16_bits(out) if dtype == "bf16" else out).astype(np.float64)
+    if dtype == "f32":
+        np.testing.assert_array_equal(out, ref.astype(np.float32))
+    else:
+        assert np.all(np.abs(of - ref) <= 2.0**-8 * np.abs(ref) + 2.0**-133)
+    assert np.all(of[0] == 0.0)
