@@ -1,6 +1,11 @@
 """Benchmark: one step = moe_permute + moe_unpermute over one batch (the whole path).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+                    [--ep N --ep-rank R --ep-layout contiguous]
+
+With ``--ep N`` the step is one expert-parallel rank's share: the
+local-expert permute (moe_permute_local, rank R's experts of an N-way split)
+and the unpermute of its output (remote slots skipped).
 
 Prints ONE JSON line.  ``value`` is whole-step achieved HBM bandwidth:
 algorithmic bytes of permute + unpermute (each input read once, each output
@@ -38,17 +43,30 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mixture_experts_token_amd", "csrc")
 
 
-def algorithmic_bytes(w) -> dict:
-    """Bytes the method must move: each input read once, each output written once."""
+def algorithmic_bytes(w, local=None) -> dict:
+    """Bytes the method must move: each input read once, each output written once.
+
+    local: None for the plain permute, else (tokens_read, local_rows,
+    num_local_experts) of a local-expert permute -- only tokens with a local
+    row are read, only local rows are written (and read back by the
+    unpermute, with their weights); every token still gets an output row.
+    """
     import workloads as W
 
     b = W.ELEMENT_BYTES[w.hidden_dtype]
     by = W.ELEMENT_BYTES[w.output_dtype]
     n, h, r, e = w.num_tokens, w.hidden_size, w.num_rows, w.num_experts
-    permute = n * h * b + r * h * b + 4 * r + 8 * r + 8 * (e + 1)
-    if w.hidden_dtype == "fp8_e4m3":
-        permute += 4 * n + 4 * r
-    unpermute = r * h * by + 4 * r + 4 * r + n * h * by
+    if local is None:
+        permute = n * h * b + r * h * b + 4 * r + 8 * r + 8 * (e + 1)
+        if w.hidden_dtype == "fp8_e4m3":
+            permute += 4 * n + 4 * r
+        unpermute = r * h * by + 4 * r + 4 * r + n * h * by
+    else:
+        t_read, m, nl = local
+        permute = t_read * h * b + m * h * b + 4 * r + 4 * e + 4 * r + 4 * m + 8 * (nl + 1)
+        if w.hidden_dtype == "fp8_e4m3":
+            permute += 4 * t_read + 4 * m
+        unpermute = m * h * by + 4 * r + 4 * m + n * h * by
     return {"permute": permute, "unpermute": unpermute, "total": permute + unpermute}
 
 
@@ -97,15 +115,18 @@ def load_probe():
     return lib
 
 
-def cpu_baseline(inputs_host, w, budget_s: float = 10.0, max_reps: int = 50) -> dict:
+def cpu_baseline(inputs_host, w, budget_s: float = 10.0, max_reps: int = 50, local=None, emap=None) -> dict:
     """The CPU oracle (single thread) on full steps of the workload until ~budget_s."""
     import oracle
 
     x, ids, wts, y = inputs_host
-    nbytes = algorithmic_bytes(w)["total"]
+    nbytes = algorithmic_bytes(w, local)["total"]
     reps, t0 = 0, time.perf_counter()
     while True:
-        p = oracle.permute(x, ids, w.num_experts)
+        if local is None:
+            p = oracle.permute(x, ids, w.num_experts)
+        else:
+            p = oracle.permute_local(x, ids, w.num_experts, emap, local[2])
         oracle.unpermute(y, wts, p["inv_permuted_idx"], w.output_dtype)
         reps += 1
         el = time.perf_counter() - t0
@@ -130,6 +151,9 @@ def main() -> int:
                          "float32 buffer 5 times; its known traffic scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--graph", action="store_true",
                     help="capture the K steps (and each per-operation batch) in a HIP graph and time its replay")
+    ap.add_argument("--ep", type=int, default=1, help="expert-parallel ranks: time one rank's local-expert step")
+    ap.add_argument("--ep-rank", type=int, default=0)
+    ap.add_argument("--ep-layout", default="contiguous", choices=["contiguous", "round_robin", "shuffled"])
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -149,9 +173,16 @@ def main() -> int:
     w = W.WORKLOADS[args.workload]
     if args.tokens:
         w = w.with_tokens(args.tokens)
-    nb = algorithmic_bytes(w)
-
     ids_np, wts_np = W.make_routing(w, seed=0)
+    local, emap_np, emap, n_off = None, None, None, w.num_experts + 1
+    if args.ep > 1:
+        emap_np, n_local = W.expert_map_for(w.num_experts, args.ep, args.ep_rank, args.ep_layout)
+        is_local = emap_np[ids_np] >= 0
+        local = (int(is_local.any(axis=1).sum()), int(is_local.sum()), n_local)
+        emap = torch.from_numpy(emap_np).to(dev)
+        n_off = n_local + 1
+    nb = algorithmic_bytes(w, local)
+
     ids = torch.from_numpy(ids_np).to(dev)
     wts = torch.from_numpy(wts_np).to(dev)
     x0, scale0 = W.make_hidden(w, seed=0, device=dev)
@@ -167,17 +198,25 @@ def main() -> int:
             "y": y0 if i == 0 else y0.clone(),
             "xp": torch.empty((w.num_rows, w.hidden_size), dtype=hdt, device=dev),
             "sp": None if scale0 is None else torch.empty(w.num_rows, dtype=torch.float32, device=dev),
-            "off": torch.empty(w.num_experts + 1, dtype=torch.int64, device=dev),
+            "off": torch.empty(n_off, dtype=torch.int64, device=dev),
             "perm": torch.empty(w.num_rows, dtype=torch.int32, device=dev),
             "inv": torch.empty(w.num_rows, dtype=torch.int32, device=dev),
             "out": torch.empty((w.num_tokens, w.hidden_size), dtype=y0.dtype, device=dev),
         })
-    ws = torch.empty(max(16, binding.moe_permute_workspace_size(w.num_tokens, w.topk, w.num_experts)),
-                     dtype=torch.uint8, device=dev)
+    if local is None:
+        ws_bytes = binding.moe_permute_workspace_size(w.num_tokens, w.topk, w.num_experts)
+    else:
+        ws_bytes = binding.moe_permute_local_workspace_size(w.num_tokens, w.topk, w.num_experts, local[2])
+    ws = torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev)
+
     # Kernels go to torch's current stream (the capture stream while a graph is recorded).
     def permute(s):
-        binding.moe_permute(s["x"], ids, w.num_experts, s["xp"], s["off"], s["perm"], s["inv"], ws,
-                            token_scale=s["scale"], permuted_scale=s["sp"])
+        if local is None:
+            binding.moe_permute(s["x"], ids, w.num_experts, s["xp"], s["off"], s["perm"], s["inv"], ws,
+                                token_scale=s["scale"], permuted_scale=s["sp"])
+        else:
+            binding.moe_permute_local(s["x"], ids, w.num_experts, emap, local[2], s["xp"], s["off"], s["perm"],
+                                      s["inv"], ws, token_scale=s["scale"], permuted_scale=s["sp"])
 
     def unpermute(s):
         binding.moe_unpermute(s["y"], wts, s["inv"], s["out"])
@@ -239,7 +278,7 @@ def main() -> int:
     # rotating buffers; the fastest of 1/2/4/8 vectors per lane with
     # non-temporal or plain stores counts.
     ceiling = None
-    probe = load_probe()
+    probe = load_probe() if local is None else None  # the probes model the full fan-out / fan-in only
     if probe is not None:
         dev_index = dev.index if dev.index is not None else 0
         xrow = w.hidden_size * W.ELEMENT_BYTES[w.hidden_dtype]
@@ -277,7 +316,8 @@ def main() -> int:
         dom, dom_us, dom_bytes = "unpermute", unperm_avg, nb["unpermute"]
     else:
         dom, dom_us, dom_bytes = "permute", perm_avg, nb["permute"]
-    traffic, kernels = load_traffic(w.name, dom)
+    profile_key = w.name if local is None else "%s_ep%d_r%d" % (w.name, args.ep, args.ep_rank)
+    traffic, kernels = load_traffic(profile_key, dom)
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
@@ -288,7 +328,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         to_np = lambda t: (t.view(torch.int16).cpu().numpy().view("uint16") if t.dtype == torch.bfloat16  # noqa
                            else t.cpu().numpy())
-        cpu = cpu_baseline((to_np(x0), ids_np, wts_np, to_np(y0)), w)
+        cpu = cpu_baseline((to_np(x0), ids_np, wts_np, to_np(y0)), w, local=local, emap=emap_np)
 
     line = {
         "metric": METRIC,
@@ -306,7 +346,11 @@ def main() -> int:
         "config": {"workload": w.name, "num_tokens": w.num_tokens, "hidden_size": w.hidden_size,
                    "num_experts": w.num_experts, "topk": w.topk, "hidden_dtype": w.hidden_dtype,
                    "output_dtype": w.output_dtype, "routing": w.routing, "buffer_sets": nsets,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU" if local is None else
+                   "one expert-parallel rank's share on a single GPU",
+                   **({} if local is None else {"expert_parallel": {
+                       "ep_size": args.ep, "rank": args.ep_rank, "layout": args.ep_layout,
+                       "local_experts": local[2], "tokens_read": local[0], "local_rows": local[1]}})},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "us_per_step": round(ms_step * 1e3, 3),
         "permute_us": round(perm_avg, 3),

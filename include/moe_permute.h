@@ -130,6 +130,53 @@ moe_status_t moe_permute(const void *hidden_states, int32_t dtype, const float *
                          size_t workspace_bytes, void *stream);
 
 /*
+ * moe_permute_local_workspace_size -- as moe_permute_workspace_size, for
+ * moe_permute_local with this num_local_experts.  Pure host function; returns
+ * 0 outside the limits (those of moe_permute, and
+ * 1 <= num_local_experts <= MOE_MAX_EXPERTS).
+ */
+size_t moe_permute_local_workspace_size(int64_t max_num_tokens, int32_t topk, int32_t num_experts,
+                                        int32_t num_local_experts);
+
+/*
+ * moe_permute_local -- moe_permute restricted to the experts of this rank
+ * (expert parallelism).  vLLM PR #14568, PR description, lists expert
+ * parallelism through an expert map as not yet supported by its kernels; the
+ * summary of vLLM PR #43014, "key code snippets", sizes the offsets by the
+ * number of local experts.  Reading taken here:
+ *
+ *   expert_map        [num_experts] int32 (device): expert_map[g] is the local
+ *                     id of global expert g, in [0, num_local_experts), or -1
+ *                     when g lives on another rank.  Several global experts may
+ *                     share a local id; their rows then share its block.
+ *   num_local_experts number of local experts L (1..MOE_MAX_EXPERTS)
+ *
+ * A row is local when its expert's map entry is >= 0; its key is that local
+ * id.  Local rows are counted, stably ordered by local id and copied exactly
+ * as moe_permute does for experts; the outputs change as follows:
+ *   expert_first_token_offset [L + 1]: entry l = local rows with local id < l,
+ *                     entry L = number of local rows M
+ *   permuted_idx, permuted_hidden_states, permuted_scale: the first M entries
+ *                     / rows are written, the rest of each buffer is untouched
+ *   inv_permuted_idx  [N*topk]: the slot of a local row, -1 for every other row
+ * Hidden rows of tokens with no local row are not read.  moe_unpermute skips
+ * the -1 entries, so its output is this rank's share of each token's sum.
+ * All other arguments, conventions and limits are those of moe_permute
+ * (buffers are still sized for N*topk rows; workspace from
+ * moe_permute_local_workspace_size).  A topk_ids value outside
+ * [0, num_experts), or a map entry of a used expert outside
+ * [-1, num_local_experts), is detected on the device: every entry of
+ * expert_first_token_offset is set to -1 and nothing else is written.
+ */
+moe_status_t moe_permute_local(const void *hidden_states, int32_t dtype, const float *token_scale,
+                               const int32_t *topk_ids, int64_t num_tokens, int64_t hidden_size,
+                               int32_t topk, int32_t num_experts, const int32_t *expert_map,
+                               int32_t num_local_experts, void *permuted_hidden_states,
+                               float *permuted_scale, int64_t *expert_first_token_offset,
+                               int32_t *permuted_idx, int32_t *inv_permuted_idx, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * moe_unpermute -- weighted top-k reduction of the expanded grouped-GEMM
  * output back to one row per token (vLLM PR #14568, PR description):
  *     output[t] = sum_{k=0}^{topk-1} topk_weights[t][k] * expanded_output[inv_permuted_idx[t*topk+k]]
@@ -138,11 +185,15 @@ moe_status_t moe_permute(const void *hidden_states, int32_t dtype, const float *
  *   expanded_output   [N*topk, hidden_size] of `dtype`, in permuted order
  *   dtype             MOE_DTYPE_F32 or MOE_DTYPE_BF16 (else MOE_ERR_UNSUPPORTED)
  *   topk_weights      [N, topk] float
- *   inv_permuted_idx  [N*topk] int32, as written by moe_permute
+ *   inv_permuted_idx  [N*topk] int32, as written by moe_permute or
+ *                     moe_permute_local
  *   output            [N, hidden_size] of `dtype` (out)
  *
- * An inv_permuted_idx entry outside [0, N*topk) is detected on the device:
- * that token's output row is filled with NaN and no out-of-bounds read happens.
+ * An entry of -1 (a row of an expert on another rank, see moe_permute_local)
+ * adds nothing: its row is not read and its weight not used; a token whose
+ * entries are all -1 gets a zero row.  Any other entry outside [0, N*topk)
+ * is detected on the device: that token's output row is filled with NaN and
+ * no out-of-bounds read happens.
  * Needs no workspace.
  */
 moe_status_t moe_unpermute(const void *expanded_output, int32_t dtype, const float *topk_weights,

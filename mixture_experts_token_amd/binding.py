@@ -6,7 +6,8 @@ stream, and raises on a non-OK status.  There is no fallback: if the library
 is missing the first call raises.
 
 The entry points carry the C names: ``moe_permute_supported``,
-``moe_permute_workspace_size``, ``moe_permute``, ``moe_unpermute``.
+``moe_permute_workspace_size``, ``moe_permute``, ``moe_unpermute``,
+``moe_permute_local_workspace_size``, ``moe_permute_local``.
 ``MoEPermuteScratch`` follows the preallocated-buffer design of the prhub
 summary of vLLM PR #43014 (section "key code snippets", MoEPermuteScratch):
 every buffer is allocated once for ``max_num_tokens`` and reused by each call.
@@ -57,6 +58,10 @@ def load_library() -> ctypes.CDLL:
         lib.moe_permute_workspace_size.restype = sz
         lib.moe_permute.argtypes = [p, i32, p, p, i64, i64, i32, i32, p, p, p, p, p, p, sz, p]
         lib.moe_permute.restype = ctypes.c_int
+        lib.moe_permute_local_workspace_size.argtypes = [i64, i32, i32, i32]
+        lib.moe_permute_local_workspace_size.restype = sz
+        lib.moe_permute_local.argtypes = [p, i32, p, p, i64, i64, i32, i32, p, i32, p, p, p, p, p, p, sz, p]
+        lib.moe_permute_local.restype = ctypes.c_int
         lib.moe_unpermute.argtypes = [p, i32, p, p, i64, i64, i32, p, p]
         lib.moe_unpermute.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -110,6 +115,25 @@ def moe_permute_workspace_size(max_num_tokens: int, topk: int, num_experts: int)
     return int(load_library().moe_permute_workspace_size(int(max_num_tokens), int(topk), int(num_experts)))
 
 
+def moe_permute_local_workspace_size(max_num_tokens: int, topk: int, num_experts: int,
+                                     num_local_experts: int) -> int:
+    return int(load_library().moe_permute_local_workspace_size(int(max_num_tokens), int(topk), int(num_experts),
+                                                               int(num_local_experts)))
+
+
+def _permute_args(hidden_states, topk_ids, workspace):
+    import torch
+
+    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
+        raise TypeError("topk_ids must be an int32 [num_tokens, topk] tensor")
+    if hidden_states is None:
+        hidden, code, hsize = None, MOE_DTYPE_BF16, 0
+    else:
+        hidden, code, hsize = hidden_states, _dtype_code(hidden_states), hidden_states.shape[-1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return hidden, code, hsize, ws_bytes
+
+
 def moe_permute(hidden_states, topk_ids, num_experts: int, permuted_hidden_states,
                 expert_first_token_offset, permuted_idx, inv_permuted_idx, workspace=None,
                 token_scale=None, permuted_scale=None, stream=None) -> None:
@@ -119,16 +143,8 @@ def moe_permute(hidden_states, topk_ids, num_experts: int, permuted_hidden_state
     float8_e4m3fn) or None for an index-only permute; ``topk_ids`` int32
     [N, topk].  Outputs are written in place.
     """
-    import torch
-
-    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
-        raise TypeError("topk_ids must be an int32 [num_tokens, topk] tensor")
+    hidden, code, hsize, ws_bytes = _permute_args(hidden_states, topk_ids, workspace)
     n, topk = topk_ids.shape
-    if hidden_states is None:
-        hidden, code, hsize = None, MOE_DTYPE_BF16, 0
-    else:
-        hidden, code, hsize = hidden_states, _dtype_code(hidden_states), hidden_states.shape[-1]
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     status = load_library().moe_permute(
         _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), n, hsize, topk, int(num_experts),
         _ptr(permuted_hidden_states) if hsize else None, _ptr(permuted_scale),
@@ -136,6 +152,31 @@ def moe_permute(hidden_states, topk_ids, num_experts: int, permuted_hidden_state
         _ptr(workspace), ws_bytes, _stream(stream, topk_ids))
     if status != MOE_OK:
         raise MoEError(status, "moe_permute")
+
+
+def moe_permute_local(hidden_states, topk_ids, num_experts: int, expert_map, num_local_experts: int,
+                      permuted_hidden_states, expert_first_token_offset, permuted_idx, inv_permuted_idx,
+                      workspace=None, token_scale=None, permuted_scale=None, stream=None) -> None:
+    """Permute restricted to this rank's experts (see moe_permute_local in the C header).
+
+    ``expert_map`` int32 [num_experts] on the device: local id or -1.  The
+    offsets have num_local_experts + 1 entries; inv_permuted_idx is -1 for
+    rows of remote experts; only the first offsets[-1] rows are written.
+    """
+    import torch
+
+    if expert_map is None or expert_map.dtype != torch.int32 or expert_map.shape != (int(num_experts),):
+        raise TypeError("expert_map must be an int32 [num_experts] tensor")
+    hidden, code, hsize, ws_bytes = _permute_args(hidden_states, topk_ids, workspace)
+    n, topk = topk_ids.shape
+    status = load_library().moe_permute_local(
+        _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), n, hsize, topk, int(num_experts),
+        _ptr(expert_map), int(num_local_experts),
+        _ptr(permuted_hidden_states) if hsize else None, _ptr(permuted_scale),
+        _ptr(expert_first_token_offset), _ptr(permuted_idx), _ptr(inv_permuted_idx),
+        _ptr(workspace), ws_bytes, _stream(stream, topk_ids))
+    if status != MOE_OK:
+        raise MoEError(status, "moe_permute_local")
 
 
 def moe_unpermute(expanded_output, topk_weights, inv_permuted_idx, output, stream=None) -> None:
@@ -157,33 +198,44 @@ class MoEPermuteScratch:
     """Every permute buffer, allocated once for ``max_num_tokens`` and reused.
 
     Mirrors MoEPermuteScratch in the prhub summary of vLLM PR #43014 (section
-    "key code snippets"): offsets int64 [num_experts + 1]; permuted_idx and
-    inv_permuted_idx int32 [max_num_tokens * topk]; permuted_hidden_states
+    "key code snippets"): offsets int64 [num_local_experts + 1]; permuted_idx
+    and inv_permuted_idx int32 [max_num_tokens * topk]; permuted_hidden_states
     only when ``hidden_size`` is given; an opaque workspace sized by the
     library's size query.  ``validate`` performs the same checks the summary
-    lists (device, token count, topk, hidden size and type).
+    lists (device, token count, topk, hidden size and type).  With
+    ``expert_map`` (int32 [num_experts], local id or -1) every call runs the
+    local-expert permute over ``num_local_experts`` experts.
     """
 
     def __init__(self, max_num_tokens: int, topk: int, num_experts: int, device, hidden_size: int | None = None,
-                 hidden_dtype=None, with_scale: bool = False):
+                 hidden_dtype=None, with_scale: bool = False, expert_map=None, num_local_experts: int | None = None):
         import torch
 
         self.max_num_tokens = int(max_num_tokens)
         self.topk = int(topk)
         self.num_experts = int(num_experts)
+        if (expert_map is None) != (num_local_experts is None):
+            raise ValueError("expert_map and num_local_experts go together")
+        self.expert_map = expert_map
+        self.num_local_experts = self.num_experts if expert_map is None else int(num_local_experts)
         self.device = torch.device(device)
         self.hidden_size = hidden_size
         self.hidden_dtype = hidden_dtype
         self.max_expanded_rows = self.max_num_tokens * self.topk
         rows = self.max_expanded_rows
-        self.expert_first_token_offset = torch.empty(self.num_experts + 1, dtype=torch.int64, device=self.device)
+        self.expert_first_token_offset = torch.empty(self.num_local_experts + 1, dtype=torch.int64,
+                                                     device=self.device)
         self.permuted_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
         self.inv_permuted_idx = torch.empty(rows, dtype=torch.int32, device=self.device)
         self.permuted_hidden_states = None
         if hidden_size is not None:
             self.permuted_hidden_states = torch.empty(rows * hidden_size, dtype=hidden_dtype, device=self.device)
         self.permuted_scale = torch.empty(rows, dtype=torch.float32, device=self.device) if with_scale else None
-        ws = moe_permute_workspace_size(self.max_num_tokens, self.topk, self.num_experts)
+        if expert_map is None:
+            ws = moe_permute_workspace_size(self.max_num_tokens, self.topk, self.num_experts)
+        else:
+            ws = moe_permute_local_workspace_size(self.max_num_tokens, self.topk, self.num_experts,
+                                                  self.num_local_experts)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
 
     def validate(self, hidden_states, topk_ids) -> None:
@@ -216,9 +268,15 @@ class MoEPermuteScratch:
             if self.permuted_scale is None:
                 raise ValueError("scratch was created without with_scale=True")
             out_scale = self.permuted_scale[:rows]
-        moe_permute(hidden_states, topk_ids, self.num_experts, out_hidden, self.expert_first_token_offset,
-                    self.permuted_idx[:rows], self.inv_permuted_idx[:rows], self.workspace,
-                    token_scale=token_scale, permuted_scale=out_scale, stream=stream)
+        if self.expert_map is None:
+            moe_permute(hidden_states, topk_ids, self.num_experts, out_hidden, self.expert_first_token_offset,
+                        self.permuted_idx[:rows], self.inv_permuted_idx[:rows], self.workspace,
+                        token_scale=token_scale, permuted_scale=out_scale, stream=stream)
+        else:
+            moe_permute_local(hidden_states, topk_ids, self.num_experts, self.expert_map, self.num_local_experts,
+                              out_hidden, self.expert_first_token_offset, self.permuted_idx[:rows],
+                              self.inv_permuted_idx[:rows], self.workspace, token_scale=token_scale,
+                              permuted_scale=out_scale, stream=stream)
         return {
             "permuted_hidden_states": out_hidden,
             "permuted_scale": out_scale,

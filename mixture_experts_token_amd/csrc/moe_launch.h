@@ -16,10 +16,12 @@ struct PermuteArgs {
     int64_t num_tokens;
     int64_t row_vecs;               // row length in 16-byte vectors (0: indices only)
     int32_t topk;
-    int32_t num_experts;
+    int32_t num_experts;            // ids are valid in [0, num_experts)
+    const int32_t* expert_map;      // [num_experts] local id or -1, or null (every expert is local)
+    int32_t num_buckets;            // sort keys: num_experts, or the local expert count with a map
     void* permuted_hidden_states;   // [N*topk, row_vecs * 16 bytes]
     float* permuted_scale;          // [N*topk] or null
-    int64_t* expert_first_token_offset;  // [E+1]
+    int64_t* expert_first_token_offset;  // [num_buckets + 1]
     int32_t* permuted_idx;          // [N*topk]
     int32_t* inv_permuted_idx;      // [N*topk]
 };

@@ -86,17 +86,36 @@ int moe_permute_supported(int device) {
 
 size_t moe_permute_workspace_size(int64_t max_num_tokens, int32_t topk, int32_t num_experts) {
     if (!sizes_ok(max_num_tokens, topk, num_experts)) return 0;
-    return moe::workspace_bound(max_num_tokens, topk, num_experts);
+    return moe::workspace_bound(max_num_tokens, topk, num_experts, 0);
 }
 
-moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* token_scale,
-                         const int32_t* topk_ids, int64_t num_tokens, int64_t hidden_size, int32_t topk,
-                         int32_t num_experts, void* permuted_hidden_states, float* permuted_scale,
-                         int64_t* expert_first_token_offset, int32_t* permuted_idx, int32_t* inv_permuted_idx,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+size_t moe_permute_local_workspace_size(int64_t max_num_tokens, int32_t topk, int32_t num_experts,
+                                        int32_t num_local_experts) {
+    if (!sizes_ok(max_num_tokens, topk, num_experts)) return 0;
+    if (num_local_experts < 1 || num_local_experts > MOE_MAX_EXPERTS) return 0;
+    return moe::workspace_bound(max_num_tokens, topk, num_local_experts, num_experts);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Both permute entry points: expert_map == nullptr sorts by expert over
+// num_experts buckets; otherwise by local id over num_local_experts buckets.
+moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float* token_scale,
+                          const int32_t* topk_ids, int64_t num_tokens, int64_t hidden_size, int32_t topk,
+                          int32_t num_experts, const int32_t* expert_map, int32_t num_local_experts,
+                          void* permuted_hidden_states, float* permuted_scale, int64_t* expert_first_token_offset,
+                          int32_t* permuted_idx, int32_t* inv_permuted_idx, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     const int64_t eb = element_bytes(dtype);
     if (eb == 0) return MOE_ERR_INVALID_ARG;
     if (!sizes_ok(num_tokens, topk, num_experts)) return MOE_ERR_INVALID_ARG;
+    const bool mapped = expert_map != nullptr;
+    if (mapped && (num_local_experts < 1 || num_local_experts > MOE_MAX_EXPERTS)) return MOE_ERR_INVALID_ARG;
+    if (mapped && !aligned(expert_map, 4)) return MOE_ERR_MISALIGNED;
+    const int32_t buckets = mapped ? num_local_experts : num_experts;
+    const int map_entries = mapped ? num_experts : 0;
     if (hidden_size < 0 || hidden_size > kMaxRowBytes / eb) return MOE_ERR_INVALID_ARG;
     if (expert_first_token_offset == nullptr) return MOE_ERR_INVALID_ARG;
     if (!aligned(expert_first_token_offset, 8)) return MOE_ERR_MISALIGNED;
@@ -106,8 +125,8 @@ moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* 
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (num_tokens == 0) {
-        return moe::launch_fill_offsets(expert_first_token_offset, num_experts, 0, s) == hipSuccess ? MOE_OK
-                                                                                                    : MOE_ERR_HIP;
+        return moe::launch_fill_offsets(expert_first_token_offset, buckets, 0, s) == hipSuccess ? MOE_OK
+                                                                                                : MOE_ERR_HIP;
     }
     if (topk_ids == nullptr || permuted_idx == nullptr || inv_permuted_idx == nullptr) return MOE_ERR_INVALID_ARG;
     if (hidden_size > 0 && (hidden_states == nullptr || permuted_hidden_states == nullptr))
@@ -118,7 +137,7 @@ moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* 
     if (hidden_size > 0 && (!aligned(hidden_states, 16) || !aligned(permuted_hidden_states, 16)))
         return MOE_ERR_MISALIGNED;
 
-    const moe::PermutePlan plan = moe::plan_permute(num_tokens, topk, num_experts);
+    const moe::PermutePlan plan = moe::plan_permute(num_tokens, topk, buckets, map_entries);
     if (workspace_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (plan.ws_bytes > 0) {
         if (workspace == nullptr) return MOE_ERR_INVALID_ARG;
@@ -130,7 +149,7 @@ moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* 
     const Span outs[] = {
         {copy_rows ? permuted_hidden_states : nullptr, rows * (uint64_t)row_bytes},
         {permuted_scale, rows * 4},
-        {expert_first_token_offset, 8ull * (uint64_t)(num_experts + 1)},
+        {expert_first_token_offset, 8ull * (uint64_t)(buckets + 1)},
         {permuted_idx, rows * 4},
         {inv_permuted_idx, rows * 4},
         {workspace, (uint64_t)plan.ws_bytes},
@@ -139,8 +158,9 @@ moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* 
         {copy_rows ? hidden_states : nullptr, (uint64_t)num_tokens * (uint64_t)row_bytes},
         {token_scale, (uint64_t)num_tokens * 4},
         {topk_ids, rows * 4},
+        {expert_map, 4ull * (uint64_t)map_entries},
     };
-    if (any_overlap(outs, 6, ins, 3)) return MOE_ERR_INVALID_ARG;
+    if (any_overlap(outs, 6, ins, 4)) return MOE_ERR_INVALID_ARG;
 
     moe::PermuteArgs a;
     a.hidden_states = copy_rows ? hidden_states : nullptr;
@@ -150,12 +170,41 @@ moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* 
     a.row_vecs = row_bytes / 16;
     a.topk = topk;
     a.num_experts = num_experts;
+    a.expert_map = expert_map;
+    a.num_buckets = buckets;
     a.permuted_hidden_states = copy_rows ? permuted_hidden_states : nullptr;
     a.permuted_scale = permuted_scale;
     a.expert_first_token_offset = expert_first_token_offset;
     a.permuted_idx = permuted_idx;
     a.inv_permuted_idx = inv_permuted_idx;
     return moe::launch_permute(a, plan, workspace, s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* token_scale,
+                         const int32_t* topk_ids, int64_t num_tokens, int64_t hidden_size, int32_t topk,
+                         int32_t num_experts, void* permuted_hidden_states, float* permuted_scale,
+                         int64_t* expert_first_token_offset, int32_t* permuted_idx, int32_t* inv_permuted_idx,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    return permute_impl(hidden_states, dtype, token_scale, topk_ids, num_tokens, hidden_size, topk, num_experts,
+                        nullptr, 0, permuted_hidden_states, permuted_scale, expert_first_token_offset, permuted_idx,
+                        inv_permuted_idx, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_permute_local(const void* hidden_states, int32_t dtype, const float* token_scale,
+                               const int32_t* topk_ids, int64_t num_tokens, int64_t hidden_size, int32_t topk,
+                               int32_t num_experts, const int32_t* expert_map, int32_t num_local_experts,
+                               void* permuted_hidden_states, float* permuted_scale,
+                               int64_t* expert_first_token_offset, int32_t* permuted_idx,
+                               int32_t* inv_permuted_idx, void* workspace, size_t workspace_bytes, void* stream) {
+    if (expert_map == nullptr) return MOE_ERR_INVALID_ARG;
+    return permute_impl(hidden_states, dtype, token_scale, topk_ids, num_tokens, hidden_size, topk, num_experts,
+                        expert_map, num_local_experts, permuted_hidden_states, permuted_scale,
+                        expert_first_token_offset, permuted_idx, inv_permuted_idx, workspace, workspace_bytes,
+                        stream);
 }
 
 moe_status_t moe_unpermute(const void* expanded_output, int32_t dtype, const float* topk_weights,

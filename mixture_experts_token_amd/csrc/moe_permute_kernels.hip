@@ -69,6 +69,58 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ----------------------------------------------------------------------------
+// Sort keys.  Without a map a row's key is its expert id.  With a local-expert
+// map (expert parallelism: the offsets cover this rank's experts only) the key
+// is the expert's local id, and a row whose expert lives on another rank gets
+// no key: it is not ranked, copied or counted, and its inverse index is -1.
+// ----------------------------------------------------------------------------
+constexpr int kRemoteKey = -1;  // expert on another rank
+constexpr int kBadKey = -2;     // id outside [0, E), or a map entry outside [-1, B)
+
+// kMap: the kernel was built for a map (map_s is its LDS copy); otherwise
+// map_s is not read and the key is the expert id.
+template <bool kMap>
+__device__ __forceinline__ int bucket_of(int id, int E, const int* map_s, int B) {
+    if ((unsigned)id >= (unsigned)E) return kBadKey;
+    if constexpr (!kMap) {
+        return id;
+    } else {
+        const int m = map_s[id];
+        if (m == -1) return kRemoteKey;
+        return (unsigned)m < (unsigned)B ? m : kBadKey;
+    }
+}
+
+// The map, read into registers with the other early index loads (before any
+// row prefetch: the vector-memory counter retires in issue order) and written
+// to LDS before the first barrier.  Empty without a map.
+template <int NT, bool kMap>
+struct MapStage {
+    static constexpr int kPer = kMap ? (kMaxExperts + NT - 1) / NT : 0;
+    int v[kPer > 0 ? kPer : 1];
+
+    __device__ __forceinline__ void load(const PermuteArgs& a) {
+        const int E = a.num_experts;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = (int)threadIdx.x + j * NT;
+            v[j] = a.expert_map[i < E ? i : E - 1];
+        }
+    }
+
+    // Returns the LDS copy (null without a map).
+    __device__ __forceinline__ const int* store(const PermuteArgs& a, int* map_s) const {
+        if constexpr (!kMap) return nullptr;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = (int)threadIdx.x + j * NT;
+            if (i < a.num_experts) map_s[i] = v[j];
+        }
+        return map_s;
+    }
+};
+
 // Exclusive prefix sum of data[0..n) in LDS, in place; returns the total.
 // Every thread of the workgroup must call it.  tmp: NT/64 ints of LDS.
 template <int NT>
@@ -107,24 +159,24 @@ __device__ int block_exclusive_scan(int* data, int n, int* tmp) {
 // ----------------------------------------------------------------------------
 // Stable ranks within one tile of expanded rows, keys already in LDS.
 //
-// key_s[i] is the expert of tile row i, or -1 for a row whose id is out of
-// range (such rows get no rank).  Wave w owns rows [w*span, (w+1)*span) and
+// key_s[i] is the bucket of tile row i, or -1 for a row without one (an
+// out-of-range id or a remote expert; such rows get no rank).  Wave w owns rows [w*span, (w+1)*span) and
 // walks them 64 at a time, so a row's rank is (rows of its expert in earlier
 // waves) + (rows of its expert earlier in its own wave).  On return, after a
 // barrier:
-//   rank_s[i] rank of row i among the tile's rows with the same expert
-//   cnt_s[e]  rows of the tile routed to expert e
-// wave_s (NT/64 * E ints) must be zero on entry; it is clobbered.
+//   rank_s[i] rank of row i among the tile's rows with the same key
+//   cnt_s[e]  rows of the tile with key e (B keys)
+// wave_s (NT/64 * B ints) must be zero on entry; it is clobbered.
 // ----------------------------------------------------------------------------
 template <int NT>
-__device__ void rank_tile(const int* key_s, int tile_rows, int E, int nbits, int* rank_s, int* wave_s, int* cnt_s) {
+__device__ void rank_tile(const int* key_s, int tile_rows, int B, int nbits, int* rank_s, int* wave_s, int* cnt_s) {
     constexpr int W = NT / kWaveSize;
     const int w = wave_index();
     const int lane = threadIdx.x % kWaveSize;
     const int span = (tile_rows + NT - 1) / NT * kWaveSize;
     const int beg = w * span;
     const int end = min(beg + span, tile_rows);
-    int* run = wave_s + w * E;
+    int* run = wave_s + w * B;
     for (int base = beg; base < end; base += kWaveSize) {
         const int i = base + lane;
         const int key = i < end ? key_s[i] : -1;
@@ -140,12 +192,12 @@ __device__ void rank_tile(const int* key_s, int tile_rows, int E, int nbits, int
         }
     }
     lds_barrier();
-    for (int e = threadIdx.x; e < E; e += NT) {
+    for (int e = threadIdx.x; e < B; e += NT) {
         int s = 0;
 #pragma unroll
         for (int v = 0; v < W; ++v) {
-            const int c = wave_s[v * E + e];
-            wave_s[v * E + e] = s;
+            const int c = wave_s[v * B + e];
+            wave_s[v * B + e] = s;
             s += c;
         }
         cnt_s[e] = s;
@@ -153,7 +205,7 @@ __device__ void rank_tile(const int* key_s, int tile_rows, int E, int nbits, int
     lds_barrier();
     for (int i = threadIdx.x; i < tile_rows; i += NT) {
         const int key = key_s[i];
-        if (key >= 0) rank_s[i] += wave_s[(i / span) * E + key];
+        if (key >= 0) rank_s[i] += wave_s[(i / span) * B + key];
     }
     lds_barrier();
 }
@@ -163,36 +215,84 @@ __device__ void rank_tile(const int* key_s, int tile_rows, int E, int nbits, int
 // of U*64 16-byte vectors); wave w takes items w, w+W, ...  dest_s[tl*topk+k]
 // is the permuted row of the tile's token tl, slot k.
 // ----------------------------------------------------------------------------
-template <int U, bool kNTStore>
+template <int U, bool kNTStore, bool kSparse>
 struct TileCopy {
     const u32x4* __restrict__ src;  // first row of the tile
     u32x4* __restrict__ dst;        // permuted_hidden_states
+    const int32_t* ids;             // topk_ids of the tile's first token
+    const int32_t* emap;            // expert map (kSparse)
     int64_t rv;                     // row length in vectors
     int64_t rows_total;             // N * topk
     int nchunks;
     int items;
     int K;
+    int E;
     int lane;
 
     __device__ TileCopy(const PermuteArgs& a, int64_t t0, int ntok)
         : src(reinterpret_cast<const u32x4*>(a.hidden_states) + t0 * a.row_vecs),
           dst(reinterpret_cast<u32x4*>(a.permuted_hidden_states)),
+          ids(a.topk_ids + t0 * a.topk),
+          emap(a.expert_map),
           rv(a.row_vecs),
           rows_total(a.num_tokens * a.topk),
           nchunks((int)((a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize))),
           items(ntok * (int)((a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize))),
           K(a.topk),
+          E(a.num_experts),
           lane((int)(threadIdx.x % kWaveSize)) {}
 
-    __device__ __forceinline__ void load(int it, u32x4 (&v)[U]) const {
+    __device__ __forceinline__ void load_rows(int it, u32x4 (&v)[U], bool live) const {
         const int tl = it / nchunks;
         const int64_t base = (int64_t)(it - tl * nchunks) * (U * kWaveSize) + lane;
         const u32x4* s = src + tl * rv;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t idx = base + u * kWaveSize;
-            v[u] = idx < rv ? __builtin_nontemporal_load(s + idx) : u32x4{0u, 0u, 0u, 0u};
+            v[u] = (live && idx < rv) ? __builtin_nontemporal_load(s + idx) : u32x4{0u, 0u, 0u, 0u};
         }
+    }
+
+    // Loads item it's chunk.  kSparse (a local-expert map: some rows have no
+    // destination): a token with no destination is not read at all.
+    __device__ __forceinline__ void load(int it, u32x4 (&v)[U], const int* dest_s) const {
+        bool live = true;
+        if constexpr (kSparse) {
+            const int tl = it / nchunks;
+            live = false;
+            for (int k = 0; k < K; ++k) live |= (uint32_t)dest_s[tl * K + k] < (uint64_t)rows_total;
+        }
+        load_rows(it, v, live);
+    }
+
+    // Early load of wave w's first item, before the destinations exist.  With
+    // kSparse the token is read only if one of its experts is local; its ids
+    // and their map entries sit at wave-uniform addresses, so those reads go
+    // through the scalar path and leave the vector-memory counter to the row
+    // loads.  A token with nothing local is not read (none of its chunks is
+    // stored).
+    __device__ __forceinline__ void prefetch(int w, u32x4 (&v)[U]) const {
+        if (rv == 0 || w >= items) return;
+        bool live = true;
+        if constexpr (kSparse) {
+            // Eight ids, then their eight map entries, per round trip (clamped
+            // addresses, so every read is in bounds and none waits on a branch).
+            const int tl = __builtin_amdgcn_readfirstlane(w / nchunks);
+            const int32_t* tid = ids + tl * K;
+            live = false;
+            int any = 0;
+            for (int k0 = 0; k0 < K; k0 += 8) {
+                int id[8], m[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) id[q] = tid[min(k0 + q, K - 1)];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) m[q] = emap[min((unsigned)id[q], (unsigned)(E - 1))];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) any |= (int)((unsigned)id[q] < (unsigned)E) & (int)(m[q] >= 0);
+            }
+            live = any != 0;
+        }
+        load_rows(w, v, live);
     }
 
     __device__ __forceinline__ void store(int it, const u32x4 (&v)[U], const int* dest_s) const {
@@ -218,14 +318,15 @@ struct TileCopy {
 
 // Store every item of wave w, starting from `cur` (already loaded for item w),
 // loading item it+W while item it is stored.
-template <int U, int NT, bool kNTStore>
-__device__ __forceinline__ void copy_items_pipelined(const TileCopy<U, kNTStore>& tc, u32x4 (&cur)[U],
+// cur already holds the wave's first item (TileCopy::prefetch).
+template <int U, int NT, bool kNTStore, bool kSparse>
+__device__ __forceinline__ void copy_items_pipelined(const TileCopy<U, kNTStore, kSparse>& tc, u32x4 (&cur)[U],
                                                      const int* dest_s) {
     constexpr int W = NT / kWaveSize;
     for (int it = wave_index(); it < tc.items; it += W) {
         u32x4 nxt[U];
         const bool more = it + W < tc.items;
-        if (more) tc.load(it + W, nxt);
+        if (more) tc.load(it + W, nxt, dest_s);
         tc.store(it, cur, dest_s);
         if (more) {
 #pragma unroll
@@ -251,7 +352,8 @@ __device__ __forceinline__ void copy_tile_scales(const PermuteArgs& a, int64_t t
 // [w*span, w*span + span), span = ceil(T / NT) * 64, at most kB batches of 64.
 // ----------------------------------------------------------------------------
 
-// Expert ids of this wave's tile rows (issued early, independent loads).
+// Expert ids of this wave's tile rows (issued early, independent loads);
+// tile_keys_to_buckets turns them into sort keys once the map is in LDS.
 template <int kB>
 __device__ __forceinline__ void load_tile_keys(const int32_t* __restrict__ ids, int row0, int T, int span, int w,
                                                int lane, int (&tkey)[kB]) {
@@ -262,15 +364,23 @@ __device__ __forceinline__ void load_tile_keys(const int32_t* __restrict__ ids, 
     }
 }
 
+template <bool kMap, int kB>
+__device__ __forceinline__ void tile_keys_to_buckets(int (&tkey)[kB], int E, const int* map_s, int B) {
+#pragma unroll
+    for (int b = 0; b < kB; ++b) tkey[b] = bucket_of<kMap>(tkey[b], E, map_s, B);
+}
+
 __device__ __forceinline__ bool own_row(int b, int i, int T, int span, int w) {
     return b * kWaveSize < span && i < T && i < w * span + span;
 }
 
 // Stable ranks of this wave's tile rows among the wave's rows with the same
-// expert (ballot match + mbcnt); the lowest lane of each equal-key group adds
-// the group size to the wave's running count run[key].  Returns the number of
-// out-of-range ids among the wave's rows (this lane's share).
-template <int kB>
+// key (ballot match + mbcnt); the lowest lane of each equal-key group adds
+// the group size to the wave's running count run[key].  Rows without a key
+// are not ranked.  Returns the number of bad ids or map entries among the
+// wave's rows (this lane's share).  Without a map tkey holds the raw expert
+// ids (valid in [0, E)); with one, the keys from tile_keys_to_buckets.
+template <bool kMap, int kB>
 __device__ __forceinline__ int rank_own_rows(const int (&tkey)[kB], int T, int span, int E, int nbits, int w,
                                              int lane, int* run, int (&trank)[kB]) {
     int nbad = 0;
@@ -281,8 +391,14 @@ __device__ __forceinline__ int rank_own_rows(const int (&tkey)[kB], int T, int s
         if (b * kWaveSize < span && base < T) {  // wave-uniform
             const int i = base + lane;
             const bool in_tile = own_row(b, i, T, span, w);
-            const bool ok = in_tile && (unsigned)tkey[b] < (unsigned)E;
-            nbad += (in_tile && !ok) ? 1 : 0;
+            bool ok;
+            if constexpr (kMap) {
+                ok = in_tile && tkey[b] >= 0;
+                nbad += (in_tile && tkey[b] == kBadKey) ? 1 : 0;
+            } else {
+                ok = in_tile && (unsigned)tkey[b] < (unsigned)E;
+                nbad += (in_tile && !ok) ? 1 : 0;
+            }
             const uint64_t same = lanes_with_same_key(tkey[b], ok, nbits);
             const int below = lanes_below(same);
             if (ok) {
@@ -295,14 +411,15 @@ __device__ __forceinline__ int rank_own_rows(const int (&tkey)[kB], int T, int s
     return nbad;
 }
 
-// Per expert e (kPer consecutive experts per thread): turn the per-wave counts
-// wave_s[v*E + e] into prefixes over waves, take the expert's total rows
-// total_of(e, rows_in_tile), scan the totals over experts (one barrier) into
-// expert_first_token_offset (written when write_off), and store the tile's
-// base in each expert, offset + before_of(e), into base_s[e].  Each expert is
-// read and written by one thread only, so base_s may alias before_of's data.
+// Per bucket e of B (kPer consecutive buckets per thread): turn the per-wave
+// counts wave_s[v*B + e] into prefixes over waves, take the bucket's total
+// rows total_of(e, rows_in_tile), scan the totals over buckets (one barrier)
+// into expert_first_token_offset[0..B] (written when write_off), and store the
+// tile's base in each bucket, offset + before_of(e), into base_s[e].  Each
+// bucket is read and written by one thread only, so base_s may alias
+// before_of's data.
 template <int NT, int kPer, class TotalFn, class BeforeFn>
-__device__ __forceinline__ void expert_bases(int E, int* wave_s, int* base_s, int* scan_tmp, int64_t* off_out,
+__device__ __forceinline__ void expert_bases(int B, int* wave_s, int* base_s, int* scan_tmp, int64_t* off_out,
                                              bool write_off, TotalFn total_of, BeforeFn before_of) {
     constexpr int W = NT / kWaveSize;
     const int w = threadIdx.x / kWaveSize, lane = threadIdx.x % kWaveSize;
@@ -313,12 +430,12 @@ __device__ __forceinline__ void expert_bases(int E, int* wave_s, int* base_s, in
     for (int q = 0; q < kPer; ++q) {
         const int e = e0 + q;
         tot[q] = 0;
-        if (e < E) {
+        if (e < B) {
             int c = 0;
 #pragma unroll
             for (int v = 0; v < W; ++v) {
-                const int x = wave_s[v * E + e];
-                wave_s[v * E + e] = c;
+                const int x = wave_s[v * B + e];
+                wave_s[v * B + e] = c;
                 c += x;
             }
             tot[q] = total_of(e, c);
@@ -343,20 +460,20 @@ __device__ __forceinline__ void expert_bases(int E, int* wave_s, int* base_s, in
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int e = e0 + q;
-        if (e < E) {
+        if (e < B) {
             if (write_off) off_out[e] = excl;
             base_s[e] = excl + before_of(e);
             excl += tot[q];
         }
     }
-    if (write_off && threadIdx.x == 0) off_out[E] = total;
+    if (write_off && threadIdx.x == 0) off_out[B] = total;
 }
 
-// Destinations of this wave's tile rows: tile base + rows of the same expert
-// in earlier waves + rank within the wave.
-template <int kB>
+// Destinations of this wave's tile rows: tile base + rows of the same key in
+// earlier waves + rank within the wave; -1 for a row of a remote expert.
+template <bool kMap, int kB>
 __device__ __forceinline__ void write_dests(const PermuteArgs& a, const int (&tkey)[kB], const int (&trank)[kB],
-                                            int row0, int T, int span, int E, int w, int lane, const int* base_s,
+                                            int row0, int T, int span, int B, int w, int lane, const int* base_s,
                                             const int* wave_s, int* dest_s) {
     const int64_t R = a.num_tokens * a.topk;
 #pragma unroll
@@ -364,7 +481,14 @@ __device__ __forceinline__ void write_dests(const PermuteArgs& a, const int (&tk
         const int i = w * span + b * kWaveSize + lane;
         if (own_row(b, i, T, span, w)) {
             const int key = tkey[b];
-            const int dest = base_s[key] + wave_s[w * E + key] + trank[b];
+            if constexpr (kMap) {
+                if (key < 0) {  // remote expert (bad keys never get here)
+                    dest_s[i] = -1;
+                    a.inv_permuted_idx[row0 + i] = -1;
+                    continue;
+                }
+            }
+            const int dest = base_s[key] + wave_s[w * B + key] + trank[b];
             dest_s[i] = dest;
             a.inv_permuted_idx[row0 + i] = dest;
             if ((uint32_t)dest < (uint64_t)R) a.permuted_idx[dest] = row0 + i;
@@ -378,15 +502,16 @@ __device__ __forceinline__ void write_dests(const PermuteArgs& a, const int (&tk
 // ranks its own rows, derives expert_first_token_offset and its own base per
 // expert, scatters permuted_idx / inv_permuted_idx and copies its rows.
 // ----------------------------------------------------------------------------
-template <int NT, int U, bool kNTStore>
+template <int NT, int U, bool kNTStore, bool kMap>
 __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int tokens_per_tile, int nbits) {
     constexpr int W = NT / kWaveSize;
     constexpr int kIds = kFusedMaxRows / NT;                       // expert ids held per thread
     constexpr int kBatches = (kMaxTileRows + NT - 1) / NT;         // tile batches of 64 per wave
-    constexpr int kPer = (kMaxExperts + NT - 1) / NT;              // experts per thread in the scan
+    constexpr int kPer = (kMaxExperts + NT - 1) / NT;              // buckets per thread in the scan
     static_assert(kFusedMaxRows % NT == 0, "fused row bound must be a multiple of the workgroup size");
     extern __shared__ int smem[];
     const int E = a.num_experts;
+    const int B = a.num_buckets;
     const int K = a.topk;
     const int w = wave_index();
     const int lane = threadIdx.x % kWaveSize;
@@ -398,29 +523,32 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
     const int R = (int)(a.num_tokens * K);  // <= kFusedMaxRows
     const int span = (T + NT - 1) / NT * kWaveSize;
 
-    // Loads, all independent: every expert id of the problem, this wave's own
-    // tile rows, then the first row chunk of this wave.  The vector-memory
-    // counter retires in issue order, so the row loads stay in flight while
-    // the ids are consumed.
+    // Loads, all independent: every expert id of the problem, the map, this
+    // wave's own tile rows, then the first row chunk of this wave.  The
+    // vector-memory counter retires in issue order, so the row loads stay in
+    // flight while the ids are consumed.
     int idv[kIds];
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
         const int r = (int)threadIdx.x + j * NT;
         idv[j] = a.topk_ids[r < R ? r : R - 1];
     }
+    MapStage<NT, kMap> ms;
+    ms.load(a);
     int tkey[kBatches];
     load_tile_keys<kBatches>(a.topk_ids, row0, T, span, w, lane, tkey);
-    const TileCopy<U, kNTStore> tc(a, t0, ntok);
+    const TileCopy<U, kNTStore, kMap> tc(a, t0, ntok);
     u32x4 cur[U];
-    if (a.row_vecs > 0 && w < tc.items) tc.load(w, cur);
+    tc.prefetch(w, cur);
 
-    int* before_s = smem;                 // [E] rows before the tile, then the tile's base per expert
-    int* after_s = before_s + E;          // [E] rows after the tile
-    int* wave_s = after_s + E;            // [W * E] per-wave counts inside the tile, then prefixes
-    int* dest_s = wave_s + W * E;         // [tile_cap] destination of each tile row
+    int* before_s = smem;                 // [B] rows before the tile, then the tile's base per bucket
+    int* after_s = before_s + B;          // [B] rows after the tile
+    int* wave_s = after_s + B;            // [W * B] per-wave counts inside the tile, then prefixes
+    int* dest_s = wave_s + W * B;         // [tile_cap] destination of each tile row
     int* misc_s = dest_s + tile_cap;      // [16]: [0] bad ids, [1..W] scan scratch
+    const int* map_s = ms.store(a, misc_s + 16);  // [E] with a map
 
-    for (int i = threadIdx.x; i < (2 + W) * E; i += NT) smem[i] = 0;
+    for (int i = threadIdx.x; i < (2 + W) * B; i += NT) smem[i] = 0;
     if (threadIdx.x < 16) misc_s[threadIdx.x] = 0;
     lds_barrier();
 
@@ -430,56 +558,69 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
         const int r = (int)threadIdx.x + j * NT;
-        const int key = idv[j];
-        const bool ok = (unsigned)key < (unsigned)E;
         if (r < R && (r < row0 || r >= row0 + T)) {
-            nbad += ok ? 0 : 1;
-            if (ok) atomicAdd(r < row0 ? &before_s[key] : &after_s[key], 1);
+            if constexpr (kMap) {
+                const int key = bucket_of<true>(idv[j], E, map_s, B);
+                nbad += key == kBadKey ? 1 : 0;
+                if (key >= 0) atomicAdd(r < row0 ? &before_s[key] : &after_s[key], 1);
+            } else {
+                const int key = idv[j];
+                const bool ok = (unsigned)key < (unsigned)E;
+                nbad += ok ? 0 : 1;
+                if (ok) atomicAdd(r < row0 ? &before_s[key] : &after_s[key], 1);
+            }
         }
     }
+    if constexpr (kMap) tile_keys_to_buckets<true, kBatches>(tkey, E, map_s, B);
     int trank[kBatches];
-    nbad += rank_own_rows<kBatches>(tkey, T, span, E, nbits, w, lane, wave_s + w * E, trank);
+    nbad += rank_own_rows<kMap, kBatches>(tkey, T, span, E, nbits, w, lane, wave_s + w * B, trank);
     if (nbad) atomicAdd(&misc_s[0], nbad);
     lds_barrier();
     if (misc_s[0] != 0) {  // every workgroup saw every id, so all take this branch together
         if (blockIdx.x == 0)
-            for (int e = threadIdx.x; e <= E; e += NT) a.expert_first_token_offset[e] = -1;
+            for (int e = threadIdx.x; e <= B; e += NT) a.expert_first_token_offset[e] = -1;
         return;
     }
 
-    // Phase 2: offsets and this tile's base per expert.
+    // Phase 2: offsets and this tile's base per bucket.
     expert_bases<NT, kPer>(
-        E, wave_s, before_s, misc_s + 1, a.expert_first_token_offset, blockIdx.x == 0,
+        B, wave_s, before_s, misc_s + 1, a.expert_first_token_offset, blockIdx.x == 0,
         [&](int e, int in_tile) { return before_s[e] + in_tile + after_s[e]; }, [&](int e) { return before_s[e]; });
     lds_barrier();
 
     // Phase 3: destinations of this wave's tile rows, then the row copy.
-    write_dests<kBatches>(a, tkey, trank, row0, T, span, E, w, lane, before_s, wave_s, dest_s);
+    write_dests<kMap, kBatches>(a, tkey, trank, row0, T, span, B, w, lane, before_s, wave_s, dest_s);
     lds_barrier();
-    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore>(tc, cur, dest_s);
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore, kMap>(tc, cur, dest_s);
     copy_tile_scales<NT>(a, t0, ntok, dest_s);
 }
 
 // ----------------------------------------------------------------------------
-// Coarse permute, kernel 1 of 2: expert counts of each coarse tile of
-// coarse_rows expanded rows.  hist[c][e] = rows of coarse tile c with expert
-// e; hist[c][E] = rows with an out-of-range id.
+// Coarse permute, kernel 1 of 2: bucket counts of each coarse tile of
+// coarse_rows expanded rows.  hist[c][b] = rows of coarse tile c with key b;
+// hist[c][B] = rows with a bad id or map entry.  Rows of remote experts are
+// not counted.
 // ----------------------------------------------------------------------------
-template <int NT>
-__global__ __launch_bounds__(NT) void permute_coarse_hist_kernel(const int32_t* __restrict__ ids, int R, int E,
-                                                                 int coarse_rows, int32_t* __restrict__ hist) {
-    extern __shared__ int smem[];  // [E + 1]
-    for (int e = threadIdx.x; e <= E; e += NT) smem[e] = 0;
+template <int NT, bool kMap>
+__global__ __launch_bounds__(NT) void permute_coarse_hist_kernel(const int32_t* __restrict__ ids,
+                                                                 const int32_t* __restrict__ expert_map, int R, int E,
+                                                                 int B, int coarse_rows, int32_t* __restrict__ hist) {
+    extern __shared__ int smem[];  // [B + 1], then the map [E] when there is one
+    int* map_w = smem + B + 1;
+    for (int e = threadIdx.x; e <= B; e += NT) smem[e] = 0;
+    if constexpr (kMap)
+        for (int e = threadIdx.x; e < E; e += NT) map_w[e] = expert_map[e];
     lds_barrier();
+    const int* map_s = map_w;
     const int r0 = (int)blockIdx.x * coarse_rows;
     const int r1 = min(r0 + coarse_rows, R);
     for (int r = r0 + (int)threadIdx.x; r < r1; r += NT) {
-        const int key = ids[r];
-        atomicAdd(&smem[(unsigned)key < (unsigned)E ? key : E], 1);
+        const int key = bucket_of<kMap>(ids[r], E, map_s, B);
+        if (key != kRemoteKey) atomicAdd(&smem[key >= 0 ? key : B], 1);
     }
     lds_barrier();
-    int32_t* row = hist + (int64_t)blockIdx.x * (E + 1);
-    for (int e = threadIdx.x; e <= E; e += NT) row[e] = smem[e];
+    int32_t* row = hist + (int64_t)blockIdx.x * (B + 1);
+    for (int e = threadIdx.x; e <= B; e += NT) row[e] = smem[e];
 }
 
 // ----------------------------------------------------------------------------
@@ -488,7 +629,7 @@ __global__ __launch_bounds__(NT) void permute_coarse_hist_kernel(const int32_t* 
 // coarse histogram (held in LDS) plus a count of the rows that precede the
 // tile inside its own coarse tile.  Tiles never straddle coarse tiles.
 // ----------------------------------------------------------------------------
-template <int NT, int U, bool kNTStore>
+template <int NT, int U, bool kNTStore, bool kMap>
 __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs a, int tokens_per_tile, int nbits,
                                                                     int coarse_rows, int num_coarse,
                                                                     const int32_t* __restrict__ hist) {
@@ -500,6 +641,7 @@ __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs 
     static_assert(kCoarseMaxHist % NT == 0 && kCoarseMaxRowsPerTile % NT == 0, "coarse bounds vs workgroup size");
     extern __shared__ int smem[];
     const int E = a.num_experts;
+    const int B = a.num_buckets;
     const int K = a.topk;
     const int w = wave_index();
     const int lane = threadIdx.x % kWaveSize;
@@ -511,10 +653,11 @@ __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs 
     const int span = (T + NT - 1) / NT * kWaveSize;
     const int cc = row0 / coarse_rows;  // this tile's coarse tile
     const int c_start = cc * coarse_rows;
-    const int hist_n = num_coarse * (E + 1);
+    const int hist_n = num_coarse * (B + 1);
 
     // Independent loads first: the coarse histogram, the rows that precede
-    // this tile in its coarse tile, this wave's tile keys; then row chunks.
+    // this tile in its coarse tile, the map, this wave's tile keys; then row
+    // chunks.
     int hv[kHist];
 #pragma unroll
     for (int j = 0; j < kHist; ++j) {
@@ -527,24 +670,27 @@ __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs 
         const int r = c_start + (int)threadIdx.x + j * NT;
         pv[j] = a.topk_ids[r < row0 ? r : row0];  // row0 is a valid row (T >= 1)
     }
+    MapStage<NT, kMap> ms;
+    ms.load(a);
     int tkey[kBatches];
     load_tile_keys<kBatches>(a.topk_ids, row0, T, span, w, lane, tkey);
-    const TileCopy<U, kNTStore> tc(a, t0, ntok);
+    const TileCopy<U, kNTStore, kMap> tc(a, t0, ntok);
     u32x4 cur[U];
-    if (a.row_vecs > 0 && w < tc.items) tc.load(w, cur);
+    tc.prefetch(w, cur);
 
-    int* hist_s = smem;                   // [num_coarse * (E + 1)]
-    int* before_s = hist_s + hist_n;      // [E] preceding rows in the coarse tile, then the tile's base
-    int* wave_s = before_s + E;           // [W * E]
-    int* dest_s = wave_s + W * E;         // [tile_cap]
+    int* hist_s = smem;                   // [num_coarse * (B + 1)]
+    int* before_s = hist_s + hist_n;      // [B] preceding rows in the coarse tile, then the tile's base
+    int* wave_s = before_s + B;           // [W * B]
+    int* dest_s = wave_s + W * B;         // [tile_cap]
     int* misc_s = dest_s + tile_cap;      // [16]: [0] bad ids, [1..W] scan scratch
+    const int* map_s = ms.store(a, misc_s + 16);  // [E] with a map
 
 #pragma unroll
     for (int j = 0; j < kHist; ++j) {
         const int i = (int)threadIdx.x + j * NT;
         if (i < hist_n) hist_s[i] = hv[j];
     }
-    for (int i = threadIdx.x; i < (1 + W) * E; i += NT) before_s[i] = 0;
+    for (int i = threadIdx.x; i < (1 + W) * B; i += NT) before_s[i] = 0;
     if (threadIdx.x < 16) misc_s[threadIdx.x] = 0;
     lds_barrier();
 
@@ -553,56 +699,65 @@ __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs 
 #pragma unroll
     for (int j = 0; j < kPartial; ++j) {
         const int r = c_start + (int)threadIdx.x + j * NT;
-        if (r < row0 && (unsigned)pv[j] < (unsigned)E) atomicAdd(&before_s[pv[j]], 1);
+        if (r < row0) {
+            if constexpr (kMap) {
+                const int key = bucket_of<true>(pv[j], E, map_s, B);
+                if (key >= 0) atomicAdd(&before_s[key], 1);
+            } else {
+                if ((unsigned)pv[j] < (unsigned)E) atomicAdd(&before_s[pv[j]], 1);
+            }
+        }
     }
+    if constexpr (kMap) tile_keys_to_buckets<true, kBatches>(tkey, E, map_s, B);
     int trank[kBatches];
-    rank_own_rows<kBatches>(tkey, T, span, E, nbits, w, lane, wave_s + w * E, trank);
+    rank_own_rows<kMap, kBatches>(tkey, T, span, E, nbits, w, lane, wave_s + w * B, trank);
     if (threadIdx.x == 0) {
         int bad = 0;
-        for (int c = 0; c < num_coarse; ++c) bad += hist_s[c * (E + 1) + E];
+        for (int c = 0; c < num_coarse; ++c) bad += hist_s[c * (B + 1) + B];
         misc_s[0] = bad;
     }
     lds_barrier();
     if (misc_s[0] != 0) {  // the histogram covers every id, so all workgroups agree
         if (blockIdx.x == 0)
-            for (int e = threadIdx.x; e <= E; e += NT) a.expert_first_token_offset[e] = -1;
+            for (int e = threadIdx.x; e <= B; e += NT) a.expert_first_token_offset[e] = -1;
         return;
     }
 
-    // Phase 2: offsets and this tile's base per expert.
+    // Phase 2: offsets and this tile's base per bucket.
     expert_bases<NT, kPer>(
-        E, wave_s, before_s, misc_s + 1, a.expert_first_token_offset, blockIdx.x == 0,
+        B, wave_s, before_s, misc_s + 1, a.expert_first_token_offset, blockIdx.x == 0,
         [&](int e, int) {
             int t = 0;
-            for (int c = 0; c < num_coarse; ++c) t += hist_s[c * (E + 1) + e];
+            for (int c = 0; c < num_coarse; ++c) t += hist_s[c * (B + 1) + e];
             return t;
         },
         [&](int e) {
             int b = before_s[e];
-            for (int c = 0; c < cc; ++c) b += hist_s[c * (E + 1) + e];
+            for (int c = 0; c < cc; ++c) b += hist_s[c * (B + 1) + e];
             return b;
         });
     lds_barrier();
 
     // Phase 3: destinations, then the row copy.
-    write_dests<kBatches>(a, tkey, trank, row0, T, span, E, w, lane, before_s, wave_s, dest_s);
+    write_dests<kMap, kBatches>(a, tkey, trank, row0, T, span, B, w, lane, before_s, wave_s, dest_s);
     lds_barrier();
-    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore>(tc, cur, dest_s);
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore, kMap>(tc, cur, dest_s);
     copy_tile_scales<NT>(a, t0, ntok, dest_s);
 }
 
 // ----------------------------------------------------------------------------
-// Staged permute, kernel 1: per tile, stable ranks and the expert histogram.
-// rank_ws[r] = rank of row r within its tile; tile_hist[e][tile] = count,
-// tile_hist[E][tile] = rows with an out-of-range id.
+// Staged permute, kernel 1: per tile, stable ranks and the bucket histogram.
+// rank_ws[r] = rank of row r within its tile; tile_hist[b][tile] = count,
+// tile_hist[B][tile] = rows with a bad id or map entry.
 // ----------------------------------------------------------------------------
-template <int NT>
+template <int NT, bool kMap>
 __global__ __launch_bounds__(NT) void permute_rank_tiles_kernel(PermuteArgs a, int tokens_per_tile, int nbits,
                                                                 int64_t num_tiles, int32_t* rank_ws,
                                                                 int32_t* tile_hist) {
     constexpr int W = NT / kWaveSize;
     extern __shared__ int smem[];
     const int E = a.num_experts;
+    const int B = a.num_buckets;
     const int K = a.topk;
     const int64_t tile = blockIdx.x;
     const int64_t t0 = tile * tokens_per_tile;
@@ -611,28 +766,31 @@ __global__ __launch_bounds__(NT) void permute_rank_tiles_kernel(PermuteArgs a, i
     const int T = ntok * K;
     const int tile_cap = tokens_per_tile * K;
 
-    int* cnt_s = smem;                    // [E]
-    int* wave_s = cnt_s + E;              // [W * E]
-    int* key_s = wave_s + W * E;          // [tile_cap]
+    int* cnt_s = smem;                    // [B]
+    int* wave_s = cnt_s + B;              // [W * B]
+    int* key_s = wave_s + W * B;          // [tile_cap]
     int* rank_s = key_s + tile_cap;       // [tile_cap]
     int* misc_s = rank_s + tile_cap;      // [16]
+    int* map_w = misc_s + 16;             // [E] with a map
 
-    for (int i = threadIdx.x; i < (1 + W) * E; i += NT) smem[i] = 0;
+    for (int i = threadIdx.x; i < (1 + W) * B; i += NT) smem[i] = 0;
     if (threadIdx.x < 16) misc_s[threadIdx.x] = 0;
+    if constexpr (kMap)
+        for (int e = threadIdx.x; e < E; e += NT) map_w[e] = a.expert_map[e];
     lds_barrier();
+    const int* map_s = map_w;
     int nbad = 0;
     for (int i = threadIdx.x; i < T; i += NT) {
-        const int key = a.topk_ids[row0 + i];
-        const bool ok = (unsigned)key < (unsigned)E;
-        nbad += ok ? 0 : 1;
-        key_s[i] = ok ? key : -1;
+        const int key = bucket_of<kMap>(a.topk_ids[row0 + i], E, map_s, B);
+        nbad += key == kBadKey ? 1 : 0;
+        key_s[i] = key >= 0 ? key : -1;
     }
     if (nbad) atomicAdd(&misc_s[0], nbad);
     lds_barrier();
-    rank_tile<NT>(key_s, T, E, nbits, rank_s, wave_s, cnt_s);
+    rank_tile<NT>(key_s, T, B, nbits, rank_s, wave_s, cnt_s);
     for (int i = threadIdx.x; i < T; i += NT) rank_ws[row0 + i] = rank_s[i];
-    for (int e = threadIdx.x; e < E; e += NT) tile_hist[(int64_t)e * num_tiles + tile] = cnt_s[e];
-    if (threadIdx.x == 0) tile_hist[(int64_t)E * num_tiles + tile] = misc_s[0];
+    for (int e = threadIdx.x; e < B; e += NT) tile_hist[(int64_t)e * num_tiles + tile] = cnt_s[e];
+    if (threadIdx.x == 0) tile_hist[(int64_t)B * num_tiles + tile] = misc_s[0];
 }
 
 // ----------------------------------------------------------------------------
@@ -687,17 +845,18 @@ __global__ __launch_bounds__(NT) void permute_scan_tiles_kernel(int32_t* tile_hi
 }
 
 // ----------------------------------------------------------------------------
-// Staged permute, kernel 3: offsets from the per-expert totals, destinations
+// Staged permute, kernel 3: offsets from the per-bucket totals, destinations
 // from offset + tile base + rank, index scatter, and the row copy.
 // ----------------------------------------------------------------------------
-template <int NT, int U, bool kNTStore>
+template <int NT, int U, bool kNTStore, bool kMap>
 __global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int tokens_per_tile, int64_t num_tiles,
                                                              const int32_t* rank_ws, const int32_t* tile_base,
                                                              const int32_t* total) {
-    constexpr int kE = (kMaxExperts + 1 + NT - 1) / NT;  // per-expert values held per thread
+    constexpr int kE = (kMaxExperts + 1 + NT - 1) / NT;  // per-bucket values held per thread
     constexpr int kT = (kMaxTileRows + NT - 1) / NT;     // tile rows held per thread
     extern __shared__ int smem[];
     const int E = a.num_experts;
+    const int B = a.num_buckets;
     const int K = a.topk;
     const int64_t tile = blockIdx.x;
     const int64_t t0 = tile * tokens_per_tile;
@@ -713,8 +872,8 @@ __global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int 
 #pragma unroll
     for (int j = 0; j < kE; ++j) {
         const int e = (int)threadIdx.x + j * NT;
-        tot[j] = total[e <= E ? e : E];
-        tb[j] = tile_base[(int64_t)(e < E ? e : E - 1) * num_tiles + tile];
+        tot[j] = total[e <= B ? e : B];
+        tb[j] = tile_base[(int64_t)(e < B ? e : B - 1) * num_tiles + tile];
     }
 #pragma unroll
     for (int j = 0; j < kT; ++j) {
@@ -723,44 +882,57 @@ __global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int 
         key[j] = a.topk_ids[r];
         rk[j] = rank_ws[r];
     }
-    const TileCopy<U, kNTStore> tc(a, t0, ntok);
+    MapStage<NT, kMap> ms;
+    ms.load(a);
+    const TileCopy<U, kNTStore, kMap> tc(a, t0, ntok);
     u32x4 cur[U];
-    if (a.row_vecs > 0 && wave_index() < tc.items) tc.load(wave_index(), cur);
+    tc.prefetch(wave_index(), cur);
 
-    int* off_s = smem;                // [E + 1] totals, then offsets
-    int* base_s = off_s + (E + 1);    // [E]     this tile's base within each expert
-    int* dest_s = base_s + E;         // [tile_cap]
+    int* off_s = smem;                // [B + 1] totals, then offsets
+    int* base_s = off_s + (B + 1);    // [B]     this tile's base within each bucket
+    int* dest_s = base_s + B;         // [tile_cap]
     int* misc_s = dest_s + tile_cap;  // [16]
+    const int* map_s = ms.store(a, misc_s + 16);  // [E] with a map
 
 #pragma unroll
     for (int j = 0; j < kE; ++j) {
         const int e = (int)threadIdx.x + j * NT;
-        if (e <= E) off_s[e] = tot[j];
-        if (e < E) base_s[e] = tb[j];
+        if (e <= B) off_s[e] = tot[j];
+        if (e < B) base_s[e] = tb[j];
     }
     lds_barrier();
-    if (off_s[E] != 0) {  // some id was out of range: report through the offsets, write nothing else
+    if (off_s[B] != 0) {  // a bad id or map entry: report through the offsets, write nothing else
         if (tile == 0)
-            for (int e = threadIdx.x; e <= E; e += NT) a.expert_first_token_offset[e] = -1;
+            for (int e = threadIdx.x; e <= B; e += NT) a.expert_first_token_offset[e] = -1;
         return;
     }
-    const int rows_total = block_exclusive_scan<NT>(off_s, E, misc_s);
+    const int rows_total = block_exclusive_scan<NT>(off_s, B, misc_s);
     if (tile == 0) {
-        for (int e = threadIdx.x; e < E; e += NT) a.expert_first_token_offset[e] = off_s[e];
-        if (threadIdx.x == 0) a.expert_first_token_offset[E] = rows_total;
+        for (int e = threadIdx.x; e < B; e += NT) a.expert_first_token_offset[e] = off_s[e];
+        if (threadIdx.x == 0) a.expert_first_token_offset[B] = rows_total;
     }
 #pragma unroll
     for (int j = 0; j < kT; ++j) {
         const int i = (int)threadIdx.x + j * NT;
         if (i >= T) continue;
-        const int e = min(max(key[j], 0), E - 1);  // all ids are in range here (no bad-id count)
+        int e;
+        if constexpr (kMap) {
+            e = bucket_of<true>(key[j], E, map_s, B);  // never bad here (no bad-id count)
+            if (e < 0) {  // remote expert
+                dest_s[i] = -1;
+                a.inv_permuted_idx[row0 + i] = -1;
+                continue;
+            }
+        } else {
+            e = min(max(key[j], 0), E - 1);  // all ids are in range here (no bad-id count)
+        }
         const int dest = off_s[e] + base_s[e] + rk[j];
         dest_s[i] = dest;
         a.inv_permuted_idx[row0 + i] = dest;
         if ((uint32_t)dest < (uint64_t)R) a.permuted_idx[dest] = (int32_t)(row0 + i);
     }
     lds_barrier();
-    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore>(tc, cur, dest_s);
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore, kMap>(tc, cur, dest_s);
     copy_tile_scales<NT>(a, t0, ntok, dest_s);
 }
 
@@ -772,7 +944,9 @@ __global__ void fill_offsets_kernel(int64_t* off, int n, int64_t value) {
 // Unpermute: one wave per (token, chunk of U*64 16-byte vectors).  The loads
 // of all topk rows of the chunk are issued before any arithmetic (G rows at a
 // time when topk is not a compile-time constant), then summed in fp32 in
-// ascending k and rounded once to the element type.
+// ascending k and rounded once to the element type.  A slot whose inverse
+// index is -1 (its expert lives on another rank) is skipped: no load, no term.
+// Any other index outside [0, N*topk) turns the token's row into NaN.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -827,6 +1001,7 @@ __device__ __forceinline__ void unpermute_issue(const u32x4* __restrict__ y, con
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const bool ok = it.j[k] >= 0 && (int64_t)it.j[k] < R;
+        if (!ok) it.wk[k] = 0.0f;  // the zero row then adds exactly nothing
         const u32x4* src = y + (int64_t)(ok ? it.j[k] : 0) * rv;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -868,7 +1043,7 @@ __device__ __forceinline__ void unpermute_finish(u32x4* __restrict__ out, int64_
     bool bad = false;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        bad |= !(it.j[k] >= 0 && (int64_t)it.j[k] < R);
+        bad |= !(it.j[k] >= -1 && (int64_t)it.j[k] < R);
         accumulate<kBF16, U>(acc, it.v[k], it.wk[k]);
     }
     store_outputs<kBF16, U>(out + t * rv, rv, base, acc, bad);
@@ -924,7 +1099,8 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict_
                 for (int g = 0; g < kGroup; ++g) {
                     const bool live = k0 + g < K;
                     const bool ok = live && j[g] >= 0 && (int64_t)j[g] < R;
-                    bad |= live && !ok;
+                    bad |= live && !(j[g] >= -1 && (int64_t)j[g] < R);
+                    if (!ok) wk[g] = 0.0f;
                     const u32x4* src = y + (int64_t)(ok ? j[g] : 0) * rv;
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
@@ -966,42 +1142,71 @@ static bool plain_row_stores(const PermuteArgs& a) {
     return a.topk >= kPlainStoreMinTopk && a.num_tokens * a.topk * a.row_vecs * 16 >= kPlainStoreMinBytes;
 }
 
-template <int U>
-static void launch_fused_u(const PermuteArgs& a, const PermutePlan& p, hipStream_t stream) {
-    const size_t lds = fused_lds_bytes(a.num_experts, p.tile_rows);
+static int map_entries(const PermuteArgs& a) { return a.expert_map != nullptr ? a.num_experts : 0; }
+
+template <int U, bool kMap>
+static void launch_fused_um(const PermuteArgs& a, const PermutePlan& p, hipStream_t stream) {
+    const size_t lds = fused_lds_bytes(a.num_buckets, p.tile_rows, map_entries(a));
     if (plain_row_stores(a))
-        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, false>), dim3((unsigned)p.num_tiles),
+        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, false, kMap>), dim3((unsigned)p.num_tiles),
                            dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile, p.nbits);
     else
-        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, true>), dim3((unsigned)p.num_tiles),
+        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, true, kMap>), dim3((unsigned)p.num_tiles),
                            dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile, p.nbits);
+}
+
+template <int U, bool kMap>
+static void launch_coarse_um(const PermuteArgs& a, const PermutePlan& p, const int32_t* hist, hipStream_t stream) {
+    const size_t lds = coarse_scatter_lds_bytes(a.num_buckets, p.tile_rows, p.num_coarse, map_entries(a));
+    if (plain_row_stores(a))
+        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, false, kMap>),
+                           dim3((unsigned)p.num_tiles), dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile,
+                           p.nbits, p.coarse_rows, p.num_coarse, hist);
+    else
+        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, true, kMap>),
+                           dim3((unsigned)p.num_tiles), dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile,
+                           p.nbits, p.coarse_rows, p.num_coarse, hist);
+}
+
+template <int U, bool kMap>
+static void launch_scatter_um(const PermuteArgs& a, const PermutePlan& p, const int32_t* rank_ws,
+                              const int32_t* tile_base, const int32_t* total, hipStream_t stream) {
+    const size_t lds = scatter_lds_bytes(a.num_buckets, p.tile_rows, map_entries(a));
+    if (plain_row_stores(a))
+        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, false, kMap>), dim3((unsigned)p.num_tiles),
+                           dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
+                           total);
+    else
+        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, true, kMap>), dim3((unsigned)p.num_tiles),
+                           dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
+                           total);
+}
+
+// The map is a compile-time parameter of the row-moving kernels, so the
+// plain permute carries none of its code.
+template <int U>
+static void launch_fused_u(const PermuteArgs& a, const PermutePlan& p, hipStream_t stream) {
+    if (a.expert_map != nullptr)
+        launch_fused_um<U, true>(a, p, stream);
+    else
+        launch_fused_um<U, false>(a, p, stream);
 }
 
 template <int U>
 static void launch_coarse_u(const PermuteArgs& a, const PermutePlan& p, const int32_t* hist, hipStream_t stream) {
-    const size_t lds = coarse_scatter_lds_bytes(a.num_experts, p.tile_rows, p.num_coarse);
-    if (plain_row_stores(a))
-        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, false>), dim3((unsigned)p.num_tiles),
-                           dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile, p.nbits, p.coarse_rows,
-                           p.num_coarse, hist);
+    if (a.expert_map != nullptr)
+        launch_coarse_um<U, true>(a, p, hist, stream);
     else
-        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, true>), dim3((unsigned)p.num_tiles),
-                           dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile, p.nbits, p.coarse_rows,
-                           p.num_coarse, hist);
+        launch_coarse_um<U, false>(a, p, hist, stream);
 }
 
 template <int U>
 static void launch_scatter_u(const PermuteArgs& a, const PermutePlan& p, const int32_t* rank_ws,
                              const int32_t* tile_base, const int32_t* total, hipStream_t stream) {
-    const size_t lds = scatter_lds_bytes(a.num_experts, p.tile_rows);
-    if (plain_row_stores(a))
-        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, false>), dim3((unsigned)p.num_tiles),
-                           dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
-                           total);
+    if (a.expert_map != nullptr)
+        launch_scatter_um<U, true>(a, p, rank_ws, tile_base, total, stream);
     else
-        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, true>), dim3((unsigned)p.num_tiles),
-                           dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
-                           total);
+        launch_scatter_um<U, false>(a, p, rank_ws, tile_base, total, stream);
 }
 
 #define MOE_DISPATCH_U(u, CALL) \
@@ -1017,7 +1222,8 @@ static void launch_scatter_u(const PermuteArgs& a, const PermutePlan& p, const i
     }
 
 hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream) {
-    const int E = a.num_experts;
+    const int B = a.num_buckets;
+    const int M = map_entries(a);
     const int u = a.topk >= 4 ? choose_unroll(a.row_vecs, kCopyUnrollsWideFanout, 4)
                               : choose_unroll(a.row_vecs, kCopyUnrolls, 8);
     if (p.fused) {
@@ -1029,9 +1235,14 @@ hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* work
     char* ws = static_cast<char*>(workspace);
     if (p.coarse) {
         int32_t* hist = reinterpret_cast<int32_t*>(ws);
-        hipLaunchKernelGGL((permute_coarse_hist_kernel<kCoarseThreads>), dim3((unsigned)p.num_coarse),
-                           dim3(kCoarseThreads), coarse_hist_lds_bytes(E), stream, a.topk_ids, (int)p.rows, E,
-                           p.coarse_rows, hist);
+        if (a.expert_map != nullptr)
+            hipLaunchKernelGGL((permute_coarse_hist_kernel<kCoarseThreads, true>), dim3((unsigned)p.num_coarse),
+                               dim3(kCoarseThreads), coarse_hist_lds_bytes(B, M), stream, a.topk_ids, a.expert_map,
+                               (int)p.rows, a.num_experts, B, p.coarse_rows, hist);
+        else
+            hipLaunchKernelGGL((permute_coarse_hist_kernel<kCoarseThreads, false>), dim3((unsigned)p.num_coarse),
+                               dim3(kCoarseThreads), coarse_hist_lds_bytes(B, M), stream, a.topk_ids, a.expert_map,
+                               (int)p.rows, a.num_experts, B, p.coarse_rows, hist);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
 #define MOE_COARSE(U) launch_coarse_u<U>(a, p, hist, stream)
@@ -1042,12 +1253,17 @@ hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* work
     int32_t* rank_ws = reinterpret_cast<int32_t*>(ws + p.ws_rank);
     int32_t* tile_hist = reinterpret_cast<int32_t*>(ws + p.ws_tile_hist);
     int32_t* total = reinterpret_cast<int32_t*>(ws + p.ws_total);
-    hipLaunchKernelGGL((permute_rank_tiles_kernel<kRankThreads>), dim3((unsigned)p.num_tiles), dim3(kRankThreads),
-                       rank_lds_bytes(E, p.tile_rows), stream, a, p.tokens_per_tile, p.nbits, p.num_tiles, rank_ws,
-                       tile_hist);
+    if (a.expert_map != nullptr)
+        hipLaunchKernelGGL((permute_rank_tiles_kernel<kRankThreads, true>), dim3((unsigned)p.num_tiles),
+                           dim3(kRankThreads), rank_lds_bytes(B, p.tile_rows, M), stream, a, p.tokens_per_tile,
+                           p.nbits, p.num_tiles, rank_ws, tile_hist);
+    else
+        hipLaunchKernelGGL((permute_rank_tiles_kernel<kRankThreads, false>), dim3((unsigned)p.num_tiles),
+                           dim3(kRankThreads), rank_lds_bytes(B, p.tile_rows, M), stream, a, p.tokens_per_tile,
+                           p.nbits, p.num_tiles, rank_ws, tile_hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((permute_scan_tiles_kernel<kScanThreads, kScanPerThread>), dim3((unsigned)(E + 1)),
+    hipLaunchKernelGGL((permute_scan_tiles_kernel<kScanThreads, kScanPerThread>), dim3((unsigned)(B + 1)),
                        dim3(kScanThreads), 0, stream, tile_hist, p.num_tiles, total);
     err = hipGetLastError();
     if (err != hipSuccess) return err;

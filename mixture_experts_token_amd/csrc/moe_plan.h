@@ -14,6 +14,9 @@
 //                 size);
 //   * how expanded rows are cut into tiles (whole tokens per tile);
 //   * where each piece of the workspace lives.
+// The sort runs over `buckets` keys: the experts, or with a local-expert map
+// the local experts (rows of remote experts get no bucket).  `map_entries` is
+// the length of that map (0 without one); the kernels stage it in LDS.
 #pragma once
 
 #include <cstddef>
@@ -57,9 +60,9 @@ inline int choose_unroll(int64_t row_vecs, const int* allowed, int n_allowed) {
     return allowed[n_allowed - 1];
 }
 
-inline int key_bits(int num_experts) {
+inline int key_bits(int buckets) {
     int b = 0;
-    while ((1 << b) < num_experts) ++b;
+    while ((1 << b) < buckets) ++b;
     return b;
 }
 
@@ -75,10 +78,11 @@ struct PermutePlan {
     int nbits = 0;
     // staged-schedule workspace layout (bytes from the workspace base)
     size_t ws_rank = 0;           // int32 [rows]           rank of each row within its tile
-    size_t ws_tile_hist = 0;      // int32 [E+1][num_tiles] per-tile counts, then per-tile bases
-    size_t ws_total = 0;          // int32 [E+1]            rows per expert (+ bad-id count)
+    size_t ws_tile_hist = 0;      // int32 [B+1][num_tiles] per-tile counts, then per-tile bases
+    size_t ws_total = 0;          // int32 [B+1]            rows per bucket (+ bad-id count)
     size_t ws_bytes = 0;          // bytes this call needs
-    // coarse schedule workspace: int32 [num_coarse][E+1] counts per coarse tile (+ bad ids)
+    // coarse schedule workspace: int32 [num_coarse][B+1] counts per coarse tile (+ bad ids)
+    // (B = buckets: experts, or local experts with a map)
 };
 
 // Tokens per staged tile: about kStagedTileRows expanded rows, whole tokens.
@@ -87,20 +91,21 @@ inline int staged_tokens_per_tile(int topk) {
     return t < 1 ? 1 : t;
 }
 
-inline size_t staged_workspace_bytes(int64_t rows, int64_t num_tiles, int num_experts) {
+inline size_t staged_workspace_bytes(int64_t rows, int64_t num_tiles, int buckets) {
     size_t b = align_up(sizeof(int32_t) * (size_t)rows, kWorkspaceAlign);
-    b += align_up(sizeof(int32_t) * (size_t)(num_experts + 1) * (size_t)num_tiles, kWorkspaceAlign);
-    b += align_up(sizeof(int32_t) * (size_t)(num_experts + 1), kWorkspaceAlign);
+    b += align_up(sizeof(int32_t) * (size_t)(buckets + 1) * (size_t)num_tiles, kWorkspaceAlign);
+    b += align_up(sizeof(int32_t) * (size_t)(buckets + 1), kWorkspaceAlign);
     return b;
 }
 
 // Coarse tiles a problem may use: bounded by kMaxCoarseTiles, by the LDS held
-// histogram (entries and the whole workgroup's LDS), for E experts and tiles
-// of tile_rows rows.
-inline int max_coarse_tiles(int num_experts, int tile_rows) {
+// histogram (entries and the whole workgroup's LDS), for B buckets, a map of
+// map_entries ints and tiles of tile_rows rows.
+inline int max_coarse_tiles(int buckets, int tile_rows, int map_entries) {
     int n = kMaxCoarseTiles;
-    const int by_hist = kCoarseMaxHist / (num_experts + 1);
-    const int by_lds = (kMaxLdsInts - 16 - (1 + kCoarseThreads / kWaveSize) * num_experts - tile_rows) / (num_experts + 1);
+    const int by_hist = kCoarseMaxHist / (buckets + 1);
+    const int by_lds =
+        (kMaxLdsInts - 16 - map_entries - (1 + kCoarseThreads / kWaveSize) * buckets - tile_rows) / (buckets + 1);
     if (by_hist < n) n = by_hist;
     if (by_lds < n) n = by_lds;
     return n;
@@ -108,8 +113,8 @@ inline int max_coarse_tiles(int num_experts, int tile_rows) {
 
 // Coarse tile length for R rows (a multiple of tile_rows), or 0 when the
 // coarse schedule does not apply (too many rows per coarse tile).
-inline int64_t coarse_rows_for(int64_t rows, int num_experts, int tile_rows) {
-    const int nmax = max_coarse_tiles(num_experts, tile_rows);
+inline int64_t coarse_rows_for(int64_t rows, int buckets, int tile_rows, int map_entries) {
+    const int nmax = max_coarse_tiles(buckets, tile_rows, map_entries);
     if (nmax < 1) return 0;
     const int64_t per = (rows + nmax - 1) / nmax;
     const int64_t m = (per + tile_rows - 1) / tile_rows;
@@ -117,32 +122,32 @@ inline int64_t coarse_rows_for(int64_t rows, int num_experts, int tile_rows) {
     return cr - tile_rows <= kCoarseMaxRowsPerTile ? cr : 0;
 }
 
-inline size_t coarse_workspace_bytes(int num_coarse, int num_experts) {
-    return align_up(sizeof(int32_t) * (size_t)num_coarse * (size_t)(num_experts + 1), kWorkspaceAlign);
+inline size_t coarse_workspace_bytes(int num_coarse, int buckets) {
+    return align_up(sizeof(int32_t) * (size_t)num_coarse * (size_t)(buckets + 1), kWorkspaceAlign);
 }
 
 // Workspace of a call with max_num_tokens tokens; every call with fewer tokens
 // needs no more: the schedules go fused -> coarse -> staged as the row count
-// grows, a coarse call needs at most max_coarse_tiles(E) histogram rows, and
+// grows, a coarse call needs at most max_coarse_tiles(B) histogram rows, and
 // the staged size grows with the row and tile counts (the tile size depends
 // on topk only).
-inline size_t workspace_bound(int64_t max_num_tokens, int topk, int num_experts) {
+inline size_t workspace_bound(int64_t max_num_tokens, int topk, int buckets, int map_entries) {
     const int64_t rows = max_num_tokens * topk;
     if (rows <= kFusedMaxRows) return 0;
     const int tpt = staged_tokens_per_tile(topk);
     const int tile_rows = tpt * topk;
-    const int nmax = max_coarse_tiles(num_experts, tile_rows);
-    const size_t coarse = nmax > 0 ? coarse_workspace_bytes(nmax, num_experts) : 0;
-    if (coarse_rows_for(rows, num_experts, tile_rows) > 0) return coarse;
+    const int nmax = max_coarse_tiles(buckets, tile_rows, map_entries);
+    const size_t coarse = nmax > 0 ? coarse_workspace_bytes(nmax, buckets) : 0;
+    if (coarse_rows_for(rows, buckets, tile_rows, map_entries) > 0) return coarse;
     const int64_t tiles = (max_num_tokens + tpt - 1) / tpt;
-    const size_t staged = staged_workspace_bytes(rows, tiles, num_experts);
+    const size_t staged = staged_workspace_bytes(rows, tiles, buckets);
     return staged > coarse ? staged : coarse;
 }
 
-inline PermutePlan plan_permute(int64_t num_tokens, int topk, int num_experts) {
+inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int map_entries) {
     PermutePlan p;
     p.rows = num_tokens * topk;
-    p.nbits = key_bits(num_experts);
+    p.nbits = key_bits(buckets);
     if (p.rows <= kFusedMaxRows) {
         p.fused = true;
         // Enough workgroups to spread the row copy, at most kFusedThreads rows per tile.
@@ -158,37 +163,42 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int num_experts) {
     p.tile_rows = p.tokens_per_tile * topk;
     p.num_tiles = num_tokens == 0 ? 0 : (num_tokens + p.tokens_per_tile - 1) / p.tokens_per_tile;
     if (!p.fused) {
-        const int64_t cr = coarse_rows_for(p.rows, num_experts, p.tile_rows);
+        const int64_t cr = coarse_rows_for(p.rows, buckets, p.tile_rows, map_entries);
         if (cr > 0) {
             p.coarse = true;
             p.coarse_rows = (int)cr;
             p.num_coarse = (int)((p.rows + cr - 1) / cr);
-            p.ws_bytes = coarse_workspace_bytes(p.num_coarse, num_experts);
+            p.ws_bytes = coarse_workspace_bytes(p.num_coarse, buckets);
         } else {
             p.ws_rank = 0;
             p.ws_tile_hist = align_up(sizeof(int32_t) * (size_t)p.rows, kWorkspaceAlign);
             p.ws_total = p.ws_tile_hist +
-                         align_up(sizeof(int32_t) * (size_t)(num_experts + 1) * (size_t)p.num_tiles, kWorkspaceAlign);
-            p.ws_bytes = staged_workspace_bytes(p.rows, p.num_tiles, num_experts);
+                         align_up(sizeof(int32_t) * (size_t)(buckets + 1) * (size_t)p.num_tiles, kWorkspaceAlign);
+            p.ws_bytes = staged_workspace_bytes(p.rows, p.num_tiles, buckets);
         }
     }
     return p;
 }
 
-// Dynamic LDS bytes of the fused and staged kernels for one tile shape.
-inline size_t fused_lds_bytes(int num_experts, int tile_rows) {
-    return sizeof(int) * ((size_t)(2 + kFusedThreads / kWaveSize) * num_experts + (size_t)tile_rows + 16);
+// Dynamic LDS bytes of each kernel for one tile shape (B buckets; the map,
+// when there is one, sits after everything else).
+inline size_t fused_lds_bytes(int buckets, int tile_rows, int map_entries) {
+    return sizeof(int) *
+           ((size_t)(2 + kFusedThreads / kWaveSize) * buckets + (size_t)tile_rows + 16 + (size_t)map_entries);
 }
-inline size_t rank_lds_bytes(int num_experts, int tile_rows) {
-    return sizeof(int) * ((size_t)(1 + kRankThreads / kWaveSize) * num_experts + 2 * (size_t)tile_rows + 16);
+inline size_t rank_lds_bytes(int buckets, int tile_rows, int map_entries) {
+    return sizeof(int) *
+           ((size_t)(1 + kRankThreads / kWaveSize) * buckets + 2 * (size_t)tile_rows + 16 + (size_t)map_entries);
 }
-inline size_t coarse_hist_lds_bytes(int num_experts) { return sizeof(int) * (size_t)(num_experts + 1); }
-inline size_t coarse_scatter_lds_bytes(int num_experts, int tile_rows, int num_coarse) {
-    return sizeof(int) * ((size_t)num_coarse * (num_experts + 1) + (size_t)(1 + kCoarseThreads / kWaveSize) * num_experts +
-                          (size_t)tile_rows + 16);
+inline size_t coarse_hist_lds_bytes(int buckets, int map_entries) {
+    return sizeof(int) * ((size_t)(buckets + 1) + (size_t)map_entries);
 }
-inline size_t scatter_lds_bytes(int num_experts, int tile_rows) {
-    return sizeof(int) * ((size_t)(2 * num_experts + 1) + (size_t)tile_rows + 16);
+inline size_t coarse_scatter_lds_bytes(int buckets, int tile_rows, int num_coarse, int map_entries) {
+    return sizeof(int) * ((size_t)num_coarse * (buckets + 1) + (size_t)(1 + kCoarseThreads / kWaveSize) * buckets +
+                          (size_t)tile_rows + 16 + (size_t)map_entries);
+}
+inline size_t scatter_lds_bytes(int buckets, int tile_rows, int map_entries) {
+    return sizeof(int) * ((size_t)(2 * buckets + 1) + (size_t)tile_rows + 16 + (size_t)map_entries);
 }
 
 }  // namespace moe

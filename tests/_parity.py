@@ -99,3 +99,57 @@ def assert_unpermute_close(got: np.ndarray, ref: np.ndarray, dtype: str):
     worst = float(err.max()) if err.size else 0.0
     assert worst <= tolerance(dtype), "max scaled error %.3g > %.3g" % (worst, tolerance(dtype))
     return worst
+
+
+def gpu_permute_local(hidden, ids, num_experts, expert_map, num_local, token_scale=None, workspace=None, stream=None,
+                      outs=None):
+    """Run moe_permute_local into poisoned (or given) outputs; returns the output tensors."""
+    dev = ids.device
+    n, k = ids.shape
+    rows = n * k
+    if outs is None:
+        outs = {
+            "permuted_hidden_states": None if hidden is None else poisoned((rows, hidden.shape[1]), hidden.dtype, dev),
+            "permuted_scale": None if token_scale is None else poisoned((rows,), torch.float32, dev),
+            "expert_first_token_offset": poisoned((num_local + 1,), torch.int64, dev),
+            "permuted_idx": poisoned((rows,), torch.int32, dev),
+            "inv_permuted_idx": poisoned((rows,), torch.int32, dev),
+        }
+    if workspace is None:
+        ws = binding.moe_permute_local_workspace_size(n, k, num_experts, num_local)
+        workspace = poisoned((max(ws, 16),), torch.uint8, dev)
+    emap = torch.as_tensor(np.asarray(expert_map, dtype=np.int32)).to(dev)
+    binding.moe_permute_local(hidden, ids, num_experts, emap, num_local, outs["permuted_hidden_states"],
+                              outs["expert_first_token_offset"], outs["permuted_idx"], outs["inv_permuted_idx"],
+                              workspace, token_scale=token_scale, permuted_scale=outs["permuted_scale"],
+                              stream=stream)
+    return outs
+
+
+def oracle_permute_local(hidden, ids, num_experts, expert_map, num_local, token_scale=None):
+    h = to_np(hidden) if hidden is not None else np.zeros((ids.shape[0], 0), np.float32)
+    return oracle.permute_local(h, to_np(ids), num_experts, np.asarray(expert_map, dtype=np.int32), num_local,
+                                None if token_scale is None else to_np(token_scale))
+
+
+def assert_permute_local_equal(outs, ref):
+    """Offsets and inverse indices whole; the first M permuted entries equal the
+    oracle's and the rest of each permuted buffer still holds the poison."""
+    np.testing.assert_array_equal(to_np(outs["expert_first_token_offset"]), ref["expert_first_token_offset"])
+    np.testing.assert_array_equal(to_np(outs["inv_permuted_idx"]), ref["inv_permuted_idx"])
+    m = int(ref["expert_first_token_offset"][-1])
+    perm = to_np(outs["permuted_idx"])
+    np.testing.assert_array_equal(perm[:m], ref["permuted_idx"])
+    assert np.all(perm[m:].view(np.uint32) == 0xFFFFFFFF), "permuted_idx written past the local rows"
+    if outs["permuted_hidden_states"] is not None:
+        got = to_np(outs["permuted_hidden_states"])
+        gb = got.view(np.uint8).reshape(got.shape[0], -1)
+        eb = ref["permuted_hidden_states"].view(np.uint8).reshape(m, gb.shape[1])
+        if not np.array_equal(gb[:m], eb):
+            bad = np.nonzero(np.any(gb[:m] != eb, axis=1))[0]
+            raise AssertionError("local permuted rows differ at %d rows, first %s" % (bad.size, bad[:8].tolist()))
+        assert np.all(gb[m:] == POISON), "permuted rows written past the local rows"
+    if outs.get("permuted_scale") is not None:
+        sc = to_np(outs["permuted_scale"]).view(np.uint32)
+        np.testing.assert_array_equal(sc[:m], ref["permuted_scale"].view(np.uint32))
+        assert np.all(sc[m:] == 0xFFFFFFFF), "permuted_scale written past the local rows"

@@ -46,8 +46,9 @@ host_only = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer checks run on
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["moe_permute", "moe_permute_supported", "moe_permute_workspace_size",
-                                    "moe_status_string", "moe_unpermute"]
+    assert declared_functions() == ["moe_permute", "moe_permute_local", "moe_permute_local_workspace_size",
+                                    "moe_permute_supported", "moe_permute_workspace_size", "moe_status_string",
+                                    "moe_unpermute"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -158,6 +159,52 @@ def test_permute_rejects(lib, kw, status):
 def test_permute_workspace_boundary(lib):
     need = lib.moe_permute_workspace_size(20000, 8, 256)
     assert permute_call(lib, n=20000, k=8, e=256, ws_bytes=need - 1) == TOO_SMALL
+
+
+def test_local_workspace_size_pure_and_monotone(lib):
+    for k, e, nl in [(1, 1, 1), (2, 8, 4), (8, 128, 16), (8, 256, 32), (8, 256, 256), (16, 1024, 1024), (2, 8, 1024)]:
+        prev = 0
+        for n in [0, 1, 7, 100, 2048, 2049, 4096, 16384, 100000, 1 << 20]:
+            s = lib.moe_permute_local_workspace_size(n, k, e, nl)
+            assert s == lib.moe_permute_local_workspace_size(n, k, e, nl)
+            assert s >= prev
+            prev = s
+    assert lib.moe_permute_local_workspace_size(10, 2, 8, 0) == 0
+    assert lib.moe_permute_local_workspace_size(10, 2, 8, 1025) == 0
+    assert lib.moe_permute_local_workspace_size(10, 9, 8, 4) == 0
+    assert lib.moe_permute_local_workspace_size(16384, 8, 256, 32) > 0
+
+
+def local_call(lib, **kw):
+    args = dict(hidden=addr(0), dtype=BF16, scale=None, ids=addr(1), n=4096, h=4096, k=2, e=8, emap=addr(8), nl=4,
+                out=addr(2), pscale=None, off=addr(3), perm=addr(4), inv=addr(5), ws=addr(6), ws_bytes=1 << 30,
+                stream=None)
+    args.update(kw)
+    return lib.moe_permute_local(args["hidden"], args["dtype"], args["scale"], args["ids"], args["n"], args["h"],
+                                 args["k"], args["e"], args["emap"], args["nl"], args["out"], args["pscale"],
+                                 args["off"], args["perm"], args["inv"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(emap=None), INVALID),
+    (dict(nl=0), INVALID),
+    (dict(nl=1025), INVALID),
+    (dict(emap=addr(8, 2)), MISALIGNED),
+    (dict(off=addr(8)), INVALID),                           # offsets alias the map
+    (dict(k=9), INVALID),
+    (dict(dtype=5), INVALID),
+    (dict(n=20000, k=8, e=256, nl=32, ws_bytes=0), TOO_SMALL),
+])
+def test_permute_local_rejects(lib, kw, status):
+    assert local_call(lib, **kw) == status
+
+
+@host_only
+def test_permute_local_workspace_boundary(lib):
+    need = lib.moe_permute_local_workspace_size(20000, 8, 256, 32)
+    assert need > 0
+    assert local_call(lib, n=20000, k=8, e=256, nl=32, ws_bytes=need - 1) == TOO_SMALL
 
 
 def unpermute_call(lib, **kw):

@@ -1,0 +1,253 @@
+"""GPU parity of the local-expert permute (expert parallelism) against the oracle.
+
+The reading pinned in the oracle: the expert map sends a global expert to its
+local id or -1; local rows are counted, stably ordered by local id and copied;
+other rows get inverse index -1, are not copied, and add nothing when
+unpermuted.  Bar as for the plain permute: offsets, indices, rows and scales
+bit-exact (the permuted buffers past the local rows must keep their poison);
+unpermute within 2^-7 * max(1, |ref|) for bf16, 1e-5 * max(1, |ref|) for fp32.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _parity import (POISON, assert_permute_equal, assert_permute_local_equal, assert_unpermute_close, gpu_permute,
+                     gpu_permute_local, gpu_unpermute, oracle_permute_local, poisoned, to_np)
+from mixture_experts_token_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print("[case] " + msg, flush=True)
+
+
+def _inputs(name, dev, seed=0, n=None):
+    w = W.WORKLOADS[name]
+    if n is not None:
+        w = w.with_tokens(n)
+    gen_dev = "cpu" if w.num_rows * w.hidden_size <= (1 << 22) else dev
+    inp = W.make_all(w, seed=seed, device=gen_dev)
+    for key in ("topk_ids", "topk_weights", "hidden_states", "token_scale", "expert_output"):
+        if inp[key] is not None:
+            inp[key] = inp[key].to(dev)
+    return w, inp
+
+
+def _unpermute_ref(y, wts, inv, k, dtype, sample_tokens=None):
+    """Oracle unpermute, on every token or on a sample gathered into a sub-problem
+    (a -1 slot stays -1; the other slots point at their gathered rows)."""
+    if sample_tokens is None:
+        return oracle.unpermute(y, wts, inv, dtype)
+    slots = inv.reshape(-1, k)[sample_tokens].reshape(-1)
+    live = slots >= 0
+    sub_inv = np.full(slots.size, -1, dtype=np.int32)
+    sub_inv[live] = np.arange(int(live.sum()), dtype=np.int32)
+    sub_y = y[slots[live]]
+    if sub_y.shape[0] == 0:
+        sub_y = y[:1]
+    return oracle.unpermute(sub_y, wts[sample_tokens], sub_inv, dtype)
+
+
+CASES = [
+    # (workload, ep_size, rank, layout, tokens or None, sample unpermute)
+    ("tiny", 2, 1, "contiguous", None, False),
+    ("mixtral", 2, 0, "contiguous", None, False),
+    ("mixtral", 4, 3, "shuffled", None, False),
+    ("qwen3", 4, 1, "round_robin", None, False),
+    ("qwen3", 8, 7, "shuffled", None, False),
+    ("dsv3", 8, 0, "contiguous", None, True),      # the most popular experts sit in some rank's share
+    ("dsv3", 8, 5, "round_robin", 6000, True),
+    ("decode", 8, 5, "contiguous", None, False),   # fp8 codes + per-token scales
+    ("decode", 8, 2, "shuffled", 1, False),
+]
+
+
+@pytest.mark.parametrize("name,ep,rank,layout,n,sample", CASES, ids=["-".join(map(str, c[:5])) for c in CASES])
+def test_local_workload_parity(hip_device, name, ep, rank, layout, n, sample):
+    w, inp = _inputs(name, hip_device, n=n)
+    emap, nl = W.expert_map_for(w.num_experts, ep, rank, layout)
+    _say("local %s N=%d E=%d topk=%d ep=%d rank=%d %s" % (name, w.num_tokens, w.num_experts, w.topk, ep, rank, layout))
+    outs = gpu_permute_local(inp["hidden_states"], inp["topk_ids"], w.num_experts, emap, nl,
+                             token_scale=inp["token_scale"])
+    out = gpu_unpermute(inp["expert_output"], inp["topk_weights"], outs["inv_permuted_idx"])
+    torch.cuda.synchronize()
+    ref = oracle_permute_local(inp["hidden_states"], inp["topk_ids"], w.num_experts, emap, nl, inp["token_scale"])
+    assert_permute_local_equal(outs, ref)
+    y, wts, inv = to_np(inp["expert_output"]), to_np(inp["topk_weights"]), ref["inv_permuted_idx"]
+    if sample:
+        rng = np.random.default_rng(5)
+        tokens = np.unique(np.concatenate([[0, w.num_tokens - 1], rng.choice(w.num_tokens, 2000, replace=False)]))
+        assert_unpermute_close(to_np(out)[tokens], _unpermute_ref(y, wts, inv, w.topk, w.output_dtype, tokens),
+                               w.output_dtype)
+    else:
+        assert_unpermute_close(to_np(out), _unpermute_ref(y, wts, inv, w.topk, w.output_dtype), w.output_dtype)
+
+
+def _ids(rng, n, k, e, mode):
+    if mode == "distinct":
+        return np.stack([rng.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    return rng.integers(0, e, size=(n, k)).astype(np.int32)
+
+
+EDGE = [
+    # (N, topk, E, H, dtype, ids mode, map kind) -- the schedules: fused up to 16384 rows, then coarse, staged
+    (1, 1, 4, 8, "f32", "distinct", "half"),
+    (3, 2, 8, 64, "bf16", "distinct", "none_local"),
+    (1000, 4, 16, 64, "f32", "dups", "identity"),
+    (1000, 4, 16, 64, "bf16", "dups", "shared_local"),
+    (4097, 3, 12, 136, "bf16", "distinct", "odd"),
+    (16384, 2, 64, 72, "f32", "dups", "half"),          # 32768 rows: coarse
+    (30000, 8, 256, 8, "bf16", "distinct", "odd"),      # coarse, many tiles
+    (140000, 2, 16, 8, "bf16", "dups", "half"),         # staged
+    (140000, 2, 16, 8, "bf16", "dups", "none_local"),   # staged, nothing local
+]
+
+
+def _edge_map(kind, e, rng):
+    if kind == "identity":
+        return np.arange(e, dtype=np.int32), e
+    if kind == "none_local":
+        return np.full(e, -1, dtype=np.int32), 1
+    if kind == "half":
+        m = np.full(e, -1, dtype=np.int32)
+        m[e // 2:] = np.arange(e - e // 2)
+        return m, e - e // 2
+    if kind == "shared_local":  # global experts g and g + e/2 share local id g
+        m = np.full(e, -1, dtype=np.int32)
+        m[: e // 4] = np.arange(e // 4)
+        m[e // 2: e // 2 + e // 4] = np.arange(e // 4)
+        return m, e // 4
+    if kind == "odd":  # odd experts, numbered in a random order
+        odd = np.arange(1, e, 2)
+        m = np.full(e, -1, dtype=np.int32)
+        m[odd] = rng.permutation(odd.size)
+        return m, odd.size
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("n,k,e,h,dtype,mode,kind", EDGE, ids=["-".join(map(str, c)) for c in EDGE])
+def test_local_edge_parity(hip_device, n, k, e, h, dtype, mode, kind):
+    dev = hip_device
+    rng = np.random.default_rng(n * 17 + k * 5 + e)
+    ids = torch.from_numpy(_ids(rng, n, k, e, mode)).to(dev)
+    emap, nl = _edge_map(kind, e, rng)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    x = torch.randn((n, h), generator=torch.Generator().manual_seed(n + h)).to(tdt).to(dev)
+    y = torch.randn((n * k, h), generator=torch.Generator().manual_seed(n + h + 1)).to(tdt).to(dev)
+    wts = torch.rand((n, k), generator=torch.Generator().manual_seed(n + 2)).to(dev)
+    _say("local edge N=%d topk=%d E=%d H=%d %s %s %s" % (n, k, e, h, dtype, mode, kind))
+    outs = gpu_permute_local(x, ids, e, emap, nl)
+    out = gpu_unpermute(y, wts, outs["inv_permuted_idx"])
+    torch.cuda.synchronize()
+    ref = oracle_permute_local(x, ids, e, emap, nl)
+    assert_permute_local_equal(outs, ref)
+    assert_unpermute_close(to_np(out), oracle.unpermute(to_np(y), to_np(wts), ref["inv_permuted_idx"], dtype), dtype)
+    if kind == "identity":  # every expert local: exactly the plain permute
+        plain = gpu_permute(x, ids, e)
+        torch.cuda.synchronize()
+        for key in ("expert_first_token_offset", "permuted_idx", "inv_permuted_idx"):
+            assert torch.equal(plain[key], outs[key]), key
+        assert torch.equal(plain["permuted_hidden_states"].view(torch.uint8),
+                           outs["permuted_hidden_states"].view(torch.uint8))
+
+
+def test_local_zero_tokens_writes_zero_offsets(hip_device):
+    ids = torch.zeros((0, 2), dtype=torch.int32, device=hip_device)
+    emap, nl = W.expert_map_for(8, 2, 1)
+    _say("local zero tokens")
+    outs = gpu_permute_local(None, ids, 8, emap, nl)
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == [0] * (nl + 1)
+
+
+@pytest.mark.parametrize("n,k,e,bad", [(50, 2, 8, "past_local"), (50, 2, 8, "below_minus_one"),
+                                       (30000, 8, 256, "past_local"), (140000, 2, 16, "below_minus_one")])
+def test_local_bad_map_entry_detected(hip_device, n, k, e, bad):
+    """A used expert whose map entry is outside [-1, L): offsets -1, nothing else written."""
+    rng = np.random.default_rng(3)
+    ids_np = rng.integers(0, e, size=(n, k)).astype(np.int32)
+    emap, nl = W.expert_map_for(e, 2, 0)
+    used = int(ids_np[n // 2, 0])
+    emap[used] = nl if bad == "past_local" else -5
+    ids = torch.from_numpy(ids_np).to(hip_device)
+    _say("local bad map N=%d E=%d %s" % (n, e, bad))
+    outs = gpu_permute_local(None, ids, e, emap, nl)
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == [-1] * (nl + 1)
+    assert np.all(to_np(outs["inv_permuted_idx"]).view(np.uint32) == 0xFFFFFFFF)
+    assert np.all(to_np(outs["permuted_idx"]).view(np.uint32) == 0xFFFFFFFF)
+
+
+def test_local_bad_entry_of_unused_expert_is_ignored(hip_device):
+    n, k, e = 64, 2, 8
+    ids_np = np.random.default_rng(4).integers(0, 4, size=(n, k)).astype(np.int32)  # experts 0..3 only
+    emap = np.array([0, -1, 1, -1, 7, 9, -3, 2], dtype=np.int32)  # bad entries only for experts 4..6
+    ids = torch.from_numpy(ids_np).to(hip_device)
+    _say("local bad entry of an unused expert")
+    outs = gpu_permute_local(None, ids, e, emap, 3)
+    torch.cuda.synchronize()
+    assert_permute_local_equal(outs, oracle_permute_local(None, ids, e, emap, 3))
+
+
+def test_local_scratch_reuse_and_ranks_cover_every_slot(hip_device):
+    """Scratch built with an expert map, reused across ranks' maps of one
+    problem: every expanded row is local on exactly one rank, each rank's
+    offsets count its rows, and a second call repeats the first bit for bit."""
+    w, inp = _inputs("qwen3", hip_device, n=3000)
+    ep = 4
+    covered = np.zeros(w.num_rows, dtype=np.int64)
+    for rank in range(ep):
+        emap, nl = W.expert_map_for(w.num_experts, ep, rank, "round_robin")
+        emap_t = torch.from_numpy(emap).to(hip_device)
+        scratch = binding.MoEPermuteScratch(w.num_tokens, w.topk, w.num_experts, hip_device,
+                                            hidden_size=w.hidden_size, hidden_dtype=torch.bfloat16,
+                                            expert_map=emap_t, num_local_experts=nl)
+        assert scratch.expert_first_token_offset.numel() == nl + 1
+        _say("local scratch rank %d" % rank)
+        r1 = scratch.permute(inp["hidden_states"], inp["topk_ids"])
+        snap = {k: v.clone() for k, v in r1.items() if v is not None}
+        scratch.workspace.fill_(POISON)
+        r2 = scratch.permute(inp["hidden_states"], inp["topk_ids"])
+        torch.cuda.synchronize()
+        for key, v in r2.items():
+            if v is not None:
+                assert torch.equal(v.view(torch.uint8) if v.dtype == torch.bfloat16 else v,
+                                   snap[key].view(torch.uint8) if v.dtype == torch.bfloat16 else snap[key]), key
+        inv = to_np(r2["inv_permuted_idx"])
+        covered += inv >= 0
+        assert int(to_np(r2["expert_first_token_offset"])[-1]) == int((inv >= 0).sum())
+    assert covered.tolist() == [1] * w.num_rows
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 8])
+def test_unpermute_minus_one_slots_skip_and_others_nan(hip_device, k):
+    """-1 slots add nothing (their rows are not read); any other out-of-range
+    index still turns its token into NaN."""
+    n, h = 64, 128
+    rng = np.random.default_rng(k)
+    inv_np = rng.permutation(n * k).astype(np.int32)
+    inv_np[rng.random(n * k) < 0.3] = -1
+    inv_np[0:k] = -1                     # token 0: nothing local, zero row
+    inv_np[7 * k] = -2                   # token 7: invalid
+    inv = torch.from_numpy(inv_np).to(hip_device)
+    y = torch.randn((n * k, h), device=hip_device).to(torch.bfloat16)
+    wts = torch.rand((n, k), device=hip_device)
+    wts[3, 0] = float("inf")             # weight of a -1 slot is never used
+    inv[3 * k] = -1
+    inv_np[3 * k] = -1
+    _say("unpermute -1 slots topk=%d" % k)
+    out = gpu_unpermute(y, wts, inv)
+    torch.cuda.synchronize()
+    o = to_np(out)
+    of = out.float().cpu()
+    assert torch.isnan(of[7]).all()
+    keep = [t for t in range(n) if t != 7]
+    valid = inv_np.copy()
+    valid[7 * k] = -1  # the oracle rejects the invalid entry; token 7 is not compared
+    ref = oracle.unpermute(to_np(y), to_np(wts), valid, "bf16")
+    assert_unpermute_close(o[keep], ref[keep], "bf16")
+    assert np.all(o[0] == 0)

@@ -9,6 +9,8 @@ walks a grid of shapes and asserts, for every plan:
     tile <= kCoarseMaxRowsPerTile, LDS of the scatter kernel <= 64 KiB;
   * the workspace query bounds the requirement of every smaller call and is
     monotone in the token count.
+The grid covers the plain sort over E experts and the local-expert sort over
+B buckets with an E-entry map held in LDS.
 """
 
 import os
@@ -29,47 +31,53 @@ int main() {
   const int Ks[] = {1, 2, 3, 8, 16, 64, 512, 1024};
   const int Es[] = {1, 8, 37, 128, 256, 1000, 1024};
   const long long Ns[] = {1, 7, 100, 2047, 2048, 2049, 4096, 8192, 8193, 16384, 30000, 65536, 140000, 1000000};
-  for (int K : Ks) for (int E : Es) {
+  for (int K : Ks) for (int E : Es) for (int mode = 0; mode < 3; ++mode) {
     if (K > E) continue;
+    const int B = mode == 0 ? E : (mode == 1 ? (E / 8 > 0 ? E / 8 : 1) : E);  // buckets
+    const int M = mode == 0 ? 0 : E;                                         // map entries
     size_t prev = 0;
     for (long long N : Ns) {
       if (N * K >= (1LL << 31)) continue;
-      const PermutePlan p = plan_permute(N, K, E);
-      const size_t bound = workspace_bound(N, K, E);
-      CHECK(bound >= p.ws_bytes, "N=%lld K=%d E=%d bound %zu < need %zu", N, K, E, bound, p.ws_bytes);
-      CHECK(bound >= prev, "N=%lld K=%d E=%d bound not monotone", N, K, E);
+      const PermutePlan p = plan_permute(N, K, B, M);
+      const size_t bound = workspace_bound(N, K, B, M);
+      CHECK(bound >= p.ws_bytes, "N=%lld K=%d B=%d M=%d bound %zu < need %zu", N, K, B, M, bound, p.ws_bytes);
+      CHECK(bound >= prev, "N=%lld K=%d B=%d M=%d bound not monotone", N, K, B, M);
       prev = bound;
       for (long long n2 : {N / 2, N - 1, N / 3 + 1}) {
         if (n2 < 1) continue;
-        const PermutePlan q = plan_permute(n2, K, E);
-        CHECK(q.ws_bytes <= bound, "N=%lld smaller %lld K=%d E=%d needs %zu > %zu", N, n2, K, E, q.ws_bytes, bound);
+        const PermutePlan q = plan_permute(n2, K, B, M);
+        CHECK(q.ws_bytes <= bound, "N=%lld smaller %lld K=%d B=%d needs %zu > %zu", N, n2, K, B, q.ws_bytes, bound);
       }
+      CHECK(p.nbits >= 0 && (1 << p.nbits) >= B, "key bits");
       CHECK(p.tile_rows == p.tokens_per_tile * K, "tile rows");
       CHECK(p.tile_rows <= kMaxTileRows, "N=%lld K=%d tile rows %d", N, K, p.tile_rows);
       if (p.fused) {
         CHECK(p.rows <= kFusedMaxRows, "fused rows");
-        CHECK(fused_lds_bytes(E, p.tile_rows) <= 4 * kMaxLdsInts, "fused lds");
+        CHECK(fused_lds_bytes(B, p.tile_rows, M) <= 4 * kMaxLdsInts, "fused lds");
       } else if (p.coarse) {
         CHECK(p.coarse_rows % p.tile_rows == 0, "coarse rows %d not whole tiles of %d", p.coarse_rows, p.tile_rows);
         CHECK(p.num_coarse >= 1 && p.num_coarse <= kMaxCoarseTiles, "num coarse %d", p.num_coarse);
         CHECK((long long)p.num_coarse * p.coarse_rows >= p.rows, "coarse tiles cover the rows");
         CHECK((long long)(p.num_coarse - 1) * p.coarse_rows < p.rows, "no empty coarse tile");
-        CHECK(p.num_coarse * (E + 1) <= kCoarseMaxHist, "hist entries %d", p.num_coarse * (E + 1));
+        CHECK(p.num_coarse * (B + 1) <= kCoarseMaxHist, "hist entries %d", p.num_coarse * (B + 1));
         CHECK(p.coarse_rows - p.tile_rows <= kCoarseMaxRowsPerTile, "rows before a tile %d", p.coarse_rows - p.tile_rows);
-        CHECK(coarse_scatter_lds_bytes(E, p.tile_rows, p.num_coarse) <= 4 * (size_t)kMaxLdsInts, "coarse lds");
-        CHECK(p.ws_bytes >= sizeof(int) * (size_t)p.num_coarse * (E + 1), "coarse workspace");
+        CHECK(coarse_scatter_lds_bytes(B, p.tile_rows, p.num_coarse, M) <= 4 * (size_t)kMaxLdsInts, "coarse lds");
+        CHECK(coarse_hist_lds_bytes(B, M) <= 4 * (size_t)kMaxLdsInts, "coarse hist lds");
+        CHECK(p.ws_bytes >= sizeof(int) * (size_t)p.num_coarse * (B + 1), "coarse workspace");
       } else {
-        CHECK(p.ws_bytes >= staged_workspace_bytes(p.rows, p.num_tiles, E), "staged workspace");
-        CHECK(rank_lds_bytes(E, p.tile_rows) <= 4 * (size_t)kMaxLdsInts, "rank lds");
+        CHECK(p.ws_bytes >= staged_workspace_bytes(p.rows, p.num_tiles, B), "staged workspace");
+        CHECK(rank_lds_bytes(B, p.tile_rows, M) <= 4 * (size_t)kMaxLdsInts, "rank lds");
+        CHECK(scatter_lds_bytes(B, p.tile_rows, M) <= 4 * (size_t)kMaxLdsInts, "scatter lds");
       }
     }
   }
   // the named workloads take the schedules the design notes describe
-  CHECK(plan_permute(4096, 2, 8).fused, "mixtral fused");
-  CHECK(plan_permute(8192, 8, 128).coarse, "qwen3 coarse");
-  CHECK(plan_permute(16384, 8, 256).coarse, "dsv3 coarse");
-  CHECK(plan_permute(256, 8, 256).fused, "decode fused");
-  CHECK(!plan_permute(140000, 2, 16).coarse && !plan_permute(140000, 2, 16).fused, "large staged");
+  CHECK(plan_permute(4096, 2, 8, 0).fused, "mixtral fused");
+  CHECK(plan_permute(8192, 8, 128, 0).coarse, "qwen3 coarse");
+  CHECK(plan_permute(16384, 8, 256, 0).coarse, "dsv3 coarse");
+  CHECK(plan_permute(256, 8, 256, 0).fused, "decode fused");
+  CHECK(!plan_permute(140000, 2, 16, 0).coarse && !plan_permute(140000, 2, 16, 0).fused, "large staged");
+  CHECK(plan_permute(16384, 8, 32, 256).coarse, "dsv3 one of eight expert ranks: coarse");
   std::printf("%s (%d failures)\n", fails ? "FAILED" : "ok", fails);
   return fails ? 1 : 0;
 }

@@ -33,6 +33,11 @@ Recipe (every workload, seed 0 unless a test says otherwise):
 * fp8 activations: per-token scale ``max_h |x[t,h]| / 448`` (float32, 1 for an
   all-zero row), codes = OCP E4M3FN rounding of ``x / scale`` (clamped to
   +-448), stored as raw bytes.
+* Expert maps (expert parallelism over ``ep_size`` ranks): ``contiguous``
+  gives rank r the experts ``[r*E/ep, (r+1)*E/ep)`` in order, ``round_robin``
+  the experts ``g`` with ``g % ep == r``; local ids count the owned experts in
+  ascending global id; ``shuffled`` takes the contiguous set and numbers it
+  in a seeded random order.  Every other expert maps to -1.
 """
 
 from __future__ import annotations
@@ -79,6 +84,24 @@ WORKLOADS: dict[str, MoEWorkload] = {
 }
 
 DECODE_SWEEP = (1, 4, 16, 64, 256)
+
+
+def expert_map_for(num_experts: int, ep_size: int, rank: int, layout: str = "contiguous", seed: int = 0):
+    """(expert_map int32 [num_experts], num_local_experts) of one rank; see the module recipe."""
+    if not 0 <= rank < ep_size:
+        raise ValueError("rank outside [0, ep_size)")
+    if layout == "round_robin":
+        owned = [g for g in range(num_experts) if g % ep_size == rank]
+    else:
+        owned = [g for g in range(num_experts) if g * ep_size // num_experts == rank]
+    if layout == "shuffled":
+        owned = [owned[i] for i in np.random.default_rng(seed).permutation(len(owned))]
+    elif layout not in ("contiguous", "round_robin"):
+        raise ValueError("unknown layout %r" % layout)
+    emap = np.full(num_experts, -1, dtype=np.int32)
+    for local, g in enumerate(owned):
+        emap[g] = local
+    return emap, max(len(owned), 1)
 
 ELEMENT_BYTES = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}
 
