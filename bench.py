@@ -360,6 +360,7 @@ def main() -> int:
         "permute_GBps": round(nb["permute"] / (perm_avg * 1e-6) / 1e9, 1),
         "unpermute_GBps": round(nb["unpermute"] / (unperm_avg * 1e-6) / 1e9, 1),
         "algorithmic_bytes_per_step": nb["total"],
+        "algorithmic_bytes_per_op": {"permute": nb["permute"], "unpermute": nb["unpermute"]},
         "wall_s_timed_region": round(wall, 4),
         "ceiling": ceiling,
         "roofline": roofline,
