@@ -82,6 +82,8 @@ def _load():
         lib.oracle_moe_permute.restype = ctypes.c_int
         lib.oracle_moe_permute_local.argtypes = [p, i64, p, p, i64, i32, i32, p, i32, p, p, p, p, p]
         lib.oracle_moe_permute_local.restype = ctypes.c_int
+        lib.oracle_ids_from_int64.argtypes = [p, i64, i32, p]
+        lib.oracle_ids_from_int64.restype = ctypes.c_int
         lib.oracle_unpermute_f32.argtypes = [p, p, p, i64, i32, i64, p]
         lib.oracle_unpermute_f32.restype = ctypes.c_int
         lib.oracle_unpermute_bf16.argtypes = [p, p, p, i64, i32, i64, p]
@@ -107,8 +109,18 @@ def _check(status: int):
                            BAD_INV: "inv_permuted_idx out of range"}.get(status, str(status)))
 
 
-def _ids2d(topk_ids) -> np.ndarray:
-    ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
+def _ids2d(topk_ids, num_experts: int | None = None) -> np.ndarray:
+    """int32 [N, topk] ids.  int64 ids go through oracle_ids_from_int64, which
+    rejects every value outside [0, num_experts) instead of truncating it."""
+    arr = np.asarray(topk_ids)
+    if arr.dtype == np.int64:
+        if num_experts is None:
+            raise ValueError("int64 ids need num_experts to be checked")
+        src = np.ascontiguousarray(arr)
+        ids = np.zeros(src.shape, dtype=np.int32)
+        _check(_load().oracle_ids_from_int64(_ptr(src), src.size, num_experts, _ptr(ids)))
+    else:
+        ids = np.ascontiguousarray(arr, dtype=np.int32)
     if ids.ndim != 2:
         raise ValueError("topk_ids must be [num_tokens, topk]")
     return ids
@@ -119,7 +131,7 @@ def _ids2d(topk_ids) -> np.ndarray:
 # --------------------------------------------------------------------------
 def expert_counts(topk_ids, num_experts: int) -> np.ndarray:
     """Step 1: expanded rows routed to each expert (int64 [E])."""
-    ids = _ids2d(topk_ids)
+    ids = _ids2d(topk_ids, num_experts)
     counts = np.zeros(num_experts, dtype=np.int64)
     _check(_load().oracle_expert_counts(_ptr(ids), ids.shape[0], ids.shape[1], num_experts, _ptr(counts)))
     return counts
@@ -135,7 +147,7 @@ def expert_first_token_offset(counts) -> np.ndarray:
 
 def stable_expert_order(topk_ids, num_experts: int, offsets) -> tuple[np.ndarray, np.ndarray]:
     """Step 3: (permuted_idx, inv_permuted_idx), both int32 [N*topk]."""
-    ids = _ids2d(topk_ids)
+    ids = _ids2d(topk_ids, num_experts)
     offsets = np.ascontiguousarray(offsets, dtype=np.int64)
     rows = ids.size
     perm = np.zeros(rows, dtype=np.int32)
@@ -171,8 +183,9 @@ def permute(hidden: np.ndarray, topk_ids, num_experts: int, token_scale=None) ->
     fp8 codes as uint8); the permuted rows come back with the same element
     type.  Returns a dict with ``expert_first_token_offset``, ``permuted_idx``,
     ``inv_permuted_idx``, ``permuted_hidden_states`` and ``permuted_scale``.
+    ``topk_ids`` may be int32 or int64 (checked, never truncated).
     """
-    ids = _ids2d(topk_ids)
+    ids = _ids2d(topk_ids, num_experts)
     n, topk = ids.shape
     h = np.ascontiguousarray(hidden)
     if h.shape[0] != n:
@@ -204,9 +217,9 @@ def permute_local(hidden: np.ndarray, topk_ids, num_experts: int, expert_map, nu
     Returns the same keys as ``permute``; ``expert_first_token_offset`` has
     num_local_experts + 1 entries, ``permuted_idx`` / ``permuted_hidden_states``
     / ``permuted_scale`` hold only the local rows, and ``inv_permuted_idx`` is
-    -1 for rows of experts on other ranks.
+    -1 for rows of experts on other ranks.  ``topk_ids`` may be int32 or int64.
     """
-    ids = _ids2d(topk_ids)
+    ids = _ids2d(topk_ids, num_experts)
     n, topk = ids.shape
     emap = np.ascontiguousarray(expert_map, dtype=np.int32)
     if emap.shape != (num_experts,):

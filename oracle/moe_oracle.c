@@ -143,6 +143,25 @@ void oracle_gather_rows(const uint8_t *hidden_states, int64_t row_bytes,
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Expert ids given as int64.  [P3] key code snippets, prepare_topk_ids: ids  */
+/* of another integer type are cast to int32 before the permute.  The         */
+/* permute depends only on the id values, so int64 ids pose the same problem  */
+/* once every value is known to lie in [0, num_experts): copy them to int32,  */
+/* or fail on a value outside that range (no value is ever truncated).        */
+/* ------------------------------------------------------------------------ */
+int oracle_ids_from_int64(const int64_t *ids64, int64_t count, int32_t num_experts, int32_t *ids32)
+{
+    if (count < 0 || num_experts < 1)
+        return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < count; ++i) {
+        if (ids64[i] < 0 || ids64[i] >= (int64_t)num_experts)
+            return ORACLE_BAD_ID;
+        ids32[i] = (int32_t)ids64[i];
+    }
+    return ORACLE_OK;
+}
+
 /* The whole permute: steps 1 to 4 in order. */
 int oracle_moe_permute(const uint8_t *hidden_states, int64_t row_bytes,
                        const float *token_scale, const int32_t *topk_ids,

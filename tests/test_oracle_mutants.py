@@ -45,6 +45,10 @@ MUTANTS = {
         "for (int32_t k = 0; k < topk - 1; ++k) {\n                int64_t r = t * topk + k;\n"
         "                int64_t j = inv_permuted_idx[r];\n                if (j < 0)\n                    continue;\n"
         "                acc += (double)topk_weights[r] * (double)"),
+    # int64 ids
+    "int64_ids_truncated": (
+        "if (ids64[i] < 0 || ids64[i] >= (int64_t)num_experts)",
+        "if ((int32_t)ids64[i] < 0 || (int32_t)ids64[i] >= num_experts)"),
     # local-expert filter
     "local_remote_rows_get_slot_zero": (
         "inv_permuted_idx[r] = -1;\n                continue;",

@@ -516,3 +516,31 @@ def test_unpermute_minus_one_slots_match_masked_einsum(dtype):
     else:
         assert np.all(np.abs(of - ref) <= 2.0**-8 * np.abs(ref) + 2.0**-133)
     assert np.all(of[0] == 0.0)
+
+
+# --------------------------------------------------------------------------
+# int64 expert ids.  The permute depends only on the id values; an int64 value
+# outside [0, E) is an error even when its low 32 bits are a valid id.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n,k,e", [(0, 2, 4), (1, 1, 1), (7, 3, 8), (16, 8, 8), (50, 4, 300)])
+def test_int64_ids_permute_like_their_values(n, k, e):
+    rng = np.random.default_rng(300 + n + k + e)
+    ids64 = rng.integers(0, e, size=(n, k)).astype(np.int64)
+    hidden = rng.standard_normal((n, 4)).astype(np.float32)
+    got = oracle.permute(hidden, ids64, e)
+    off, perm, inv, gathered = brute_permute([[int(v) for v in row] for row in ids64.tolist()], e,
+                                             [row.tobytes() for row in hidden])
+    assert got["expert_first_token_offset"].tolist() == off
+    assert got["permuted_idx"].tolist() == perm
+    assert got["inv_permuted_idx"].tolist() == inv
+    assert [row.tobytes() for row in got["permuted_hidden_states"]] == gathered
+
+
+@pytest.mark.parametrize("bad", [8, -1, 2**31, 2**32 + 3, -(2**32), -(2**32) + 5, 2**63 - 1, -(2**63)])
+def test_int64_ids_outside_range_rejected_not_truncated(bad):
+    ids = np.array([[0, 1], [2, 3]], dtype=np.int64)
+    ids[1, 0] = bad
+    with pytest.raises(oracle.OracleError):
+        oracle.permute(np.zeros((2, 4), np.float32), ids, 8)
+    with pytest.raises(oracle.OracleError):
+        oracle.permute_local(np.zeros((2, 4), np.float32), ids, 8, list(range(8)), 8)
