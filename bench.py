@@ -43,7 +43,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mixture_experts_token_amd", "csrc")
 
 
-def algorithmic_bytes(w, local=None) -> dict:
+def algorithmic_bytes(w, local=None, id_bytes: int = 4) -> dict:
     """Bytes the method must move: each input read once, each output written once.
 
     local: None for the plain permute, else (tokens_read, local_rows,
@@ -57,13 +57,13 @@ def algorithmic_bytes(w, local=None) -> dict:
     by = W.ELEMENT_BYTES[w.output_dtype]
     n, h, r, e = w.num_tokens, w.hidden_size, w.num_rows, w.num_experts
     if local is None:
-        permute = n * h * b + r * h * b + 4 * r + 8 * r + 8 * (e + 1)
+        permute = n * h * b + r * h * b + id_bytes * r + 8 * r + 8 * (e + 1)
         if w.hidden_dtype == "fp8_e4m3":
             permute += 4 * n + 4 * r
         unpermute = r * h * by + 4 * r + 4 * r + n * h * by
     else:
         t_read, m, nl = local
-        permute = t_read * h * b + m * h * b + 4 * r + 4 * e + 4 * r + 4 * m + 8 * (nl + 1)
+        permute = t_read * h * b + m * h * b + id_bytes * r + 4 * e + 4 * r + 4 * m + 8 * (nl + 1)
         if w.hidden_dtype == "fp8_e4m3":
             permute += 4 * t_read + 4 * m
         unpermute = m * h * by + 4 * r + 4 * m + n * h * by
@@ -154,6 +154,8 @@ def main() -> int:
     ap.add_argument("--ep", type=int, default=1, help="expert-parallel ranks: time one rank's local-expert step")
     ap.add_argument("--ep-rank", type=int, default=0)
     ap.add_argument("--ep-layout", default="contiguous", choices=["contiguous", "round_robin", "shuffled"])
+    ap.add_argument("--ids", default="int32", choices=["int32", "int64"],
+                    help="expert id type handed to the permute (int64 is read directly, no cast pass)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -161,7 +163,7 @@ def main() -> int:
               "(the path shards by token or by expert, see the design notes)" % args.gpus, file=sys.stderr)
         return 2
 
-    import numpy as np  # noqa: F401
+    import numpy as np
     import torch
 
     import workloads as W
@@ -181,9 +183,9 @@ def main() -> int:
         local = (int(is_local.any(axis=1).sum()), int(is_local.sum()), n_local)
         emap = torch.from_numpy(emap_np).to(dev)
         n_off = n_local + 1
-    nb = algorithmic_bytes(w, local)
+    nb = algorithmic_bytes(w, local, 8 if args.ids == "int64" else 4)
 
-    ids = torch.from_numpy(ids_np).to(dev)
+    ids = torch.from_numpy(ids_np.astype(np.int64) if args.ids == "int64" else ids_np).to(dev)
     wts = torch.from_numpy(wts_np).to(dev)
     x0, scale0 = W.make_hidden(w, seed=0, device=dev)
     y0 = W.make_expert_output(w, seed=0, device=dev)
@@ -345,7 +347,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "num_tokens": w.num_tokens, "hidden_size": w.hidden_size,
                    "num_experts": w.num_experts, "topk": w.topk, "hidden_dtype": w.hidden_dtype,
-                   "output_dtype": w.output_dtype, "routing": w.routing, "buffer_sets": nsets,
+                   "output_dtype": w.output_dtype, "routing": w.routing, "ids_dtype": args.ids, "buffer_sets": nsets,
                    "parallelism": "single GPU" if local is None else
                    "one expert-parallel rank's share on a single GPU",
                    **({} if local is None else {"expert_parallel": {

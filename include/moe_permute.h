@@ -45,7 +45,7 @@
  *     failed check returns its status and leaves every buffer untouched.
  *   - Alignment: hidden / expanded / output row pointers 16 bytes, and the
  *     row length in bytes (hidden_size * element size) a multiple of 16;
- *     int32 and float arrays 4 bytes; int64 arrays 8 bytes.
+ *     int32 and float arrays 4 bytes; int64 arrays (offsets, int64 ids) 8 bytes.
  *   - Limits: 1 <= num_experts <= MOE_MAX_EXPERTS; 1 <= topk <= num_experts;
  *     num_tokens >= 0; num_tokens * topk < 2^31 (int32 indices).
  */
@@ -69,9 +69,11 @@ typedef enum moe_status {
 } moe_status_t;
 
 typedef enum moe_dtype {
-    MOE_DTYPE_F32 = 0,     /* IEEE binary32 */
-    MOE_DTYPE_BF16 = 1,    /* bfloat16 */
-    MOE_DTYPE_FP8_E4M3 = 2 /* OCP fp8 E4M3FN codes (permute moves them as bytes) */
+    MOE_DTYPE_F32 = 0,      /* IEEE binary32 */
+    MOE_DTYPE_BF16 = 1,     /* bfloat16 */
+    MOE_DTYPE_FP8_E4M3 = 2, /* OCP fp8 E4M3FN codes (permute moves them as bytes) */
+    MOE_DTYPE_INT32 = 3,    /* expert ids (topk_ids_dtype only) */
+    MOE_DTYPE_INT64 = 4     /* expert ids (topk_ids_dtype only) */
 } moe_dtype_t;
 
 #define MOE_MAX_EXPERTS 1024
@@ -104,7 +106,11 @@ size_t moe_permute_workspace_size(int64_t max_num_tokens, int32_t topk, int32_t 
  *   hidden_states            [N, hidden_size] of `dtype`; ignored when hidden_size == 0
  *   dtype                    MOE_DTYPE_F32 / BF16 / FP8_E4M3 (rows are moved as raw bytes)
  *   token_scale              [N] float, per-token activation scale, or NULL
- *   topk_ids                 [N, topk] int32, every value in [0, num_experts)
+ *   topk_ids                 [N, topk] of topk_ids_dtype, every value in [0, num_experts)
+ *   topk_ids_dtype           MOE_DTYPE_INT32 or MOE_DTYPE_INT64.  int64 ids are read as
+ *                            such and range-checked, never truncated; this removes the
+ *                            separate int64 -> int32 cast pass that the summary of vLLM
+ *                            PR #43014 shows in prepare_topk_ids ("key code snippets").
  *   num_tokens, hidden_size, topk, num_experts   sizes (hidden_size 0: indices only)
  *   permuted_hidden_states   [N*topk, hidden_size] of `dtype` (out); ignored when hidden_size == 0
  *   permuted_scale           [N*topk] float (out); non-NULL exactly when token_scale is
@@ -118,16 +124,17 @@ size_t moe_permute_workspace_size(int64_t max_num_tokens, int32_t topk, int32_t 
  *
  * Results never depend on earlier contents of the outputs or the workspace.
  * With num_tokens == 0 only the offsets are written (all zero).
- * An expert id outside [0, num_experts) is detected on the device: then every
- * entry of expert_first_token_offset is set to -1 and nothing else is
- * written; no out-of-bounds access happens.
+ * An expert id outside [0, num_experts) (for int64 ids: any such int64 value)
+ * is detected on the device: then every entry of expert_first_token_offset is
+ * set to -1 and nothing else is written; no out-of-bounds access happens.
  */
 moe_status_t moe_permute(const void *hidden_states, int32_t dtype, const float *token_scale,
-                         const int32_t *topk_ids, int64_t num_tokens, int64_t hidden_size,
-                         int32_t topk, int32_t num_experts, void *permuted_hidden_states,
-                         float *permuted_scale, int64_t *expert_first_token_offset,
-                         int32_t *permuted_idx, int32_t *inv_permuted_idx, void *workspace,
-                         size_t workspace_bytes, void *stream);
+                         const void *topk_ids, int32_t topk_ids_dtype, int64_t num_tokens,
+                         int64_t hidden_size, int32_t topk, int32_t num_experts,
+                         void *permuted_hidden_states, float *permuted_scale,
+                         int64_t *expert_first_token_offset, int32_t *permuted_idx,
+                         int32_t *inv_permuted_idx, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /*
  * moe_permute_local_workspace_size -- as moe_permute_workspace_size, for
@@ -169,8 +176,9 @@ size_t moe_permute_local_workspace_size(int64_t max_num_tokens, int32_t topk, in
  * expert_first_token_offset is set to -1 and nothing else is written.
  */
 moe_status_t moe_permute_local(const void *hidden_states, int32_t dtype, const float *token_scale,
-                               const int32_t *topk_ids, int64_t num_tokens, int64_t hidden_size,
-                               int32_t topk, int32_t num_experts, const int32_t *expert_map,
+                               const void *topk_ids, int32_t topk_ids_dtype, int64_t num_tokens,
+                               int64_t hidden_size, int32_t topk, int32_t num_experts,
+                               const int32_t *expert_map,
                                int32_t num_local_experts, void *permuted_hidden_states,
                                float *permuted_scale, int64_t *expert_first_token_offset,
                                int32_t *permuted_idx, int32_t *inv_permuted_idx, void *workspace,

@@ -30,6 +30,8 @@ MOE_ERR_HIP = 5
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 MOE_DTYPE_FP8_E4M3 = 2
+MOE_DTYPE_INT32 = 3
+MOE_DTYPE_INT64 = 4
 MOE_MAX_EXPERTS = 1024
 
 
@@ -56,11 +58,11 @@ def load_library() -> ctypes.CDLL:
         lib.moe_permute_supported.restype = ctypes.c_int
         lib.moe_permute_workspace_size.argtypes = [i64, i32, i32]
         lib.moe_permute_workspace_size.restype = sz
-        lib.moe_permute.argtypes = [p, i32, p, p, i64, i64, i32, i32, p, p, p, p, p, p, sz, p]
+        lib.moe_permute.argtypes = [p, i32, p, p, i32, i64, i64, i32, i32, p, p, p, p, p, p, sz, p]
         lib.moe_permute.restype = ctypes.c_int
         lib.moe_permute_local_workspace_size.argtypes = [i64, i32, i32, i32]
         lib.moe_permute_local_workspace_size.restype = sz
-        lib.moe_permute_local.argtypes = [p, i32, p, p, i64, i64, i32, i32, p, i32, p, p, p, p, p, p, sz, p]
+        lib.moe_permute_local.argtypes = [p, i32, p, p, i32, i64, i64, i32, i32, p, i32, p, p, p, p, p, p, sz, p]
         lib.moe_permute_local.restype = ctypes.c_int
         lib.moe_unpermute.argtypes = [p, i32, p, p, i64, i64, i32, p, p]
         lib.moe_unpermute.restype = ctypes.c_int
@@ -124,14 +126,15 @@ def moe_permute_local_workspace_size(max_num_tokens: int, topk: int, num_experts
 def _permute_args(hidden_states, topk_ids, workspace):
     import torch
 
-    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
-        raise TypeError("topk_ids must be an int32 [num_tokens, topk] tensor")
+    if topk_ids.dtype not in (torch.int32, torch.int64) or topk_ids.dim() != 2:
+        raise TypeError("topk_ids must be an int32 or int64 [num_tokens, topk] tensor")
+    ids_code = MOE_DTYPE_INT64 if topk_ids.dtype == torch.int64 else MOE_DTYPE_INT32
     if hidden_states is None:
         hidden, code, hsize = None, MOE_DTYPE_BF16, 0
     else:
         hidden, code, hsize = hidden_states, _dtype_code(hidden_states), hidden_states.shape[-1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    return hidden, code, hsize, ws_bytes
+    return hidden, code, hsize, ws_bytes, ids_code
 
 
 def moe_permute(hidden_states, topk_ids, num_experts: int, permuted_hidden_states,
@@ -140,13 +143,14 @@ def moe_permute(hidden_states, topk_ids, num_experts: int, permuted_hidden_state
     """Enqueue the permute on ``stream`` (default: torch's current stream).
 
     ``hidden_states`` [N, H] (float32, bfloat16, or fp8 codes as uint8 /
-    float8_e4m3fn) or None for an index-only permute; ``topk_ids`` int32
-    [N, topk].  Outputs are written in place.
+    float8_e4m3fn) or None for an index-only permute; ``topk_ids`` int32 or
+    int64 [N, topk] (int64 is read directly, no cast pass).  Outputs are
+    written in place.
     """
-    hidden, code, hsize, ws_bytes = _permute_args(hidden_states, topk_ids, workspace)
+    hidden, code, hsize, ws_bytes, ids_code = _permute_args(hidden_states, topk_ids, workspace)
     n, topk = topk_ids.shape
     status = load_library().moe_permute(
-        _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), n, hsize, topk, int(num_experts),
+        _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), ids_code, n, hsize, topk, int(num_experts),
         _ptr(permuted_hidden_states) if hsize else None, _ptr(permuted_scale),
         _ptr(expert_first_token_offset), _ptr(permuted_idx), _ptr(inv_permuted_idx),
         _ptr(workspace), ws_bytes, _stream(stream, topk_ids))
@@ -167,10 +171,10 @@ def moe_permute_local(hidden_states, topk_ids, num_experts: int, expert_map, num
 
     if expert_map is None or expert_map.dtype != torch.int32 or expert_map.shape != (int(num_experts),):
         raise TypeError("expert_map must be an int32 [num_experts] tensor")
-    hidden, code, hsize, ws_bytes = _permute_args(hidden_states, topk_ids, workspace)
+    hidden, code, hsize, ws_bytes, ids_code = _permute_args(hidden_states, topk_ids, workspace)
     n, topk = topk_ids.shape
     status = load_library().moe_permute_local(
-        _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), n, hsize, topk, int(num_experts),
+        _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), ids_code, n, hsize, topk, int(num_experts),
         _ptr(expert_map), int(num_local_experts),
         _ptr(permuted_hidden_states) if hsize else None, _ptr(permuted_scale),
         _ptr(expert_first_token_offset), _ptr(permuted_idx), _ptr(inv_permuted_idx),

@@ -12,7 +12,8 @@ namespace moe {
 struct PermuteArgs {
     const void* hidden_states;      // [N, row_vecs * 16 bytes] or null when row_vecs == 0
     const float* token_scale;       // [N] or null
-    const int32_t* topk_ids;        // [N, topk]
+    const void* topk_ids;           // [N, topk] int32, or int64 when ids64
+    bool ids64;
     int64_t num_tokens;
     int64_t row_vecs;               // row length in 16-byte vectors (0: indices only)
     int32_t topk;

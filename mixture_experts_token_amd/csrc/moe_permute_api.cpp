@@ -102,8 +102,8 @@ namespace {
 
 // Both permute entry points: expert_map == nullptr sorts by expert over
 // num_experts buckets; otherwise by local id over num_local_experts buckets.
-moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float* token_scale,
-                          const int32_t* topk_ids, int64_t num_tokens, int64_t hidden_size, int32_t topk,
+moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float* token_scale, const void* topk_ids,
+                          int32_t ids_dtype, int64_t num_tokens, int64_t hidden_size, int32_t topk,
                           int32_t num_experts, const int32_t* expert_map, int32_t num_local_experts,
                           void* permuted_hidden_states, float* permuted_scale, int64_t* expert_first_token_offset,
                           int32_t* permuted_idx, int32_t* inv_permuted_idx, void* workspace,
@@ -114,6 +114,8 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
     const bool mapped = expert_map != nullptr;
     if (mapped && (num_local_experts < 1 || num_local_experts > MOE_MAX_EXPERTS)) return MOE_ERR_INVALID_ARG;
     if (mapped && !aligned(expert_map, 4)) return MOE_ERR_MISALIGNED;
+    if (ids_dtype != MOE_DTYPE_INT32 && ids_dtype != MOE_DTYPE_INT64) return MOE_ERR_INVALID_ARG;
+    const uint64_t id_bytes = ids_dtype == MOE_DTYPE_INT64 ? 8 : 4;
     const int32_t buckets = mapped ? num_local_experts : num_experts;
     const int map_entries = mapped ? num_experts : 0;
     if (hidden_size < 0 || hidden_size > kMaxRowBytes / eb) return MOE_ERR_INVALID_ARG;
@@ -131,7 +133,7 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
     if (topk_ids == nullptr || permuted_idx == nullptr || inv_permuted_idx == nullptr) return MOE_ERR_INVALID_ARG;
     if (hidden_size > 0 && (hidden_states == nullptr || permuted_hidden_states == nullptr))
         return MOE_ERR_INVALID_ARG;
-    if (!aligned(topk_ids, 4) || !aligned(permuted_idx, 4) || !aligned(inv_permuted_idx, 4))
+    if (!aligned(topk_ids, id_bytes) || !aligned(permuted_idx, 4) || !aligned(inv_permuted_idx, 4))
         return MOE_ERR_MISALIGNED;
     if (token_scale != nullptr && (!aligned(token_scale, 4) || !aligned(permuted_scale, 4))) return MOE_ERR_MISALIGNED;
     if (hidden_size > 0 && (!aligned(hidden_states, 16) || !aligned(permuted_hidden_states, 16)))
@@ -157,7 +159,7 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
     const Span ins[] = {
         {copy_rows ? hidden_states : nullptr, (uint64_t)num_tokens * (uint64_t)row_bytes},
         {token_scale, (uint64_t)num_tokens * 4},
-        {topk_ids, rows * 4},
+        {topk_ids, rows * id_bytes},
         {expert_map, 4ull * (uint64_t)map_entries},
     };
     if (any_overlap(outs, 6, ins, 4)) return MOE_ERR_INVALID_ARG;
@@ -166,6 +168,7 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
     a.hidden_states = copy_rows ? hidden_states : nullptr;
     a.token_scale = token_scale;
     a.topk_ids = topk_ids;
+    a.ids64 = ids_dtype == MOE_DTYPE_INT64;
     a.num_tokens = num_tokens;
     a.row_vecs = row_bytes / 16;
     a.topk = topk;
@@ -184,25 +187,26 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
 
 extern "C" {
 
-moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* token_scale,
-                         const int32_t* topk_ids, int64_t num_tokens, int64_t hidden_size, int32_t topk,
+moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* token_scale, const void* topk_ids,
+                         int32_t topk_ids_dtype, int64_t num_tokens, int64_t hidden_size, int32_t topk,
                          int32_t num_experts, void* permuted_hidden_states, float* permuted_scale,
                          int64_t* expert_first_token_offset, int32_t* permuted_idx, int32_t* inv_permuted_idx,
                          void* workspace, size_t workspace_bytes, void* stream) {
-    return permute_impl(hidden_states, dtype, token_scale, topk_ids, num_tokens, hidden_size, topk, num_experts,
-                        nullptr, 0, permuted_hidden_states, permuted_scale, expert_first_token_offset, permuted_idx,
-                        inv_permuted_idx, workspace, workspace_bytes, stream);
+    return permute_impl(hidden_states, dtype, token_scale, topk_ids, topk_ids_dtype, num_tokens, hidden_size, topk,
+                        num_experts, nullptr, 0, permuted_hidden_states, permuted_scale, expert_first_token_offset,
+                        permuted_idx, inv_permuted_idx, workspace, workspace_bytes, stream);
 }
 
 moe_status_t moe_permute_local(const void* hidden_states, int32_t dtype, const float* token_scale,
-                               const int32_t* topk_ids, int64_t num_tokens, int64_t hidden_size, int32_t topk,
-                               int32_t num_experts, const int32_t* expert_map, int32_t num_local_experts,
+                               const void* topk_ids, int32_t topk_ids_dtype, int64_t num_tokens,
+                               int64_t hidden_size, int32_t topk, int32_t num_experts, const int32_t* expert_map,
+                               int32_t num_local_experts,
                                void* permuted_hidden_states, float* permuted_scale,
                                int64_t* expert_first_token_offset, int32_t* permuted_idx,
                                int32_t* inv_permuted_idx, void* workspace, size_t workspace_bytes, void* stream) {
     if (expert_map == nullptr) return MOE_ERR_INVALID_ARG;
-    return permute_impl(hidden_states, dtype, token_scale, topk_ids, num_tokens, hidden_size, topk, num_experts,
-                        expert_map, num_local_experts, permuted_hidden_states, permuted_scale,
+    return permute_impl(hidden_states, dtype, token_scale, topk_ids, topk_ids_dtype, num_tokens, hidden_size, topk,
+                        num_experts, expert_map, num_local_experts, permuted_hidden_states, permuted_scale,
                         expert_first_token_offset, permuted_idx, inv_permuted_idx, workspace, workspace_bytes,
                         stream);
 }

@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "moe_launch.h"
 #include "moe_plan.h"
@@ -90,6 +91,14 @@ __device__ __forceinline__ int bucket_of(int id, int E, const int* map_s, int B)
         if (m == -1) return kRemoteKey;
         return (unsigned)m < (unsigned)B ? m : kBadKey;
     }
+}
+
+// Expert id of expanded row r.  int64 ids outside [0, 2^31) become -1, which
+// every caller treats as out of range: a value is never truncated into range.
+__device__ __forceinline__ int load_id(const int32_t* ids, int64_t r) { return ids[r]; }
+__device__ __forceinline__ int load_id(const int64_t* ids, int64_t r) {
+    const int64_t v = ids[r];
+    return (v >= 0 && v <= INT32_MAX) ? (int)v : -1;
 }
 
 // The map, read into registers with the other early index loads (before any
@@ -215,11 +224,11 @@ __device__ void rank_tile(const int* key_s, int tile_rows, int B, int nbits, int
 // of U*64 16-byte vectors); wave w takes items w, w+W, ...  dest_s[tl*topk+k]
 // is the permuted row of the tile's token tl, slot k.
 // ----------------------------------------------------------------------------
-template <int U, bool kNTStore, bool kSparse>
+template <int U, bool kNTStore, bool kSparse, typename IdT>
 struct TileCopy {
     const u32x4* __restrict__ src;  // first row of the tile
     u32x4* __restrict__ dst;        // permuted_hidden_states
-    const int32_t* ids;             // topk_ids of the tile's first token
+    const IdT* ids;                 // topk_ids of the tile's first token
     const int32_t* emap;            // expert map (kSparse)
     int64_t rv;                     // row length in vectors
     int64_t rows_total;             // N * topk
@@ -232,7 +241,7 @@ struct TileCopy {
     __device__ TileCopy(const PermuteArgs& a, int64_t t0, int ntok)
         : src(reinterpret_cast<const u32x4*>(a.hidden_states) + t0 * a.row_vecs),
           dst(reinterpret_cast<u32x4*>(a.permuted_hidden_states)),
-          ids(a.topk_ids + t0 * a.topk),
+          ids(static_cast<const IdT*>(a.topk_ids) + t0 * a.topk),
           emap(a.expert_map),
           rv(a.row_vecs),
           rows_total(a.num_tokens * a.topk),
@@ -278,13 +287,13 @@ struct TileCopy {
             // Eight ids, then their eight map entries, per round trip (clamped
             // addresses, so every read is in bounds and none waits on a branch).
             const int tl = __builtin_amdgcn_readfirstlane(w / nchunks);
-            const int32_t* tid = ids + tl * K;
+            const IdT* tid = ids + tl * K;
             live = false;
             int any = 0;
             for (int k0 = 0; k0 < K; k0 += 8) {
                 int id[8], m[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) id[q] = tid[min(k0 + q, K - 1)];
+                for (int q = 0; q < 8; ++q) id[q] = load_id(tid, min(k0 + q, K - 1));
 #pragma unroll
                 for (int q = 0; q < 8; ++q) m[q] = emap[min((unsigned)id[q], (unsigned)(E - 1))];
 #pragma unroll
@@ -319,8 +328,8 @@ struct TileCopy {
 // Store every item of wave w, starting from `cur` (already loaded for item w),
 // loading item it+W while item it is stored.
 // cur already holds the wave's first item (TileCopy::prefetch).
-template <int U, int NT, bool kNTStore, bool kSparse>
-__device__ __forceinline__ void copy_items_pipelined(const TileCopy<U, kNTStore, kSparse>& tc, u32x4 (&cur)[U],
+template <int U, int NT, bool kNTStore, bool kSparse, typename IdT>
+__device__ __forceinline__ void copy_items_pipelined(const TileCopy<U, kNTStore, kSparse, IdT>& tc, u32x4 (&cur)[U],
                                                      const int* dest_s) {
     constexpr int W = NT / kWaveSize;
     for (int it = wave_index(); it < tc.items; it += W) {
@@ -354,13 +363,13 @@ __device__ __forceinline__ void copy_tile_scales(const PermuteArgs& a, int64_t t
 
 // Expert ids of this wave's tile rows (issued early, independent loads);
 // tile_keys_to_buckets turns them into sort keys once the map is in LDS.
-template <int kB>
-__device__ __forceinline__ void load_tile_keys(const int32_t* __restrict__ ids, int row0, int T, int span, int w,
+template <int kB, typename IdT>
+__device__ __forceinline__ void load_tile_keys(const IdT* __restrict__ ids, int row0, int T, int span, int w,
                                                int lane, int (&tkey)[kB]) {
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
         const int i = w * span + b * kWaveSize + lane;
-        tkey[b] = ids[row0 + (i < T ? i : T - 1)];
+        tkey[b] = load_id(ids, row0 + (i < T ? i : T - 1));
     }
 }
 
@@ -502,7 +511,7 @@ __device__ __forceinline__ void write_dests(const PermuteArgs& a, const int (&tk
 // ranks its own rows, derives expert_first_token_offset and its own base per
 // expert, scatters permuted_idx / inv_permuted_idx and copies its rows.
 // ----------------------------------------------------------------------------
-template <int NT, int U, bool kNTStore, bool kMap>
+template <int NT, int U, bool kNTStore, bool kMap, typename IdT>
 __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int tokens_per_tile, int nbits) {
     constexpr int W = NT / kWaveSize;
     constexpr int kIds = kFusedMaxRows / NT;                       // expert ids held per thread
@@ -522,6 +531,7 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
     const int tile_cap = tokens_per_tile * K;
     const int R = (int)(a.num_tokens * K);  // <= kFusedMaxRows
     const int span = (T + NT - 1) / NT * kWaveSize;
+    const IdT* ids = static_cast<const IdT*>(a.topk_ids);
 
     // Loads, all independent: every expert id of the problem, the map, this
     // wave's own tile rows, then the first row chunk of this wave.  The
@@ -531,13 +541,13 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
         const int r = (int)threadIdx.x + j * NT;
-        idv[j] = a.topk_ids[r < R ? r : R - 1];
+        idv[j] = load_id(ids, r < R ? r : R - 1);
     }
     MapStage<NT, kMap> ms;
     ms.load(a);
     int tkey[kBatches];
-    load_tile_keys<kBatches>(a.topk_ids, row0, T, span, w, lane, tkey);
-    const TileCopy<U, kNTStore, kMap> tc(a, t0, ntok);
+    load_tile_keys<kBatches>(ids, row0, T, span, w, lane, tkey);
+    const TileCopy<U, kNTStore, kMap, IdT> tc(a, t0, ntok);
     u32x4 cur[U];
     tc.prefetch(w, cur);
 
@@ -591,7 +601,7 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
     // Phase 3: destinations of this wave's tile rows, then the row copy.
     write_dests<kMap, kBatches>(a, tkey, trank, row0, T, span, B, w, lane, before_s, wave_s, dest_s);
     lds_barrier();
-    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore, kMap>(tc, cur, dest_s);
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore, kMap, IdT>(tc, cur, dest_s);
     copy_tile_scales<NT>(a, t0, ntok, dest_s);
 }
 
@@ -601,8 +611,8 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
 // hist[c][B] = rows with a bad id or map entry.  Rows of remote experts are
 // not counted.
 // ----------------------------------------------------------------------------
-template <int NT, bool kMap>
-__global__ __launch_bounds__(NT) void permute_coarse_hist_kernel(const int32_t* __restrict__ ids,
+template <int NT, bool kMap, typename IdT>
+__global__ __launch_bounds__(NT) void permute_coarse_hist_kernel(const IdT* __restrict__ ids,
                                                                  const int32_t* __restrict__ expert_map, int R, int E,
                                                                  int B, int coarse_rows, int32_t* __restrict__ hist) {
     extern __shared__ int smem[];  // [B + 1], then the map [E] when there is one
@@ -615,7 +625,7 @@ __global__ __launch_bounds__(NT) void permute_coarse_hist_kernel(const int32_t* 
     const int r0 = (int)blockIdx.x * coarse_rows;
     const int r1 = min(r0 + coarse_rows, R);
     for (int r = r0 + (int)threadIdx.x; r < r1; r += NT) {
-        const int key = bucket_of<kMap>(ids[r], E, map_s, B);
+        const int key = bucket_of<kMap>(load_id(ids, r), E, map_s, B);
         if (key != kRemoteKey) atomicAdd(&smem[key >= 0 ? key : B], 1);
     }
     lds_barrier();
@@ -629,7 +639,7 @@ __global__ __launch_bounds__(NT) void permute_coarse_hist_kernel(const int32_t* 
 // coarse histogram (held in LDS) plus a count of the rows that precede the
 // tile inside its own coarse tile.  Tiles never straddle coarse tiles.
 // ----------------------------------------------------------------------------
-template <int NT, int U, bool kNTStore, bool kMap>
+template <int NT, int U, bool kNTStore, bool kMap, typename IdT>
 __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs a, int tokens_per_tile, int nbits,
                                                                     int coarse_rows, int num_coarse,
                                                                     const int32_t* __restrict__ hist) {
@@ -654,6 +664,7 @@ __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs 
     const int cc = row0 / coarse_rows;  // this tile's coarse tile
     const int c_start = cc * coarse_rows;
     const int hist_n = num_coarse * (B + 1);
+    const IdT* ids = static_cast<const IdT*>(a.topk_ids);
 
     // Independent loads first: the coarse histogram, the rows that precede
     // this tile in its coarse tile, the map, this wave's tile keys; then row
@@ -668,13 +679,13 @@ __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs 
 #pragma unroll
     for (int j = 0; j < kPartial; ++j) {
         const int r = c_start + (int)threadIdx.x + j * NT;
-        pv[j] = a.topk_ids[r < row0 ? r : row0];  // row0 is a valid row (T >= 1)
+        pv[j] = load_id(ids, r < row0 ? r : row0);  // row0 is a valid row (T >= 1)
     }
     MapStage<NT, kMap> ms;
     ms.load(a);
     int tkey[kBatches];
-    load_tile_keys<kBatches>(a.topk_ids, row0, T, span, w, lane, tkey);
-    const TileCopy<U, kNTStore, kMap> tc(a, t0, ntok);
+    load_tile_keys<kBatches>(ids, row0, T, span, w, lane, tkey);
+    const TileCopy<U, kNTStore, kMap, IdT> tc(a, t0, ntok);
     u32x4 cur[U];
     tc.prefetch(w, cur);
 
@@ -741,7 +752,7 @@ __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs 
     // Phase 3: destinations, then the row copy.
     write_dests<kMap, kBatches>(a, tkey, trank, row0, T, span, B, w, lane, before_s, wave_s, dest_s);
     lds_barrier();
-    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore, kMap>(tc, cur, dest_s);
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore, kMap, IdT>(tc, cur, dest_s);
     copy_tile_scales<NT>(a, t0, ntok, dest_s);
 }
 
@@ -750,7 +761,7 @@ __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs 
 // rank_ws[r] = rank of row r within its tile; tile_hist[b][tile] = count,
 // tile_hist[B][tile] = rows with a bad id or map entry.
 // ----------------------------------------------------------------------------
-template <int NT, bool kMap>
+template <int NT, bool kMap, typename IdT>
 __global__ __launch_bounds__(NT) void permute_rank_tiles_kernel(PermuteArgs a, int tokens_per_tile, int nbits,
                                                                 int64_t num_tiles, int32_t* rank_ws,
                                                                 int32_t* tile_hist) {
@@ -781,7 +792,7 @@ __global__ __launch_bounds__(NT) void permute_rank_tiles_kernel(PermuteArgs a, i
     const int* map_s = map_w;
     int nbad = 0;
     for (int i = threadIdx.x; i < T; i += NT) {
-        const int key = bucket_of<kMap>(a.topk_ids[row0 + i], E, map_s, B);
+        const int key = bucket_of<kMap>(load_id(static_cast<const IdT*>(a.topk_ids), row0 + i), E, map_s, B);
         nbad += key == kBadKey ? 1 : 0;
         key_s[i] = key >= 0 ? key : -1;
     }
@@ -848,7 +859,7 @@ __global__ __launch_bounds__(NT) void permute_scan_tiles_kernel(int32_t* tile_hi
 // Staged permute, kernel 3: offsets from the per-bucket totals, destinations
 // from offset + tile base + rank, index scatter, and the row copy.
 // ----------------------------------------------------------------------------
-template <int NT, int U, bool kNTStore, bool kMap>
+template <int NT, int U, bool kNTStore, bool kMap, typename IdT>
 __global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int tokens_per_tile, int64_t num_tiles,
                                                              const int32_t* rank_ws, const int32_t* tile_base,
                                                              const int32_t* total) {
@@ -879,12 +890,12 @@ __global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int 
     for (int j = 0; j < kT; ++j) {
         const int i = (int)threadIdx.x + j * NT;
         const int64_t r = row0 + (i < T ? i : T - 1);
-        key[j] = a.topk_ids[r];
+        key[j] = load_id(static_cast<const IdT*>(a.topk_ids), r);
         rk[j] = rank_ws[r];
     }
     MapStage<NT, kMap> ms;
     ms.load(a);
-    const TileCopy<U, kNTStore, kMap> tc(a, t0, ntok);
+    const TileCopy<U, kNTStore, kMap, IdT> tc(a, t0, ntok);
     u32x4 cur[U];
     tc.prefetch(wave_index(), cur);
 
@@ -932,7 +943,7 @@ __global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int 
         if ((uint32_t)dest < (uint64_t)R) a.permuted_idx[dest] = (int32_t)(row0 + i);
     }
     lds_barrier();
-    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore, kMap>(tc, cur, dest_s);
+    if (a.row_vecs > 0) copy_items_pipelined<U, NT, kNTStore, kMap, IdT>(tc, cur, dest_s);
     copy_tile_scales<NT>(a, t0, ntok, dest_s);
 }
 
@@ -1144,69 +1155,85 @@ static bool plain_row_stores(const PermuteArgs& a) {
 
 static int map_entries(const PermuteArgs& a) { return a.expert_map != nullptr ? a.num_experts : 0; }
 
-template <int U, bool kMap>
-static void launch_fused_um(const PermuteArgs& a, const PermutePlan& p, hipStream_t stream) {
+// The map and the id type are compile-time parameters of every permute
+// kernel, so the plain int32 permute carries none of their code.  f receives
+// std::integral_constant<bool, map> and a null `const IdT*` naming the id type.
+template <class F>
+static void with_variant(const PermuteArgs& a, F&& f) {
+    if (a.expert_map != nullptr) {
+        if (a.ids64) f(std::true_type{}, static_cast<const int64_t*>(nullptr));
+        else f(std::true_type{}, static_cast<const int32_t*>(nullptr));
+    } else {
+        if (a.ids64) f(std::false_type{}, static_cast<const int64_t*>(nullptr));
+        else f(std::false_type{}, static_cast<const int32_t*>(nullptr));
+    }
+}
+
+template <int U, bool kMap, typename IdT>
+static void launch_fused_v(const PermuteArgs& a, const PermutePlan& p, hipStream_t stream) {
     const size_t lds = fused_lds_bytes(a.num_buckets, p.tile_rows, map_entries(a));
     if (plain_row_stores(a))
-        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, false, kMap>), dim3((unsigned)p.num_tiles),
+        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, false, kMap, IdT>), dim3((unsigned)p.num_tiles),
                            dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile, p.nbits);
     else
-        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, true, kMap>), dim3((unsigned)p.num_tiles),
+        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, true, kMap, IdT>), dim3((unsigned)p.num_tiles),
                            dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile, p.nbits);
 }
 
-template <int U, bool kMap>
-static void launch_coarse_um(const PermuteArgs& a, const PermutePlan& p, const int32_t* hist, hipStream_t stream) {
+template <int U, bool kMap, typename IdT>
+static void launch_coarse_v(const PermuteArgs& a, const PermutePlan& p, const int32_t* hist, hipStream_t stream) {
     const size_t lds = coarse_scatter_lds_bytes(a.num_buckets, p.tile_rows, p.num_coarse, map_entries(a));
     if (plain_row_stores(a))
-        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, false, kMap>),
+        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, false, kMap, IdT>),
                            dim3((unsigned)p.num_tiles), dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile,
                            p.nbits, p.coarse_rows, p.num_coarse, hist);
     else
-        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, true, kMap>),
+        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, true, kMap, IdT>),
                            dim3((unsigned)p.num_tiles), dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile,
                            p.nbits, p.coarse_rows, p.num_coarse, hist);
 }
 
-template <int U, bool kMap>
-static void launch_scatter_um(const PermuteArgs& a, const PermutePlan& p, const int32_t* rank_ws,
-                              const int32_t* tile_base, const int32_t* total, hipStream_t stream) {
+template <int U, bool kMap, typename IdT>
+static void launch_scatter_v(const PermuteArgs& a, const PermutePlan& p, const int32_t* rank_ws,
+                             const int32_t* tile_base, const int32_t* total, hipStream_t stream) {
     const size_t lds = scatter_lds_bytes(a.num_buckets, p.tile_rows, map_entries(a));
     if (plain_row_stores(a))
-        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, false, kMap>), dim3((unsigned)p.num_tiles),
+        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, false, kMap, IdT>), dim3((unsigned)p.num_tiles),
                            dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
                            total);
     else
-        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, true, kMap>), dim3((unsigned)p.num_tiles),
+        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, true, kMap, IdT>), dim3((unsigned)p.num_tiles),
                            dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
                            total);
 }
 
-// The map is a compile-time parameter of the row-moving kernels, so the
-// plain permute carries none of its code.
+#define MOE_VARIANT_TYPES                                 \
+    constexpr bool kMap = decltype(map_tag)::value;       \
+    using IdT = std::remove_const_t<std::remove_pointer_t<decltype(id_tag)>>
+
 template <int U>
 static void launch_fused_u(const PermuteArgs& a, const PermutePlan& p, hipStream_t stream) {
-    if (a.expert_map != nullptr)
-        launch_fused_um<U, true>(a, p, stream);
-    else
-        launch_fused_um<U, false>(a, p, stream);
+    with_variant(a, [&](auto map_tag, auto id_tag) {
+        MOE_VARIANT_TYPES;
+        launch_fused_v<U, kMap, IdT>(a, p, stream);
+    });
 }
 
 template <int U>
 static void launch_coarse_u(const PermuteArgs& a, const PermutePlan& p, const int32_t* hist, hipStream_t stream) {
-    if (a.expert_map != nullptr)
-        launch_coarse_um<U, true>(a, p, hist, stream);
-    else
-        launch_coarse_um<U, false>(a, p, hist, stream);
+    with_variant(a, [&](auto map_tag, auto id_tag) {
+        MOE_VARIANT_TYPES;
+        launch_coarse_v<U, kMap, IdT>(a, p, hist, stream);
+    });
 }
 
 template <int U>
 static void launch_scatter_u(const PermuteArgs& a, const PermutePlan& p, const int32_t* rank_ws,
                              const int32_t* tile_base, const int32_t* total, hipStream_t stream) {
-    if (a.expert_map != nullptr)
-        launch_scatter_um<U, true>(a, p, rank_ws, tile_base, total, stream);
-    else
-        launch_scatter_um<U, false>(a, p, rank_ws, tile_base, total, stream);
+    with_variant(a, [&](auto map_tag, auto id_tag) {
+        MOE_VARIANT_TYPES;
+        launch_scatter_v<U, kMap, IdT>(a, p, rank_ws, tile_base, total, stream);
+    });
 }
 
 #define MOE_DISPATCH_U(u, CALL) \
@@ -1235,14 +1262,13 @@ hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* work
     char* ws = static_cast<char*>(workspace);
     if (p.coarse) {
         int32_t* hist = reinterpret_cast<int32_t*>(ws);
-        if (a.expert_map != nullptr)
-            hipLaunchKernelGGL((permute_coarse_hist_kernel<kCoarseThreads, true>), dim3((unsigned)p.num_coarse),
-                               dim3(kCoarseThreads), coarse_hist_lds_bytes(B, M), stream, a.topk_ids, a.expert_map,
-                               (int)p.rows, a.num_experts, B, p.coarse_rows, hist);
-        else
-            hipLaunchKernelGGL((permute_coarse_hist_kernel<kCoarseThreads, false>), dim3((unsigned)p.num_coarse),
-                               dim3(kCoarseThreads), coarse_hist_lds_bytes(B, M), stream, a.topk_ids, a.expert_map,
-                               (int)p.rows, a.num_experts, B, p.coarse_rows, hist);
+        with_variant(a, [&](auto map_tag, auto id_tag) {
+            MOE_VARIANT_TYPES;
+            hipLaunchKernelGGL((permute_coarse_hist_kernel<kCoarseThreads, kMap, IdT>), dim3((unsigned)p.num_coarse),
+                               dim3(kCoarseThreads), coarse_hist_lds_bytes(B, M), stream,
+                               static_cast<const IdT*>(a.topk_ids), a.expert_map, (int)p.rows, a.num_experts, B,
+                               p.coarse_rows, hist);
+        });
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
 #define MOE_COARSE(U) launch_coarse_u<U>(a, p, hist, stream)
@@ -1253,14 +1279,12 @@ hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* work
     int32_t* rank_ws = reinterpret_cast<int32_t*>(ws + p.ws_rank);
     int32_t* tile_hist = reinterpret_cast<int32_t*>(ws + p.ws_tile_hist);
     int32_t* total = reinterpret_cast<int32_t*>(ws + p.ws_total);
-    if (a.expert_map != nullptr)
-        hipLaunchKernelGGL((permute_rank_tiles_kernel<kRankThreads, true>), dim3((unsigned)p.num_tiles),
+    with_variant(a, [&](auto map_tag, auto id_tag) {
+        MOE_VARIANT_TYPES;
+        hipLaunchKernelGGL((permute_rank_tiles_kernel<kRankThreads, kMap, IdT>), dim3((unsigned)p.num_tiles),
                            dim3(kRankThreads), rank_lds_bytes(B, p.tile_rows, M), stream, a, p.tokens_per_tile,
                            p.nbits, p.num_tiles, rank_ws, tile_hist);
-    else
-        hipLaunchKernelGGL((permute_rank_tiles_kernel<kRankThreads, false>), dim3((unsigned)p.num_tiles),
-                           dim3(kRankThreads), rank_lds_bytes(B, p.tile_rows, M), stream, a, p.tokens_per_tile,
-                           p.nbits, p.num_tiles, rank_ws, tile_hist);
+    });
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((permute_scan_tiles_kernel<kScanThreads, kScanPerThread>), dim3((unsigned)(B + 1)),

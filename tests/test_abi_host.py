@@ -20,6 +20,7 @@ HEADER = os.path.join(ROOT, "include", "moe_permute.h")
 
 OK, INVALID, TOO_SMALL, MISALIGNED, UNSUPPORTED = 0, 1, 2, 3, 4
 BF16, F32, FP8 = binding.MOE_DTYPE_BF16, binding.MOE_DTYPE_F32, binding.MOE_DTYPE_FP8_E4M3
+I32, I64 = binding.MOE_DTYPE_INT32, binding.MOE_DTYPE_INT64
 
 
 def declared_functions():
@@ -110,10 +111,12 @@ def addr(i, extra=0):
 
 
 def permute_call(lib, **kw):
-    args = dict(hidden=addr(0), dtype=BF16, scale=None, ids=addr(1), n=4096, h=4096, k=2, e=8, out=addr(2),
-                pscale=None, off=addr(3), perm=addr(4), inv=addr(5), ws=addr(6), ws_bytes=1 << 30, stream=None)
+    args = dict(hidden=addr(0), dtype=BF16, scale=None, ids=addr(1), ids_dtype=I32, n=4096, h=4096, k=2, e=8,
+                out=addr(2), pscale=None, off=addr(3), perm=addr(4), inv=addr(5), ws=addr(6), ws_bytes=1 << 30,
+                stream=None)
     args.update(kw)
-    return lib.moe_permute(args["hidden"], args["dtype"], args["scale"], args["ids"], args["n"], args["h"],
+    return lib.moe_permute(args["hidden"], args["dtype"], args["scale"], args["ids"], args["ids_dtype"], args["n"],
+                           args["h"],
                            args["k"], args["e"], args["out"], args["pscale"], args["off"], args["perm"], args["inv"],
                            args["ws"], args["ws_bytes"], args["stream"])
 
@@ -150,6 +153,11 @@ def permute_call(lib, **kw):
     (dict(n=20000, k=8, e=256, ws_bytes=0), TOO_SMALL),    # staged schedule needs a workspace
     (dict(n=20000, k=8, e=256, ws=None), INVALID),
     (dict(n=20000, k=8, e=256, ws=addr(6, 8)), MISALIGNED),
+    (dict(ids_dtype=BF16), INVALID),                       # ids must be int32 or int64
+    (dict(ids_dtype=7), INVALID),
+    (dict(ids_dtype=I64, ids=addr(1, 4)), MISALIGNED),     # int64 ids: 8-byte alignment
+    (dict(dtype=I32), INVALID),                            # an id type is not a hidden type
+    (dict(ids_dtype=I64, inv=addr(1, 1 << 15)), INVALID),  # output inside the (longer) int64 id buffer
 ])
 def test_permute_rejects(lib, kw, status):
     assert permute_call(lib, **kw) == status
@@ -176,11 +184,12 @@ def test_local_workspace_size_pure_and_monotone(lib):
 
 
 def local_call(lib, **kw):
-    args = dict(hidden=addr(0), dtype=BF16, scale=None, ids=addr(1), n=4096, h=4096, k=2, e=8, emap=addr(8), nl=4,
-                out=addr(2), pscale=None, off=addr(3), perm=addr(4), inv=addr(5), ws=addr(6), ws_bytes=1 << 30,
-                stream=None)
+    args = dict(hidden=addr(0), dtype=BF16, scale=None, ids=addr(1), ids_dtype=I32, n=4096, h=4096, k=2, e=8,
+                emap=addr(8), nl=4, out=addr(2), pscale=None, off=addr(3), perm=addr(4), inv=addr(5), ws=addr(6),
+                ws_bytes=1 << 30, stream=None)
     args.update(kw)
-    return lib.moe_permute_local(args["hidden"], args["dtype"], args["scale"], args["ids"], args["n"], args["h"],
+    return lib.moe_permute_local(args["hidden"], args["dtype"], args["scale"], args["ids"], args["ids_dtype"],
+                                 args["n"], args["h"],
                                  args["k"], args["e"], args["emap"], args["nl"], args["out"], args["pscale"],
                                  args["off"], args["perm"], args["inv"], args["ws"], args["ws_bytes"], args["stream"])
 
@@ -195,6 +204,8 @@ def local_call(lib, **kw):
     (dict(k=9), INVALID),
     (dict(dtype=5), INVALID),
     (dict(n=20000, k=8, e=256, nl=32, ws_bytes=0), TOO_SMALL),
+    (dict(ids_dtype=FP8), INVALID),
+    (dict(ids_dtype=I64, ids=addr(1, 4)), MISALIGNED),
 ])
 def test_permute_local_rejects(lib, kw, status):
     assert local_call(lib, **kw) == status

@@ -17,8 +17,8 @@ import torch
 
 import oracle
 import workloads as W
-from _parity import (POISON, assert_permute_equal, assert_unpermute_close, gpu_permute, gpu_unpermute,
-                     oracle_permute, poisoned, to_np)
+from _parity import (POISON, assert_permute_equal, assert_permute_local_equal, assert_unpermute_close, gpu_permute,
+                     gpu_permute_local, gpu_unpermute, oracle_permute, oracle_permute_local, poisoned, to_np)
 from mixture_experts_token_amd import binding
 
 pytestmark = pytest.mark.gpu
@@ -390,3 +390,56 @@ def test_graph_replay_matches_eager(hip_device, name, n):
             if v is not None:
                 assert np.array_equal(to_np(v).view(np.uint8), ref_bytes[k]), (rep, k)
         assert np.array_equal(to_np(out).view(np.uint8), ref_out), rep
+
+
+# ----------------------------------------------------------------------------
+# int64 expert ids, read directly (no cast pass).
+# ----------------------------------------------------------------------------
+I64_CASES = [("tiny", None), ("mixtral", None), ("qwen3", None), ("dsv3", 3000), ("decode", 256)]
+
+
+@pytest.mark.parametrize("name,n", I64_CASES, ids=["%s-%s" % c for c in I64_CASES])
+def test_int64_ids_match_oracle_and_int32_path(hip_device, name, n):
+    w, inp = _inputs(name, hip_device, n=n)
+    ids64 = inp["topk_ids"].to(torch.int64)
+    _say("int64 ids %s N=%d" % (name, w.num_tokens))
+    o64 = gpu_permute(inp["hidden_states"], ids64, w.num_experts, token_scale=inp["token_scale"])
+    o32 = gpu_permute(inp["hidden_states"], inp["topk_ids"], w.num_experts, token_scale=inp["token_scale"])
+    torch.cuda.synchronize()
+    ref = oracle_permute(inp["hidden_states"], ids64, w.num_experts, inp["token_scale"])
+    assert_permute_equal(o64, ref)
+    for key, v in o64.items():
+        if v is not None:
+            assert torch.equal(v.view(torch.uint8), o32[key].view(torch.uint8)), key
+
+
+@pytest.mark.parametrize("n,k,e", [(3000, 2, 16), (30000, 8, 256), (140000, 2, 16)])
+def test_int64_ids_all_schedules_and_local(hip_device, n, k, e):
+    rng = np.random.default_rng(n + k)
+    ids64 = torch.from_numpy(rng.integers(0, e, size=(n, k)).astype(np.int64)).to(hip_device)
+    x = torch.randn((n, 64), device=hip_device).to(torch.bfloat16)
+    _say("int64 ids N=%d topk=%d E=%d" % (n, k, e))
+    outs = gpu_permute(x, ids64, e)
+    emap, nl = W.expert_map_for(e, 4, 1, "shuffled")
+    louts = gpu_permute_local(x, ids64, e, emap, nl)
+    torch.cuda.synchronize()
+    assert_permute_equal(outs, oracle_permute(x, ids64, e))
+    assert_permute_local_equal(louts, oracle_permute_local(x, ids64, e, emap, nl))
+
+
+@pytest.mark.parametrize("bad", [2**32 + 3, -1, 2**31, -(2**32)])
+@pytest.mark.parametrize("n,k,e", [(50, 2, 8), (4000, 8, 64), (30000, 8, 256), (140000, 2, 16)])
+def test_int64_ids_outside_range_detected_not_truncated(hip_device, n, k, e, bad):
+    """Values whose low 32 bits would be a valid id must still be rejected."""
+    rng = np.random.default_rng(7)
+    ids_np = rng.integers(0, e, size=(n, k)).astype(np.int64)
+    ids_np[n // 3, k - 1] = bad
+    ids64 = torch.from_numpy(ids_np).to(hip_device)
+    _say("int64 bad id %d N=%d E=%d" % (bad, n, e))
+    outs = gpu_permute(None, ids64, e)
+    emap, nl = W.expert_map_for(e, 2, 0)
+    louts = gpu_permute_local(None, ids64, e, emap, nl)
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == [-1] * (e + 1)
+    assert np.all(to_np(outs["inv_permuted_idx"]).view(np.uint32) == 0xFFFFFFFF)
+    assert to_np(louts["expert_first_token_offset"]).tolist() == [-1] * (nl + 1)
