@@ -541,7 +541,12 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
         const int r = (int)threadIdx.x + j * NT;
-        idv[j] = load_id(ids, r < R ? r : R - 1);
+        if constexpr (sizeof(IdT) == 8) {  // skip batches wholly past R: 8-byte ids cost twice the L2 reads
+            idv[j] = 0;
+            if (j * NT < R) idv[j] = load_id(ids, r < R ? r : R - 1);
+        } else {  // int32: unconditional loads measured faster, even when most are repeats
+            idv[j] = load_id(ids, r < R ? r : R - 1);
+        }
     }
     MapStage<NT, kMap> ms;
     ms.load(a);
