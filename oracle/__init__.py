@@ -92,6 +92,12 @@ def _load():
         lib.oracle_bf16_to_double.restype = ctypes.c_double
         lib.oracle_double_to_bf16.argtypes = [ctypes.c_double]
         lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_to_double.restype = ctypes.c_double
+        lib.oracle_double_to_e4m3.argtypes = [ctypes.c_double]
+        lib.oracle_double_to_e4m3.restype = ctypes.c_uint8
+        lib.oracle_quantize_fp8_rows.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p]
+        lib.oracle_quantize_fp8_rows.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -283,3 +289,43 @@ def bf16_to_double(bits: int) -> float:
 
 def double_to_bf16(x: float) -> int:
     return int(_load().oracle_double_to_bf16(float(x)))
+
+
+def e4m3_to_double(code: int) -> float:
+    return float(_load().oracle_e4m3_to_double(int(code) & 0xFF))
+
+
+def double_to_e4m3(x: float) -> int:
+    return int(_load().oracle_double_to_e4m3(float(x)))
+
+
+def quantize_fp8_rows(x: np.ndarray, dtype: str, group: int | None = None):
+    """(codes uint8 [rows, h], scales float32 [rows, h / group]) of the dynamic
+    fp8 quantiser; ``x`` is float32 ("f32") or bf16 bit patterns ("bf16");
+    group None means one scale per row."""
+    src = np.ascontiguousarray(x, dtype=np.float32 if dtype == "f32" else np.uint16)
+    rows, h = src.shape
+    g = h if group is None else int(group)
+    codes = np.zeros((rows, h), dtype=np.uint8)
+    scales = np.zeros((rows, h // g if g else 0), dtype=np.float32)
+    _check(_load().oracle_quantize_fp8_rows(_ptr(src), 1 if dtype == "bf16" else 0, rows, h, g, _ptr(codes),
+                                            _ptr(scales)))
+    return codes, scales
+
+
+def permute_quant_fp8(hidden: np.ndarray, dtype: str, topk_ids, num_experts: int, group: int | None = None,
+                      expert_map=None, num_local_experts: int | None = None) -> dict:
+    """Quantise every token row to fp8 (see quantize_fp8_rows), then permute the
+    codes and move each row's scales with it: the plain permute, or the
+    local-expert permute when ``expert_map`` is given.  ``permuted_scale`` is
+    [rows out, h / group].  Quantisation acts on each row alone, so quantising
+    before or after the permute gives the same rows."""
+    codes, scales = quantize_fp8_rows(hidden, dtype, group)
+    if expert_map is None:
+        res = permute(codes, topk_ids, num_experts)
+    else:
+        res = permute_local(codes, topk_ids, num_experts, expert_map, num_local_experts)
+    topk = np.asarray(topk_ids).shape[1]
+    sb, _ = gather_rows(as_row_bytes(scales), res["permuted_idx"], topk)
+    res["permuted_scale"] = sb.view(np.float32).reshape(res["permuted_idx"].shape[0], scales.shape[1])
+    return res

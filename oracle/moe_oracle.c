@@ -317,6 +317,97 @@ uint16_t oracle_double_to_bf16(double x)
 }
 
 /* ------------------------------------------------------------------------ */
+/* fp8 E4M3FN, written from the format (the OCP 8-bit floating-point E4M3     */
+/* encoding without infinities): a sign bit, 4 exponent bits with bias 7 and  */
+/* 3 fraction bits.  Exponent field 0 holds the subnormals frac * 2^-9; the   */
+/* all-ones pattern S.1111.111 is NaN, so the largest finite magnitude is     */
+/* 1.75 * 2^8 = 448 (S.1111.110).                                             */
+/* ------------------------------------------------------------------------ */
+double oracle_e4m3_to_double(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int expo = (code >> 3) & 0xF;
+    int frac = code & 0x7;
+    double mag;
+    if (expo == 0xF && frac == 0x7)
+        mag = NAN;
+    else if (expo == 0)
+        mag = ldexp((double)frac, -9);
+    else
+        mag = ldexp(8.0 + (double)frac, expo - 7 - 3);
+    return sign ? -mag : mag;
+}
+
+/* Nearest E4M3FN value, ties to the even fraction, after clamping the input  */
+/* to [-448, 448] (saturation, as quantisers do).  NaN maps to S.1111.111.    */
+uint8_t oracle_double_to_e4m3(double x)
+{
+    uint8_t sign = signbit(x) ? 0x80u : 0u;
+    if (isnan(x))
+        return (uint8_t)(sign | 0x7Fu);
+    double a = fabs(x);
+    if (a > 448.0)
+        a = 448.0;
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);              /* a lies in [2^(e2-1), 2^e2) */
+    int p = e2 - 1;             /* binade exponent */
+    if (p < -6)
+        p = -6;                 /* below the normal range the spacing stays 2^-9 */
+    double quantum = ldexp(1.0, p - 3);
+    double v = nearbyint(a / quantum) * quantum; /* a / quantum is exact; nearest-even */
+    if (v < ldexp(1.0, -6))     /* subnormal (a value rounded up to 2^-6 is handled below) */
+        return (uint8_t)(sign | (uint8_t)(v / ldexp(1.0, -9)));
+    frexp(v, &e2);
+    int expo = e2 - 1 + 7;
+    int frac = (int)(v / ldexp(1.0, e2 - 1 - 3)) - 8;
+    return (uint8_t)(sign | (uint8_t)(expo << 3) | (uint8_t)frac);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic fp8 quantisation of activation rows.                              */
+/* [P2] vLLM PR #19636 "[Kernels] MoE refactor", highlights: activations are  */
+/* quantised per token (per-token activation quantisation parameters), and   */
+/* the quantisation configuration carries a block shape.  Reading taken: the  */
+/* row is cut into groups of `group` consecutive elements (group = h: one     */
+/* scale per token); per group                                                */
+/*   amax  = the largest |x| (exact),                                         */
+/*   scale = amax / 448 as one float division (1 when amax is 0),             */
+/*   code  = E4M3FN of the float quotient x / scale (one float division,      */
+/*           then the rounding above).                                        */
+/* x is float32 (x_is_bf16 = 0) or bfloat16 bit patterns (x_is_bf16 = 1).     */
+/* scales is [rows][h / group].                                               */
+/* ------------------------------------------------------------------------ */
+int oracle_quantize_fp8_rows(const void *x, int x_is_bf16, int64_t rows, int64_t h, int64_t group,
+                             uint8_t *codes, float *scales)
+{
+    if (rows < 0 || h < 1 || group < 1 || h % group != 0)
+        return ORACLE_BAD_ARG;
+    int64_t groups = h / group;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t g = 0; g < groups; ++g) {
+            float amax = 0.0f;
+            for (int64_t i = g * group; i < (g + 1) * group; ++i) {
+                float v = x_is_bf16 ? (float)oracle_bf16_to_double(((const uint16_t *)x)[r * h + i])
+                                    : ((const float *)x)[r * h + i];
+                if (fabsf(v) > amax)
+                    amax = fabsf(v);
+            }
+            float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+            scales[r * groups + g] = scale;
+            for (int64_t i = g * group; i < (g + 1) * group; ++i) {
+                float v = x_is_bf16 ? (float)oracle_bf16_to_double(((const uint16_t *)x)[r * h + i])
+                                    : ((const float *)x)[r * h + i];
+                float q = v / scale;
+                codes[r * h + i] = oracle_double_to_e4m3((double)q);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Unpermute.                                                                 */
 /* [P1] PR description: reduce the expanded grouped-GEMM output back per      */
 /* token and scale each contribution by its topk_weight:                      */

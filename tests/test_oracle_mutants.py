@@ -45,6 +45,25 @@ MUTANTS = {
         "for (int32_t k = 0; k < topk - 1; ++k) {\n                int64_t r = t * topk + k;\n"
         "                int64_t j = inv_permuted_idx[r];\n                if (j < 0)\n                    continue;\n"
         "                acc += (double)topk_weights[r] * (double)"),
+    # fp8 E4M3FN and the quantiser
+    "e4m3_ties_away": (
+        "double v = nearbyint(a / quantum) * quantum;",
+        "double v = round(a / quantum) * quantum;"),
+    "e4m3_no_saturation": (
+        "if (a > 448.0)\n        a = 448.0;",
+        "if (a > 1e30)\n        a = 448.0;"),
+    "e4m3_wrong_bias": (
+        "mag = ldexp(8.0 + (double)frac, expo - 7 - 3);",
+        "mag = ldexp(8.0 + (double)frac, expo - 8 - 3);"),
+    "quant_wrong_fp8_max": (
+        "amax > 0.0f ? amax / 448.0f : 1.0f;",
+        "amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    "quant_amax_over_whole_row": (
+        "for (int64_t i = g * group; i < (g + 1) * group; ++i) {\n                float v = x_is_bf16",
+        "for (int64_t i = 0; i < h; ++i) {\n                float v = x_is_bf16"),
+    "quant_multiplies_by_scale": (
+        "float q = v / scale;",
+        "float q = v * scale;"),
     # int64 ids
     "int64_ids_truncated": (
         "if (ids64[i] < 0 || ids64[i] >= (int64_t)num_experts)",

@@ -544,3 +544,163 @@ def test_int64_ids_outside_range_rejected_not_truncated(bad):
         oracle.permute(np.zeros((2, 4), np.float32), ids, 8)
     with pytest.raises(oracle.OracleError):
         oracle.permute_local(np.zeros((2, 4), np.float32), ids, 8, list(range(8)), 8)
+
+
+# --------------------------------------------------------------------------
+# fp8 E4M3FN and the dynamic fp8 quantiser (quantise while permuting).
+# --------------------------------------------------------------------------
+def _e4m3_finite_table():
+    """(value, code) for every finite E4M3FN code, decoded by torch."""
+    import torch
+
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    vals = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return [(float(vals[c]), c) for c in range(256) if not np.isnan(vals[c])]
+
+
+def test_e4m3_decode_all_codes_against_torch():
+    import torch
+
+    vals = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        got = oracle.e4m3_to_double(c)
+        if np.isnan(vals[c]):
+            assert np.isnan(got), c
+        else:
+            assert got == vals[c], (c, got, vals[c])
+    assert oracle.e4m3_to_double(0x7E) == 448.0 and np.isnan(oracle.e4m3_to_double(0x7F))
+
+
+def brute_nearest_e4m3(x: float) -> int:
+    """Exhaustive search over the finite codes of the clamped value; ties go to the
+    code with an even fraction; zero keeps the sign of x."""
+    if np.isnan(x):
+        return 0xFF if np.signbit(x) else 0x7F
+    a = min(abs(x), 448.0)
+    best = None
+    for v, c in _E4M3:
+        if v < 0 or (v == 0 and c != 0):
+            continue
+        d = abs(Fraction(v) - Fraction(a))
+        if best is None or d < best[0] or (d == best[0] and (c & 1) == 0):
+            best = (d, c)
+    code = best[1]
+    return code | 0x80 if np.signbit(x) else code
+
+
+_E4M3 = None
+
+
+def test_e4m3_encode_against_exhaustive_nearest():
+    global _E4M3
+    _E4M3 = _e4m3_finite_table()
+    pos = sorted(v for v, c in _E4M3 if v >= 0 and not (v == 0 and c != 0))
+    probes = [0.0, -0.0, 448.0, 449.0, 464.0, 465.0, 1e9, -1e9, 2.0**-12, 2.0**-10, 2.0**-9, 2.0**-6 - 2.0**-10]
+    for lo, hi in zip(pos, pos[1:]):
+        mid = (lo + hi) / 2
+        probes += [lo, mid, np.nextafter(mid, 0.0), np.nextafter(mid, 1e9), -mid]
+    rng = np.random.default_rng(13)
+    probes += list(rng.uniform(-460, 460, 3000)) + list(rng.uniform(-2.0**-5, 2.0**-5, 1000))
+    for x in probes:
+        assert oracle.double_to_e4m3(float(x)) == brute_nearest_e4m3(float(x)), x
+    assert oracle.double_to_e4m3(float("nan")) == 0x7F
+
+
+def test_e4m3_encode_against_torch_in_range():
+    import torch
+
+    rng = np.random.default_rng(14)
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.uniform(-1, 1, 20000),
+                        rng.uniform(-2.0**-6, 2.0**-6, 5000)]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.double_to_e4m3(float(v)) for v in x], dtype=np.uint8)
+    np.testing.assert_array_equal(got, want)
+
+
+def _rows(rng, n, h, dtype):
+    x = (rng.standard_normal((n, h)) * rng.choice([1e-3, 1.0, 50.0], size=(n, 1))).astype(np.float32)
+    return _bf16_bits_from_f32(x) if dtype == "bf16" else x
+
+
+def _as_f32(x, dtype):
+    return _f32_from_bf16_bits(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("group", [None, 8, 32, 128])
+def test_quantizer_properties(dtype, group):
+    rng = np.random.default_rng(15)
+    n, h = 40, 256
+    x = _rows(rng, n, h, dtype)
+    xf = _as_f32(x, dtype).astype(np.float64)
+    codes, scales = oracle.quantize_fp8_rows(x, dtype, group)
+    g = h if group is None else group
+    assert scales.shape == (n, h // g)
+    dq = np.vectorize(oracle.e4m3_to_double)(codes)
+    for r in range(n):
+        for q in range(h // g):
+            seg = slice(q * g, (q + 1) * g)
+            amax = np.max(np.abs(xf[r, seg]))
+            s = float(scales[r, q])
+            # scale is amax / 448 to float precision
+            assert abs(s - amax / 448.0) <= 2.0**-24 * amax / 448.0
+            # the element of largest magnitude lands on +-448
+            i = q * g + int(np.argmax(np.abs(xf[r, seg])))
+            assert codes[r, i] & 0x7F == 0x7E
+            # every element is within half an fp8 step (relative 2^-4) plus one float rounding
+            y = xf[r, seg] / s
+            err = np.abs(dq[r, seg] - y)
+            step = np.maximum(np.abs(y), 2.0**-6) * 2.0**-3
+            assert np.all(err <= step / 2 * (1 + 2.0**-20) + 1e-30)
+            # signs are kept
+            nz = xf[r, seg] != 0
+            assert np.all((codes[r, seg][nz] >= 0x80) == (xf[r, seg][nz] < 0) | (codes[r, seg][nz] == 0x80) |
+                          (codes[r, seg][nz] == 0))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantizer_special_cases(dtype):
+    h = 64
+    x = np.zeros((3, h), np.float32)
+    x[1, 5] = -3.0
+    x[2] = np.linspace(-1, 1, h, dtype=np.float32)
+    if dtype == "bf16":
+        x = _bf16_bits_from_f32(x)
+    codes, scales = oracle.quantize_fp8_rows(x, dtype)
+    assert scales[0, 0] == 1.0 and np.all(codes[0] == 0)          # all-zero row
+    assert scales[1, 0] == np.float32(3.0) / np.float32(448.0)
+    assert codes[1, 5] == 0xFE and np.all(np.delete(codes[1], 5) == 0)
+    # sign symmetry (every code's sign bit flips, zeros to -0) and power-of-two scaling
+    xf = _as_f32(x, dtype)
+    neg, dbl = -xf, xf * 2
+    if dtype == "bf16":
+        neg, dbl = _bf16_bits_from_f32(neg), _bf16_bits_from_f32(dbl)
+    c_neg, s_neg = oracle.quantize_fp8_rows(neg, dtype)
+    np.testing.assert_array_equal(c_neg, codes ^ 0x80)
+    np.testing.assert_array_equal(s_neg, scales)
+    c_dbl, s_dbl = oracle.quantize_fp8_rows(dbl, dtype)
+    np.testing.assert_array_equal(c_dbl, codes)
+    np.testing.assert_array_equal(s_dbl[1:], scales[1:] * 2)
+    assert s_dbl[0, 0] == 1.0
+
+
+def test_quantizer_group_is_not_the_whole_row():
+    # two groups with very different magnitudes get different scales
+    x = np.concatenate([np.full((1, 8), 1000.0), np.full((1, 8), 0.001)], axis=1).astype(np.float32)
+    codes, scales = oracle.quantize_fp8_rows(x, "f32", 8)
+    assert scales.shape == (1, 2) and scales[0, 0] > 1.0 and scales[0, 1] < 1e-5
+    assert np.all(codes == 0x7E)
+
+
+@pytest.mark.parametrize("local", [False, True])
+def test_permute_quant_moves_scales_with_rows(local):
+    rng = np.random.default_rng(16)
+    n, k, e, h = 33, 3, 8, 64
+    ids = np.stack([rng.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    x = _bf16_bits_from_f32(rng.standard_normal((n, h)).astype(np.float32))
+    emap, nl = (W.expert_map_for(e, 2, 1, "shuffled") if local else (None, None))
+    res = oracle.permute_quant_fp8(x, "bf16", ids, e, 16, emap, nl)
+    codes, scales = oracle.quantize_fp8_rows(x, "bf16", 16)
+    perm = res["permuted_idx"]
+    np.testing.assert_array_equal(res["permuted_hidden_states"], codes[perm // k])
+    np.testing.assert_array_equal(res["permuted_scale"], scales[perm // k])
