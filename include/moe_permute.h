@@ -185,6 +185,48 @@ moe_status_t moe_permute_local(const void *hidden_states, int32_t dtype, const f
                                size_t workspace_bytes, void *stream);
 
 /*
+ * moe_permute_quant_fp8 -- quantise while permuting: the permute (or, with an
+ * expert map, the local-expert permute) of bf16 or f32 token rows whose
+ * moved rows are fp8 E4M3FN codes with their scales, quantised on the way
+ * (vLLM PR #19636 "[Kernels] MoE refactor", highlights: per-token activation
+ * quantisation and block shapes; the permute per vLLM PR #14568).
+ *
+ * Per group of group_size consecutive elements of a token row (group_size 0:
+ * the whole row, one scale per token):
+ *     scale = amax / 448 as one float division (1 when amax is 0; NaN
+ *             elements do not count towards amax)
+ *     code  = E4M3FN(x / scale): the float quotient rounded to the nearest
+ *             code, ties to even, saturated at +-448; a NaN quotient -> 0x7F
+ *
+ *   hidden_states     [N, hidden_size] of dtype MOE_DTYPE_BF16 or MOE_DTYPE_F32;
+ *                     rows of at most 16 KiB (8192 bf16 / 4096 f32 elements)
+ *   topk_ids .. num_experts   as for moe_permute
+ *   expert_map, num_local_experts   NULL and 0 for the plain permute, else as
+ *                     for moe_permute_local
+ *   group_size        0, or a power of two dividing hidden_size, at least 8
+ *                     (bf16) / 4 (f32) elements and at most 64 times that
+ *   permuted_codes    [N*topk, hidden_size] bytes (out), 16-byte aligned
+ *   permuted_scale    [N*topk, hidden_size / group_size] float (out; one
+ *                     column for group_size 0)
+ *   expert_first_token_offset, permuted_idx, inv_permuted_idx   as for
+ *                     moe_permute / moe_permute_local
+ *   workspace         sized by moe_permute_workspace_size, or by
+ *                     moe_permute_local_workspace_size with a map
+ *
+ * Codes and scales of a row are written to every destination of its token
+ * (only the first M rows with a map).  A bad id or map entry: offsets -1,
+ * nothing else written.
+ */
+moe_status_t moe_permute_quant_fp8(const void *hidden_states, int32_t dtype, const void *topk_ids,
+                                   int32_t topk_ids_dtype, int64_t num_tokens, int64_t hidden_size,
+                                   int32_t topk, int32_t num_experts, const int32_t *expert_map,
+                                   int32_t num_local_experts, int64_t group_size,
+                                   uint8_t *permuted_codes, float *permuted_scale,
+                                   int64_t *expert_first_token_offset, int32_t *permuted_idx,
+                                   int32_t *inv_permuted_idx, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/*
  * moe_unpermute -- weighted top-k reduction of the expanded grouped-GEMM
  * output back to one row per token (vLLM PR #14568, PR description):
  *     output[t] = sum_{k=0}^{topk-1} topk_weights[t][k] * expanded_output[inv_permuted_idx[t*topk+k]]

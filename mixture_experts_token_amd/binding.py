@@ -7,7 +7,8 @@ is missing the first call raises.
 
 The entry points carry the C names: ``moe_permute_supported``,
 ``moe_permute_workspace_size``, ``moe_permute``, ``moe_unpermute``,
-``moe_permute_local_workspace_size``, ``moe_permute_local``.
+``moe_permute_local_workspace_size``, ``moe_permute_local``,
+``moe_permute_quant_fp8``.
 ``MoEPermuteScratch`` follows the preallocated-buffer design of the prhub
 summary of vLLM PR #43014 (section "key code snippets", MoEPermuteScratch):
 every buffer is allocated once for ``max_num_tokens`` and reused by each call.
@@ -64,6 +65,9 @@ def load_library() -> ctypes.CDLL:
         lib.moe_permute_local_workspace_size.restype = sz
         lib.moe_permute_local.argtypes = [p, i32, p, p, i32, i64, i64, i32, i32, p, i32, p, p, p, p, p, p, sz, p]
         lib.moe_permute_local.restype = ctypes.c_int
+        lib.moe_permute_quant_fp8.argtypes = [p, i32, p, i32, i64, i64, i32, i32, p, i32, i64, p, p, p, p, p, p,
+                                              sz, p]
+        lib.moe_permute_quant_fp8.restype = ctypes.c_int
         lib.moe_unpermute.argtypes = [p, i32, p, p, i64, i64, i32, p, p]
         lib.moe_unpermute.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -181,6 +185,33 @@ def moe_permute_local(hidden_states, topk_ids, num_experts: int, expert_map, num
         _ptr(workspace), ws_bytes, _stream(stream, topk_ids))
     if status != MOE_OK:
         raise MoEError(status, "moe_permute_local")
+
+
+def moe_permute_quant_fp8(hidden_states, topk_ids, num_experts: int, permuted_codes, permuted_scale,
+                          expert_first_token_offset, permuted_idx, inv_permuted_idx, workspace=None,
+                          group_size: int = 0, expert_map=None, num_local_experts: int = 0, stream=None) -> None:
+    """Quantise while permuting (see moe_permute_quant_fp8 in the C header).
+
+    ``hidden_states`` bfloat16 or float32 [N, H]; ``permuted_codes`` uint8 (or
+    float8_e4m3fn) [N*topk, H]; ``permuted_scale`` float32 [N*topk, H / group]
+    (one column for group_size 0); with ``expert_map`` the local-expert
+    permute over ``num_local_experts``.
+    """
+    import torch
+
+    if hidden_states.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("hidden_states must be bfloat16 or float32")
+    if expert_map is not None and (expert_map.dtype != torch.int32 or expert_map.shape != (int(num_experts),)):
+        raise TypeError("expert_map must be an int32 [num_experts] tensor")
+    _, code, hsize, ws_bytes, ids_code = _permute_args(hidden_states, topk_ids, workspace)
+    n, topk = topk_ids.shape
+    status = load_library().moe_permute_quant_fp8(
+        _ptr(hidden_states), code, _ptr(topk_ids), ids_code, n, hsize, topk, int(num_experts), _ptr(expert_map),
+        int(num_local_experts) if expert_map is not None else 0, int(group_size), _ptr(permuted_codes),
+        _ptr(permuted_scale), _ptr(expert_first_token_offset), _ptr(permuted_idx), _ptr(inv_permuted_idx),
+        _ptr(workspace), ws_bytes, _stream(stream, topk_ids))
+    if status != MOE_OK:
+        raise MoEError(status, "moe_permute_quant_fp8")
 
 
 def moe_unpermute(expanded_output, topk_weights, inv_permuted_idx, output, stream=None) -> None:

@@ -37,7 +37,20 @@ struct UnpermuteArgs {
     void* output;                   // [N, row_vecs * 16 bytes]
 };
 
+struct QuantArgs {
+    const void* hidden_states;      // [N, row_vecs * 16 bytes] bf16 or f32
+    const int32_t* inv_permuted_idx;  // [N*topk], -1 for rows with no destination
+    const int64_t* expert_first_token_offset;  // entry 0 is -1 when the index permute failed
+    int64_t num_tokens;
+    int64_t row_vecs;               // input row length in 16-byte vectors (<= kQuantMaxRowVecs)
+    int32_t topk;
+    int32_t group_vecs;             // 16-byte input vectors per scale group; 0: one scale per token
+    uint8_t* permuted_codes;        // [N*topk, H] E4M3FN
+    float* permuted_scale;          // [N*topk, groups]
+};
+
 hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t value, hipStream_t stream);
+hipError_t launch_quant_scatter(const QuantArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream);
 hipError_t launch_unpermute(const UnpermuteArgs& a, bool bf16, hipStream_t stream);
 

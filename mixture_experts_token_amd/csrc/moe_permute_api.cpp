@@ -211,6 +211,71 @@ moe_status_t moe_permute_local(const void* hidden_states, int32_t dtype, const f
                         stream);
 }
 
+moe_status_t moe_permute_quant_fp8(const void* hidden_states, int32_t dtype, const void* topk_ids,
+                                   int32_t topk_ids_dtype, int64_t num_tokens, int64_t hidden_size, int32_t topk,
+                                   int32_t num_experts, const int32_t* expert_map, int32_t num_local_experts,
+                                   int64_t group_size, uint8_t* permuted_codes, float* permuted_scale,
+                                   int64_t* expert_first_token_offset, int32_t* permuted_idx,
+                                   int32_t* inv_permuted_idx, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    // Quantiser checks first; permute_impl then checks the rest before it
+    // enqueues anything, so a rejected call has no side effect.
+    if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+    const int64_t eb = element_bytes(dtype);
+    const int64_t epv = 16 / eb;  // elements per 16-byte vector
+    if (hidden_size < 1 || hidden_size > (int64_t)moe::kQuantMaxRowVecs * epv) return MOE_ERR_INVALID_ARG;
+    if (hidden_size % epv != 0) return MOE_ERR_MISALIGNED;
+    if (expert_map == nullptr && num_local_experts != 0) return MOE_ERR_INVALID_ARG;
+    const int64_t g = group_size == 0 ? hidden_size : group_size;
+    if (group_size != 0) {
+        const bool pow2 = group_size > 0 && (group_size & (group_size - 1)) == 0;
+        if (!pow2 || group_size < epv || group_size > 64 * epv || hidden_size % group_size != 0)
+            return MOE_ERR_INVALID_ARG;
+    }
+    if (num_tokens > 0 && (permuted_codes == nullptr || permuted_scale == nullptr || hidden_states == nullptr))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(permuted_codes, 16) || !aligned(permuted_scale, 4) || !aligned(hidden_states, 16))
+        return MOE_ERR_MISALIGNED;
+    if (num_tokens >= 0 && topk >= 1 && num_tokens <= kMaxRows / topk) {
+        const uint64_t rows = (uint64_t)num_tokens * (uint64_t)topk;
+        const int32_t buckets = expert_map != nullptr ? num_local_experts : num_experts;
+        const uint64_t id_bytes = topk_ids_dtype == MOE_DTYPE_INT64 ? 8 : 4;
+        const Span outs[] = {
+            {permuted_codes, rows * (uint64_t)hidden_size},
+            {permuted_scale, rows * 4ull * (uint64_t)(hidden_size / g)},
+        };
+        const Span others[] = {
+            {hidden_states, (uint64_t)num_tokens * (uint64_t)(hidden_size * eb)},
+            {topk_ids, rows * id_bytes},
+            {expert_map, 4ull * (uint64_t)(expert_map != nullptr ? num_experts : 0)},
+            {expert_first_token_offset, 8ull * (uint64_t)(buckets > 0 ? buckets + 1 : 1)},
+            {permuted_idx, rows * 4},
+            {inv_permuted_idx, rows * 4},
+            {workspace, (uint64_t)workspace_bytes},
+        };
+        if (any_overlap(outs, 2, others, 7)) return MOE_ERR_INVALID_ARG;
+    }
+    // Index permute (no rows moved), then the quantise-scatter.
+    const moe_status_t st = permute_impl(nullptr, dtype, nullptr, topk_ids, topk_ids_dtype, num_tokens, 0, topk,
+                                         num_experts, expert_map, num_local_experts, nullptr, nullptr,
+                                         expert_first_token_offset, permuted_idx, inv_permuted_idx, workspace,
+                                         workspace_bytes, stream);
+    if (st != MOE_OK || num_tokens == 0) return st;
+    moe::QuantArgs q;
+    q.hidden_states = hidden_states;
+    q.inv_permuted_idx = inv_permuted_idx;
+    q.expert_first_token_offset = expert_first_token_offset;
+    q.num_tokens = num_tokens;
+    q.row_vecs = hidden_size * eb / 16;
+    q.topk = topk;
+    q.group_vecs = group_size == 0 ? 0 : (int32_t)(group_size / epv);
+    q.permuted_codes = permuted_codes;
+    q.permuted_scale = permuted_scale;
+    return moe::launch_quant_scatter(q, dtype == MOE_DTYPE_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+}
+
 moe_status_t moe_unpermute(const void* expanded_output, int32_t dtype, const float* topk_weights,
                            const int32_t* inv_permuted_idx, int64_t num_tokens, int64_t hidden_size, int32_t topk,
                            void* output, void* stream) {

@@ -42,6 +42,7 @@ constexpr int kStagedTileRows = 128;               // target expanded rows per s
 constexpr int kFusedTargetBlocks = 512;
 constexpr int kMaxTileRows = 1024;                 // LDS staging bound for one tile
 constexpr size_t kWorkspaceAlign = 256;
+constexpr int kQuantMaxRowVecs = 1024;             // quantise-scatter: a wave holds the whole row (16 KiB)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

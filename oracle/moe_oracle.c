@@ -375,7 +375,9 @@ uint8_t oracle_double_to_e4m3(double x)
 /*   amax  = the largest |x| (exact),                                         */
 /*   scale = amax / 448 as one float division (1 when amax is 0),             */
 /*   code  = E4M3FN of the float quotient x / scale (one float division,      */
-/*           then the rounding above).                                        */
+/*           then the rounding above); a NaN quotient (a NaN input, or inf /  */
+/*           inf) gets the positive NaN code 0x7F, whatever its sign bit.     */
+/* NaN never counts towards amax (no comparison with it holds).               */
 /* x is float32 (x_is_bf16 = 0) or bfloat16 bit patterns (x_is_bf16 = 1).     */
 /* scales is [rows][h / group].                                               */
 /* ------------------------------------------------------------------------ */
@@ -400,7 +402,7 @@ int oracle_quantize_fp8_rows(const void *x, int x_is_bf16, int64_t rows, int64_t
                 float v = x_is_bf16 ? (float)oracle_bf16_to_double(((const uint16_t *)x)[r * h + i])
                                     : ((const float *)x)[r * h + i];
                 float q = v / scale;
-                codes[r * h + i] = oracle_double_to_e4m3((double)q);
+                codes[r * h + i] = isnan(q) ? 0x7Fu : oracle_double_to_e4m3((double)q);
             }
         }
     }

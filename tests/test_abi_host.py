@@ -26,7 +26,7 @@ I32, I64 = binding.MOE_DTYPE_INT32, binding.MOE_DTYPE_INT64
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -48,14 +48,14 @@ host_only = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer checks run on
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["moe_permute", "moe_permute_local", "moe_permute_local_workspace_size",
-                                    "moe_permute_supported", "moe_permute_workspace_size", "moe_status_string",
-                                    "moe_unpermute"]
+                                    "moe_permute_quant_fp8", "moe_permute_supported", "moe_permute_workspace_size",
+                                    "moe_status_string", "moe_unpermute"]
 
 
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
-    exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
+    exported = set(re.findall(r"\bT (moe_[a-z0-9_]+)\b", out))
     for name in declared_functions():
         assert name in exported, name
         assert getattr(lib, name) is not None
@@ -216,6 +216,43 @@ def test_permute_local_workspace_boundary(lib):
     need = lib.moe_permute_local_workspace_size(20000, 8, 256, 32)
     assert need > 0
     assert local_call(lib, n=20000, k=8, e=256, nl=32, ws_bytes=need - 1) == TOO_SMALL
+
+
+def quant_call(lib, **kw):
+    args = dict(hidden=addr(0), dtype=BF16, ids=addr(1), ids_dtype=I32, n=4096, h=4096, k=2, e=8, emap=None, nl=0,
+                group=0, codes=addr(2), scales=addr(9), off=addr(3), perm=addr(4), inv=addr(5), ws=addr(6),
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.moe_permute_quant_fp8(args["hidden"], args["dtype"], args["ids"], args["ids_dtype"], args["n"],
+                                     args["h"], args["k"], args["e"], args["emap"], args["nl"], args["group"],
+                                     args["codes"], args["scales"], args["off"], args["perm"], args["inv"], args["ws"],
+                                     args["ws_bytes"], args["stream"])
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=FP8), UNSUPPORTED),      # input must be bf16 or f32
+    (dict(dtype=9), UNSUPPORTED),
+    (dict(h=8200), INVALID),             # bf16 rows above 16 KiB
+    (dict(dtype=F32, h=4100), INVALID),  # f32 rows above 16 KiB
+    (dict(h=4092), MISALIGNED),          # not whole 16-byte vectors
+    (dict(group=100), INVALID),          # not a power of two
+    (dict(group=4), INVALID),            # below one vector of bf16
+    (dict(group=1024), INVALID),         # above 64 vectors
+    (dict(group=8192), INVALID),         # does not divide h
+    (dict(nl=4), INVALID),               # local count without a map
+    (dict(codes=None), INVALID),
+    (dict(scales=None), INVALID),
+    (dict(codes=addr(2, 8)), MISALIGNED),
+    (dict(scales=addr(9, 2)), MISALIGNED),
+    (dict(codes=addr(0)), INVALID),      # codes alias the input
+    (dict(scales=addr(5)), INVALID),     # scales alias inv_permuted_idx
+    (dict(ids_dtype=BF16), INVALID),
+    (dict(k=9), INVALID),
+    (dict(n=20000, k=8, e=256, ws_bytes=0), TOO_SMALL),
+])
+def test_permute_quant_rejects(lib, kw, status):
+    assert quant_call(lib, **kw) == status
 
 
 def unpermute_call(lib, **kw):

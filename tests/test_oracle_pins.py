@@ -704,3 +704,14 @@ def test_permute_quant_moves_scales_with_rows(local):
     perm = res["permuted_idx"]
     np.testing.assert_array_equal(res["permuted_hidden_states"], codes[perm // k])
     np.testing.assert_array_equal(res["permuted_scale"], scales[perm // k])
+
+
+def test_quantizer_non_finite_inputs():
+    x = np.array([[1.0, np.nan, -2.0, 0.5], [np.inf, 1.0, -1.0, 0.0], [-np.inf, np.inf, 3.0, -0.0]], np.float32)
+    codes, scales = oracle.quantize_fp8_rows(x, "f32")
+    # NaN is ignored by amax and coded 0x7F; the rest quantise against amax 2
+    assert scales[0, 0] == np.float32(2.0) / np.float32(448.0)
+    assert codes[0, 1] == 0x7F and codes[0, 2] == 0xFE
+    # an infinite amax gives an infinite scale: finite values go to (signed) zero, inf / inf is NaN
+    assert np.isinf(scales[1, 0]) and codes[1].tolist() == [0x7F, 0x00, 0x80, 0x00]
+    assert codes[2].tolist() == [0x7F, 0x7F, 0x00, 0x80]

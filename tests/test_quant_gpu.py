@@ -1,0 +1,206 @@
+"""GPU parity of quantise-while-permuting (moe_permute_quant_fp8) against the oracle.
+
+The oracle quantises every token row (per token or per group: scale = amax /
+448 in float, code = E4M3FN of the float quotient, nearest-even, saturating)
+and permutes the codes with their scales.  Bar: offsets, indices, codes and
+scales bit-exact; with an expert map, nothing past the local rows written.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _parity import POISON, poisoned, to_np
+from mixture_experts_token_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print("[case] " + msg, flush=True)
+
+
+def gpu_quant(x, ids, e, group=0, emap=None, nl=0):
+    dev = ids.device
+    n, k = ids.shape
+    rows, h = n * k, x.shape[1]
+    groups = 1 if group == 0 else h // group
+    nb = nl if emap is not None else e
+    outs = {
+        "permuted_hidden_states": poisoned((rows, h), torch.uint8, dev),
+        "permuted_scale": poisoned((rows, groups), torch.float32, dev),
+        "expert_first_token_offset": poisoned((nb + 1,), torch.int64, dev),
+        "permuted_idx": poisoned((rows,), torch.int32, dev),
+        "inv_permuted_idx": poisoned((rows,), torch.int32, dev),
+    }
+    if emap is None:
+        ws = binding.moe_permute_workspace_size(n, k, e)
+        emap_t = None
+    else:
+        ws = binding.moe_permute_local_workspace_size(n, k, e, nl)
+        emap_t = torch.from_numpy(np.asarray(emap, np.int32)).to(dev)
+    workspace = poisoned((max(ws, 16),), torch.uint8, dev)
+    binding.moe_permute_quant_fp8(x, ids, e, outs["permuted_hidden_states"], outs["permuted_scale"],
+                                  outs["expert_first_token_offset"], outs["permuted_idx"], outs["inv_permuted_idx"],
+                                  workspace, group_size=group, expert_map=emap_t, num_local_experts=nl)
+    return outs
+
+
+def oracle_quant(x, ids, e, group=0, emap=None, nl=None):
+    dtype = "bf16" if x.dtype == torch.bfloat16 else "f32"
+    return oracle.permute_quant_fp8(to_np(x), dtype, to_np(ids), e, None if group == 0 else group, emap, nl)
+
+
+def assert_quant_equal(outs, ref):
+    np.testing.assert_array_equal(to_np(outs["expert_first_token_offset"]), ref["expert_first_token_offset"])
+    np.testing.assert_array_equal(to_np(outs["inv_permuted_idx"]), ref["inv_permuted_idx"])
+    m = int(ref["expert_first_token_offset"][-1])
+    perm = to_np(outs["permuted_idx"])
+    np.testing.assert_array_equal(perm[:m], ref["permuted_idx"])
+    codes = to_np(outs["permuted_hidden_states"])
+    if not np.array_equal(codes[:m], ref["permuted_hidden_states"]):
+        bad = np.argwhere(codes[:m] != ref["permuted_hidden_states"])
+        r, c = bad[0]
+        raise AssertionError("codes differ at %d places, first row %d col %d: got %#x want %#x" % (
+            len(bad), r, c, codes[r, c], ref["permuted_hidden_states"][r, c]))
+    sc = to_np(outs["permuted_scale"]).view(np.uint32)
+    np.testing.assert_array_equal(sc[:m], ref["permuted_scale"].view(np.uint32))
+    assert np.all(codes[m:] == POISON) and np.all(sc[m:] == 0xFFFFFFFF) and np.all(perm[m:].view(np.uint32) == 0xFFFFFFFF)
+
+
+def _inputs(name, dev, n=None, dtype=torch.bfloat16):
+    w = W.WORKLOADS[name]
+    if n is not None:
+        w = w.with_tokens(n)
+    ids_np, _ = W.make_routing(w, seed=0)
+    g = torch.Generator(device="cpu").manual_seed(w.num_tokens * 7 + w.hidden_size)
+    # a spread of row magnitudes so scales differ by orders of magnitude
+    mag = torch.exp(torch.randn((w.num_tokens, 1), generator=g) * 3)
+    x = (torch.randn((w.num_tokens, w.hidden_size), generator=g) * mag).to(dtype).to(dev)
+    return w, torch.from_numpy(ids_np).to(dev), x
+
+
+CASES = [
+    # (workload, tokens, group, input dtype, expert split (ep, rank, layout) or None)
+    ("tiny", None, 0, torch.float32, None),
+    ("tiny", None, 4, torch.float32, None),
+    ("tiny", None, 32, torch.float32, None),
+    ("mixtral", None, 0, torch.bfloat16, None),
+    ("mixtral", None, 128, torch.bfloat16, None),
+    ("mixtral", 1000, 0, torch.float32, None),
+    ("qwen3", None, 0, torch.bfloat16, None),
+    ("qwen3", None, 64, torch.bfloat16, (4, 1, "round_robin")),
+    ("dsv3", 4000, 0, torch.bfloat16, None),
+    ("dsv3", 4000, 128, torch.bfloat16, (8, 3, "contiguous")),
+    ("decode", 1, 0, torch.bfloat16, None),
+    ("decode", 256, 128, torch.bfloat16, None),
+    ("decode", 64, 0, torch.bfloat16, (8, 0, "contiguous")),
+]
+
+
+@pytest.mark.parametrize("name,n,group,dtype,ep", CASES, ids=["-".join(map(str, c)) for c in CASES])
+def test_quant_parity(hip_device, name, n, group, dtype, ep):
+    w, ids, x = _inputs(name, hip_device, n, dtype)
+    emap, nl = (None, None) if ep is None else W.expert_map_for(w.num_experts, *ep)
+    _say("quant %s N=%d H=%d group=%d %s ep=%s" % (name, w.num_tokens, w.hidden_size, group, dtype, ep))
+    outs = gpu_quant(x, ids, w.num_experts, group, emap, nl or 0)
+    torch.cuda.synchronize()
+    assert_quant_equal(outs, oracle_quant(x, ids, w.num_experts, group, emap, nl))
+
+
+@pytest.mark.parametrize("group", [0, 128])
+def test_quant_dsv3_full_size_sampled(hip_device, group):
+    """DSv3 shape at full size: indices whole, codes and scales of a sample of
+    tokens (quantised one by one by the oracle) at every destination."""
+    w, ids, x = _inputs("dsv3", hip_device)
+    _say("quant dsv3 full N=%d group=%d" % (w.num_tokens, group))
+    outs = gpu_quant(x, ids, w.num_experts, group)
+    torch.cuda.synchronize()
+    ref = oracle.permute(np.zeros((w.num_tokens, 0), np.uint8), to_np(ids), w.num_experts)
+    np.testing.assert_array_equal(to_np(outs["expert_first_token_offset"]), ref["expert_first_token_offset"])
+    np.testing.assert_array_equal(to_np(outs["permuted_idx"]), ref["permuted_idx"])
+    inv = to_np(outs["inv_permuted_idx"])
+    np.testing.assert_array_equal(inv, ref["inv_permuted_idx"])
+    rng = np.random.default_rng(3)
+    tokens = np.unique(np.concatenate([[0, w.num_tokens - 1], rng.choice(w.num_tokens, 1500, replace=False)]))
+    codes_ref, scales_ref = oracle.quantize_fp8_rows(to_np(x[torch.from_numpy(tokens).to(hip_device)]), "bf16",
+                                                     None if group == 0 else group)
+    dest = inv.reshape(-1, w.topk)[tokens]  # [sample, topk]
+    dest_t = torch.from_numpy(dest.reshape(-1).astype(np.int64)).to(hip_device)
+    got_codes = to_np(outs["permuted_hidden_states"].index_select(0, dest_t)).reshape(len(tokens), w.topk, -1)
+    got_scales = to_np(outs["permuted_scale"].index_select(0, dest_t)).reshape(len(tokens), w.topk, -1)
+    for k in range(w.topk):
+        np.testing.assert_array_equal(got_codes[:, k], codes_ref)
+        np.testing.assert_array_equal(got_scales[:, k].view(np.uint32), scales_ref.view(np.uint32))
+
+
+def _e4m3_boundary_row():
+    """448 (so the scale is exactly 1) followed by every finite E4M3FN value,
+    every midpoint between neighbours and the floats next to each midpoint."""
+    vals = sorted({oracle.e4m3_to_double(c) for c in range(0x7F) if not np.isnan(oracle.e4m3_to_double(c))})
+    probes = [448.0]
+    for lo, hi in zip(vals, vals[1:]):
+        mid = np.float32((lo + hi) / 2)
+        probes += [lo, mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1e9))]
+    probes += [-p for p in probes[1:]]
+    probes += [0.0, -0.0, 2.0**-12, -(2.0**-12), 447.99, 448.0]
+    row = np.array(probes, np.float32)
+    pad = (-row.size) % 4
+    return np.concatenate([row, np.zeros(pad, np.float32)])
+
+
+def test_quant_e4m3_rounding_boundaries(hip_device):
+    row = _e4m3_boundary_row()
+    h = row.size
+    x = torch.from_numpy(np.stack([row, -row, row * 0.5])).to(hip_device)  # 0.5 * row: scale 0.5, same quotients
+    ids = torch.tensor([[0], [1], [0]], dtype=torch.int32, device=hip_device)
+    _say("quant e4m3 boundaries H=%d" % h)
+    outs = gpu_quant(x, ids, 2)
+    torch.cuda.synchronize()
+    assert_quant_equal(outs, oracle_quant(x, ids, 2))
+
+
+def test_quant_non_finite_and_zero_rows(hip_device):
+    h = 64
+    x = np.random.default_rng(4).standard_normal((6, h)).astype(np.float32)
+    x[0] = 0.0
+    x[1, 3] = np.nan
+    x[2, 7] = np.inf
+    x[3, 9] = -np.inf
+    x[3, 10] = np.inf
+    x[4] = -0.0
+    x[5, ::2] = np.nan
+    xt = torch.from_numpy(x).to(hip_device)
+    ids = torch.arange(6, dtype=torch.int32, device=hip_device).reshape(6, 1) % 3
+    _say("quant non-finite rows")
+    for group in (0, 16):
+        outs = gpu_quant(xt, ids, 3, group)
+        torch.cuda.synchronize()
+        assert_quant_equal(outs, oracle_quant(xt, ids, 3, group))
+
+
+def test_quant_int64_ids_and_bad_id(hip_device):
+    w, ids, x = _inputs("qwen3", hip_device, 2000)
+    ids64 = ids.to(torch.int64)
+    _say("quant int64 ids")
+    outs = gpu_quant(x, ids64, w.num_experts, 128)
+    torch.cuda.synchronize()
+    assert_quant_equal(outs, oracle_quant(x, ids64, w.num_experts, 128))
+    bad = ids64.clone()
+    bad[77, 3] = 2**32 + 5
+    outs = gpu_quant(x, bad, w.num_experts, 0)
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == [-1] * (w.num_experts + 1)
+    assert np.all(to_np(outs["permuted_hidden_states"]) == POISON)
+    assert np.all(to_np(outs["permuted_scale"]).view(np.uint32) == 0xFFFFFFFF)
+
+
+def test_quant_zero_tokens(hip_device):
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=hip_device)
+    ids = torch.zeros((0, 2), dtype=torch.int32, device=hip_device)
+    _say("quant zero tokens")
+    outs = gpu_quant(x, ids, 4)
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == [0] * 5
