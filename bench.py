@@ -43,17 +43,28 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mixture_experts_token_amd", "csrc")
 
 
-def algorithmic_bytes(w, local=None, id_bytes: int = 4) -> dict:
+def algorithmic_bytes(w, local=None, id_bytes: int = 4, quant_groups: int = 0) -> dict:
     """Bytes the method must move: each input read once, each output written once.
 
     local: None for the plain permute, else (tokens_read, local_rows,
     num_local_experts) of a local-expert permute -- only tokens with a local
     row are read, only local rows are written (and read back by the
     unpermute, with their weights); every token still gets an output row.
+    quant_groups > 0: the permute reads bf16 rows and writes one fp8 byte per
+    element plus quant_groups float scales per permuted row.
     """
     import workloads as W
 
     b = W.ELEMENT_BYTES[w.hidden_dtype]
+    if quant_groups:
+        n, h, r, e = w.num_tokens, w.hidden_size, w.num_rows, w.num_experts
+        by = W.ELEMENT_BYTES[w.output_dtype]
+        t_read, m, nl = local if local is not None else (n, r, e)
+        permute = t_read * h * 2 + m * (h + 4 * quant_groups) + id_bytes * r + 4 * r + 4 * m + 8 * (nl + 1)
+        if local is not None:
+            permute += 4 * e
+        unpermute = m * h * by + 4 * r + 4 * m + n * h * by
+        return {"permute": permute, "unpermute": unpermute, "total": permute + unpermute}
     by = W.ELEMENT_BYTES[w.output_dtype]
     n, h, r, e = w.num_tokens, w.hidden_size, w.num_rows, w.num_experts
     if local is None:
@@ -154,6 +165,10 @@ def main() -> int:
     ap.add_argument("--ep", type=int, default=1, help="expert-parallel ranks: time one rank's local-expert step")
     ap.add_argument("--ep-rank", type=int, default=0)
     ap.add_argument("--ep-layout", default="contiguous", choices=["contiguous", "round_robin", "shuffled"])
+    ap.add_argument("--quant", default="none", choices=["none", "fp8"],
+                    help="fp8: the permute quantises bf16 rows to E4M3FN codes + scales on the way "
+                         "(moe_permute_quant_fp8)")
+    ap.add_argument("--group", type=int, default=0, help="quantisation group size in elements (0: per token)")
     ap.add_argument("--ids", default="int32", choices=["int32", "int64"],
                     help="expert id type handed to the permute (int64 is read directly, no cast pass)")
     args = ap.parse_args()
@@ -183,7 +198,15 @@ def main() -> int:
         local = (int(is_local.any(axis=1).sum()), int(is_local.sum()), n_local)
         emap = torch.from_numpy(emap_np).to(dev)
         n_off = n_local + 1
-    nb = algorithmic_bytes(w, local, 8 if args.ids == "int64" else 4)
+    quant = args.quant == "fp8"
+    if quant:
+        from dataclasses import replace as dc_replace
+
+        w = dc_replace(w, hidden_dtype="bf16")  # the quantiser reads bf16 rows
+        if args.group and (w.hidden_size % args.group or args.group & (args.group - 1)):
+            raise SystemExit("--group must be a power of two dividing the hidden size")
+    quant_groups = (w.hidden_size // args.group if args.group else 1) if quant else 0
+    nb = algorithmic_bytes(w, local, 8 if args.ids == "int64" else 4, quant_groups)
 
     ids = torch.from_numpy(ids_np.astype(np.int64) if args.ids == "int64" else ids_np).to(dev)
     wts = torch.from_numpy(wts_np).to(dev)
@@ -198,8 +221,9 @@ def main() -> int:
             "x": x0 if i == 0 else x0.clone(),
             "scale": scale0,
             "y": y0 if i == 0 else y0.clone(),
-            "xp": torch.empty((w.num_rows, w.hidden_size), dtype=hdt, device=dev),
-            "sp": None if scale0 is None else torch.empty(w.num_rows, dtype=torch.float32, device=dev),
+            "xp": torch.empty((w.num_rows, w.hidden_size), dtype=torch.uint8 if quant else hdt, device=dev),
+            "sp": (torch.empty((w.num_rows, quant_groups), dtype=torch.float32, device=dev) if quant else
+                   None if scale0 is None else torch.empty(w.num_rows, dtype=torch.float32, device=dev)),
             "off": torch.empty(n_off, dtype=torch.int64, device=dev),
             "perm": torch.empty(w.num_rows, dtype=torch.int32, device=dev),
             "inv": torch.empty(w.num_rows, dtype=torch.int32, device=dev),
@@ -213,7 +237,11 @@ def main() -> int:
 
     # Kernels go to torch's current stream (the capture stream while a graph is recorded).
     def permute(s):
-        if local is None:
+        if quant:
+            binding.moe_permute_quant_fp8(s["x"], ids, w.num_experts, s["xp"], s["sp"], s["off"], s["perm"], s["inv"],
+                                          ws, group_size=args.group, expert_map=emap,
+                                          num_local_experts=local[2] if local is not None else 0)
+        elif local is None:
             binding.moe_permute(s["x"], ids, w.num_experts, s["xp"], s["off"], s["perm"], s["inv"], ws,
                                 token_scale=s["scale"], permuted_scale=s["sp"])
         else:
@@ -280,7 +308,8 @@ def main() -> int:
     # rotating buffers; the fastest of 1/2/4/8 vectors per lane with
     # non-temporal or plain stores counts.
     ceiling = None
-    probe = load_probe() if local is None else None  # the probes model the full fan-out / fan-in only
+    # the probes model the full fan-out / fan-in of unchanged rows only
+    probe = load_probe() if local is None and not quant else None
     if probe is not None:
         dev_index = dev.index if dev.index is not None else 0
         xrow = w.hidden_size * W.ELEMENT_BYTES[w.hidden_dtype]
@@ -319,6 +348,8 @@ def main() -> int:
     else:
         dom, dom_us, dom_bytes = "permute", perm_avg, nb["permute"]
     profile_key = w.name if local is None else "%s_ep%d_r%d" % (w.name, args.ep, args.ep_rank)
+    if quant:
+        profile_key += "_fp8" + ("_g%d" % args.group if args.group else "")
     traffic, kernels = load_traffic(profile_key, dom)
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -330,7 +361,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         to_np = lambda t: (t.view(torch.int16).cpu().numpy().view("uint16") if t.dtype == torch.bfloat16  # noqa
                            else t.cpu().numpy())
-        cpu = cpu_baseline((to_np(x0), ids_np, wts_np, to_np(y0)), w, local=local, emap=emap_np)
+        cpu = None if quant else cpu_baseline((to_np(x0), ids_np, wts_np, to_np(y0)), w, local=local, emap=emap_np)
 
     line = {
         "metric": METRIC,
@@ -347,7 +378,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "num_tokens": w.num_tokens, "hidden_size": w.hidden_size,
                    "num_experts": w.num_experts, "topk": w.topk, "hidden_dtype": w.hidden_dtype,
-                   "output_dtype": w.output_dtype, "routing": w.routing, "ids_dtype": args.ids, "buffer_sets": nsets,
+                   "output_dtype": w.output_dtype, "routing": w.routing, "ids_dtype": args.ids,
+                   "quantise": None if not quant else {"to": "fp8_e4m3fn", "group": args.group or w.hidden_size},
+                   "buffer_sets": nsets,
                    "parallelism": "single GPU" if local is None else
                    "one expert-parallel rank's share on a single GPU",
                    **({} if local is None else {"expert_parallel": {

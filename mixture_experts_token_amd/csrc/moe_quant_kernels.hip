@@ -12,9 +12,10 @@
 // rounded to nearest with ties to even and saturated at 448; a NaN quotient
 // gets the code 0x7F.
 //
-// One wave per token: the whole row (at most 1024 16-byte vectors) is held in
-// registers, U vectors per lane, so the amax is a register and cross-lane
-// reduction and the row is read exactly once.  The destinations come from the
+// The whole row (at most 1024 16-byte vectors) is held in registers -- by one
+// wave per token when there are many tokens, by 4 or 16 waves when there are
+// few (their amax meets in LDS) -- so the amax is a register, cross-lane and
+// at most one LDS reduction, and the row is read exactly once.  The destinations come from the
 // inverse index the index permute wrote (-1: not on this rank, not written);
 // a token with no destination is not read.
 
@@ -32,27 +33,21 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kQuantThreads = 256;
 constexpr float kE4M3Max = 448.0f;
 
-// E4M3FN code of q: clamp the magnitude to 448, then round to the nearest
-// value with ties to the even fraction.  Below 2^-6 the values are the
-// multiples of 2^-9; above, the float's exponent and its fraction rounded to
-// three bits (a carry out of the fraction moves to the next exponent).
-__device__ __forceinline__ uint32_t e4m3_code(float q) {
-    const uint32_t u = __float_as_uint(q);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7Fu;  // NaN
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const float a = fminf(__uint_as_float(u & 0x7FFFFFFFu), kE4M3Max);
-    uint32_t code;
-    if (a < 0.015625f) {
-        code = (uint32_t)__builtin_rintf(a * 512.0f);  // exact scaling; rint rounds to nearest even
-    } else {
-        const uint32_t ua = __float_as_uint(a);
-        const uint32_t m = ua & 0x7FFFFFu;
-        code = (((ua >> 23) - 120u) << 3) + ((m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20);
-    }
-    return sign | code;
+// E4M3FN codes of four floats, packed little-endian into one word: each
+// value is clamped to [-448, 448] and converted by the gfx950 OCP fp8
+// conversion (nearest, ties to even; a bounded probe compared it with a
+// software encoder written from the format on every float in [-448, 448]:
+// identical).  A NaN gets 0x7F.
+__device__ __forceinline__ uint32_t e4m3_pack4(float q0, float q1, float q2, float q3) {
+    const float c0 = fminf(fmaxf(q0, -kE4M3Max), kE4M3Max), c1 = fminf(fmaxf(q1, -kE4M3Max), kE4M3Max);
+    const float c2 = fminf(fmaxf(q2, -kE4M3Max), kE4M3Max), c3 = fminf(fmaxf(q3, -kE4M3Max), kE4M3Max);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+    const uint32_t nan = (q0 != q0 ? 0x000000FFu : 0u) | (q1 != q1 ? 0x0000FF00u : 0u) |
+                         (q2 != q2 ? 0x00FF0000u : 0u) | (q3 != q3 ? 0xFF000000u : 0u);
+    return ((uint32_t)w & ~nan) | (0x7F7F7F7Fu & nan);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -87,45 +82,45 @@ template <bool kBF16>
 __device__ __forceinline__ u32x2 vec_codes(const u32x4& v, float scale) {
     u32x2 out;
     if constexpr (kBF16) {
-        uint32_t w[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t c0 = e4m3_code(__fdiv_rn(bf16_lo(v[2 * h]), scale));
-            const uint32_t c1 = e4m3_code(__fdiv_rn(bf16_hi(v[2 * h]), scale));
-            const uint32_t c2 = e4m3_code(__fdiv_rn(bf16_lo(v[2 * h + 1]), scale));
-            const uint32_t c3 = e4m3_code(__fdiv_rn(bf16_hi(v[2 * h + 1]), scale));
-            w[h] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-        }
-        out.x = w[0];
-        out.y = w[1];
+        out.x = e4m3_pack4(__fdiv_rn(bf16_lo(v[0]), scale), __fdiv_rn(bf16_hi(v[0]), scale),
+                           __fdiv_rn(bf16_lo(v[1]), scale), __fdiv_rn(bf16_hi(v[1]), scale));
+        out.y = e4m3_pack4(__fdiv_rn(bf16_lo(v[2]), scale), __fdiv_rn(bf16_hi(v[2]), scale),
+                           __fdiv_rn(bf16_lo(v[3]), scale), __fdiv_rn(bf16_hi(v[3]), scale));
     } else {
-        uint32_t c[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) c[q] = e4m3_code(__fdiv_rn(__uint_as_float(v[q]), scale));
-        out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        out.x = e4m3_pack4(__fdiv_rn(__uint_as_float(v[0]), scale), __fdiv_rn(__uint_as_float(v[1]), scale),
+                           __fdiv_rn(__uint_as_float(v[2]), scale), __fdiv_rn(__uint_as_float(v[3]), scale));
         out.y = 0u;
     }
     return out;
 }
 
-// One wave per token t.  U: vectors per lane (U*64 >= row_vecs).  group_vecs:
-// vectors per scale group (a power of two <= 64, so a group is an aligned run
-// of lanes within one u), or 0 for one scale per token.
-template <bool kBF16, int U, bool kNTStore>
-__global__ __launch_bounds__(kQuantThreads) void quant_scatter_kernel(
+// TPT threads per token (64: one wave; 256 or 1024: several waves whose
+// amax meets in LDS), BT = max(TPT, 256) threads per block, BT / TPT tokens
+// per block.  Thread gt of a token holds vectors gt, gt + TPT, ...  (U of
+// them, U*TPT >= row_vecs).  group_vecs: vectors per scale group (a power of
+// two <= 64, so a group is an aligned run of lanes of one wave), or 0 for one
+// scale per token.
+template <bool kBF16, int U, int TPT, bool kNTStore>
+__global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ inv, const int64_t* __restrict__ off,
     uint8_t* __restrict__ codes, float* __restrict__ scales, int64_t num_tokens, int64_t rv, int topk,
-    int group_vecs, int64_t total_waves) {
-    constexpr int kEpv = kBF16 ? 8 : 4;  // elements (and code bytes) per 16-byte input vector
-    if (off[0] < 0) return;              // the index permute rejected an id: write nothing
-    const int lane = (int)(threadIdx.x % 64);
+    int group_vecs) {
+    constexpr int BT = TPT > 256 ? TPT : 256;
+    constexpr int TB = BT / TPT;           // tokens per block
+    constexpr int WPT = TPT / 64;          // waves per token
+    constexpr int kEpv = kBF16 ? 8 : 4;    // elements (and code bytes) per 16-byte input vector
+    __shared__ float red_s[WPT > 1 ? WPT : 1];
+    if (off[0] < 0) return;                // the index permute rejected an id: write nothing
+    const int gt = (int)(threadIdx.x % TPT);
     const int64_t rows = num_tokens * topk;
-    const int64_t row_bytes = rv * kEpv;  // code bytes per row = H
+    const int64_t row_bytes = rv * kEpv;   // code bytes per row = H
     const int64_t groups = group_vecs > 0 ? rv / group_vecs : 1;
-    for (int64_t t = (int64_t)blockIdx.x * (kQuantThreads / 64) + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64));
-         t < num_tokens; t += total_waves) {
+    const int64_t stride = (int64_t)gridDim.x * TB;
+    for (int64_t t = (int64_t)blockIdx.x * TB + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / TPT));
+         t < num_tokens; t += stride) {
         const int64_t tt = __builtin_amdgcn_readfirstlane((int)t);
-        // Any destination on this rank?  (Wave-uniform reads, scalar path.)
+        // Any destination on this rank?  (Wave-uniform reads, scalar path; the
+        // same answer for every wave of the token, so the block stays together.)
         bool any = false;
         for (int k = 0; k < topk; ++k) {
             const int32_t d = inv[tt * topk + k];
@@ -136,10 +131,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_scatter_kernel(
         const u32x4* src = x + tt * rv;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t idx = lane + 64 * u;
+            const int64_t idx = gt + (int64_t)TPT * u;
             v[u] = idx < rv ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
         }
-        // Scales: per vector amax, reduced over its group's lanes (or the wave).
+        // Scales: per vector amax, reduced over its group's lanes (or the token).
         float sc[U];
         if (group_vecs == 0) {
             float m = 0.0f;
@@ -150,6 +145,13 @@ __global__ __launch_bounds__(kQuantThreads) void quant_scatter_kernel(
             }
 #pragma unroll
             for (int s = 1; s < 64; s <<= 1) m = max_xor(m, s);
+            if constexpr (WPT > 1) {
+                if (gt % 64 == 0) red_s[gt / 64] = m;
+                __syncthreads();
+#pragma unroll
+                for (int w = 0; w < WPT; ++w) m = red_s[w] > m ? red_s[w] : m;
+                __syncthreads();  // red_s is rewritten for the next token
+            }
             const float scale = m > 0.0f ? __fdiv_rn(m, kE4M3Max) : 1.0f;
 #pragma unroll
             for (int u = 0; u < U; ++u) sc[u] = scale;
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_scatter_kernel(
             uint8_t* orow = codes + (int64_t)d * row_bytes;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t idx = lane + 64 * u;
+                const int64_t idx = gt + (int64_t)TPT * u;
                 if (idx >= rv) continue;
                 if constexpr (kBF16) {
                     u32x2* o = reinterpret_cast<u32x2*>(orow) + idx;
@@ -184,11 +186,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_scatter_kernel(
             }
             float* srow = scales + (int64_t)d * groups;
             if (group_vecs == 0) {
-                if (lane == 0) srow[0] = sc[0];
+                if (gt == 0) srow[0] = sc[0];
             } else {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int64_t idx = lane + 64 * u;
+                    const int64_t idx = gt + (int64_t)TPT * u;
                     if (idx < rv && idx % group_vecs == 0) srow[idx / group_vecs] = sc[u];
                 }
             }
@@ -196,50 +198,51 @@ __global__ __launch_bounds__(kQuantThreads) void quant_scatter_kernel(
     }
 }
 
-// Vectors per lane: the smallest listed U with U*64 >= row_vecs.
-constexpr int kQuantUnrolls[] = {1, 2, 3, 4, 6, 8, 10, 12, 14, 16};
-
-template <bool kBF16, int U>
-hipError_t launch_quant_u(const QuantArgs& a, hipStream_t stream) {
-    const int64_t waves_needed = a.num_tokens;
-    const int64_t per_block = kQuantThreads / 64;
-    const int64_t blocks_needed = (waves_needed + per_block - 1) / per_block;
+template <bool kBF16, int U, int TPT>
+hipError_t launch_quant_ut(const QuantArgs& a, hipStream_t stream) {
+    constexpr int BT = TPT > 256 ? TPT : 256;
+    constexpr int64_t TB = BT / TPT;
+    const int64_t blocks_needed = (a.num_tokens + TB - 1) / TB;
     const int64_t blocks = blocks_needed < kMaxGridBlocks ? blocks_needed : kMaxGridBlocks;
     // Plain stores for wide fan-out into large outputs, as in the permute row copy.
     const bool plain = a.topk >= 4 && a.num_tokens * a.topk * a.row_vecs * (kBF16 ? 8 : 4) >= (int64_t(32) << 20);
     if (plain)
-        hipLaunchKernelGGL((quant_scatter_kernel<kBF16, U, false>), dim3((unsigned)blocks), dim3(kQuantThreads), 0,
-                           stream, reinterpret_cast<const u32x4*>(a.hidden_states), a.inv_permuted_idx,
+        hipLaunchKernelGGL((quant_scatter_kernel<kBF16, U, TPT, false>), dim3((unsigned)blocks), dim3(BT), 0, stream,
+                           reinterpret_cast<const u32x4*>(a.hidden_states), a.inv_permuted_idx,
                            a.expert_first_token_offset, a.permuted_codes, a.permuted_scale, a.num_tokens, a.row_vecs,
-                           a.topk, a.group_vecs, blocks * per_block);
+                           a.topk, a.group_vecs);
     else
-        hipLaunchKernelGGL((quant_scatter_kernel<kBF16, U, true>), dim3((unsigned)blocks), dim3(kQuantThreads), 0,
-                           stream, reinterpret_cast<const u32x4*>(a.hidden_states), a.inv_permuted_idx,
+        hipLaunchKernelGGL((quant_scatter_kernel<kBF16, U, TPT, true>), dim3((unsigned)blocks), dim3(BT), 0, stream,
+                           reinterpret_cast<const u32x4*>(a.hidden_states), a.inv_permuted_idx,
                            a.expert_first_token_offset, a.permuted_codes, a.permuted_scale, a.num_tokens, a.row_vecs,
-                           a.topk, a.group_vecs, blocks * per_block);
+                           a.topk, a.group_vecs);
     return hipGetLastError();
 }
 
+// Threads per token: one wave for short rows while tokens alone fill the
+// chip; four waves for long rows or fewer tokens (measured faster from 8 KiB
+// rows up: shorter serial chains per wave, more waves in flight); sixteen
+// when there are very few tokens.
+constexpr int64_t kQuantOneWaveMinTokens = 1024;
+constexpr int64_t kQuantOneWaveMaxRowVecs = 256;
+constexpr int64_t kQuantFourWaveMinTokens = 64;
+
 template <bool kBF16>
 hipError_t launch_quant_dtype(const QuantArgs& a, hipStream_t stream) {
-    int u = kQuantUnrolls[sizeof(kQuantUnrolls) / sizeof(int) - 1];
-    for (int c : kQuantUnrolls)
-        if ((int64_t)c * 64 >= a.row_vecs) {
-            u = c;
-            break;
-        }
-    switch (u) {
-        case 1: return launch_quant_u<kBF16, 1>(a, stream);
-        case 2: return launch_quant_u<kBF16, 2>(a, stream);
-        case 3: return launch_quant_u<kBF16, 3>(a, stream);
-        case 4: return launch_quant_u<kBF16, 4>(a, stream);
-        case 6: return launch_quant_u<kBF16, 6>(a, stream);
-        case 8: return launch_quant_u<kBF16, 8>(a, stream);
-        case 10: return launch_quant_u<kBF16, 10>(a, stream);
-        case 12: return launch_quant_u<kBF16, 12>(a, stream);
-        case 14: return launch_quant_u<kBF16, 14>(a, stream);
-        default: return launch_quant_u<kBF16, 16>(a, stream);
+    const int64_t rv = a.row_vecs;
+    if (a.num_tokens >= kQuantOneWaveMinTokens && rv <= kQuantOneWaveMaxRowVecs) {
+        if (rv <= 64) return launch_quant_ut<kBF16, 1, 64>(a, stream);
+        if (rv <= 128) return launch_quant_ut<kBF16, 2, 64>(a, stream);
+        if (rv <= 192) return launch_quant_ut<kBF16, 3, 64>(a, stream);
+        return launch_quant_ut<kBF16, 4, 64>(a, stream);
     }
+    if (a.num_tokens >= kQuantFourWaveMinTokens) {
+        if (rv <= 256) return launch_quant_ut<kBF16, 1, 256>(a, stream);
+        if (rv <= 512) return launch_quant_ut<kBF16, 2, 256>(a, stream);
+        if (rv <= 768) return launch_quant_ut<kBF16, 3, 256>(a, stream);
+        return launch_quant_ut<kBF16, 4, 256>(a, stream);
+    }
+    return launch_quant_ut<kBF16, 1, 1024>(a, stream);  // rv <= 1024 (checked on the host)
 }
 
 }  // namespace
