@@ -98,6 +98,8 @@ def _load():
         lib.oracle_double_to_e4m3.restype = ctypes.c_uint8
         lib.oracle_quantize_fp8_rows.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p]
         lib.oracle_quantize_fp8_rows.restype = ctypes.c_int
+        lib.oracle_grouped_gemm_bf16.argtypes = [p, p, p, i32, i64, i64, p]
+        lib.oracle_grouped_gemm_bf16.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -311,6 +313,21 @@ def quantize_fp8_rows(x: np.ndarray, dtype: str, group: int | None = None):
     _check(_load().oracle_quantize_fp8_rows(_ptr(src), 1 if dtype == "bf16" else 0, rows, h, g, _ptr(codes),
                                             _ptr(scales)))
     return codes, scales
+
+
+def grouped_gemm_bf16(x: np.ndarray, w: np.ndarray, offsets) -> np.ndarray:
+    """y[j] = x[j] @ w[e]^T for the rows j of expert e ([off[e], off[e+1])), double
+    accumulation rounded once to bf16.  x: bf16 bits [rows, k]; w: bf16 bits
+    [E, n, k]; returns bf16 bits [off[E], n]."""
+    xs = np.ascontiguousarray(x, dtype=np.uint16)
+    ws = np.ascontiguousarray(w, dtype=np.uint16)
+    off = np.ascontiguousarray(offsets, dtype=np.int64)
+    e, n, k = ws.shape
+    if off.shape != (e + 1,) or xs.ndim != 2 or xs.shape[1] != k or xs.shape[0] < off[-1]:
+        raise ValueError("shapes of x, w and offsets disagree")
+    y = np.zeros((int(off[-1]), n), dtype=np.uint16)
+    _check(_load().oracle_grouped_gemm_bf16(_ptr(xs), _ptr(ws), _ptr(off), e, n, k, _ptr(y)))
+    return y
 
 
 def permute_quant_fp8(hidden: np.ndarray, dtype: str, topk_ids, num_experts: int, group: int | None = None,

@@ -410,6 +410,39 @@ int oracle_quantize_fp8_rows(const void *x, int x_is_bf16, int64_t rows, int64_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* Grouped GEMM over the permuted rows.                                       */
+/* [P1] PR description: the permute makes each expert's tokens contiguous so  */
+/* that a grouped GEMM can run the experts over them, and the unpermute then  */
+/* reduces that GEMM's expanded output.  Reading taken: expert e's weight is  */
+/* w[e] with n_out rows of k_in elements (a linear layer: y = x w[e]^T), the  */
+/* rows of expert e are permuted rows [off[e], off[e+1]), and                 */
+/*   y[j][n] = sum over k of x[j][k] * w[e][n][k]                             */
+/* in double precision, rounded once to bfloat16.  x, w and y are bfloat16    */
+/* bit patterns; y is in permuted order, as the unpermute reads it.           */
+/* ------------------------------------------------------------------------ */
+int oracle_grouped_gemm_bf16(const uint16_t *x, const uint16_t *w, const int64_t *off, int32_t num_experts,
+                             int64_t n_out, int64_t k_in, uint16_t *y)
+{
+    if (num_experts < 1 || n_out < 1 || k_in < 1 || off[0] != 0)
+        return ORACLE_BAD_ARG;
+    for (int32_t e = 0; e < num_experts; ++e)
+        if (off[e + 1] < off[e])
+            return ORACLE_BAD_ARG;
+    for (int32_t e = 0; e < num_experts; ++e) {
+        const uint16_t *we = w + (int64_t)e * n_out * k_in;
+        for (int64_t j = off[e]; j < off[e + 1]; ++j) {
+            for (int64_t n = 0; n < n_out; ++n) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < k_in; ++k)
+                    acc += oracle_bf16_to_double(x[j * k_in + k]) * oracle_bf16_to_double(we[n * k_in + k]);
+                y[j * n_out + n] = oracle_double_to_bf16(acc);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Unpermute.                                                                 */
 /* [P1] PR description: reduce the expanded grouped-GEMM output back per      */
 /* token and scale each contribution by its topk_weight:                      */

@@ -64,6 +64,16 @@ MUTANTS = {
     "quant_multiplies_by_scale": (
         "float q = v / scale;",
         "float q = v * scale;"),
+    # grouped GEMM
+    "gemm_next_expert_weight": (
+        "const uint16_t *we = w + (int64_t)e * n_out * k_in;",
+        "const uint16_t *we = w + (int64_t)((e + 1) % num_experts) * n_out * k_in;"),
+    "gemm_weight_transposed": (
+        "* oracle_bf16_to_double(we[n * k_in + k]);",
+        "* oracle_bf16_to_double(we[k * n_out + n]);"),
+    "gemm_drops_last_k": (
+        "for (int64_t k = 0; k < k_in; ++k)\n                    acc +=",
+        "for (int64_t k = 0; k < k_in - 1; ++k)\n                    acc +="),
     # int64 ids
     "int64_ids_truncated": (
         "if (ids64[i] < 0 || ids64[i] >= (int64_t)num_experts)",

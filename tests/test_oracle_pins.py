@@ -715,3 +715,71 @@ def test_quantizer_non_finite_inputs():
     # an infinite amax gives an infinite scale: finite values go to (signed) zero, inf / inf is NaN
     assert np.isinf(scales[1, 0]) and codes[1].tolist() == [0x7F, 0x00, 0x80, 0x00]
     assert codes[2].tolist() == [0x7F, 0x7F, 0x00, 0x80]
+
+
+# --------------------------------------------------------------------------
+# Grouped GEMM over the permuted rows: y[j] = x[j] w[e]^T for the rows of expert e.
+# --------------------------------------------------------------------------
+def _random_offsets(rng, e, rows, empties=()):
+    counts = rng.multinomial(rows, np.ones(e) / e)
+    for x in empties:
+        rows_moved = counts[x]
+        counts[x] = 0
+        counts[(x + 1) % e] += rows_moved
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+
+
+def test_grouped_gemm_against_float64_matmul():
+    rng = np.random.default_rng(21)
+    e, n, k, rows = 5, 24, 40, 70
+    off = _random_offsets(rng, e, rows, empties=(2,))
+    x = _bf16_bits_from_f32(rng.standard_normal((rows, k)).astype(np.float32))
+    w = _bf16_bits_from_f32(rng.standard_normal((e, n, k)).astype(np.float32) * 0.1)
+    y = oracle.grouped_gemm_bf16(x, w, off)
+    xf = _f32_from_bf16_bits(x).astype(np.float64)
+    wf = _f32_from_bf16_bits(w).astype(np.float64)
+    for ex in range(e):
+        seg = slice(off[ex], off[ex + 1])
+        ref = xf[seg] @ wf[ex].T
+        got = _f32_from_bf16_bits(y[seg]).astype(np.float64)
+        # every output is the nearest bf16 of the float64 product sum
+        assert np.all(np.abs(got - ref) <= 2.0**-8 * np.abs(ref) + 2.0**-133)
+        for v_got, v_ref in list(zip(y[seg].reshape(-1), ref.reshape(-1)))[::17]:
+            assert int(v_got) == brute_nearest_bf16(float(v_ref))
+
+
+def test_grouped_gemm_exact_small_integers():
+    # small integers: every product and sum is exact, so y is the integer result
+    rng = np.random.default_rng(22)
+    e, n, k, rows = 3, 8, 16, 11
+    off = np.array([0, 4, 4, 11], np.int64)
+    xi = rng.integers(-4, 5, size=(rows, k))
+    wi = rng.integers(-3, 4, size=(e, n, k))
+    y = oracle.grouped_gemm_bf16(_bf16_bits_from_f32(xi.astype(np.float32)),
+                                 _bf16_bits_from_f32(wi.astype(np.float32)), off)
+    for ex in range(e):
+        for j in range(off[ex], off[ex + 1]):
+            for c in range(n):
+                want = sum(int(xi[j, q]) * int(wi[ex, c, q]) for q in range(k))
+                assert _f32_from_bf16_bits(y[j:j + 1, c:c + 1])[0, 0] == want
+
+
+def test_grouped_gemm_routes_rows_to_their_expert():
+    # w[e] = (e + 1) * I: each row comes back scaled by its expert's number
+    e, k, rows = 4, 16, 13
+    off = np.array([0, 3, 3, 9, 13], np.int64)
+    x = _bf16_bits_from_f32(np.arange(rows * k, dtype=np.float32).reshape(rows, k) % 7 - 3)
+    w = _bf16_bits_from_f32(np.stack([np.eye(k, dtype=np.float32) * (ex + 1) for ex in range(e)]))
+    y = _f32_from_bf16_bits(oracle.grouped_gemm_bf16(x, w, off))
+    xf = _f32_from_bf16_bits(x)
+    for ex in range(e):
+        np.testing.assert_array_equal(y[off[ex]:off[ex + 1]], xf[off[ex]:off[ex + 1]] * (ex + 1))
+
+
+def test_grouped_gemm_rejects_bad_offsets():
+    x = np.zeros((4, 8), np.uint16)
+    w = np.zeros((2, 8, 8), np.uint16)
+    with pytest.raises(oracle.OracleError):
+        oracle.grouped_gemm_bf16(x, w, np.array([0, 3, 2], np.int64))
+    with pytest.raises(oracle.OracleError):
+        oracle.grouped_gemm_bf16(x, w, np.array([1, 2, 3], np.int64))
