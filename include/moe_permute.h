@@ -227,6 +227,33 @@ moe_status_t moe_permute_quant_fp8(const void *hidden_states, int32_t dtype, con
                                    size_t workspace_bytes, void *stream);
 
 /*
+ * moe_grouped_gemm_bf16 -- the expert GEMM between permute and unpermute
+ * (vLLM PR #14568, PR description: the permute makes each expert's tokens
+ * contiguous for a grouped GEMM, whose expanded output the unpermute then
+ * reduces).  For every expert e and permuted row j in [off[e], off[e+1]):
+ *     y[j][c] = sum over i of x[j][i] * w[e][c][i]
+ * bf16 inputs, fp32 accumulation on the matrix cores, rounded once to bf16
+ * (round to nearest even).  y is in permuted order, ready for moe_unpermute.
+ *
+ *   x                 [max_rows, k] bf16, permuted rows (e.g. permuted_hidden_states)
+ *   w                 [num_experts, n, k] bf16 (expert e: n output rows of k, a
+ *                     linear layer's weight)
+ *   expert_first_token_offset  [num_experts + 1] int64 on the device, as the
+ *                     permute wrote it (the row counts are never read by the host)
+ *   num_experts       1 .. MOE_MAX_EXPERTS
+ *   max_rows          rows x and y hold; off[num_experts] must not exceed it
+ *   n, k              n a multiple of 128, k a multiple of 64
+ *   y                 [max_rows, n] bf16 (out); rows >= off[num_experts] untouched
+ *
+ * Offsets that are not a valid prefix (off[0] != 0, a decreasing entry, the
+ * -1 the permute writes for a rejected id, or off[E] > max_rows) are detected
+ * on the device: nothing is written.  Needs no workspace.
+ */
+moe_status_t moe_grouped_gemm_bf16(const void *x, const void *w, const int64_t *expert_first_token_offset,
+                                   int32_t num_experts, int64_t max_rows, int64_t n, int64_t k, void *y,
+                                   void *stream);
+
+/*
  * moe_unpermute -- weighted top-k reduction of the expanded grouped-GEMM
  * output back to one row per token (vLLM PR #14568, PR description):
  *     output[t] = sum_{k=0}^{topk-1} topk_weights[t][k] * expanded_output[inv_permuted_idx[t*topk+k]]

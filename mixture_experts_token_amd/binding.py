@@ -8,7 +8,7 @@ is missing the first call raises.
 The entry points carry the C names: ``moe_permute_supported``,
 ``moe_permute_workspace_size``, ``moe_permute``, ``moe_unpermute``,
 ``moe_permute_local_workspace_size``, ``moe_permute_local``,
-``moe_permute_quant_fp8``.
+``moe_permute_quant_fp8``, ``moe_grouped_gemm_bf16``.
 ``MoEPermuteScratch`` follows the preallocated-buffer design of the prhub
 summary of vLLM PR #43014 (section "key code snippets", MoEPermuteScratch):
 every buffer is allocated once for ``max_num_tokens`` and reused by each call.
@@ -68,6 +68,8 @@ def load_library() -> ctypes.CDLL:
         lib.moe_permute_quant_fp8.argtypes = [p, i32, p, i32, i64, i64, i32, i32, p, i32, i64, p, p, p, p, p, p,
                                               sz, p]
         lib.moe_permute_quant_fp8.restype = ctypes.c_int
+        lib.moe_grouped_gemm_bf16.argtypes = [p, p, p, i32, i64, i64, i64, p, p]
+        lib.moe_grouped_gemm_bf16.restype = ctypes.c_int
         lib.moe_unpermute.argtypes = [p, i32, p, p, i64, i64, i32, p, p]
         lib.moe_unpermute.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -212,6 +214,23 @@ def moe_permute_quant_fp8(hidden_states, topk_ids, num_experts: int, permuted_co
         _ptr(workspace), ws_bytes, _stream(stream, topk_ids))
     if status != MOE_OK:
         raise MoEError(status, "moe_permute_quant_fp8")
+
+
+def moe_grouped_gemm_bf16(x, w, expert_first_token_offset, y, stream=None) -> None:
+    """y[j] = x[j] @ w[e]^T for the permuted rows j of expert e (see the C header).
+
+    ``x`` bfloat16 [max_rows, k]; ``w`` bfloat16 [E, n, k]; offsets int64
+    [E + 1] on the device; ``y`` bfloat16 [max_rows, n].
+    """
+    import torch
+
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or y.dtype != torch.bfloat16:
+        raise TypeError("x, w and y must be bfloat16")
+    e, n, k = w.shape
+    status = load_library().moe_grouped_gemm_bf16(_ptr(x), _ptr(w), _ptr(expert_first_token_offset), e,
+                                                   x.shape[0], n, k, _ptr(y), _stream(stream, y))
+    if status != MOE_OK:
+        raise MoEError(status, "moe_grouped_gemm_bf16")
 
 
 def moe_unpermute(expanded_output, topk_weights, inv_permuted_idx, output, stream=None) -> None:

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_permute.so")
 PROBE_LIB = os.path.join(PKG, "libhbm_probe.so")
 
-SOURCES = ["moe_permute_kernels.hip", "moe_quant_kernels.hip", "moe_permute_api.cpp"]
+SOURCES = ["moe_permute_kernels.hip", "moe_quant_kernels.hip", "moe_gemm_kernels.hip", "moe_permute_api.cpp"]
 HEADERS = ["moe_launch.h", "moe_plan.h"]
 PROBE_SOURCES = ["hbm_probe.hip"]  # streaming-ceiling kernels used by bench.py only
 

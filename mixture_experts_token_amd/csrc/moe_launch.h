@@ -49,7 +49,19 @@ struct QuantArgs {
     float* permuted_scale;          // [N*topk, groups]
 };
 
+struct GemmArgs {
+    const void* x;                  // [max_rows, k] bf16 (permuted rows)
+    const void* w;                  // [num_experts, n, k] bf16
+    const int64_t* offsets;         // [num_experts + 1] (device)
+    int32_t num_experts;
+    int64_t max_rows;
+    int64_t n;                      // multiple of 128
+    int64_t k;                      // multiple of 64
+    void* y;                        // [max_rows, n] bf16
+};
+
 hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t value, hipStream_t stream);
+hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, int num_cus, hipStream_t stream);
 hipError_t launch_quant_scatter(const QuantArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream);
 hipError_t launch_unpermute(const UnpermuteArgs& a, bool bf16, hipStream_t stream);

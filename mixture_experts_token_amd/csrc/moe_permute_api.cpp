@@ -276,6 +276,41 @@ moe_status_t moe_permute_quant_fp8(const void* hidden_states, int32_t dtype, con
                : MOE_ERR_HIP;
 }
 
+moe_status_t moe_grouped_gemm_bf16(const void* x, const void* w, const int64_t* expert_first_token_offset,
+                                   int32_t num_experts, int64_t max_rows, int64_t n, int64_t k, void* y,
+                                   void* stream) {
+    if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS || max_rows < 0) return MOE_ERR_INVALID_ARG;
+    if (n < 128 || n % 128 != 0 || k < 64 || k % 64 != 0) return MOE_ERR_INVALID_ARG;
+    if (n > (int64_t(1) << 40) / 2 || k > (int64_t(1) << 40) / 2 || max_rows > kMaxRows) return MOE_ERR_INVALID_ARG;
+    if (expert_first_token_offset == nullptr || w == nullptr) return MOE_ERR_INVALID_ARG;
+    if (max_rows > 0 && (x == nullptr || y == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(expert_first_token_offset, 8))
+        return MOE_ERR_MISALIGNED;
+    const Span outs[] = {{y, (uint64_t)max_rows * (uint64_t)n * 2}};
+    const Span ins[] = {
+        {x, (uint64_t)max_rows * (uint64_t)k * 2},
+        {w, (uint64_t)num_experts * (uint64_t)n * (uint64_t)k * 2},
+        {expert_first_token_offset, 8ull * (uint64_t)(num_experts + 1)},
+    };
+    if (any_overlap(outs, 1, ins, 3)) return MOE_ERR_INVALID_ARG;
+    if (max_rows == 0) return MOE_OK;
+    int device = 0, cus = 0;
+    if (hipGetDevice(&device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1)
+        return MOE_ERR_HIP;
+    moe::GemmArgs g;
+    g.x = x;
+    g.w = w;
+    g.offsets = expert_first_token_offset;
+    g.num_experts = num_experts;
+    g.max_rows = max_rows;
+    g.n = n;
+    g.k = k;
+    g.y = y;
+    return moe::launch_grouped_gemm_bf16(g, cus, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK
+                                                                                                 : MOE_ERR_HIP;
+}
+
 moe_status_t moe_unpermute(const void* expanded_output, int32_t dtype, const float* topk_weights,
                            const int32_t* inv_permuted_idx, int64_t num_tokens, int64_t hidden_size, int32_t topk,
                            void* output, void* stream) {

@@ -47,9 +47,10 @@ host_only = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer checks run on
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["moe_permute", "moe_permute_local", "moe_permute_local_workspace_size",
-                                    "moe_permute_quant_fp8", "moe_permute_supported", "moe_permute_workspace_size",
-                                    "moe_status_string", "moe_unpermute"]
+    assert declared_functions() == ["moe_grouped_gemm_bf16", "moe_permute", "moe_permute_local",
+                                    "moe_permute_local_workspace_size", "moe_permute_quant_fp8",
+                                    "moe_permute_supported", "moe_permute_workspace_size", "moe_status_string",
+                                    "moe_unpermute"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -253,6 +254,39 @@ def quant_call(lib, **kw):
 ])
 def test_permute_quant_rejects(lib, kw, status):
     assert quant_call(lib, **kw) == status
+
+
+def gemm_call(lib, **kw):
+    args = dict(x=addr(0), w=addr(1), off=addr(2), e=8, rows=8192, n=1024, k=4096, y=addr(3), stream=None)
+    args.update(kw)
+    return lib.moe_grouped_gemm_bf16(args["x"], args["w"], args["off"], args["e"], args["rows"], args["n"],
+                                     args["k"], args["y"], args["stream"])
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(e=0), INVALID),
+    (dict(e=1025), INVALID),
+    (dict(rows=-1), INVALID),
+    (dict(n=100), INVALID),           # n must be a multiple of 128
+    (dict(n=0), INVALID),
+    (dict(k=96), INVALID),            # k must be a multiple of 64
+    (dict(off=None), INVALID),
+    (dict(w=None), INVALID),
+    (dict(x=None), INVALID),
+    (dict(y=None), INVALID),
+    (dict(x=addr(0, 8)), MISALIGNED),
+    (dict(y=addr(3, 2)), MISALIGNED),
+    (dict(off=addr(2, 4)), MISALIGNED),
+    (dict(y=addr(0)), INVALID),       # output aliases the rows
+    (dict(y=addr(2)), INVALID),       # output aliases the offsets
+])
+def test_grouped_gemm_rejects(lib, kw, status):
+    assert gemm_call(lib, **kw) == status
+
+
+def test_grouped_gemm_zero_rows_is_a_no_op(lib):
+    assert gemm_call(lib, rows=0, x=None, y=None) == OK
 
 
 def unpermute_call(lib, **kw):

@@ -1,0 +1,161 @@
+"""GPU parity of the grouped GEMM over permuted rows (moe_grouped_gemm_bf16).
+
+Reference: the oracle's per-expert double-precision sum of products rounded
+once to bf16.  The kernel accumulates in fp32 on the matrix cores, in an order
+of its own, then rounds once, so the bar is
+    |gpu - ref| <= 2^-7 |ref| + k * 2^-22 * sum_i |x_i w_i|
+(two bf16 roundings of half an ulp each, plus four times the worst-case fp32
+accumulation error k * 2^-24 of a k-term sum).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from _parity import POISON, gpu_permute, gpu_unpermute, oracle_permute, poisoned, to_np
+from mixture_experts_token_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print("[case] " + msg, flush=True)
+
+
+def _bf16(t):
+    return t.to(torch.bfloat16)
+
+
+def _f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_gemm_close(got_bits, ref_bits, x_bits, w_bits, off):
+    got, ref = _f64(got_bits), _f64(ref_bits)
+    xa, wa = np.abs(_f64(x_bits)), np.abs(_f64(w_bits))
+    k = x_bits.shape[1]
+    for e in range(w_bits.shape[0]):
+        seg = slice(int(off[e]), int(off[e + 1]))
+        if off[e + 1] == off[e]:
+            continue
+        mag = xa[seg] @ wa[e].T
+        tol = 2.0**-7 * np.abs(ref[seg]) + k * 2.0**-22 * mag + 1e-30
+        err = np.abs(got[seg] - ref[seg])
+        if not np.all(err <= tol):
+            i = np.unravel_index(np.argmax(err - tol), err.shape)
+            raise AssertionError("expert %d row %d col %d: got %g want %g (tol %g)" % (
+                e, seg.start + i[0], i[1], got[seg][i], ref[seg][i], tol[i]))
+
+
+def _offsets(rng, e, rows, mode):
+    if mode == "even":
+        counts = np.full(e, rows // e)
+        counts[: rows % e] += 1
+    elif mode == "skewed":
+        p = 1.0 / np.arange(1, e + 1) ** 1.2
+        counts = rng.multinomial(rows, p / p.sum())
+        counts[1] += counts[e // 2]  # one empty expert in the middle
+        counts[e // 2] = 0
+    else:  # one expert only
+        counts = np.zeros(e, int)
+        counts[e - 1] = rows
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+
+
+CASES = [
+    # (experts, rows, n, k, offsets mode)
+    (1, 1, 128, 64, "even"),
+    (4, 130, 128, 64, "even"),          # ragged last row tile
+    (8, 1000, 256, 512, "skewed"),      # empty expert, several row / column tiles and k steps
+    (16, 700, 384, 192, "skewed"),
+    (5, 300, 128, 1024, "one"),
+    (3, 2, 640, 128, "even"),           # fewer rows than experts
+]
+
+
+@pytest.mark.parametrize("e,rows,n,k,mode", CASES, ids=["-".join(map(str, c)) for c in CASES])
+def test_grouped_gemm_parity(hip_device, e, rows, n, k, mode):
+    rng = np.random.default_rng(rows + n + k)
+    off = _offsets(rng, e, rows, mode)
+    g = torch.Generator().manual_seed(rows * 3 + k)
+    x = _bf16(torch.randn((rows, k), generator=g))
+    w = _bf16(torch.randn((e, n, k), generator=g) * k**-0.5)
+    spare = 37  # rows past off[E] must stay untouched
+    xs = torch.cat([x, _bf16(torch.randn((spare, k), generator=g))]).to(hip_device)
+    y = poisoned((rows + spare, n), torch.bfloat16, hip_device)
+    _say("grouped gemm E=%d rows=%d n=%d k=%d %s" % (e, rows, n, k, mode))
+    binding.moe_grouped_gemm_bf16(xs, w.to(hip_device), torch.from_numpy(off).to(hip_device), y)
+    torch.cuda.synchronize()
+    got = to_np(y)
+    ref = oracle.grouped_gemm_bf16(to_np(x), to_np(w), off)
+    assert_gemm_close(got[:rows], ref, to_np(x), to_np(w), off)
+    assert np.all(got[rows:].view(np.uint8) == POISON)
+
+
+def test_grouped_gemm_rejected_offsets_write_nothing(hip_device):
+    x = _bf16(torch.randn((64, 128))).to(hip_device)
+    w = _bf16(torch.randn((2, 128, 128))).to(hip_device)
+    for bad in ([-1, -1, -1], [0, 40, 30], [0, 10, 65], [3, 10, 20]):
+        y = poisoned((64, 128), torch.bfloat16, hip_device)
+        _say("grouped gemm bad offsets %s" % bad)
+        binding.moe_grouped_gemm_bf16(x, w, torch.tensor(bad, dtype=torch.int64, device=hip_device), y)
+        torch.cuda.synchronize()
+        assert np.all(to_np(y).view(np.uint8) == POISON)
+
+
+def test_moe_layer_permute_gemm_unpermute(hip_device):
+    """The three steps chained on the device (permute -> grouped GEMM -> unpermute)
+    against the oracle chain: permuted rows and offsets bit-exact, expert output
+    within the GEMM bar, final output within the unpermute bar."""
+    w8 = W.WORKLOADS["mixtral"].with_tokens(512)
+    inp = W.make_all(w8, seed=3, device="cpu")
+    e, k, n = w8.num_experts, w8.hidden_size, 256
+    g = torch.Generator().manual_seed(5)
+    wts = _bf16(torch.randn((e, n, k), generator=g) * k**-0.5)
+    ids, x = inp["topk_ids"].to(hip_device), inp["hidden_states"].to(hip_device)
+    _say("moe layer N=%d k=%d n=%d" % (w8.num_tokens, k, n))
+    outs = gpu_permute(x, ids, e)
+    y = poisoned((w8.num_rows, n), torch.bfloat16, hip_device)
+    binding.moe_grouped_gemm_bf16(outs["permuted_hidden_states"], wts.to(hip_device),
+                                  outs["expert_first_token_offset"], y)
+    out = gpu_unpermute(y, inp["topk_weights"].to(hip_device), outs["inv_permuted_idx"])
+    torch.cuda.synchronize()
+    ref_p = oracle_permute(x, ids, e)
+    np.testing.assert_array_equal(to_np(outs["permuted_hidden_states"]), ref_p["permuted_hidden_states"])
+    ref_y = oracle.grouped_gemm_bf16(ref_p["permuted_hidden_states"], to_np(wts), ref_p["expert_first_token_offset"])
+    assert_gemm_close(to_np(y), ref_y, ref_p["permuted_hidden_states"], to_np(wts), ref_p["expert_first_token_offset"])
+    # unpermute of the GPU's own expert output against the oracle's unpermute of it
+    ref_out = oracle.unpermute(to_np(y), to_np(inp["topk_weights"]), ref_p["inv_permuted_idx"], "bf16")
+    got = _f64(to_np(out))
+    want = _f64(ref_out)
+    assert np.all(np.abs(got - want) <= 2.0**-7 * np.maximum(1.0, np.abs(want)))
+
+
+@pytest.mark.parametrize("name,n", [("qwen3", 1536), ("dsv3", 4096)])
+def test_grouped_gemm_full_size_sampled_rows(hip_device, name, n):
+    """Model-shaped routing at full size: every row computed on the GPU, a
+    sample of rows (one expert each) recomputed by the oracle."""
+    w8 = W.WORKLOADS[name]
+    ids_np, _ = W.make_routing(w8, seed=0)
+    e, k = w8.num_experts, w8.hidden_size
+    counts = np.bincount(ids_np.reshape(-1), minlength=e)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    rows = int(off[-1])
+    gen = torch.Generator(device=hip_device).manual_seed(9)
+    x = torch.randn((rows, k), device=hip_device, generator=gen).to(torch.bfloat16)
+    wts = (torch.randn((e, n, k), device=hip_device, generator=gen) * k**-0.5).to(torch.bfloat16)
+    y = poisoned((rows, n), torch.bfloat16, hip_device)
+    _say("grouped gemm full %s rows=%d n=%d k=%d" % (name, rows, n, k))
+    binding.moe_grouped_gemm_bf16(x, wts, torch.from_numpy(off).to(hip_device), y)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, 120, replace=False),
+                                       off[1:-1][counts[1:] > 0][:20]]))
+    expert_of = np.searchsorted(off, sample, side="right") - 1
+    for j, ex in zip(sample, expert_of):
+        xr = to_np(x[int(j):int(j) + 1])
+        wr = to_np(wts[int(ex):int(ex) + 1])
+        ref = oracle.grouped_gemm_bf16(xr, wr, np.array([0, 1], np.int64))
+        assert_gemm_close(to_np(y[int(j):int(j) + 1]), ref, xr, wr, np.array([0, 1], np.int64))
