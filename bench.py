@@ -126,6 +126,75 @@ def load_probe():
     return lib
 
 
+# Output width of the expert GEMM per workload: the gate and up projections of
+# the expert MLP side by side (2 x the expert intermediate size).
+GEMM_N = {"tiny": 256, "mixtral": 2 * 14336, "qwen3": 2 * 768, "dsv3": 2 * 2048, "decode": 2 * 2048}
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_gemm(args, w, ids_np, dev) -> int:
+    """One line for the grouped GEMM over the permuted rows (moe_grouped_gemm_bf16)."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_token_amd import binding
+
+    n, k, e = args.gemm_n or GEMM_N[w.name], w.hidden_size, w.num_experts
+    counts = np.bincount(ids_np.reshape(-1), minlength=e)
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)).to(dev)
+    rows = int(counts.sum())
+    gen = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn((rows, k), device=dev, generator=gen).to(torch.bfloat16)
+    wts = (torch.randn((e, n, k), device=dev, generator=gen) * k**-0.5).to(torch.bfloat16)
+    y = torch.empty((rows, n), dtype=torch.bfloat16, device=dev)
+    flops = 2.0 * rows * n * k
+    used = int((counts > 0).sum())
+    nbytes = rows * k * 2 + used * n * k * 2 + rows * n * 2  # rows, weights of experts with rows, output
+    for _ in range(args.warmup):
+        binding.moe_grouped_gemm_bf16(x, wts, off, y)
+    torch.cuda.synchronize(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        binding.moe_grouped_gemm_bf16(x, wts, off, y)
+    end.record()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    us = start.elapsed_time(end) * 1e3 / args.steps
+    tflops = flops / (us * 1e-6) / 1e12
+    traffic, kernels = load_traffic("%s_gemm" % w.name, "gemm")
+    # The bound is the roof the shape hits first: below the ridge point
+    # (peak FLOP/s over peak bytes/s) the weights' HBM traffic limits it.
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    if flops / nbytes >= ridge:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    line = {
+        "metric": "grouped GEMM over permuted rows, achieved TFLOP/s (bf16 in, fp32 accumulate)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name + "_expert_gemm", "rows": rows, "n": n, "k": k, "num_experts": e,
+                   "experts_with_rows": used, "routing": w.routing, "parallelism": "single GPU"},
+        "us_per_call": round(us, 3), "flops_per_call": flops, "algorithmic_bytes_per_call": nbytes,
+        "hbm_GBps_at_algorithmic_bytes": round(gbps, 1),
+        "arithmetic_intensity_flop_per_byte": round(flops / nbytes, 1),
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": dict(roof, traffic=traffic,
+                         kernel=" + ".join(kernels) if kernels else "grouped_gemm_bf16_kernel",
+                         algorithmic_flops_per_launch=flops, algorithmic_bytes_per_launch=nbytes,
+                         avg_launch_us=round(us, 3)),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def cpu_baseline(inputs_host, w, budget_s: float = 10.0, max_reps: int = 50, local=None, emap=None) -> dict:
     """The CPU oracle (single thread) on full steps of the workload until ~budget_s."""
     import oracle
@@ -169,6 +238,9 @@ def main() -> int:
                     help="fp8: the permute quantises bf16 rows to E4M3FN codes + scales on the way "
                          "(moe_permute_quant_fp8)")
     ap.add_argument("--group", type=int, default=0, help="quantisation group size in elements (0: per token)")
+    ap.add_argument("--gemm", action="store_true",
+                    help="time the grouped GEMM over the permuted rows instead (moe_grouped_gemm_bf16)")
+    ap.add_argument("--gemm-n", type=int, default=0, help="GEMM output width (default: 2 x expert intermediate)")
     ap.add_argument("--ids", default="int32", choices=["int32", "int64"],
                     help="expert id type handed to the permute (int64 is read directly, no cast pass)")
     args = ap.parse_args()
@@ -191,6 +263,8 @@ def main() -> int:
     if args.tokens:
         w = w.with_tokens(args.tokens)
     ids_np, wts_np = W.make_routing(w, seed=0)
+    if args.gemm:
+        return bench_gemm(args, w, ids_np, dev)
     local, emap_np, emap, n_off = None, None, None, w.num_experts + 1
     if args.ep > 1:
         emap_np, n_local = W.expert_map_for(w.num_experts, args.ep, args.ep_rank, args.ep_layout)
