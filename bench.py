@@ -81,12 +81,19 @@ def algorithmic_bytes(w, local=None, id_bytes: int = 4, quant_groups: int = 0) -
     return {"permute": permute, "unpermute": unpermute, "total": permute + unpermute}
 
 
-def kernel_source_digest() -> str:
-    """SHA-256 over the permute library's sources (what the counters were taken on)."""
-    from mixture_experts_token_amd import build_lib
+# Sources whose kernels a counter summary measured: a summary stays valid while
+# these files are unchanged.
+DIGEST_FILES = {
+    "permute": ["moe_permute_kernels.hip", "moe_launch.h", "moe_plan.h"],
+    "unpermute": ["moe_permute_kernels.hip", "moe_launch.h", "moe_plan.h"],
+    "gemm": ["moe_gemm_kernels.hip", "moe_launch.h", "moe_plan.h"],
+}
 
+
+def kernel_source_digest(op: str = "permute") -> str:
+    """SHA-256 over the sources of `op`'s kernels (what the counters were taken on)."""
     h = hashlib.sha256()
-    for name in sorted(build_lib.SOURCES + build_lib.HEADERS):
+    for name in sorted(DIGEST_FILES[op]):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -106,7 +113,7 @@ def load_traffic(workload: str, op: str):
     if not entry:
         return None, None
     kernels = entry.get("kernels")
-    if rec.get("kernel_source_sha256") != kernel_source_digest():
+    if rec.get("kernel_source_sha256") != kernel_source_digest(op):
         return None, kernels
     return entry.get("hbm_bytes_per_call"), kernels
 
@@ -124,6 +131,19 @@ def load_probe():
                        ctypes.c_void_p]
         fn.restype = ctypes.c_int
     return lib
+
+
+def copy_calibration(mib: int, dev) -> None:
+    """A plain elementwise copy kernel (negation) over a fresh mib-MiB float32
+    buffer, 5 times: its known traffic scales the rocprofv3 byte counters."""
+    import torch
+
+    src = torch.ones((mib << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize(dev)
+    del src, dst
 
 
 # Output width of the expert GEMM per workload: the gate and up projections of
@@ -147,6 +167,8 @@ def bench_gemm(args, w, ids_np, dev) -> int:
     x = torch.randn((rows, k), device=dev, generator=gen).to(torch.bfloat16)
     wts = (torch.randn((e, n, k), device=dev, generator=gen) * k**-0.5).to(torch.bfloat16)
     y = torch.empty((rows, n), dtype=torch.bfloat16, device=dev)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, dev)
     flops = 2.0 * rows * n * k
     used = int((counts > 0).sum())
     nbytes = rows * k * 2 + used * n * k * 2 + rows * n * 2  # rows, weights of experts with rows, output
@@ -354,12 +376,7 @@ def main() -> int:
         return start.elapsed_time(end) * 1e3 / k, time.perf_counter() - t0
 
     if args.copy_calibration:
-        src = torch.ones((args.copy_calibration << 20) // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize(dev)
-        del src, dst
+        copy_calibration(args.copy_calibration, dev)
 
     for i in range(args.warmup):
         s = sets[i % nsets]
