@@ -8,14 +8,14 @@
 // with bf16 x and w, fp32 accumulation (MFMA), rounded once to bf16.
 //
 // Design:
-//   * tiles of 128 rows x 256 output columns (128 x 128 when n is not a
-//     multiple of 256); a workgroup of 4 waves, each wave a quadrant of 32 x 32
-//     v_mfma_f32_32x32x16_bf16 tiles; k advances 64 at a time;
-//   * both operands are "row, 8 consecutive k" fragments, staged in LDS with a
-//     row pitch of 72 elements (144 bytes) so the 16-byte fragment reads of 32
-//     consecutive rows fall in different banks; two LDS stages: while a step
-//     computes, the next step's rows go from registers into the other stage and
-//     the loads of the step after are in flight (one barrier per step);
+//   * tiles of 128 rows x 128 output columns; a workgroup of 4 waves, each
+//     wave a 64 x 64 quadrant of 2 x 2 v_mfma_f32_32x32x16_bf16 tiles; k
+//     advances 64 at a time;
+//   * both operands go from global memory straight into LDS (global_load_lds,
+//     16 bytes per lane), 128-byte rows with the 16-byte k-vectors of row r
+//     stored in slot (kvec ^ r % 8), so the fragment reads of 32 consecutive
+//     rows hit every bank once; two LDS stages: while a step computes from one,
+//     the next step's loads fill the other (one barrier per step);
 //   * the tile list lives on the device: the offsets come from the permute, so
 //     every workgroup derives the per-expert tile counts from them (prefix in
 //     LDS) and walks tiles persistently.  Order: per expert, groups of 8 row
