@@ -242,7 +242,7 @@ moe_status_t moe_permute_quant_fp8(const void *hidden_states, int32_t dtype, con
  *                     permute wrote it (the row counts are never read by the host)
  *   num_experts       1 .. MOE_MAX_EXPERTS
  *   max_rows          rows x and y hold; off[num_experts] must not exceed it
- *   n, k              n a multiple of 128, k a multiple of 64
+ *   n, k              n a multiple of 128, k a multiple of 64 and at most 2^20
  *   y                 [max_rows, n] bf16 (out); rows >= off[num_experts] untouched
  *
  * Offsets that are not a valid prefix (off[0] != 0, a decreasing entry, the

@@ -8,14 +8,22 @@
 // with bf16 x and w, fp32 accumulation (MFMA), rounded once to bf16.
 //
 // Design:
-//   * tiles of 128 rows x 128 output columns; a workgroup of 4 waves, each
-//     wave a 64 x 64 quadrant of 2 x 2 v_mfma_f32_32x32x16_bf16 tiles; k
-//     advances 64 at a time;
-//   * both operands go from global memory straight into LDS (global_load_lds,
-//     16 bytes per lane), 128-byte rows with the 16-byte k-vectors of row r
-//     stored in slot (kvec ^ r % 8), so the fragment reads of 32 consecutive
-//     rows hit every bank once; two LDS stages: while a step computes from one,
-//     the next step's loads fill the other (one barrier per step);
+//   * output tiles of 128 rows x 256 columns, a workgroup of 8 waves, each
+//     wave a 64 x 64 block of 2 x 2 v_mfma_f32_32x32x16_bf16 tiles, three LDS
+//     stages (one workgroup per CU); 128 x 128 tiles of 4 waves, two stages,
+//     two workgroups per CU when n is not a multiple of 256; k advances 64
+//     per step;
+//   * both operands go from global memory straight into LDS (16 bytes per
+//     lane, no register round trip), 128-byte rows with the 16-byte k-vectors
+//     of row r stored in slot (kvec ^ r % 8), so the fragment reads of 32
+//     consecutive rows hit every bank once; the wide tiles load through buffer
+//     resources (one lane offset register per operand, row group and k step
+//     in the scalar offset) and spread a step's loads over its four 16-wide k
+//     slices instead of issuing them all after the barrier;
+//   * the pipeline's waits are explicit: before step ks each wave waits only
+//     for its own loads of step ks (those of ks + 1 stay in flight), then one
+//     barrier; fragment reads are explicit ds_read_b128 so the compiler adds
+//     no wait for loads still landing in other stages;
 //   * the tile list lives on the device: the offsets come from the permute, so
 //     every workgroup derives the per-expert tile counts from them (prefix in
 //     LDS) and walks tiles persistently.  Order: per expert, groups of 8 row
@@ -28,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "moe_launch.h"
 #include "moe_plan.h"
@@ -41,14 +50,67 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64;
-constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8;             // row tiles per group in the tile order
 constexpr int kXcds = 8;
+
+// Tile shape: BM x BN outputs per workgroup of WM x WN waves, each wave a
+// (BM/WM) x (BN/WN) block of 32 x 32 MFMA tiles; STAGES LDS buffers per
+// operand; PER_CU workgroups resident per compute unit (registers and LDS are
+// budgeted for that many).  FAST: loads through buffer resources spread over
+// the k slices, fragment reads as explicit ds_read_b128 (lds_read); otherwise
+// global_load_lds issued together after the barrier and fragment reads left
+// to the compiler.
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int PER_CU_, bool FAST_>
+struct GemmShape {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_, PER_CU = PER_CU_;
+    static constexpr bool FAST = FAST_;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
+    static constexpr int MT = kWaveM / 32, NT = kWaveN / 32;
+    // direct-to-LDS instructions per wave per k-step (8 rows of 128 bytes each)
+    static constexpr int kLoadsPerStep = (BM + BN) / kWaves / 8;
+    static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile is whole 32 x 32 MFMA tiles");
+    static_assert(BM % (kWaves * 8) == 0 && BN % (kWaves * 8) == 0, "every wave loads whole 8-row groups");
+    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS stages");
+    // compiler-scheduled fragment reads would wait for every load in flight
+    static_assert(FAST || STAGES == 2, "a third stage needs the explicit fragment reads");
+    static_assert(kLoadsPerStep <= 31, "vector-memory count of one step fits the wait immediate");
+    static constexpr int kLdsBytes = STAGES * (BM + BN) * kBK * 2;
+    static_assert(kLdsBytes * PER_CU <= 150 * 1024, "stages of every resident workgroup fit the 160 KiB LDS");
+};
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
     const uint32_t u = __float_as_uint(f);
     if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Wait until at most `n` of this wave's vector-memory operations are
+// outstanding (they retire in issue order), leaving the LDS and export
+// counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the k-step pipeline: this wave's LDS reads are
+// complete (lgkmcnt) before it arrives, and no memory access is moved across
+// it.  Written as one asm statement because the compiler's own release fence
+// would also wait for every direct-to-LDS load in flight (vmcnt(0)), which is
+// exactly the overlap the pipeline exists for; the direct-to-LDS loads a step
+// needs are waited for explicitly (wait_vmem) before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A value every lane of the wave holds, moved into a scalar register (the
+// compiler cannot prove uniformity of values read from LDS).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 struct TileCoord {
@@ -78,31 +140,45 @@ __device__ __forceinline__ TileCoord tile_coord(int64_t id, const int64_t* __res
     const int64_t nt = r / gsize;
     const int64_t mi = g * kGroupM + (r - nt * gsize);
     TileCoord c;
-    c.expert = e;
-    c.row0 = off[e] + mi * BM;
-    c.rows = cnt - mi * BM < BM ? cnt - mi * BM : BM;
-    c.col0 = nt * BN;
+    c.expert = __builtin_amdgcn_readfirstlane(e);
+    c.row0 = uniform64(off[e] + mi * BM);
+    c.rows = uniform64(cnt - mi * BM < BM ? cnt - mi * BM : BM);
+    c.col0 = uniform64(nt * BN);
     return c;
 }
 
-// One k-step of one operand tile (ROWS rows x 64 bf16 = 128 bytes per row)
-// loaded straight from global memory into LDS: wave w fills rows
-// [w*ROWS/4, (w+1)*ROWS/4), one 1 KiB instruction (8 rows) at a time; lane L
-// of an instruction writes slot L % 8 of row L / 8, and reads the row's
-// k-vector (L % 8) ^ (row % 8) -- the XOR swizzle that keeps the fragment
-// reads of 32 consecutive rows free of bank conflicts.
-template <int ROWS>
-__device__ __forceinline__ void tile_to_lds(__bf16* lds, const u32x4* __restrict__ src_row0, int64_t row_stride_vecs,
-                                            int rows_valid, int64_t kvec0, int wave, int lane) {
-    constexpr int kPerWave = ROWS / 4 / 8;  // instructions per wave
-#pragma unroll
-    for (int j = 0; j < kPerWave; ++j) {
-        const int row = wave * (ROWS / 4) + j * 8 + lane / 8;
-        const int slot = lane % 8;
-        const int srow = row < rows_valid ? row : rows_valid - 1;  // clamp: a valid row, result unused
-        const u32x4* g = src_row0 + (int64_t)srow * row_stride_vecs + kvec0 + (slot ^ (row % 8));
-        __builtin_amdgcn_global_load_lds(g, lds + (wave * (ROWS / 4) + j * 8) * kBK, 16, 0, 0);
+// Operand tiles (ROWS rows x 64 bf16 = 128 bytes per row per k-step) go from
+// global memory straight into LDS, one 1 KiB instruction (8 rows) at a time:
+// lane L of an instruction writes slot L % 8 of row L / 8 of its group and
+// reads that row's k-vector (L % 8) ^ (row % 8) -- the XOR swizzle that keeps
+// the fragment reads of 32 consecutive rows free of bank conflicts.
+// One 8-row group: `row` is this lane's row (group start + L / 8), `srow` the
+// row it reads (clamped into the valid rows), `lds_group` the group's LDS rows.
+__device__ __forceinline__ void group_to_lds(__bf16* lds_group, const u32x4* __restrict__ src_row0,
+                                             int64_t row_stride_vecs, int row, int srow, int64_t kvec0, int lane) {
+    const u32x4* g = src_row0 + (int64_t)srow * row_stride_vecs + kvec0 + ((lane % 8) ^ (row % 8));
+    __builtin_amdgcn_global_load_lds(g, lds_group, 16, 0, 0);
+}
+
+// One 8-row group of the same load through a buffer resource whose base is
+// the tile's first row: lane L reads row L / 8 of the group, k-vector
+// (L % 8) ^ (L / 8) (groups are 8-aligned, so row % 8 = L / 8); the group row
+// and the k step go into the scalar offset.  With kClamp, rows past
+// rows_valid re-read the last valid row (the group start is clamped too, so
+// the lane offset never goes negative): every step issues the same number of
+// loads, which the vector-memory waits count on.
+template <bool kClamp>
+__device__ __forceinline__ void group_to_lds_buf(__bf16* lds_group, __amdgpu_buffer_rsrc_t rsrc, int stride_bytes,
+                                                 int grow, int rows_valid, int step, int lane) {
+    const int chunk = ((lane % 8) ^ (lane / 8)) * 16;
+    int g0 = grow, r = lane / 8;
+    if (kClamp) {
+        g0 = grow < rows_valid ? grow : rows_valid - 1;
+        r = (grow + r < rows_valid ? grow + r : rows_valid - 1) - g0;
     }
+    const int soffset = __builtin_amdgcn_readfirstlane(g0 * stride_bytes + step * (kBK * 2));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_group, 16,
+                                             r * stride_bytes + chunk, soffset, 0, 0);
 }
 
 // Fragment of 8 consecutive k (k-vector kvec) of tile row `row`.
@@ -110,44 +186,82 @@ __device__ __forceinline__ bf16x8 lds_frag(const __bf16* lds, int row, int kvec)
     return *reinterpret_cast<const bf16x8*>(lds + row * kBK + ((kvec ^ (row % 8)) * 8));
 }
 
-// BM x BN output tile per workgroup of 4 waves (2 x 2), each wave
-// (BM/2) x (BN/2) = MT x NT tiles of 32 x 32.  The MFMA takes the weight
-// fragment as its first operand and the row fragment as its second, so a
-// lane's 16 results are 4 runs of 4 consecutive output columns of one row
-// (8-byte stores in the epilogue).
-template <int BM, int BN>
-__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
+// The same fragment read with an explicit ds_read_b128.  The compiler does not
+// see this as an LDS read, so it adds no wait for direct-to-LDS loads still in
+// flight into other stages (it cannot tell the stages apart and would wait for
+// all of them); the caller orders the read after the barrier that publishes
+// its stage and waits for it with lds_wait before using the result.
+__device__ __forceinline__ u32x4 lds_read(const __bf16* lds, int row, int kvec) {
+    const __bf16* p = lds + row * kBK + ((kvec ^ (row % 8)) * 8);
+    // A generic address of LDS memory holds the LDS byte offset in its low 32 bits.
+    const uint32_t addr = (uint32_t)(uintptr_t)p;
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+// Wait for every lds_read issued so far; `f` then carries a dependency on the
+// wait, so no use of it is scheduled before it.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4 (&f)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
+}
+
+template <int I>
+using Int = std::integral_constant<int, I>;
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(Int<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Persistent grouped GEMM.  The MFMA takes the weight fragment as its first
+// operand and the row fragment as its second, so a lane's 16 results are 4
+// runs of 4 consecutive output columns of one row (8-byte stores in the
+// epilogue).
+template <typename S>
+__global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kernel(
     const u32x4* __restrict__ x, const u32x4* __restrict__ w, const int64_t* __restrict__ off,
     uint16_t* __restrict__ y, int num_experts, int64_t max_rows, int64_t n, int64_t k) {
-    constexpr int MT = BM / 64, NT = BN / 64;  // 32 x 32 tiles per wave along m and n
-    // Two stages per operand, each its own LDS object, so the compiler's wait
-    // tracking can tell a stage being filled from the one being read.
+    constexpr int BM = S::BM, BN = S::BN, MT = S::MT, NT = S::NT, STAGES = S::STAGES;
+    constexpr int kThreads = S::kThreads;
+    // Each stage of each operand is its own LDS object, so the compiler's
+    // wait tracking can tell a stage being filled from the ones being read.
+    constexpr int kA2 = STAGES > 2 ? BM * kBK : 8, kB2 = STAGES > 2 ? BN * kBK : 8;
     __shared__ __attribute__((aligned(1024))) __bf16 a_s0[BM * kBK];
     __shared__ __attribute__((aligned(1024))) __bf16 a_s1[BM * kBK];
+    __shared__ __attribute__((aligned(1024))) __bf16 a_s2[kA2];
     __shared__ __attribute__((aligned(1024))) __bf16 b_s0[BN * kBK];
     __shared__ __attribute__((aligned(1024))) __bf16 b_s1[BN * kBK];
+    __shared__ __attribute__((aligned(1024))) __bf16 b_s2[kB2];
     __shared__ int64_t tile_pre[kMaxExperts + 1];
-    __shared__ int64_t part[kGemmThreads];
+    __shared__ int64_t part[kThreads];
     __shared__ int bad_s;
 
     const int tid = threadIdx.x;
     const int lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int wm = wave / 2, wn = wave % 2;  // this wave's quadrant
+    const int wm = wave / S::WN, wn = wave % S::WN;  // this wave's block of the tile
     const int64_t n_tiles = n / BN;
-    const int64_t kv = k / 8;                // 16-byte vectors per row of x / w
+    const int64_t kv = k / 8;                        // 16-byte vectors per row of x / w
+    const int stride_bytes = (int)(k * 2);           // k <= 2^20 (checked on the host)
 
     // The stages are written only by direct-to-LDS loads, which the compiler
     // does not see as stores: one visible store keeps their reads from being
     // folded away as reads of never-written memory.
     if (tid == 0) {
-        a_s0[0] = a_s1[0] = b_s0[0] = b_s1[0] = (__bf16)0.0f;
+        a_s0[0] = a_s1[0] = a_s2[0] = b_s0[0] = b_s1[0] = b_s2[0] = (__bf16)0.0f;
     }
 
     // Tile counts per expert and their prefix (each thread takes kPer
     // consecutive experts; a scan over the threads in LDS), and a check of the
     // offsets (the permute writes -1 everywhere when it rejected an id).
-    constexpr int kPer = (kMaxExperts + kGemmThreads - 1) / kGemmThreads;
+    constexpr int kPer = (kMaxExperts + kThreads - 1) / kThreads;
     int64_t cnt_t[kPer];
     int64_t s = 0;
     int bad = 0;
@@ -167,7 +281,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
     part[tid] = s;
     __syncthreads();
     if (bad) atomicOr(&bad_s, 1);
-    for (int d = 1; d < kGemmThreads; d <<= 1) {
+    for (int d = 1; d < kThreads; d <<= 1) {
         const int64_t v = tid >= d ? part[tid - d] : 0;
         __syncthreads();
         part[tid] += v;
@@ -180,10 +294,21 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
         if (e < num_experts) tile_pre[e] = excl;
         excl += cnt_t[q];
     }
-    if (tid == 0) tile_pre[num_experts] = part[kGemmThreads - 1];
+    if (tid == 0) tile_pre[num_experts] = part[kThreads - 1];
     __syncthreads();
     if (bad_s) return;
     const int64_t total = tile_pre[num_experts];
+
+    auto stage_a = [&](auto st) __attribute__((always_inline)) -> __bf16* {
+        if constexpr (decltype(st)::value == 0) return a_s0;
+        else if constexpr (decltype(st)::value == 1) return a_s1;
+        else return a_s2;
+    };
+    auto stage_b = [&](auto st) __attribute__((always_inline)) -> __bf16* {
+        if constexpr (decltype(st)::value == 0) return b_s0;
+        else if constexpr (decltype(st)::value == 1) return b_s1;
+        else return b_s2;
+    };
 
     // Persistent walk: iteration i covers tiles [i*G, (i+1)*G), G = gridDim.x;
     // XCD x (blocks b with b % 8 == x) takes the contiguous chunk x*G/8 ...
@@ -204,19 +329,68 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
 #pragma unroll
             for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x16{};
 
-        auto load_step = [&](int64_t step, __bf16* as, __bf16* bs) {
-            tile_to_lds<BM>(as, xrow0, kv, rows_valid, step * (kBK / 8), wave, lane);
-            tile_to_lds<BN>(bs, wrow0, kv, BN, step * (kBK / 8), wave, lane);
+        // Buffer resources over the tile's rows (raw, 32-bit data format).
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)uniform64((int64_t)xrow0), 0, __builtin_amdgcn_readfirstlane(rows_valid * stride_bytes), 0x00020000);
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)uniform64((int64_t)wrow0), 0, __builtin_amdgcn_readfirstlane(BN * stride_bytes), 0x00020000);
+
+        // Load instructions I0 .. I1 - 1 of one k-step for this wave: its 8-row
+        // groups of the row tile first, then those of the weight tile.  Every
+        // step issues all kGA + kGB of them (clamped rows instead of skipped
+        // groups), which the vector-memory waits count on.
+        constexpr int kGA = BM / S::kWaves / 8, kGB = BN / S::kWaves / 8;
+        auto load_part = [&](int64_t step, auto st, auto i0, auto i1) __attribute__((always_inline)) {
+            static_for<decltype(i0)::value, decltype(i1)::value>([&](auto i) __attribute__((always_inline)) {
+                constexpr int ii = decltype(i)::value;
+                if constexpr (S::FAST) {
+                    if constexpr (ii < kGA) {
+                        const int grow = wave * (BM / S::kWaves) + ii * 8;
+                        group_to_lds_buf<true>(stage_a(st) + grow * kBK, xr, stride_bytes, grow, rows_valid, (int)step, lane);
+                    } else {
+                        const int grow = wave * (BN / S::kWaves) + (ii - kGA) * 8;
+                        group_to_lds_buf<false>(stage_b(st) + grow * kBK, wr, stride_bytes, grow, BN, (int)step, lane);
+                    }
+                } else {
+                    if constexpr (ii < kGA) {
+                        const int row = wave * (BM / S::kWaves) + ii * 8 + lane / 8;
+                        const int srow = row < rows_valid ? row : rows_valid - 1;  // clamp: a valid row, result unused
+                        group_to_lds(stage_a(st) + (row - lane / 8) * kBK, xrow0, kv, row, srow, step * (kBK / 8), lane);
+                    } else {
+                        const int row = wave * (BN / S::kWaves) + (ii - kGA) * 8 + lane / 8;
+                        group_to_lds(stage_b(st) + (row - lane / 8) * kBK, wrow0, kv, row, row, step * (kBK / 8), lane);
+                    }
+                }
+            });
         };
-        auto compute_step = [&](const __bf16* as, const __bf16* bs) {
+        // One k-step from stage st: four 16-wide k slices; hook(kk) runs
+        // before slice kk's MFMAs (it issues part of the next step's loads).
+        auto compute_step = [&](auto st, auto&& hook) __attribute__((always_inline)) {
+            const __bf16* as = stage_a(st);
+            const __bf16* bs = stage_b(st);
 #pragma unroll
             for (int kk = 0; kk < kBK / 16; ++kk) {
                 const int kvec = kk * 2 + lane / 32;
                 bf16x8 af[MT], bfr[NT];
+                if constexpr (S::FAST) {
+                    u32x4 fa[MT], fb[NT];
 #pragma unroll
-                for (int mi = 0; mi < MT; ++mi) af[mi] = lds_frag(as, wm * (BM / 2) + mi * 32 + lane % 32, kvec);
+                    for (int mi = 0; mi < MT; ++mi) fa[mi] = lds_read(as, wm * S::kWaveM + mi * 32 + lane % 32, kvec);
 #pragma unroll
-                for (int ni = 0; ni < NT; ++ni) bfr[ni] = lds_frag(bs, wn * (BN / 2) + ni * 32 + lane % 32, kvec);
+                    for (int ni = 0; ni < NT; ++ni) fb[ni] = lds_read(bs, wn * S::kWaveN + ni * 32 + lane % 32, kvec);
+                    lds_wait(fa);
+                    lds_wait(fb);
+#pragma unroll
+                    for (int mi = 0; mi < MT; ++mi) af[mi] = __builtin_bit_cast(bf16x8, fa[mi]);
+#pragma unroll
+                    for (int ni = 0; ni < NT; ++ni) bfr[ni] = __builtin_bit_cast(bf16x8, fb[ni]);
+                } else {
+#pragma unroll
+                    for (int mi = 0; mi < MT; ++mi) af[mi] = lds_frag(as, wm * S::kWaveM + mi * 32 + lane % 32, kvec);
+#pragma unroll
+                    for (int ni = 0; ni < NT; ++ni) bfr[ni] = lds_frag(bs, wn * S::kWaveN + ni * 32 + lane % 32, kvec);
+                }
+                hook(kk);
 #pragma unroll
                 for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
@@ -225,27 +399,52 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
             }
         };
 
-        // Step ks computes from stage ks % 2 while step ks + 1 loads into the
-        // other; one barrier per step (after it, step ks's data is visible and
-        // every wave is done reading the stage that step ks + 1 overwrites).
+        // Software pipeline over k-steps: step ks computes from stage
+        // ks % STAGES while the loads of the next STAGES - 1 steps are in
+        // flight.  Before step ks: this wave's loads of step ks have landed
+        // (the ones issued after them may not have), then one LDS barrier --
+        // after it every wave's step-ks data is in LDS and every wave is done
+        // reading the stage that step ks + STAGES - 1 refills.
         const int64_t ksteps = k / kBK;
-        __syncthreads();  // the previous tile is done with both stages
-        load_step(0, a_s0, b_s0);
+        lds_barrier();  // the previous tile is done with every stage
+        static_for<0, STAGES - 1>([&](auto st) __attribute__((always_inline)) {
+            if (decltype(st)::value < ksteps) load_part(decltype(st)::value, st, Int<0>{}, Int<kGA + kGB>{});
+        });
+        auto step = [&](int64_t ks, auto st) __attribute__((always_inline)) {
+            constexpr int kSt = decltype(st)::value;
+            if (STAGES == 3 && ks + 1 < ksteps) wait_vmem<(STAGES == 3 ? 1 : 0) * S::kLoadsPerStep>();
+            else wait_vmem<0>();
+            lds_barrier();
+            constexpr auto nst = Int<(kSt + STAGES - 1) % STAGES>{};
+            const int64_t nstep = ks + STAGES - 1;
+            if (nstep < ksteps) {
+                if constexpr (S::FAST) {
+                    // the next step's loads go out a quarter at a time, one
+                    // part before each k slice's MFMAs
+                    constexpr int n4 = kGA + kGB;
+                    compute_step(st, [&](int kk) __attribute__((always_inline)) {
+                        if (kk == 0) load_part(nstep, nst, Int<0>{}, Int<n4 / 4>{});
+                        else if (kk == 1) load_part(nstep, nst, Int<n4 / 4>{}, Int<n4 / 2>{});
+                        else if (kk == 2) load_part(nstep, nst, Int<n4 / 2>{}, Int<3 * n4 / 4>{});
+                        else load_part(nstep, nst, Int<3 * n4 / 4>{}, Int<n4>{});
+                    });
+                } else {
+                    load_part(nstep, nst, Int<0>{}, Int<kGA + kGB>{});
+                    __builtin_amdgcn_sched_barrier(0);  // the loads go out before this step's LDS reads
+                    compute_step(st, [](int) __attribute__((always_inline)) {});
+                }
+            } else {
+                compute_step(st, [](int) __attribute__((always_inline)) {});
+            }
+        };
+        // Whole rounds of STAGES steps, then the last ksteps % STAGES steps
+        // (stages 0, 1, ... again): the accumulators see no branch inside a round.
         int64_t ks = 0;
-        for (; ks + 1 < ksteps; ks += 2) {  // steps ks (stage 0) and ks + 1 (stage 1)
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of step ks have landed
-            __syncthreads();
-            load_step(ks + 1, a_s1, b_s1);
-            compute_step(a_s0, b_s0);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (ks + 2 < ksteps) load_step(ks + 2, a_s0, b_s0);
-            compute_step(a_s1, b_s1);
-        }
-        if (ks < ksteps) {  // an odd last step, in stage 0
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            compute_step(a_s0, b_s0);
+        for (; ks + STAGES <= ksteps; ks += STAGES)
+            static_for<0, STAGES>([&](auto st) __attribute__((always_inline)) { step(ks + decltype(st)::value, st); });
+        if (ks < ksteps) step(ks, Int<0>{});
+        if constexpr (STAGES == 3) {
+            if (ks + 1 < ksteps) step(ks + 1, Int<1>{});
         }
 
         // Epilogue: for the 32 x 32 tile (weight rows n, x rows m), lane l,
@@ -253,14 +452,14 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
         // registers 4j .. 4j+3 are four consecutive output columns of row m.
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
-            const int row = wm * (BM / 2) + mi * 32 + lane % 32;
+            const int row = wm * S::kWaveM + mi * 32 + lane % 32;
             if (row >= tc.rows) continue;
             uint16_t* yrow = y + (tc.row0 + row) * n;
 #pragma unroll
             for (int ni = 0; ni < NT; ++ni) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int64_t col = tc.col0 + wn * (BN / 2) + ni * 32 + (lane / 32) * 4 + j * 8;
+                    const int64_t col = tc.col0 + wn * S::kWaveN + ni * 32 + (lane / 32) * 4 + j * 8;
                     const uint32_t lo = bf16_bits_rne(acc[mi][ni][4 * j]) | (bf16_bits_rne(acc[mi][ni][4 * j + 1]) << 16);
                     const uint32_t hi =
                         bf16_bits_rne(acc[mi][ni][4 * j + 2]) | (bf16_bits_rne(acc[mi][ni][4 * j + 3]) << 16);
@@ -271,16 +470,12 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
     }
 }
 
-}  // namespace
-
-namespace {
-
-template <int BM, int BN>
-hipError_t launch_gemm_tiles(const GemmArgs& a, int num_cus, int per_cu, hipStream_t stream) {
-    // Persistent grid: per_cu workgroups per compute unit, a multiple of the XCD count.
-    int64_t blocks = (int64_t)num_cus * per_cu;
+template <typename S>
+hipError_t launch_gemm_tiles(const GemmArgs& a, int num_cus, hipStream_t stream) {
+    // Persistent grid: PER_CU workgroups per compute unit, a multiple of the XCD count.
+    int64_t blocks = (int64_t)num_cus * S::PER_CU;
     blocks = blocks < kXcds ? kXcds : blocks / kXcds * kXcds;
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN>), dim3((unsigned)blocks), dim3(kGemmThreads), 0, stream,
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<S>), dim3((unsigned)blocks), dim3(S::kThreads), 0, stream,
                        reinterpret_cast<const u32x4*>(a.x), reinterpret_cast<const u32x4*>(a.w), a.offsets,
                        reinterpret_cast<uint16_t*>(a.y), a.num_experts, a.max_rows, a.n, a.k);
     return hipGetLastError();
@@ -289,7 +484,8 @@ hipError_t launch_gemm_tiles(const GemmArgs& a, int num_cus, int per_cu, hipStre
 }  // namespace
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, int num_cus, hipStream_t stream) {
-    return launch_gemm_tiles<128, 128>(a, num_cus, 2, stream);
+    if (a.n % 256 == 0) return launch_gemm_tiles<GemmShape<128, 256, 2, 4, 3, 1, true>>(a, num_cus, stream);
+    return launch_gemm_tiles<GemmShape<128, 128, 2, 2, 2, 2, false>>(a, num_cus, stream);
 }
 
 }  // namespace moe

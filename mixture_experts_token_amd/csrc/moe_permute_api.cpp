@@ -281,7 +281,8 @@ moe_status_t moe_grouped_gemm_bf16(const void* x, const void* w, const int64_t* 
                                    void* stream) {
     if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS || max_rows < 0) return MOE_ERR_INVALID_ARG;
     if (n < 128 || n % 128 != 0 || k < 64 || k % 64 != 0) return MOE_ERR_INVALID_ARG;
-    if (n > (int64_t(1) << 40) / 2 || k > (int64_t(1) << 40) / 2 || max_rows > kMaxRows) return MOE_ERR_INVALID_ARG;
+    // k <= 2^20: the kernels address a tile's rows with 32-bit byte offsets (256 rows of 2k bytes)
+    if (n > (int64_t(1) << 40) / 2 || k > (int64_t(1) << 20) || max_rows > kMaxRows) return MOE_ERR_INVALID_ARG;
     if (expert_first_token_offset == nullptr || w == nullptr) return MOE_ERR_INVALID_ARG;
     if (max_rows > 0 && (x == nullptr || y == nullptr)) return MOE_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(expert_first_token_offset, 8))

@@ -271,6 +271,7 @@ def gemm_call(lib, **kw):
     (dict(n=100), INVALID),           # n must be a multiple of 128
     (dict(n=0), INVALID),
     (dict(k=96), INVALID),            # k must be a multiple of 64
+    (dict(k=(1 << 20) + 64), INVALID),  # and at most 2^20
     (dict(off=None), INVALID),
     (dict(w=None), INVALID),
     (dict(x=None), INVALID),
