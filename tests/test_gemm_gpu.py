@@ -72,6 +72,11 @@ CASES = [
     (16, 700, 384, 192, "skewed"),
     (5, 300, 128, 1024, "one"),
     (3, 2, 640, 128, "even"),           # fewer rows than experts
+    # n a multiple of 256: 128 x 256 tiles with three LDS stages
+    (2, 300, 256, 64, "even"),          # a single k-step
+    (4, 257, 512, 128, "skewed"),       # two k-steps
+    (4, 129, 256, 320, "even"),         # a round of three k-steps, then two
+    (6, 700, 768, 192, "one"),          # exactly one round
 ]
 
 
