@@ -263,6 +263,9 @@ def main() -> int:
     ap.add_argument("--gemm", action="store_true",
                     help="time the grouped GEMM over the permuted rows instead (moe_grouped_gemm_bf16)")
     ap.add_argument("--gemm-n", type=int, default=0, help="GEMM output width (default: 2 x expert intermediate)")
+    ap.add_argument("--alloc-per-call", action="store_true",
+                    help="also time the same K steps with every output and the workspace allocated per call "
+                         "(torch.empty, eager only), the pattern preallocated scratch replaces")
     ap.add_argument("--ids", default="int32", choices=["int32", "int64"],
                     help="expert id type handed to the permute (int64 is read directly, no cast pass)")
     args = ap.parse_args()
@@ -333,16 +336,17 @@ def main() -> int:
 
     # Kernels go to torch's current stream (the capture stream while a graph is recorded).
     def permute(s):
+        wsp = s.get("ws", ws)
         if quant:
             binding.moe_permute_quant_fp8(s["x"], ids, w.num_experts, s["xp"], s["sp"], s["off"], s["perm"], s["inv"],
-                                          ws, group_size=args.group, expert_map=emap,
+                                          wsp, group_size=args.group, expert_map=emap,
                                           num_local_experts=local[2] if local is not None else 0)
         elif local is None:
-            binding.moe_permute(s["x"], ids, w.num_experts, s["xp"], s["off"], s["perm"], s["inv"], ws,
+            binding.moe_permute(s["x"], ids, w.num_experts, s["xp"], s["off"], s["perm"], s["inv"], wsp,
                                 token_scale=s["scale"], permuted_scale=s["sp"])
         else:
             binding.moe_permute_local(s["x"], ids, w.num_experts, emap, local[2], s["xp"], s["off"], s["perm"],
-                                      s["inv"], ws, token_scale=s["scale"], permuted_scale=s["sp"])
+                                      s["inv"], wsp, token_scale=s["scale"], permuted_scale=s["sp"])
 
     def unpermute(s):
         binding.moe_unpermute(s["y"], wts, s["inv"], s["out"])
@@ -430,6 +434,27 @@ def main() -> int:
                    "pct_of_step_ceiling": round(100 * value / step_ceiling, 2)}
         torch.cuda.synchronize(dev)
 
+    # The same steps with every output buffer and the workspace allocated per
+    # call through torch's caching allocator (what a caller without
+    # preallocated scratch does); eager launches only.
+    alloc_cmp = None
+    if args.alloc_per_call and not args.graph:
+        def step_alloc(i):
+            s = dict(sets[i % nsets])
+            for key in ("xp", "sp", "off", "perm", "inv", "out"):
+                if s[key] is not None:
+                    s[key] = torch.empty_like(s[key])
+            s["ws"] = torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev)
+            permute(s)
+            unpermute(s)
+
+        for i in range(args.warmup):
+            step_alloc(i)
+        us_alloc, _ = timed(step_alloc, k)
+        alloc_cmp = {"kind": "outputs and workspace allocated per call (torch.empty), eager",
+                     "us_per_step": round(us_alloc, 3),
+                     "reuse_saves_pct": round(100 * (us_alloc - us_step) / us_alloc, 2)}
+
     tiny = torch.zeros(1, device=dev)
     floor_args = args.graph
     launch_floor_us = timed(lambda i: tiny.add_(1.0), k)[0] if floor_args else None
@@ -489,6 +514,7 @@ def main() -> int:
         "algorithmic_bytes_per_op": {"permute": nb["permute"], "unpermute": nb["unpermute"]},
         "wall_s_timed_region": round(wall, 4),
         "ceiling": ceiling,
+        **({} if alloc_cmp is None else {"alloc_per_call": alloc_cmp}),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
