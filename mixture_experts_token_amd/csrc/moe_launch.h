@@ -45,6 +45,7 @@ struct QuantArgs {
     int64_t row_vecs;               // input row length in 16-byte vectors (<= kQuantMaxRowVecs)
     int32_t topk;
     int32_t group_vecs;             // 16-byte input vectors per scale group; 0: one scale per token
+    bool all_local;                 // no expert map: every token has topk destinations
     uint8_t* permuted_codes;        // [N*topk, H] E4M3FN
     float* permuted_scale;          // [N*topk, groups]
 };

@@ -269,6 +269,7 @@ moe_status_t moe_permute_quant_fp8(const void* hidden_states, int32_t dtype, con
     q.row_vecs = hidden_size * eb / 16;
     q.topk = topk;
     q.group_vecs = group_size == 0 ? 0 : (int32_t)(group_size / epv);
+    q.all_local = expert_map == nullptr;
     q.permuted_codes = permuted_codes;
     q.permuted_scale = permuted_scale;
     return moe::launch_quant_scatter(q, dtype == MOE_DTYPE_BF16, static_cast<hipStream_t>(stream)) == hipSuccess

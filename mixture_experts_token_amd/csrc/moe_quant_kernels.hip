@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "moe_launch.h"
 #include "moe_plan.h"
@@ -99,8 +100,11 @@ __device__ __forceinline__ u32x2 vec_codes(const u32x4& v, float scale) {
 // per block.  Thread gt of a token holds vectors gt, gt + TPT, ...  (U of
 // them, U*TPT >= row_vecs).  group_vecs: vectors per scale group (a power of
 // two <= 64, so a group is an aligned run of lanes of one wave), or 0 for one
-// scale per token.
-template <bool kBF16, int U, int TPT, bool kNTStore>
+// scale per token.  kAllLocal (no expert map): every token has topk
+// destinations, so its row is loaded before anything else is read and the
+// check for a rejected id (off[0] < 0: write nothing) follows the loads; with
+// a map the destinations are read first and tokens without one are skipped.
+template <bool kBF16, int U, int TPT, bool kNTStore, bool kAllLocal>
 __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ inv, const int64_t* __restrict__ off,
     uint8_t* __restrict__ codes, float* __restrict__ scales, int64_t num_tokens, int64_t rv, int topk,
@@ -110,7 +114,9 @@ __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
     constexpr int WPT = TPT / 64;          // waves per token
     constexpr int kEpv = kBF16 ? 8 : 4;    // elements (and code bytes) per 16-byte input vector
     __shared__ float red_s[WPT > 1 ? WPT : 1];
-    if (off[0] < 0) return;                // the index permute rejected an id: write nothing
+    if constexpr (!kAllLocal) {
+        if (off[0] < 0) return;            // the index permute rejected an id: write nothing
+    }
     const int gt = (int)(threadIdx.x % TPT);
     const int64_t rows = num_tokens * topk;
     const int64_t row_bytes = rv * kEpv;   // code bytes per row = H
@@ -121,18 +127,27 @@ __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
         const int64_t tt = __builtin_amdgcn_readfirstlane((int)t);
         // Any destination on this rank?  (Wave-uniform reads, scalar path; the
         // same answer for every wave of the token, so the block stays together.)
-        bool any = false;
-        for (int k = 0; k < topk; ++k) {
-            const int32_t d = inv[tt * topk + k];
-            any |= d >= 0 && (int64_t)d < rows;
+        if constexpr (!kAllLocal) {
+            bool any = false;
+            for (int k = 0; k < topk; ++k) {
+                const int32_t d = inv[tt * topk + k];
+                any |= d >= 0 && (int64_t)d < rows;
+            }
+            if (!any) continue;
         }
-        if (!any) continue;
         u32x4 v[U];
         const u32x4* src = x + tt * rv;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t idx = gt + (int64_t)TPT * u;
             v[u] = idx < rv ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+        }
+        if constexpr (kAllLocal) {
+            // the index permute rejected an id: write nothing.  The empty asm
+            // keeps this test after the row loads (it cannot be hoisted).
+            int64_t off0 = off[0];
+            asm volatile("" : "+s"(off0));
+            if (off0 < 0) return;
         }
         // Scales: per vector amax, reduced over its group's lanes (or the token).
         float sc[U];
@@ -206,16 +221,20 @@ hipError_t launch_quant_ut(const QuantArgs& a, hipStream_t stream) {
     const int64_t blocks = blocks_needed < kMaxGridBlocks ? blocks_needed : kMaxGridBlocks;
     // Plain stores for wide fan-out into large outputs, as in the permute row copy.
     const bool plain = a.topk >= 4 && a.num_tokens * a.topk * a.row_vecs * (kBF16 ? 8 : 4) >= (int64_t(32) << 20);
-    if (plain)
-        hipLaunchKernelGGL((quant_scatter_kernel<kBF16, U, TPT, false>), dim3((unsigned)blocks), dim3(BT), 0, stream,
+    auto go = [&](auto nt_store, auto all_local) {
+        hipLaunchKernelGGL((quant_scatter_kernel<kBF16, U, TPT, decltype(nt_store)::value, decltype(all_local)::value>),
+                           dim3((unsigned)blocks), dim3(BT), 0, stream,
                            reinterpret_cast<const u32x4*>(a.hidden_states), a.inv_permuted_idx,
                            a.expert_first_token_offset, a.permuted_codes, a.permuted_scale, a.num_tokens, a.row_vecs,
                            a.topk, a.group_vecs);
-    else
-        hipLaunchKernelGGL((quant_scatter_kernel<kBF16, U, TPT, true>), dim3((unsigned)blocks), dim3(BT), 0, stream,
-                           reinterpret_cast<const u32x4*>(a.hidden_states), a.inv_permuted_idx,
-                           a.expert_first_token_offset, a.permuted_codes, a.permuted_scale, a.num_tokens, a.row_vecs,
-                           a.topk, a.group_vecs);
+    };
+    if (plain) {
+        if (a.all_local) go(std::false_type{}, std::true_type{});
+        else go(std::false_type{}, std::false_type{});
+    } else {
+        if (a.all_local) go(std::true_type{}, std::true_type{});
+        else go(std::true_type{}, std::false_type{});
+    }
     return hipGetLastError();
 }
 
