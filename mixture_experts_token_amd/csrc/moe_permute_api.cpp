@@ -139,7 +139,8 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
     if (hidden_size > 0 && (!aligned(hidden_states, 16) || !aligned(permuted_hidden_states, 16)))
         return MOE_ERR_MISALIGNED;
 
-    const moe::PermutePlan plan = moe::plan_permute(num_tokens, topk, buckets, map_entries);
+    const moe::PermutePlan plan =
+        moe::plan_permute(num_tokens, topk, buckets, map_entries, hidden_size == 0 && token_scale == nullptr);
     if (workspace_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (plan.ws_bytes > 0) {
         if (workspace == nullptr) return MOE_ERR_INVALID_ARG;

@@ -145,7 +145,10 @@ inline size_t workspace_bound(int64_t max_num_tokens, int topk, int buckets, int
     return staged > coarse ? staged : coarse;
 }
 
-inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int map_entries) {
+// index_only: no rows are copied (the quantising permute moves them in a
+// second kernel), so fewer, larger tiles: every fused workgroup counts all ids,
+// and without a row copy to hide behind that count is the kernel's cost.
+inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int map_entries, bool index_only = false) {
     PermutePlan p;
     p.rows = num_tokens * topk;
     p.nbits = key_bits(buckets);
@@ -155,6 +158,7 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int m
         int64_t tpt = (num_tokens + kFusedTargetBlocks - 1) / kFusedTargetBlocks;
         const int64_t cap = (kFusedThreads / topk) < 1 ? 1 : (kFusedThreads / topk);
         if (tpt < 1) tpt = 1;
+        if (index_only) tpt *= 8;
         if (tpt > cap) tpt = cap;
         p.tokens_per_tile = (int)tpt;
     } else {

@@ -10,7 +10,7 @@ walks a grid of shapes and asserts, for every plan:
   * the workspace query bounds the requirement of every smaller call and is
     monotone in the token count.
 The grid covers the plain sort over E experts and the local-expert sort over
-B buckets with an E-entry map held in LDS.
+B buckets with an E-entry map held in LDS, each with and without a row copy.
 """
 
 import os
@@ -31,21 +31,22 @@ int main() {
   const int Ks[] = {1, 2, 3, 8, 16, 64, 512, 1024};
   const int Es[] = {1, 8, 37, 128, 256, 1000, 1024};
   const long long Ns[] = {1, 7, 100, 2047, 2048, 2049, 4096, 8192, 8193, 16384, 30000, 65536, 140000, 1000000};
-  for (int K : Ks) for (int E : Es) for (int mode = 0; mode < 3; ++mode) {
+  for (int K : Ks) for (int E : Es) for (int mode = 0; mode < 6; ++mode) {
     if (K > E) continue;
-    const int B = mode == 0 ? E : (mode == 1 ? (E / 8 > 0 ? E / 8 : 1) : E);  // buckets
-    const int M = mode == 0 ? 0 : E;                                         // map entries
+    const bool index_only = mode >= 3;  // no row copy: fewer, larger fused tiles
+    const int B = mode % 3 == 0 ? E : (mode % 3 == 1 ? (E / 8 > 0 ? E / 8 : 1) : E);  // buckets
+    const int M = mode % 3 == 0 ? 0 : E;                                             // map entries
     size_t prev = 0;
     for (long long N : Ns) {
       if (N * K >= (1LL << 31)) continue;
-      const PermutePlan p = plan_permute(N, K, B, M);
+      const PermutePlan p = plan_permute(N, K, B, M, index_only);
       const size_t bound = workspace_bound(N, K, B, M);
       CHECK(bound >= p.ws_bytes, "N=%lld K=%d B=%d M=%d bound %zu < need %zu", N, K, B, M, bound, p.ws_bytes);
       CHECK(bound >= prev, "N=%lld K=%d B=%d M=%d bound not monotone", N, K, B, M);
       prev = bound;
       for (long long n2 : {N / 2, N - 1, N / 3 + 1}) {
         if (n2 < 1) continue;
-        const PermutePlan q = plan_permute(n2, K, B, M);
+        const PermutePlan q = plan_permute(n2, K, B, M, index_only);
         CHECK(q.ws_bytes <= bound, "N=%lld smaller %lld K=%d B=%d needs %zu > %zu", N, n2, K, B, q.ws_bytes, bound);
       }
       CHECK(p.nbits >= 0 && (1 << p.nbits) >= B, "key bits");
