@@ -57,7 +57,7 @@ constexpr int kXcds = 8;
 // (BM/WM) x (BN/WN) block of 32 x 32 MFMA tiles; STAGES LDS buffers per
 // operand; PER_CU workgroups resident per compute unit (registers and LDS are
 // budgeted for that many).  FAST: loads through buffer resources spread over
-// the k slices, fragment reads as explicit ds_read_b128 (lds_read); otherwise
+// the k slices, fragment reads as explicit ds_read_b128 (lds_read_slice); otherwise
 // global_load_lds issued together after the barrier and fragment reads left
 // to the compiler.
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int PER_CU_, bool FAST_>
@@ -186,27 +186,32 @@ __device__ __forceinline__ bf16x8 lds_frag(const __bf16* lds, int row, int kvec)
     return *reinterpret_cast<const bf16x8*>(lds + row * kBK + ((kvec ^ (row % 8)) * 8));
 }
 
-// The same fragment read with an explicit ds_read_b128.  The compiler does not
-// see this as an LDS read, so it adds no wait for direct-to-LDS loads still in
-// flight into other stages (it cannot tell the stages apart and would wait for
-// all of them); the caller orders the read after the barrier that publishes
-// its stage and waits for it with lds_wait before using the result.
-__device__ __forceinline__ u32x4 lds_read(const __bf16* lds, int row, int kvec) {
-    const __bf16* p = lds + row * kBK + ((kvec ^ (row % 8)) * 8);
-    // A generic address of LDS memory holds the LDS byte offset in its low 32 bits.
-    const uint32_t addr = (uint32_t)(uintptr_t)p;
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
+// LDS byte address of the 16-byte fragment vector (row, kvec) of a stage: a
+// generic address of LDS memory holds the LDS byte offset in its low 32 bits.
+__device__ __forceinline__ uint32_t lds_frag_addr(const __bf16* lds, int row, int kvec) {
+    return (uint32_t)(uintptr_t)(lds + row * kBK + ((kvec ^ (row % 8)) * 8));
 }
 
-// Wait for every lds_read issued so far; `f` then carries a dependency on the
-// wait, so no use of it is scheduled before it.
-template <int N>
-__device__ __forceinline__ void lds_wait(u32x4 (&f)[N]) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
+// The four fragment reads of one 16-wide k slice (two row fragments, two
+// weight fragments) as explicit ds_read_b128, and the wait for them, in one
+// asm statement.  The compiler does not see these as LDS reads, so it adds no
+// wait for direct-to-LDS loads still in flight into other stages (it cannot
+// tell the stages apart and would wait for all of them); the caller orders
+// the statement after the barrier that publishes its stage.  The wait sits in
+// the same statement so that the destination registers are written before
+// the compiler regards them as defined, and the outputs are early-clobber so
+// that no destination shares a register with an address still to be read.
+__device__ __forceinline__ void lds_read_slice(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, u32x4& fa0,
+                                               u32x4& fa1, u32x4& fb0, u32x4& fb1) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fa0), "=&v"(fa1), "=&v"(fb0), "=&v"(fb1)
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
+        : "memory");
 }
 
 template <int I>
@@ -373,13 +378,13 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
                 const int kvec = kk * 2 + lane / 32;
                 bf16x8 af[MT], bfr[NT];
                 if constexpr (S::FAST) {
+                    static_assert(MT == 2 && NT == 2, "lds_read_slice reads 2 + 2 fragments");
                     u32x4 fa[MT], fb[NT];
-#pragma unroll
-                    for (int mi = 0; mi < MT; ++mi) fa[mi] = lds_read(as, wm * S::kWaveM + mi * 32 + lane % 32, kvec);
-#pragma unroll
-                    for (int ni = 0; ni < NT; ++ni) fb[ni] = lds_read(bs, wn * S::kWaveN + ni * 32 + lane % 32, kvec);
-                    lds_wait(fa);
-                    lds_wait(fb);
+                    lds_read_slice(lds_frag_addr(as, wm * S::kWaveM + lane % 32, kvec),
+                                   lds_frag_addr(as, wm * S::kWaveM + 32 + lane % 32, kvec),
+                                   lds_frag_addr(bs, wn * S::kWaveN + lane % 32, kvec),
+                                   lds_frag_addr(bs, wn * S::kWaveN + 32 + lane % 32, kvec), fa[0], fa[1], fb[0],
+                                   fb[1]);
 #pragma unroll
                     for (int mi = 0; mi < MT; ++mi) af[mi] = __builtin_bit_cast(bf16x8, fa[mi]);
 #pragma unroll
