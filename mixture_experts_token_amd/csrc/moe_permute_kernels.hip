@@ -961,8 +961,9 @@ __global__ void fill_offsets_kernel(int64_t* off, int n, int64_t value) {
 // of all topk rows of the chunk are issued before any arithmetic (G rows at a
 // time when topk is not a compile-time constant), then summed in fp32 in
 // ascending k and rounded once to the element type.  A slot whose inverse
-// index is -1 (its expert lives on another rank) is skipped: no load, no term.
-// Any other index outside [0, N*topk) turns the token's row into NaN.
+// index is -1 (its expert lives on another rank) is skipped: no load, no term;
+// a token with no other slot gets a zero row, stored by one wave.  Any other
+// index outside [0, N*topk) turns the token's row into NaN.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -1005,15 +1006,25 @@ struct UnpermuteItem {
     u32x4 v[K][U];
 };
 
+// Reads the token's topk indices and weights; true when every index is -1
+// (no local slot: the token's row is zero).
 template <bool kBF16, int K, int U>
-__device__ __forceinline__ void unpermute_issue(const u32x4* __restrict__ y, const float* __restrict__ wts,
-                                                const int32_t* __restrict__ inv, int64_t R, int64_t rv, int64_t t,
-                                                int64_t base, UnpermuteItem<kBF16, K, U>& it) {
+__device__ __forceinline__ bool unpermute_indices(const float* __restrict__ wts, const int32_t* __restrict__ inv,
+                                                  int64_t t, UnpermuteItem<kBF16, K, U>& it) {
+    bool remote = true;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         it.j[k] = inv[t * K + k];
         it.wk[k] = wts[t * K + k];
+        remote &= it.j[k] == -1;
     }
+    return remote;
+}
+
+// Issues the row loads of the chunk for the indices read by unpermute_indices.
+template <bool kBF16, int K, int U>
+__device__ __forceinline__ void unpermute_issue(const u32x4* __restrict__ y, int64_t R, int64_t rv, int64_t base,
+                                                UnpermuteItem<kBF16, K, U>& it) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const bool ok = it.j[k] >= 0 && (int64_t)it.j[k] < R;
@@ -1065,6 +1076,26 @@ __device__ __forceinline__ void unpermute_finish(u32x4* __restrict__ out, int64_
     store_outputs<kBF16, U>(out + t * rv, rv, base, acc, bad);
 }
 
+// A token whose every slot is -1 has all its experts on other ranks: its
+// output row is zero.  The wave of the row's first chunk stores the whole row
+// and the waves of its other chunks have nothing to do.  A zero row takes no
+// loads, so with one wave per 1 KiB chunk nearly all of a wave's time would go
+// to the index read (measured at the DSv3 shape, one rank of an 8-way expert
+// split: that rank's unpermute 101 -> 71 us).  This is the test for a
+// run-time topk; with a compile-time topk unpermute_indices makes it on the
+// indices it reads anyway.
+__device__ __forceinline__ bool token_is_remote(const int32_t* __restrict__ inv, int64_t t, int K) {
+    bool remote = true;
+    for (int k = 0; k < K; ++k) remote &= inv[t * K + k] == -1;
+    return remote;
+}
+
+// Zeros over a whole row of rv vectors (the bits of +0.0, as the weighted sum
+// over no slot rounds to); row is the token's output row.
+__device__ __forceinline__ void store_zero_row(u32x4* __restrict__ row, int64_t rv, int lane) {
+    for (int64_t c = lane; c < rv; c += kWaveSize) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, row + c);
+}
+
 // Item -> (token, first vector of this lane).  The token is the same for the
 // whole wave, which readfirstlane makes explicit.
 __device__ __forceinline__ void item_position(int64_t item, int64_t nchunks, int chunk_vecs, int64_t& t,
@@ -1087,14 +1118,23 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict_
     const int64_t items = num_tokens * nchunks;
     const int K = KC > 0 ? KC : topk;
     const int64_t R = num_tokens * K;
+    const int lane = (int)(threadIdx.x % kWaveSize);
     for (int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index(); item < items; item += total_waves) {
         int64_t t, base;
         item_position(item, nchunks, U * kWaveSize, t, base);
         if constexpr (KC > 0) {
             UnpermuteItem<kBF16, KC, U> it;
-            unpermute_issue<kBF16, KC, U>(y, wts, inv, R, rv, t, base, it);
+            if (unpermute_indices<kBF16, KC, U>(wts, inv, t, it)) {
+                if (base == lane) store_zero_row(out + t * rv, rv, lane);  // the token's first chunk
+                continue;
+            }
+            unpermute_issue<kBF16, KC, U>(y, R, rv, base, it);
             unpermute_finish<kBF16, KC, U>(out, R, rv, t, base, it);
         } else {
+            if (token_is_remote(inv, t, K)) {
+                if (base == lane) store_zero_row(out + t * rv, rv, lane);
+                continue;
+            }
             float acc[U][kEl];
 #pragma unroll
             for (int u = 0; u < U; ++u)

@@ -251,3 +251,46 @@ def test_unpermute_minus_one_slots_skip_and_others_nan(hip_device, k):
     ref = oracle.unpermute(to_np(y), to_np(wts), valid, "bf16")
     assert_unpermute_close(o[keep], ref[keep], "bf16")
     assert np.all(o[0] == 0)
+
+
+# (topk, hidden, dtype): rows of several 64-vector chunks with a ragged last one;
+# topk 3 takes the runtime-topk kernel, the others the compile-time ones.
+REMOTE_ROWS = [(2, 1560, "bf16"), (8, 1000, "f32"), (3, 1560, "bf16"), (1, 4096, "bf16"), (4, 7168, "bf16")]
+
+
+@pytest.mark.parametrize("k,h,dtype", REMOTE_ROWS, ids=["-".join(map(str, c)) for c in REMOTE_ROWS])
+def test_unpermute_tokens_with_no_local_slot_get_whole_zero_rows(hip_device, k, h, dtype):
+    """Tokens whose every slot is -1 get rows of +0.0 over the whole row (the
+    output is poisoned first, so an unwritten chunk shows); tokens with some
+    local slots are summed as usual; a token with one bad index among -1 slots
+    is not taken for remote and becomes NaN."""
+    n = 300
+    rng = np.random.default_rng(k * 1000 + h)
+    inv_np = rng.permutation(n * k).astype(np.int32)
+    remote = rng.random(n) < 0.4
+    remote[0] = remote[n - 1] = True
+    for t in np.nonzero(remote)[0]:
+        inv_np[t * k:(t + 1) * k] = -1
+    part = (~remote) & (rng.random(n) < 0.3)
+    for t in np.nonzero(part)[0]:
+        inv_np[t * k + rng.integers(0, k)] = -1
+    bad_t = 5
+    inv_np[bad_t * k:(bad_t + 1) * k] = -1
+    inv_np[bad_t * k + k - 1] = -3
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    y = torch.randn((n * k, h), generator=torch.Generator().manual_seed(h)).to(tdt).to(hip_device)
+    wts = torch.rand((n, k), generator=torch.Generator().manual_seed(k)).to(hip_device)
+    inv = torch.from_numpy(inv_np).to(hip_device)
+    _say("unpermute zero rows topk=%d H=%d %s remote=%d" % (k, h, dtype, int(remote.sum())))
+    out = gpu_unpermute(y, wts, inv)
+    torch.cuda.synchronize()
+    o = to_np(out)
+    assert torch.isnan(out[bad_t].float().cpu()).all()
+    zero_rows = np.nonzero(remote)[0]
+    zero_rows = zero_rows[zero_rows != bad_t]
+    assert np.all(o[zero_rows].view(np.uint8) == 0)
+    valid = inv_np.copy()
+    valid[bad_t * k + k - 1] = -1  # the oracle rejects the bad entry; that token is checked above
+    ref = oracle.unpermute(to_np(y), to_np(wts), valid, dtype)
+    keep = [t for t in range(n) if t != bad_t]
+    assert_unpermute_close(o[keep], ref[keep], dtype)
