@@ -572,6 +572,7 @@ __global__ __launch_bounds__(NT) void permute_fused_kernel(PermuteArgs a, int to
     int nbad = 0;
 #pragma unroll
     for (int j = 0; j < kIds; ++j) {
+        if (j * NT >= R) break;  // the same for the whole workgroup; matters at decode sizes
         const int r = (int)threadIdx.x + j * NT;
         if (r < R && (r < row0 || r >= row0 + T)) {
             if constexpr (kMap) {
@@ -703,6 +704,7 @@ __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs 
 
 #pragma unroll
     for (int j = 0; j < kHist; ++j) {
+        if (j * NT >= hist_n) break;  // the same for the whole workgroup
         const int i = (int)threadIdx.x + j * NT;
         if (i < hist_n) hist_s[i] = hv[j];
     }
@@ -714,6 +716,7 @@ __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs 
     // each wave's span, and the bad-id total from the histogram.
 #pragma unroll
     for (int j = 0; j < kPartial; ++j) {
+        if (c_start + j * NT >= row0) break;  // the same for the whole workgroup
         const int r = c_start + (int)threadIdx.x + j * NT;
         if (r < row0) {
             if constexpr (kMap) {
