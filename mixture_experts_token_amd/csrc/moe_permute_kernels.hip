@@ -965,8 +965,8 @@ __global__ void fill_offsets_kernel(int64_t* off, int n, int64_t value) {
 // time when topk is not a compile-time constant), then summed in fp32 in
 // ascending k and rounded once to the element type.  A slot whose inverse
 // index is -1 (its expert lives on another rank) is skipped: no load, no term;
-// a token with no other slot gets a zero row, stored by one wave.  Any other
-// index outside [0, N*topk) turns the token's row into NaN.
+// at topk >= 4 a token with no other slot gets a zero row stored by one wave.
+// Any other index outside [0, N*topk) turns the token's row into NaN.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -1084,9 +1084,14 @@ __device__ __forceinline__ void unpermute_finish(u32x4* __restrict__ out, int64_
 // and the waves of its other chunks have nothing to do.  A zero row takes no
 // loads, so with one wave per 1 KiB chunk nearly all of a wave's time would go
 // to the index read (measured at the DSv3 shape, one rank of an 8-way expert
-// split: that rank's unpermute 101 -> 71 us).  This is the test for a
-// run-time topk; with a compile-time topk unpermute_indices makes it on the
-// indices it reads anyway.
+// split: that rank's unpermute 101 -> 71 us).  Only for topk >= 4: with fewer
+// slots a token is rarely remote in every one (about a fifth of the tokens of
+// a 2-way split at topk 2), and the test itself cost the plain topk-2
+// unpermute 0.3 us per call (Mixtral shape).  This is the test for a run-time
+// topk; with a compile-time topk unpermute_indices makes it on the indices it
+// reads anyway.
+constexpr int kZeroRowMinTopk = 4;
+
 __device__ __forceinline__ bool token_is_remote(const int32_t* __restrict__ inv, int64_t t, int K) {
     bool remote = true;
     for (int k = 0; k < K; ++k) remote &= inv[t * K + k] == -1;
@@ -1127,14 +1132,14 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict_
         item_position(item, nchunks, U * kWaveSize, t, base);
         if constexpr (KC > 0) {
             UnpermuteItem<kBF16, KC, U> it;
-            if (unpermute_indices<kBF16, KC, U>(wts, inv, t, it)) {
+            if (unpermute_indices<kBF16, KC, U>(wts, inv, t, it) && KC >= kZeroRowMinTopk) {
                 if (base == lane) store_zero_row(out + t * rv, rv, lane);  // the token's first chunk
                 continue;
             }
             unpermute_issue<kBF16, KC, U>(y, R, rv, base, it);
             unpermute_finish<kBF16, KC, U>(out, R, rv, t, base, it);
         } else {
-            if (token_is_remote(inv, t, K)) {
+            if (K >= kZeroRowMinTopk && token_is_remote(inv, t, K)) {
                 if (base == lane) store_zero_row(out + t * rv, rv, lane);
                 continue;
             }
