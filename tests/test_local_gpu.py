@@ -254,8 +254,11 @@ def test_unpermute_minus_one_slots_skip_and_others_nan(hip_device, k):
 
 
 # (topk, hidden, dtype): rows of several 64-vector chunks with a ragged last one;
-# topk 3 takes the runtime-topk kernel, the others the compile-time ones.
-REMOTE_ROWS = [(2, 1560, "bf16"), (8, 1000, "f32"), (3, 1560, "bf16"), (1, 4096, "bf16"), (4, 7168, "bf16")]
+# topk 3 and 6 take the runtime-topk kernel, the others the compile-time ones.
+# From topk 4 a whole-remote token's row is stored by one wave; below it, chunk
+# by chunk -- both must leave no element unwritten.
+REMOTE_ROWS = [(2, 1560, "bf16"), (8, 1000, "f32"), (3, 1560, "bf16"), (1, 4096, "bf16"), (4, 7168, "bf16"),
+               (6, 1560, "bf16")]
 
 
 @pytest.mark.parametrize("k,h,dtype", REMOTE_ROWS, ids=["-".join(map(str, c)) for c in REMOTE_ROWS])
