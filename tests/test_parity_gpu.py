@@ -156,6 +156,13 @@ EDGE = [
     (513, 8, 256, 16, "fp8_e4m3", "distinct"),
     (2600, 8, 256, 7168, "fp8_e4m3", "distinct"),
     (140000, 2, 16, 8, "bf16", "dups"),        # > 2048 tiles: the tile scan takes several passes
+    # the fused kernel holds 1, 4, 16 or 32 id batches of 512 per thread: each side of each switch
+    (64, 8, 256, 16, "bf16", "distinct"),      # 512 rows: one batch
+    (65, 8, 256, 16, "bf16", "distinct"),      # 520 rows: four
+    (1024, 2, 8, 16, "bf16", "dups"),          # 2048 rows: four
+    (1025, 2, 8, 16, "bf16", "dups"),          # 2050 rows: sixteen
+    (4096, 2, 8, 16, "f32", "distinct"),       # 8192 rows: sixteen
+    (4097, 2, 8, 16, "f32", "distinct"),       # 8194 rows: thirty-two
 ]
 
 
