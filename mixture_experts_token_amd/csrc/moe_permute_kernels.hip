@@ -650,13 +650,16 @@ __global__ __launch_bounds__(NT) void permute_coarse_hist_kernel(const IdT* __re
 // coarse histogram (held in LDS) plus a count of the rows that precede the
 // tile inside its own coarse tile.  Tiles never straddle coarse tiles.
 // ----------------------------------------------------------------------------
-template <int NT, int U, bool kNTStore, bool kMap, typename IdT>
+// kHist / kPartial: batches of NT histogram entries / preceding ids each
+// thread loads, chosen by the launcher (as for the fused kernel's ids: no
+// load for entries that do not exist, no branch among the loads, and fewer
+// registers held through the index phase).
+template <int NT, int U, bool kNTStore, bool kMap, typename IdT, int kHist, int kPartial>
 __global__ __launch_bounds__(NT) void permute_coarse_scatter_kernel(PermuteArgs a, int tokens_per_tile, int nbits,
                                                                     int coarse_rows, int num_coarse,
                                                                     const int32_t* __restrict__ hist) {
     constexpr int W = NT / kWaveSize;
-    constexpr int kHist = kCoarseMaxHist / NT;                     // histogram entries loaded per thread
-    constexpr int kPartial = kCoarseMaxRowsPerTile / NT;           // preceding rows counted per thread
+    static_assert(kHist * NT <= kCoarseMaxHist && kPartial * NT <= kCoarseMaxRowsPerTile, "coarse load batches");
     constexpr int kBatches = (kMaxTileRows + NT - 1) / NT;
     constexpr int kPer = (kMaxExperts + NT - 1) / NT;
     static_assert(kCoarseMaxHist % NT == 0 && kCoarseMaxRowsPerTile % NT == 0, "coarse bounds vs workgroup size");
@@ -1252,17 +1255,34 @@ static void launch_fused_v(const PermuteArgs& a, const PermutePlan& p, hipStream
     else launch_fused_i<U, kMap, IdT, kMaxIds>(a, p, lds, stream);
 }
 
-template <int U, bool kMap, typename IdT>
-static void launch_coarse_v(const PermuteArgs& a, const PermutePlan& p, const int32_t* hist, hipStream_t stream) {
-    const size_t lds = coarse_scatter_lds_bytes(a.num_buckets, p.tile_rows, p.num_coarse, map_entries(a));
+template <int U, bool kMap, typename IdT, int kHist, int kPartial>
+static void launch_coarse_hp(const PermuteArgs& a, const PermutePlan& p, const int32_t* hist, size_t lds,
+                             hipStream_t stream) {
     if (plain_row_stores(a))
-        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, false, kMap, IdT>),
+        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, false, kMap, IdT, kHist, kPartial>),
                            dim3((unsigned)p.num_tiles), dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile,
                            p.nbits, p.coarse_rows, p.num_coarse, hist);
     else
-        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, true, kMap, IdT>),
+        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, true, kMap, IdT, kHist, kPartial>),
                            dim3((unsigned)p.num_tiles), dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile,
                            p.nbits, p.coarse_rows, p.num_coarse, hist);
+}
+
+// Coarse load batches per thread: 4 when the histogram (num_coarse * (B + 1)
+// entries) or the rows before a tile in its coarse tile fit in 4 * 512, else
+// 16 (DSv3-shaped 8-way expert split, lightly loaded rank: permute
+// 64.0 -> 61.1 us with 4 histogram batches).
+template <int U, bool kMap, typename IdT>
+static void launch_coarse_v(const PermuteArgs& a, const PermutePlan& p, const int32_t* hist, hipStream_t stream) {
+    const size_t lds = coarse_scatter_lds_bytes(a.num_buckets, p.tile_rows, p.num_coarse, map_entries(a));
+    constexpr int kFew = 4, kMany = kCoarseMaxHist / kCoarseThreads;
+    static_assert(kCoarseMaxRowsPerTile / kCoarseThreads == kMany, "one bound for both load batches");
+    const bool few_hist = (int64_t)p.num_coarse * (a.num_buckets + 1) <= kFew * kCoarseThreads;
+    const bool few_rows = (int64_t)p.coarse_rows - p.tile_rows <= kFew * kCoarseThreads;
+    if (few_hist && few_rows) launch_coarse_hp<U, kMap, IdT, kFew, kFew>(a, p, hist, lds, stream);
+    else if (few_hist) launch_coarse_hp<U, kMap, IdT, kFew, kMany>(a, p, hist, lds, stream);
+    else if (few_rows) launch_coarse_hp<U, kMap, IdT, kMany, kFew>(a, p, hist, lds, stream);
+    else launch_coarse_hp<U, kMap, IdT, kMany, kMany>(a, p, hist, lds, stream);
 }
 
 template <int U, bool kMap, typename IdT>
