@@ -1214,6 +1214,12 @@ static bool plain_row_stores(const PermuteArgs& a) {
     return a.topk >= kPlainStoreMinTopk && a.num_tokens * a.topk * a.row_vecs * 16 >= kPlainStoreMinBytes;
 }
 
+// Plain stores come with topk >= 4, whose row chunks are at most 4 vectors
+// per lane (kCopyUnrollsWideFanout), so wider chunks are built for
+// non-temporal stores only.
+static constexpr int kPlainStoreMaxUnroll = kCopyUnrollsWideFanout[0];
+static_assert(kPlainStoreMinTopk >= 4, "plain row stores only where the wide-fan-out chunk widths apply");
+
 static int map_entries(const PermuteArgs& a) { return a.expert_map != nullptr ? a.num_experts : 0; }
 
 // The map and the id type are compile-time parameters of every permute
@@ -1232,14 +1238,16 @@ static void with_variant(const PermuteArgs& a, F&& f) {
 
 template <int U, bool kMap, typename IdT, int kIds>
 static void launch_fused_i(const PermuteArgs& a, const PermutePlan& p, size_t lds, hipStream_t stream) {
-    if (plain_row_stores(a))
-        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, false, kMap, IdT, kIds>),
-                           dim3((unsigned)p.num_tiles), dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile,
-                           p.nbits);
-    else
-        hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, true, kMap, IdT, kIds>),
-                           dim3((unsigned)p.num_tiles), dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile,
-                           p.nbits);
+    if constexpr (U <= kPlainStoreMaxUnroll) {
+        if (plain_row_stores(a)) {
+            hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, false, kMap, IdT, kIds>),
+                               dim3((unsigned)p.num_tiles), dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile,
+                               p.nbits);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((permute_fused_kernel<kFusedThreads, U, true, kMap, IdT, kIds>), dim3((unsigned)p.num_tiles),
+                       dim3(kFusedThreads), lds, stream, a, p.tokens_per_tile, p.nbits);
 }
 
 // Id batches per thread: the fewest of 1, 4, 16 or 32 that cover N * topk rows
@@ -1258,14 +1266,17 @@ static void launch_fused_v(const PermuteArgs& a, const PermutePlan& p, hipStream
 template <int U, bool kMap, typename IdT, int kHist, int kPartial>
 static void launch_coarse_hp(const PermuteArgs& a, const PermutePlan& p, const int32_t* hist, size_t lds,
                              hipStream_t stream) {
-    if (plain_row_stores(a))
-        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, false, kMap, IdT, kHist, kPartial>),
-                           dim3((unsigned)p.num_tiles), dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile,
-                           p.nbits, p.coarse_rows, p.num_coarse, hist);
-    else
-        hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, true, kMap, IdT, kHist, kPartial>),
-                           dim3((unsigned)p.num_tiles), dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile,
-                           p.nbits, p.coarse_rows, p.num_coarse, hist);
+    if constexpr (U <= kPlainStoreMaxUnroll) {
+        if (plain_row_stores(a)) {
+            hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, false, kMap, IdT, kHist, kPartial>),
+                               dim3((unsigned)p.num_tiles), dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile,
+                               p.nbits, p.coarse_rows, p.num_coarse, hist);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((permute_coarse_scatter_kernel<kCoarseThreads, U, true, kMap, IdT, kHist, kPartial>),
+                       dim3((unsigned)p.num_tiles), dim3(kCoarseThreads), lds, stream, a, p.tokens_per_tile, p.nbits,
+                       p.coarse_rows, p.num_coarse, hist);
 }
 
 // Coarse load batches per thread: 4 when the histogram (num_coarse * (B + 1)
@@ -1289,14 +1300,17 @@ template <int U, bool kMap, typename IdT>
 static void launch_scatter_v(const PermuteArgs& a, const PermutePlan& p, const int32_t* rank_ws,
                              const int32_t* tile_base, const int32_t* total, hipStream_t stream) {
     const size_t lds = scatter_lds_bytes(a.num_buckets, p.tile_rows, map_entries(a));
-    if (plain_row_stores(a))
-        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, false, kMap, IdT>), dim3((unsigned)p.num_tiles),
-                           dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
-                           total);
-    else
-        hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, true, kMap, IdT>), dim3((unsigned)p.num_tiles),
-                           dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
-                           total);
+    if constexpr (U <= kPlainStoreMaxUnroll) {
+        if (plain_row_stores(a)) {
+            hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, false, kMap, IdT>),
+                               dim3((unsigned)p.num_tiles), dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile,
+                               p.num_tiles, rank_ws, tile_base, total);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, true, kMap, IdT>), dim3((unsigned)p.num_tiles),
+                       dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
+                       total);
 }
 
 #define MOE_VARIANT_TYPES                                 \
