@@ -627,17 +627,37 @@ __global__ __launch_bounds__(NT) void permute_coarse_hist_kernel(const IdT* __re
                                                                  const int32_t* __restrict__ expert_map, int R, int E,
                                                                  int B, int coarse_rows, int32_t* __restrict__ hist) {
     extern __shared__ int smem[];  // [B + 1], then the map [E] when there is one
+    // Ids go out kBatch per thread at a time; the first batch before the LDS
+    // set-up, so its loads overlap it (one load, wait and atomic after another
+    // left the kernel a chain of memory round trips).
+    constexpr int kBatch = 8;
+    const int r0 = (int)blockIdx.x * coarse_rows;
+    const int r1 = min(r0 + coarse_rows, R);
+    int v[kBatch];
+    auto load_batch = [&](int base) {
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int r = base + (int)threadIdx.x + q * NT;
+            v[q] = r < r1 ? load_id(ids, r) : 0;
+        }
+    };
+    load_batch(r0);
     int* map_w = smem + B + 1;
     for (int e = threadIdx.x; e <= B; e += NT) smem[e] = 0;
     if constexpr (kMap)
         for (int e = threadIdx.x; e < E; e += NT) map_w[e] = expert_map[e];
     lds_barrier();
     const int* map_s = map_w;
-    const int r0 = (int)blockIdx.x * coarse_rows;
-    const int r1 = min(r0 + coarse_rows, R);
-    for (int r = r0 + (int)threadIdx.x; r < r1; r += NT) {
-        const int key = bucket_of<kMap>(load_id(ids, r), E, map_s, B);
-        if (key != kRemoteKey) atomicAdd(&smem[key >= 0 ? key : B], 1);
+    for (int base = r0; base < r1; base += kBatch * NT) {
+        if (base != r0) load_batch(base);
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int r = base + (int)threadIdx.x + q * NT;
+            if (r < r1) {
+                const int key = bucket_of<kMap>(v[q], E, map_s, B);
+                if (key != kRemoteKey) atomicAdd(&smem[key >= 0 ? key : B], 1);
+            }
+        }
     }
     lds_barrier();
     int32_t* row = hist + (int64_t)blockIdx.x * (B + 1);
