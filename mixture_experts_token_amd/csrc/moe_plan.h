@@ -43,6 +43,7 @@ constexpr int kFusedTargetBlocks = 512;
 constexpr int kMaxTileRows = 1024;                 // LDS staging bound for one tile
 constexpr size_t kWorkspaceAlign = 256;
 constexpr int kQuantMaxRowVecs = 1024;             // quantise-scatter: a wave holds the whole row (16 KiB)
+constexpr int kIndexOnlyTileScale = 4;             // coarse tiles of an index-only permute, vs the standard ones
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -164,6 +165,18 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int m
     } else {
         p.fused = false;
         p.tokens_per_tile = staged_tokens_per_tile(topk);
+    }
+    if (!p.fused && index_only) {
+        // Without a row copy the fixed index work of each tile is the cost, so
+        // the coarse schedule takes tiles kIndexOnlyTileScale times larger
+        // (whole tokens, at most kMaxTileRows rows) where it still applies
+        // with them; the histogram then has no more rows than with the
+        // standard tiles, so the workspace bound holds.
+        int64_t big = (int64_t)p.tokens_per_tile * kIndexOnlyTileScale;
+        const int64_t cap = kMaxTileRows / topk;
+        if (big > cap) big = cap;
+        if (big > p.tokens_per_tile && coarse_rows_for(p.rows, buckets, (int)(big * topk), map_entries) > 0)
+            p.tokens_per_tile = (int)big;
     }
     p.tile_rows = p.tokens_per_tile * topk;
     p.num_tiles = num_tokens == 0 ? 0 : (num_tokens + p.tokens_per_tile - 1) / p.tokens_per_tile;
