@@ -1,0 +1,282 @@
+// moe_unpermute.hip -- gfx950 unpermute: the weighted topk reduction back to token order.
+//
+// What is computed: vLLM PR #14568, "permute/unpermute kernel for moe optimization",
+// PR description (the expanded expert output is gathered back per token, scaled by
+// topk_weight and summed over the topk slots).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "moe_launch.h"
+#include "moe_plan.h"
+
+namespace moe {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int wave_index() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWaveSize));
+}
+
+// ----------------------------------------------------------------------------
+// Unpermute: one wave per (token, chunk of U*64 16-byte vectors).  The loads
+// of all topk rows of the chunk are issued before any arithmetic (G rows at a
+// time when topk is not a compile-time constant), then summed in fp32 in
+// ascending k and rounded once to the element type.  A slot whose inverse
+// index is -1 (its expert lives on another rank) is skipped: no load, no term;
+// at topk >= 4 a token with no other slot gets a zero row stored by one wave.
+// Any other index outside [0, N*topk) turns the token's row into NaN.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <bool kBF16, int U>
+__device__ __forceinline__ void accumulate(float (&acc)[U][kBF16 ? 8 : 4], const u32x4 (&v)[U], float wk) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (kBF16) {
+                acc[u][2 * q] = __builtin_fmaf(wk, bf16_lo(v[u][q]), acc[u][2 * q]);
+                acc[u][2 * q + 1] = __builtin_fmaf(wk, bf16_hi(v[u][q]), acc[u][2 * q + 1]);
+            } else {
+                acc[u][q] = __builtin_fmaf(wk, __uint_as_float(v[u][q]), acc[u][q]);
+            }
+        }
+    }
+}
+
+// Unpermute kernels take separate __restrict__ pointers (not a struct) so the
+// compiler can prove the index / weight reads are never clobbered by the
+// output stores, which keeps those wave-uniform reads on the scalar path,
+// off the in-order vector-memory counter that the row loads use.
+
+// One work item of a compile-time topk: all topk indices and weights are
+// read first (independent of each other), then every row load of the chunk
+// is issued; `finish` weights, sums, rounds and stores.
+template <bool kBF16, int K, int U>
+struct UnpermuteItem {
+    int32_t j[K];
+    float wk[K];
+    u32x4 v[K][U];
+};
+
+// Reads the token's topk indices and weights; true when every index is -1
+// (no local slot: the token's row is zero).
+template <bool kBF16, int K, int U>
+__device__ __forceinline__ bool unpermute_indices(const float* __restrict__ wts, const int32_t* __restrict__ inv,
+                                                  int64_t t, UnpermuteItem<kBF16, K, U>& it) {
+    bool remote = true;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        it.j[k] = inv[t * K + k];
+        it.wk[k] = wts[t * K + k];
+        remote &= it.j[k] == -1;
+    }
+    return remote;
+}
+
+// Issues the row loads of the chunk for the indices read by unpermute_indices.
+template <bool kBF16, int K, int U>
+__device__ __forceinline__ void unpermute_issue(const u32x4* __restrict__ y, int64_t R, int64_t rv, int64_t base,
+                                                UnpermuteItem<kBF16, K, U>& it) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const bool ok = it.j[k] >= 0 && (int64_t)it.j[k] < R;
+        if (!ok) it.wk[k] = 0.0f;  // the zero row then adds exactly nothing
+        const u32x4* src = y + (int64_t)(ok ? it.j[k] : 0) * rv;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t idx = base + u * kWaveSize;
+            it.v[k][u] = (ok && idx < rv) ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+template <bool kBF16, int U>
+__device__ __forceinline__ void store_outputs(u32x4* __restrict__ out, int64_t rv, int64_t base,
+                                              const float (&acc)[U][kBF16 ? 8 : 4], bool bad) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t idx = base + u * kWaveSize;
+        if (idx >= rv) continue;
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (kBF16) {
+                o[q] = bad ? 0x7FC07FC0u : (bf16_bits(acc[u][2 * q]) | (bf16_bits(acc[u][2 * q + 1]) << 16));
+            } else {
+                o[q] = bad ? 0x7FC00000u : __float_as_uint(acc[u][q]);
+            }
+        }
+        __builtin_nontemporal_store(o, out + idx);
+    }
+}
+
+template <bool kBF16, int K, int U>
+__device__ __forceinline__ void unpermute_finish(u32x4* __restrict__ out, int64_t R, int64_t rv, int64_t t,
+                                                 int64_t base, const UnpermuteItem<kBF16, K, U>& it) {
+    constexpr int kEl = kBF16 ? 8 : 4;
+    float acc[U][kEl];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < kEl; ++e) acc[u][e] = 0.0f;
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        bad |= !(it.j[k] >= -1 && (int64_t)it.j[k] < R);
+        accumulate<kBF16, U>(acc, it.v[k], it.wk[k]);
+    }
+    store_outputs<kBF16, U>(out + t * rv, rv, base, acc, bad);
+}
+
+// A token whose every slot is -1 has all its experts on other ranks: its
+// output row is zero.  The wave of the row's first chunk stores the whole row
+// and the waves of its other chunks have nothing to do.  A zero row takes no
+// loads, so with one wave per 1 KiB chunk nearly all of a wave's time would go
+// to the index read (measured at the DSv3 shape, one rank of an 8-way expert
+// split: that rank's unpermute 101 -> 71 us).  Only for topk >= 4: with fewer
+// slots a token is rarely remote in every one (about a fifth of the tokens of
+// a 2-way split at topk 2), and the test itself cost the plain topk-2
+// unpermute 0.3 us per call (Mixtral shape).  This is the test for a run-time
+// topk; with a compile-time topk unpermute_indices makes it on the indices it
+// reads anyway.
+constexpr int kZeroRowMinTopk = 4;
+
+__device__ __forceinline__ bool token_is_remote(const int32_t* __restrict__ inv, int64_t t, int K) {
+    bool remote = true;
+    for (int k = 0; k < K; ++k) remote &= inv[t * K + k] == -1;
+    return remote;
+}
+
+// Zeros over a whole row of rv vectors (the bits of +0.0, as the weighted sum
+// over no slot rounds to); row is the token's output row.
+__device__ __forceinline__ void store_zero_row(u32x4* __restrict__ row, int64_t rv, int lane) {
+    for (int64_t c = lane; c < rv; c += kWaveSize) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, row + c);
+}
+
+// Item -> (token, first vector of this lane).  The token is the same for the
+// whole wave, which readfirstlane makes explicit.
+__device__ __forceinline__ void item_position(int64_t item, int64_t nchunks, int chunk_vecs, int64_t& t,
+                                              int64_t& base) {
+    t = __builtin_amdgcn_readfirstlane((int)(item / nchunks));
+    base = (item - t * nchunks) * chunk_vecs + (int)(threadIdx.x % kWaveSize);
+}
+
+// KC > 0: topk is exactly KC.  KC == 0: runtime topk, rows taken G at a time.
+// One item (token, chunk of U*64 vectors) per wave; only when the grid would
+// exceed kMaxGridBlocks does a wave loop over items g, g + total_waves, ...
+template <bool kBF16, int KC, int U, int G>
+__global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict__ y, const float* __restrict__ wts,
+                                                        const int32_t* __restrict__ inv, u32x4* __restrict__ out,
+                                                        int64_t num_tokens, int64_t rv, int topk,
+                                                        int64_t total_waves) {
+    constexpr int kEl = kBF16 ? 8 : 4;  // elements per 16-byte vector
+    constexpr int kGroup = KC > 0 ? KC : G;
+    const int64_t nchunks = (rv + U * kWaveSize - 1) / (U * kWaveSize);
+    const int64_t items = num_tokens * nchunks;
+    const int K = KC > 0 ? KC : topk;
+    const int64_t R = num_tokens * K;
+    const int lane = (int)(threadIdx.x % kWaveSize);
+    for (int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index(); item < items; item += total_waves) {
+        int64_t t, base;
+        item_position(item, nchunks, U * kWaveSize, t, base);
+        if constexpr (KC > 0) {
+            UnpermuteItem<kBF16, KC, U> it;
+            if (unpermute_indices<kBF16, KC, U>(wts, inv, t, it) && KC >= kZeroRowMinTopk) {
+                if (base == lane) store_zero_row(out + t * rv, rv, lane);  // the token's first chunk
+                continue;
+            }
+            unpermute_issue<kBF16, KC, U>(y, R, rv, base, it);
+            unpermute_finish<kBF16, KC, U>(out, R, rv, t, base, it);
+        } else {
+            if (K >= kZeroRowMinTopk && token_is_remote(inv, t, K)) {
+                if (base == lane) store_zero_row(out + t * rv, rv, lane);
+                continue;
+            }
+            float acc[U][kEl];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < kEl; ++e) acc[u][e] = 0.0f;
+            bool bad = false;
+            for (int k0 = 0; k0 < K; k0 += kGroup) {
+                int32_t j[kGroup];
+                float wk[kGroup];
+#pragma unroll
+                for (int g = 0; g < kGroup; ++g) {
+                    const bool live = k0 + g < K;
+                    j[g] = live ? inv[t * K + k0 + g] : 0;
+                    wk[g] = live ? wts[t * K + k0 + g] : 0.0f;
+                }
+                u32x4 v[kGroup][U];
+#pragma unroll
+                for (int g = 0; g < kGroup; ++g) {
+                    const bool live = k0 + g < K;
+                    const bool ok = live && j[g] >= 0 && (int64_t)j[g] < R;
+                    bad |= live && !(j[g] >= -1 && (int64_t)j[g] < R);
+                    if (!ok) wk[g] = 0.0f;
+                    const u32x4* src = y + (int64_t)(ok ? j[g] : 0) * rv;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int64_t idx = base + u * kWaveSize;
+                        v[g][u] = (ok && idx < rv) ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < kGroup; ++g)
+                    if (k0 + g < K) accumulate<kBF16, U>(acc, v[g], wk[g]);
+            }
+            store_outputs<kBF16, U>(out + t * rv, rv, base, acc, bad);
+        }
+    }
+}
+
+template <bool kBF16, int KC, int U, int G>
+static hipError_t launch_unpermute_t(const UnpermuteArgs& a, hipStream_t stream) {
+    const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
+    const int64_t items = a.num_tokens * nchunks;
+    const int64_t blocks_needed = (items + 3) / 4;
+    const int64_t blocks = blocks_needed < kMaxGridBlocks ? blocks_needed : kMaxGridBlocks;
+    hipLaunchKernelGGL((unpermute_kernel<kBF16, KC, U, G>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const u32x4*>(a.expanded_output), a.topk_weights, a.inv_permuted_idx,
+                       reinterpret_cast<u32x4*>(a.output), a.num_tokens, a.row_vecs, a.topk, blocks * 4);
+    return hipGetLastError();
+}
+
+
+// Unpermute dispatch: one item per wave, one 16-byte vector per lane (a
+// chunk is 64 vectors = 1 KiB of each of the topk rows).  Measured on MI355X
+// against 2, 4 and 7-8 vectors per lane and against persistent pipelined
+// waves: the narrowest chunks, i.e. the most waves in flight, were fastest for
+// every workload once the index reads stayed on the scalar path.
+template <bool kBF16, int KC, int G>
+static hipError_t launch_unpermute_k(const UnpermuteArgs& a, hipStream_t stream) {
+    return launch_unpermute_t<kBF16, KC, 1, G>(a, stream);
+}
+
+template <bool kBF16>
+static hipError_t launch_unpermute_dtype(const UnpermuteArgs& a, hipStream_t stream) {
+    switch (a.topk) {
+        case 1: return launch_unpermute_k<kBF16, 1, 1>(a, stream);
+        case 2: return launch_unpermute_k<kBF16, 2, 2>(a, stream);
+        case 4: return launch_unpermute_k<kBF16, 4, 4>(a, stream);
+        case 8: return launch_unpermute_k<kBF16, 8, 8>(a, stream);
+        default: return launch_unpermute_k<kBF16, 0, 4>(a, stream);
+    }
+}
+
+hipError_t launch_unpermute(const UnpermuteArgs& a, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_unpermute_dtype<true>(a, stream) : launch_unpermute_dtype<false>(a, stream);
+}
+
+}  // namespace moe
