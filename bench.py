@@ -1,11 +1,13 @@
 """Benchmark: one step = moe_permute + moe_unpermute over one batch (the whole path).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
-                    [--ep N --ep-rank R --ep-layout contiguous]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3]
+                    [--ep N --ep-rank R --ep-layout contiguous] [--no-sweep]
 
-With ``--ep N`` the step is one expert-parallel rank's share: the
-local-expert permute (moe_permute_local, rank R's experts of an N-way split)
-and the unpermute of its output (remote slots skipped).
+The headline workload is the largest single-GPU shape, DeepSeek-V3-shaped:
+N=16384 tokens, hidden 7168 bf16, 256 experts, topk 8, Zipf(1.2) routing with
+empty experts.  With ``--ep N`` the step is one expert-parallel rank's share:
+the local-expert permute (moe_permute_local, rank R's experts of an N-way
+split) and the unpermute of its output (remote slots skipped).
 
 Prints ONE JSON line.  ``value`` is whole-step achieved HBM bandwidth:
 algorithmic bytes of permute + unpermute (each input read once, each output
@@ -18,7 +20,10 @@ cache (fewer sets still showed some reuse through that cache).
 the stream the kernels run on; ``traffic`` carries the HBM bytes per launch
 measured with rocprofv3 counters when the committed counter summary matches
 the current kernel source (else null).  ``cpu_baseline`` times the CPU oracle
-on a bounded sample of the same workload on this host.
+on a bounded sample of the same workload on this host.  ``sweep`` (plain
+headline runs only) carries the µs-per-step curve against tokens from the
+same process: the Mixtral- and Qwen3-shaped steps, tiny, and the decode sizes
+N = 1, 4, 16, 64, 256 through one scratch preallocated for N = 256.
 """
 
 from __future__ import annotations
@@ -240,57 +245,15 @@ def cpu_baseline(inputs_host, w, budget_s: float = 10.0, max_reps: int = 50, loc
                       "host has %d cores" % (reps, w.name, w.num_tokens, el, len(os.sched_getaffinity(0)))}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mixtral")
-    ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate (default: enough to beat the LLC)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="before timing, run a plain elementwise copy kernel (negation) over a fresh MIB-MiB "
-                         "float32 buffer 5 times; its known traffic scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture the K steps (and each per-operation batch) in a HIP graph and time its replay")
-    ap.add_argument("--ep", type=int, default=1, help="expert-parallel ranks: time one rank's local-expert step")
-    ap.add_argument("--ep-rank", type=int, default=0)
-    ap.add_argument("--ep-layout", default="contiguous", choices=["contiguous", "round_robin", "shuffled"])
-    ap.add_argument("--quant", default="none", choices=["none", "fp8"],
-                    help="fp8: the permute quantises bf16 rows to E4M3FN codes + scales on the way "
-                         "(moe_permute_quant_fp8)")
-    ap.add_argument("--group", type=int, default=0, help="quantisation group size in elements (0: per token)")
-    ap.add_argument("--gemm", action="store_true",
-                    help="time the grouped GEMM over the permuted rows instead (moe_grouped_gemm_bf16)")
-    ap.add_argument("--gemm-n", type=int, default=0, help="GEMM output width (default: 2 x expert intermediate)")
-    ap.add_argument("--alloc-per-call", action="store_true",
-                    help="also time the same K steps with every output and the workspace allocated per call "
-                         "(torch.empty, eager only), the pattern preallocated scratch replaces")
-    ap.add_argument("--ids", default="int32", choices=["int32", "int64"],
-                    help="expert id type handed to the permute (int64 is read directly, no cast pass)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(the path shards by token or by expert, see the design notes)" % args.gpus, file=sys.stderr)
-        return 2
-
+def run_workload(args, w, dev) -> dict:
+    """Time args.steps steps of workload w (permute + unpermute) and return the bench line."""
     import numpy as np
     import torch
 
     import workloads as W
     from mixture_experts_token_amd import binding
 
-    binding.load_library()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = W.WORKLOADS[args.workload]
-    if args.tokens:
-        w = w.with_tokens(args.tokens)
     ids_np, wts_np = W.make_routing(w, seed=0)
-    if args.gemm:
-        return bench_gemm(args, w, ids_np, dev)
     local, emap_np, emap, n_off = None, None, None, w.num_experts + 1
     if args.ep > 1:
         emap_np, n_local = W.expert_map_for(w.num_experts, args.ep, args.ep_rank, args.ep_layout)
@@ -519,6 +482,209 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    return line
+
+
+SWEEP_EAGER = ("mixtral", "qwen3")  # large shapes: eager launches, rotating buffer sets
+SWEEP_MIN_STEPS = 100
+
+
+def sweep_enabled(args) -> bool:
+    """The sweep rides along with a plain headline line (no expert map, quantiser or id-type variant)."""
+    return (not args.no_sweep and args.ep == 1 and args.quant == "none" and args.ids == "int32" and not args.gemm
+            and not args.tokens and not args.alloc_per_call)
+
+
+def run_sweep(args, dev, skip: str) -> dict:
+    """µs per step against tokens, every workload other than the headline's, timed in this process.
+
+    The large shapes run like the headline (eager launches, rotating buffer
+    sets, same-run streaming ceiling); tiny and the decode sizes are latency
+    bound and are timed as HIP graph replays beside the same-run launch floor
+    (graph replay of a one-element kernel).  The decode sweep reuses one set of
+    buffers preallocated for N=256 (MoEPermuteScratch) in the order 1, 4, 16,
+    64, 256, and also reports eager steps with those buffers against eager
+    steps that allocate every output and the workspace per call.
+    """
+    import copy
+
+    import torch
+
+    import workloads as W
+
+    steps = max(args.steps, SWEEP_MIN_STEPS)
+    warmup = max(args.warmup, 10)
+    out = {"steps_per_entry": steps, "entries": []}
+
+    def entry(line, graph):
+        return {"workload": line["config"]["workload"], "num_tokens": line["config"]["num_tokens"],
+                "timing": "hip_graph_replay" if graph else "eager_launches",
+                "us_per_step": line["us_per_step"], "GBps": line["value"],
+                "pct_of_hbm_peak": line["pct_of_hbm_peak"], "permute_us": line["permute_us"],
+                "unpermute_us": line["unpermute_us"], "launch_floor_us": line["launch_floor_us"],
+                "pct_of_step_ceiling": (line["ceiling"] or {}).get("pct_of_step_ceiling")}
+
+    for name in SWEEP_EAGER + ("tiny",):
+        if name == skip:
+            continue
+        a = copy.copy(args)
+        a.steps, a.warmup, a.no_cpu_baseline, a.sets, a.copy_calibration = steps, warmup, True, None, 0
+        a.graph = name == "tiny"
+        line = run_workload(a, W.WORKLOADS[name], dev)
+        out["entries"].append(entry(line, a.graph))
+        torch.cuda.empty_cache()
+    out["entries"].extend(decode_sweep(dev, steps, warmup))
+    return out
+
+
+def decode_sweep(dev, steps: int, warmup: int) -> list:
+    """Decode sizes N = 1, 4, 16, 64, 256 through one MoEPermuteScratch sized for N = 256."""
+    import torch
+
+    import workloads as W
+    from mixture_experts_token_amd import binding
+
+    base = W.WORKLOADS["decode"]
+    n_max = max(W.DECODE_SWEEP)
+    scratch = binding.MoEPermuteScratch(n_max, base.topk, base.num_experts, dev, hidden_size=base.hidden_size,
+                                        hidden_dtype=torch.uint8, with_scale=True)
+    out_buf = torch.empty((n_max, base.hidden_size), dtype=torch.bfloat16, device=dev)
+    tiny = torch.zeros(1, device=dev)
+
+    def timed(body, k, graph):
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(k):
+                    body(i)
+            g.replay()
+            torch.cuda.synchronize(dev)
+            run = g.replay
+        else:
+            def run():
+                for i in range(k):
+                    body(i)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        start.record()
+        run()
+        end.record()
+        torch.cuda.synchronize(dev)
+        return start.elapsed_time(end) * 1e3 / k
+
+    res = []
+    for n in W.DECODE_SWEEP:
+        w = base.with_tokens(n)
+        ids_np, wts_np = W.make_routing(w, seed=0)
+        ids = torch.from_numpy(ids_np).to(dev)
+        wts = torch.from_numpy(wts_np).to(dev)
+        x, scale = W.make_hidden(w, seed=0, device=dev)
+        y = W.make_expert_output(w, seed=0, device=dev)
+        out = out_buf[:n]
+        nb = algorithmic_bytes(w)
+        held = {}
+
+        def permute(i):
+            held["p"] = scratch.permute(x, ids, token_scale=scale)
+
+        def unpermute(i):
+            binding.moe_unpermute(y, wts, held["p"]["inv_permuted_idx"], out)
+
+        def step(i):
+            permute(i)
+            unpermute(i)
+
+        def step_alloc(i):
+            xp = torch.empty((n * w.topk, w.hidden_size), dtype=torch.uint8, device=dev)
+            sp = torch.empty(n * w.topk, dtype=torch.float32, device=dev)
+            off = torch.empty(w.num_experts + 1, dtype=torch.int64, device=dev)
+            perm = torch.empty(n * w.topk, dtype=torch.int32, device=dev)
+            inv = torch.empty(n * w.topk, dtype=torch.int32, device=dev)
+            ws = torch.empty(max(16, binding.moe_permute_workspace_size(n, w.topk, w.num_experts)),
+                             dtype=torch.uint8, device=dev)
+            o = torch.empty((n, w.hidden_size), dtype=torch.bfloat16, device=dev)
+            binding.moe_permute(x, ids, w.num_experts, xp, off, perm, inv, ws, token_scale=scale, permuted_scale=sp)
+            binding.moe_unpermute(y, wts, inv, o)
+
+        for i in range(warmup):
+            step(i)
+            step_alloc(i)
+        torch.cuda.synchronize(dev)
+        us = timed(step, steps, True)
+        p_us = timed(permute, steps, True)
+        u_us = timed(unpermute, steps, True)
+        floor = timed(lambda i: tiny.add_(1.0), steps, True)
+        eager = timed(step, steps, False)
+        eager_alloc = timed(step_alloc, steps, False)
+        gbps = nb["total"] / (us * 1e-6) / 1e9
+        res.append({"workload": "decode", "num_tokens": n, "timing": "hip_graph_replay",
+                    "us_per_step": round(us, 3), "GBps": round(gbps, 1),
+                    "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "permute_us": round(p_us, 3),
+                    "unpermute_us": round(u_us, 3), "launch_floor_us": round(floor, 3),
+                    "pct_of_step_ceiling": None, "scratch": "one MoEPermuteScratch for N=256, reused",
+                    "eager_us_per_step_reused": round(eager, 3),
+                    "eager_us_per_step_alloc_per_call": round(eager_alloc, 3)})
+    return res
+
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv3",
+                    help="headline workload (default: the largest single-GPU shape, DeepSeek-V3-shaped)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the token sweep (the other workloads and the decode sizes, timed in the same run)")
+    ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate (default: enough to beat the LLC)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before timing, run a plain elementwise copy kernel (negation) over a fresh MIB-MiB "
+                         "float32 buffer 5 times; its known traffic scales rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K steps (and each per-operation batch) in a HIP graph and time its replay")
+    ap.add_argument("--ep", type=int, default=1, help="expert-parallel ranks: time one rank's local-expert step")
+    ap.add_argument("--ep-rank", type=int, default=0)
+    ap.add_argument("--ep-layout", default="contiguous", choices=["contiguous", "round_robin", "shuffled"])
+    ap.add_argument("--quant", default="none", choices=["none", "fp8"],
+                    help="fp8: the permute quantises bf16 rows to E4M3FN codes + scales on the way "
+                         "(moe_permute_quant_fp8)")
+    ap.add_argument("--group", type=int, default=0, help="quantisation group size in elements (0: per token)")
+    ap.add_argument("--gemm", action="store_true",
+                    help="time the grouped GEMM over the permuted rows instead (moe_grouped_gemm_bf16)")
+    ap.add_argument("--gemm-n", type=int, default=0, help="GEMM output width (default: 2 x expert intermediate)")
+    ap.add_argument("--alloc-per-call", action="store_true",
+                    help="also time the same K steps with every output and the workspace allocated per call "
+                         "(torch.empty, eager only), the pattern preallocated scratch replaces")
+    ap.add_argument("--ids", default="int32", choices=["int32", "int64"],
+                    help="expert id type handed to the permute (int64 is read directly, no cast pass)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the path shards by token or by expert, see the design notes)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as W
+    from mixture_experts_token_amd import binding
+
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[args.workload]
+    if args.tokens:
+        w = w.with_tokens(args.tokens)
+    if args.gemm:
+        ids_np, _ = W.make_routing(w, seed=0)
+        return bench_gemm(args, w, ids_np, dev)
+    line = run_workload(args, w, dev)
+    if sweep_enabled(args):
+        torch.cuda.empty_cache()
+        line["sweep"] = run_sweep(args, dev, skip=w.name)
     print(json.dumps(line), flush=True)
     return 0
 

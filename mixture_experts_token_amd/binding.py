@@ -97,6 +97,34 @@ def _dtype_code(t) -> int:
     raise TypeError("unsupported element type %s" % t.dtype)
 
 
+def _check(t, name: str, dtypes, numel: int, device, optional: bool = False) -> None:
+    """Reject a buffer the kernels would read or write out of bounds.
+
+    ``dtypes``: allowed torch dtypes; ``numel``: the element count the C entry
+    point derives from its sizes; ``device``: the device every buffer of the
+    call must be on (a GPU device).  Raises TypeError (type, device) or
+    ValueError (size, layout) before anything reaches the library.
+    """
+    if t is None:
+        if optional:
+            return
+        raise ValueError("%s is required" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s must be %s, got %s" % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+    if t.numel() != numel:
+        raise ValueError("%s must have %d elements, got %d (shape %s)" % (name, numel, t.numel(), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise TypeError("%s is on %s, expected %s (every buffer of the call on one GPU)" % (name, t.device, device))
+
+
+def _require_gpu(device) -> None:
+    """The last check of a call: its buffers (all on `device`) must be GPU memory."""
+    if device.type != "cuda":
+        raise TypeError("the MoE library takes GPU tensors; got tensors on %s" % device)
+
+
 def _ptr(t):
     """Raw device address of a contiguous tensor (None stays None)."""
     if t is None:
@@ -129,18 +157,69 @@ def moe_permute_local_workspace_size(max_num_tokens: int, topk: int, num_experts
                                                                int(num_local_experts)))
 
 
-def _permute_args(hidden_states, topk_ids, workspace):
+_ROW_TYPES = None
+
+
+def _row_types():
+    """Element types of hidden rows: float32, bfloat16, fp8 E4M3 codes (uint8 or float8_e4m3fn)."""
+    global _ROW_TYPES
+    if _ROW_TYPES is None:
+        import torch
+
+        _ROW_TYPES = (torch.float32, torch.bfloat16, torch.uint8, torch.float8_e4m3fn)
+    return _ROW_TYPES
+
+
+def _same_row_type(a, b) -> bool:
     import torch
 
-    if topk_ids.dtype not in (torch.int32, torch.int64) or topk_ids.dim() != 2:
+    fp8 = (torch.uint8, torch.float8_e4m3fn)
+    return a.dtype == b.dtype or (a.dtype in fp8 and b.dtype in fp8)
+
+
+def _permute_args(hidden_states, topk_ids, workspace, offsets, permuted_idx, inv_permuted_idx, num_offsets: int,
+                  permuted_hidden_states=None, token_scale=None, permuted_scale=None, check_rows: bool = True):
+    """Checks shared by the permute entry points; returns (hidden, dtype code, H, workspace bytes, id code)."""
+    import torch
+
+    if topk_ids is None or topk_ids.dtype not in (torch.int32, torch.int64) or topk_ids.dim() != 2:
         raise TypeError("topk_ids must be an int32 or int64 [num_tokens, topk] tensor")
+    dev = topk_ids.device
+    n, topk = topk_ids.shape
+    rows = n * topk
+    _check(topk_ids, "topk_ids", (torch.int32, torch.int64), rows, dev)
     ids_code = MOE_DTYPE_INT64 if topk_ids.dtype == torch.int64 else MOE_DTYPE_INT32
     if hidden_states is None:
         hidden, code, hsize = None, MOE_DTYPE_BF16, 0
     else:
+        if hidden_states.dim() != 2 or hidden_states.shape[0] != n:
+            raise ValueError("hidden_states must be [num_tokens=%d, hidden_size], got shape %s"
+                             % (n, tuple(hidden_states.shape)))
         hidden, code, hsize = hidden_states, _dtype_code(hidden_states), hidden_states.shape[-1]
+        _check(hidden_states, "hidden_states", _row_types(), n * hsize, dev)
+        if check_rows:
+            _check(permuted_hidden_states, "permuted_hidden_states", _row_types(), rows * hsize, dev)
+            if not _same_row_type(permuted_hidden_states, hidden_states):
+                raise TypeError("permuted_hidden_states (%s) must have the type of hidden_states (%s)"
+                                % (permuted_hidden_states.dtype, hidden_states.dtype))
+    _check(offsets, "expert_first_token_offset", (torch.int64,), num_offsets, dev)
+    _check(permuted_idx, "permuted_idx", (torch.int32,), rows, dev)
+    _check(inv_permuted_idx, "inv_permuted_idx", (torch.int32,), rows, dev)
+    if (token_scale is None) != (permuted_scale is None):
+        raise ValueError("token_scale and permuted_scale go together")
+    _check(token_scale, "token_scale", (torch.float32,), n, dev, optional=True)
+    _check(permuted_scale, "permuted_scale", (torch.float32,), rows, dev, optional=True)
+    if workspace is not None:
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        if workspace.device != dev:
+            raise TypeError("workspace is on %s, expected %s" % (workspace.device, dev))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return hidden, code, hsize, ws_bytes, ids_code
+
+
+def _permute_done(topk_ids) -> None:
+    _require_gpu(topk_ids.device)
 
 
 def moe_permute(hidden_states, topk_ids, num_experts: int, permuted_hidden_states,
@@ -153,7 +232,10 @@ def moe_permute(hidden_states, topk_ids, num_experts: int, permuted_hidden_state
     int64 [N, topk] (int64 is read directly, no cast pass).  Outputs are
     written in place.
     """
-    hidden, code, hsize, ws_bytes, ids_code = _permute_args(hidden_states, topk_ids, workspace)
+    hidden, code, hsize, ws_bytes, ids_code = _permute_args(
+        hidden_states, topk_ids, workspace, expert_first_token_offset, permuted_idx, inv_permuted_idx,
+        int(num_experts) + 1, permuted_hidden_states, token_scale, permuted_scale)
+    _permute_done(topk_ids)
     n, topk = topk_ids.shape
     status = load_library().moe_permute(
         _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), ids_code, n, hsize, topk, int(num_experts),
@@ -177,7 +259,11 @@ def moe_permute_local(hidden_states, topk_ids, num_experts: int, expert_map, num
 
     if expert_map is None or expert_map.dtype != torch.int32 or expert_map.shape != (int(num_experts),):
         raise TypeError("expert_map must be an int32 [num_experts] tensor")
-    hidden, code, hsize, ws_bytes, ids_code = _permute_args(hidden_states, topk_ids, workspace)
+    hidden, code, hsize, ws_bytes, ids_code = _permute_args(
+        hidden_states, topk_ids, workspace, expert_first_token_offset, permuted_idx, inv_permuted_idx,
+        int(num_local_experts) + 1, permuted_hidden_states, token_scale, permuted_scale)
+    _check(expert_map, "expert_map", (torch.int32,), int(num_experts), topk_ids.device)
+    _permute_done(topk_ids)
     n, topk = topk_ids.shape
     status = load_library().moe_permute_local(
         _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), ids_code, n, hsize, topk, int(num_experts),
@@ -201,12 +287,22 @@ def moe_permute_quant_fp8(hidden_states, topk_ids, num_experts: int, permuted_co
     """
     import torch
 
-    if hidden_states.dtype not in (torch.bfloat16, torch.float32):
+    if hidden_states is None or hidden_states.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("hidden_states must be bfloat16 or float32")
     if expert_map is not None and (expert_map.dtype != torch.int32 or expert_map.shape != (int(num_experts),)):
         raise TypeError("expert_map must be an int32 [num_experts] tensor")
-    _, code, hsize, ws_bytes, ids_code = _permute_args(hidden_states, topk_ids, workspace)
+    num_offsets = (int(num_local_experts) if expert_map is not None else int(num_experts)) + 1
+    _, code, hsize, ws_bytes, ids_code = _permute_args(
+        hidden_states, topk_ids, workspace, expert_first_token_offset, permuted_idx, inv_permuted_idx, num_offsets,
+        check_rows=False)
     n, topk = topk_ids.shape
+    if group_size < 0 or (group_size and hsize % group_size):
+        raise ValueError("group_size must be 0 (one scale per token) or divide the hidden size %d" % hsize)
+    groups = 1 if group_size == 0 else hsize // group_size
+    _check(permuted_codes, "permuted_codes", (torch.uint8, torch.float8_e4m3fn), n * topk * hsize, topk_ids.device)
+    _check(permuted_scale, "permuted_scale", (torch.float32,), n * topk * groups, topk_ids.device)
+    _check(expert_map, "expert_map", (torch.int32,), int(num_experts), topk_ids.device, optional=True)
+    _permute_done(topk_ids)
     status = load_library().moe_permute_quant_fp8(
         _ptr(hidden_states), code, _ptr(topk_ids), ids_code, n, hsize, topk, int(num_experts), _ptr(expert_map),
         int(num_local_experts) if expert_map is not None else 0, int(group_size), _ptr(permuted_codes),
@@ -226,7 +322,15 @@ def moe_grouped_gemm_bf16(x, w, expert_first_token_offset, y, stream=None) -> No
 
     if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or y.dtype != torch.bfloat16:
         raise TypeError("x, w and y must be bfloat16")
+    if w.dim() != 3 or x.dim() != 2 or y.dim() != 2:
+        raise ValueError("w must be [E, n, k], x [max_rows, k] and y [max_rows, n]")
     e, n, k = w.shape
+    dev = y.device
+    _check(x, "x", (torch.bfloat16,), x.shape[0] * k, dev)
+    _check(w, "w", (torch.bfloat16,), e * n * k, dev)
+    _check(y, "y", (torch.bfloat16,), x.shape[0] * n, dev)
+    _check(expert_first_token_offset, "expert_first_token_offset", (torch.int64,), e + 1, dev)
+    _require_gpu(dev)
     status = load_library().moe_grouped_gemm_bf16(_ptr(x), _ptr(w), _ptr(expert_first_token_offset), e,
                                                    x.shape[0], n, k, _ptr(y), _stream(stream, y))
     if status != MOE_OK:
@@ -240,7 +344,20 @@ def moe_unpermute(expanded_output, topk_weights, inv_permuted_idx, output, strea
     ``topk_weights`` float32 [N, topk], ``inv_permuted_idx`` int32 [N*topk],
     ``output`` [N, H] of the same type as ``expanded_output``.
     """
+    import torch
+
+    if topk_weights is None or topk_weights.dim() != 2:
+        raise ValueError("topk_weights must be a float32 [num_tokens, topk] tensor")
     n, topk = topk_weights.shape
+    if expanded_output is None or expanded_output.dim() != 2 or expanded_output.shape[0] != n * topk:
+        raise ValueError("expanded_output must be [num_tokens * topk = %d, hidden_size]" % (n * topk))
+    h = expanded_output.shape[-1]
+    dev = expanded_output.device
+    _check(expanded_output, "expanded_output", (torch.float32, torch.bfloat16), n * topk * h, dev)
+    _check(topk_weights, "topk_weights", (torch.float32,), n * topk, dev)
+    _check(inv_permuted_idx, "inv_permuted_idx", (torch.int32,), n * topk, dev)
+    _check(output, "output", (expanded_output.dtype,), n * h, dev)
+    _require_gpu(dev)
     status = load_library().moe_unpermute(
         _ptr(expanded_output), _dtype_code(expanded_output), _ptr(topk_weights), _ptr(inv_permuted_idx),
         n, expanded_output.shape[-1], topk, _ptr(output), _stream(stream, output))

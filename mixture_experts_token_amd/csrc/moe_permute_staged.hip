@@ -23,7 +23,8 @@ __global__ __launch_bounds__(NT) void permute_rank_tiles_kernel(PermuteArgs a, i
     const int E = a.num_experts;
     const int B = a.num_buckets;
     const int K = a.topk;
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;  // 2-D grid (staged_grid)
+    if (tile >= num_tiles) return;
     const int64_t t0 = tile * tokens_per_tile;
     const int ntok = (int)min((int64_t)tokens_per_tile, a.num_tokens - t0);
     const int64_t row0 = t0 * K;
@@ -122,7 +123,8 @@ __global__ __launch_bounds__(NT) void permute_scatter_kernel(PermuteArgs a, int 
     const int E = a.num_experts;
     const int B = a.num_buckets;
     const int K = a.topk;
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;  // 2-D grid (staged_grid)
+    if (tile >= num_tiles) return;
     const int64_t t0 = tile * tokens_per_tile;
     const int ntok = (int)min((int64_t)tokens_per_tile, a.num_tokens - t0);
     const int64_t row0 = t0 * K;
@@ -204,15 +206,17 @@ template <int U, bool kMap, typename IdT>
 static void launch_scatter_v(const PermuteArgs& a, const PermutePlan& p, const int32_t* rank_ws,
                              const int32_t* tile_base, const int32_t* total, hipStream_t stream) {
     const size_t lds = scatter_lds_bytes(a.num_buckets, p.tile_rows, map_entries(a));
+    unsigned gx, gy;
+    staged_grid(p.num_tiles, gx, gy);
     if constexpr (U <= kPlainStoreMaxUnroll) {
         if (plain_row_stores(a)) {
-            hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, false, kMap, IdT>),
-                               dim3((unsigned)p.num_tiles), dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile,
-                               p.num_tiles, rank_ws, tile_base, total);
+            hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, false, kMap, IdT>), dim3(gx, gy),
+                               dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws,
+                               tile_base, total);
             return;
         }
     }
-    hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, true, kMap, IdT>), dim3((unsigned)p.num_tiles),
+    hipLaunchKernelGGL((permute_scatter_kernel<kScatterThreads, U, true, kMap, IdT>), dim3(gx, gy),
                        dim3(kScatterThreads), lds, stream, a, p.tokens_per_tile, p.num_tiles, rank_ws, tile_base,
                        total);
 }
@@ -236,9 +240,11 @@ hipError_t launch_permute_staged(const PermuteArgs& a, const PermutePlan& p, voi
     int32_t* total = reinterpret_cast<int32_t*>(ws + p.ws_total);
     with_variant(a, [&](auto map_tag, auto id_tag) {
         MOE_VARIANT_TYPES;
-        hipLaunchKernelGGL((permute_rank_tiles_kernel<kRankThreads, kMap, IdT>), dim3((unsigned)p.num_tiles),
-                           dim3(kRankThreads), rank_lds_bytes(B, p.tile_rows, M), stream, a, p.tokens_per_tile,
-                           p.nbits, p.num_tiles, rank_ws, tile_hist);
+        unsigned gx, gy;
+        staged_grid(p.num_tiles, gx, gy);
+        hipLaunchKernelGGL((permute_rank_tiles_kernel<kRankThreads, kMap, IdT>), dim3(gx, gy), dim3(kRankThreads),
+                           rank_lds_bytes(B, p.tile_rows, M), stream, a, p.tokens_per_tile, p.nbits, p.num_tiles,
+                           rank_ws, tile_hist);
     });
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

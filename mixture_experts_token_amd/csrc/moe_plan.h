@@ -100,6 +100,17 @@ inline size_t staged_workspace_bytes(int64_t rows, int64_t num_tiles, int bucket
     return b;
 }
 
+// Grid of the staged kernels: one workgroup per tile, as a 2-D grid so that
+// num_tiles * threads never exceeds the 32-bit work-item count of one grid
+// dimension (tiles of fewer than 128 rows, e.g. 126 for topk 3, reach it
+// below the 2^31-row limit); workgroups past num_tiles return at once.
+constexpr int64_t kStagedGridX = 65535;
+inline void staged_grid(int64_t num_tiles, unsigned& gx, unsigned& gy) {
+    const int64_t x = num_tiles < kStagedGridX ? (num_tiles > 0 ? num_tiles : 1) : kStagedGridX;
+    gx = (unsigned)x;
+    gy = (unsigned)((num_tiles + x - 1) / x > 0 ? (num_tiles + x - 1) / x : 1);
+}
+
 // Coarse tiles a problem may use: bounded by kMaxCoarseTiles, by the LDS held
 // histogram (entries and the whole workgroup's LDS), for B buckets, a map of
 // map_entries ints and tiles of tile_rows rows.

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "moe_launch.h"
@@ -241,13 +242,52 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict_
     }
 }
 
+// Occupancy cap for large topk-8 reductions.  A topk-8 wave keeps 8 KiB of
+// row loads in flight (eight 1 KiB chunks); with every wave slot of a CU
+// filled that is 256 KiB per CU, and large grids then ran slower than with
+// fewer waves.  At the DSv3 shape (N = 16384, rows of 14 KiB, 57344
+// workgroups) three workgroups of four waves per CU (96 KiB of loads in
+// flight per CU) measured 369 -> 350 us for the unpermute alone and
+// 807 -> 766 us for the permute + unpermute step: the permute after it runs
+// faster as well.  Two, four, five and six workgroups per CU were slower than
+// three.  Small grids need every slot to cover memory latency (Qwen3 shape,
+// 8192 workgroups: fastest uncapped), so the cap applies from
+// kUnpermuteCapMinBlocks workgroups on.  The cap is imposed through dynamic
+// LDS that the kernel never touches: each workgroup reserves just over a
+// quarter of the CU's LDS, so at most three fit on a CU.
+constexpr int kUnpermuteCapTopk = 8;
+constexpr int64_t kUnpermuteCapMinBlocks = 16384;
+constexpr int kUnpermuteCapWorkgroups = 3;
+constexpr int kMaxDevices = 64;
+
+// LDS bytes per workgroup that let at most kUnpermuteCapWorkgroups workgroups
+// share a CU of the current device; 0 when the device cannot be queried.
+static size_t unpermute_cap_lds_bytes() {
+    static std::atomic<int> lds_per_cu[kMaxDevices];  // 0: not queried yet, -1: query failed
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int v = lds_per_cu[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+            v <= 0)
+            v = -1;
+        lds_per_cu[dev].store(v, std::memory_order_relaxed);
+    }
+    if (v < 0) return 0;
+    // cap * bytes <= v < (cap + 1) * bytes, whatever the allocation granularity
+    // (below v / (cap * (cap + 1)) bytes)
+    return (size_t)(v / (kUnpermuteCapWorkgroups + 1)) + 1;
+}
+
 template <bool kBF16, int KC, int U, int G>
 static hipError_t launch_unpermute_t(const UnpermuteArgs& a, hipStream_t stream) {
     const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
     const int64_t items = a.num_tokens * nchunks;
     const int64_t blocks_needed = (items + 3) / 4;
     const int64_t blocks = blocks_needed < kMaxGridBlocks ? blocks_needed : kMaxGridBlocks;
-    hipLaunchKernelGGL((unpermute_kernel<kBF16, KC, U, G>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    const size_t lds =
+        KC == kUnpermuteCapTopk && blocks >= kUnpermuteCapMinBlocks ? unpermute_cap_lds_bytes() : 0;
+    hipLaunchKernelGGL((unpermute_kernel<kBF16, KC, U, G>), dim3((unsigned)blocks), dim3(256), lds, stream,
                        reinterpret_cast<const u32x4*>(a.expanded_output), a.topk_weights, a.inv_permuted_idx,
                        reinterpret_cast<u32x4*>(a.output), a.num_tokens, a.row_vecs, a.topk, blocks * 4);
     return hipGetLastError();

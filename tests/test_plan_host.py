@@ -7,6 +7,8 @@ walks a grid of shapes and asserts, for every plan:
   * coarse: coarse tiles are whole tiles, at most kMaxCoarseTiles of them,
     histogram entries <= kCoarseMaxHist, rows before a tile inside its coarse
     tile <= kCoarseMaxRowsPerTile, LDS of the scatter kernel <= 64 KiB;
+  * staged: each grid dimension of the rank and scatter kernels within 32-bit
+    work-item counts, up to the largest accepted row count;
   * the workspace query bounds the requirement of every smaller call and is
     monotone in the token count.
 The grid covers the plain sort over E experts and the local-expert sort over
@@ -27,7 +29,28 @@ DRIVER = r'''
 using namespace moe;
 static int fails = 0;
 #define CHECK(c, ...) do { if (!(c)) { ++fails; std::printf("FAIL %s: ", #c); std::printf(__VA_ARGS__); std::printf("\n"); } } while (0)
+// Every grid dimension of the staged kernels stays within 32-bit work-item
+// counts, and the grid covers every tile.
+static void check_staged_grid(const PermutePlan& p) {
+  unsigned gx = 0, gy = 0;
+  staged_grid(p.num_tiles, gx, gy);
+  const unsigned long long lim = 0xFFFFFFFFull;
+  CHECK((unsigned long long)gx * kRankThreads <= lim && (unsigned long long)gx * kScatterThreads <= lim, "grid x %u", gx);
+  CHECK((unsigned long long)gy <= lim && gy <= 65535u, "grid y %u", gy);
+  CHECK((long long)gx * gy >= p.num_tiles, "grid %u x %u covers %lld tiles", gx, gy, (long long)p.num_tiles);
+  CHECK((long long)gx * (gy - 1) < p.num_tiles || p.num_tiles == 0, "no all-empty grid row");
+}
 int main() {
+  // the largest accepted row counts (N * topk < 2^31): tiles below 128 rows for topk 3 and 5
+  for (int K : {1, 2, 3, 5, 7, 8}) {
+    const long long N = ((1LL << 31) - 1) / K;
+    const PermutePlan p = plan_permute(N, K, 64, 0);
+    CHECK(!p.fused && !p.coarse, "K=%d N=%lld staged", K, N);
+    check_staged_grid(p);
+  }
+  // without the 2-D grid topk 3 (126-row tiles) would need more than 2^32 work-items in one dimension
+  CHECK((long long)plan_permute(((1LL << 31) - 1) / 3, 3, 64, 0).num_tiles * kScatterThreads > 0xFFFFFFFFLL,
+        "the limit case is the one the 2-D grid exists for");
   const int Ks[] = {1, 2, 3, 8, 16, 64, 512, 1024};
   const int Es[] = {1, 8, 37, 128, 256, 1000, 1024};
   const long long Ns[] = {1, 7, 100, 2047, 2048, 2049, 4096, 8192, 8193, 16384, 30000, 65536, 140000, 1000000};
@@ -69,6 +92,7 @@ int main() {
         CHECK(p.ws_bytes >= staged_workspace_bytes(p.rows, p.num_tiles, B), "staged workspace");
         CHECK(rank_lds_bytes(B, p.tile_rows, M) <= 4 * (size_t)kMaxLdsInts, "rank lds");
         CHECK(scatter_lds_bytes(B, p.tile_rows, M) <= 4 * (size_t)kMaxLdsInts, "scatter lds");
+        check_staged_grid(p);
       }
     }
   }
