@@ -21,6 +21,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <initializer_list>
 
 namespace moe {
 
@@ -39,11 +40,12 @@ constexpr int kScanPerThread = 8;                  // tile counts one scan threa
 constexpr int kMaxExperts = 1024;
 constexpr int64_t kFusedMaxRows = 16384;           // fused schedule up to this many expanded rows
 constexpr int kStagedTileRows = 128;               // target expanded rows per staged tile
+constexpr int kCoarseCopyTileRows = 64;            // coarse tiles of a copying permute without an expert map
 constexpr int kFusedTargetBlocks = 512;
 constexpr int kMaxTileRows = 1024;                 // LDS staging bound for one tile
 constexpr size_t kWorkspaceAlign = 256;
 constexpr int kQuantMaxRowVecs = 1024;             // quantise-scatter: a wave holds the whole row (16 KiB)
-constexpr int kIndexOnlyTileScale = 4;             // coarse tiles of an index-only permute, vs the standard ones
+constexpr int kIndexOnlyTileScale = 4;             // coarse tiles of an index-only permute, vs the staged ones
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -93,6 +95,19 @@ inline int staged_tokens_per_tile(int topk) {
     return t < 1 ? 1 : t;
 }
 
+// Tokens per coarse tile of a permute that copies rows and has no expert map:
+// about kCoarseCopyTileRows rows.  Twice as many tiles as with staged-size
+// tiles keeps more workgroups resident (four per CU instead of two at the
+// Qwen3 shape, whose 512 staged-size tiles filled half the wave slots):
+// Qwen3-shaped permute 63.0 -> 59.0 us; DSv3-shaped unchanged (write bound).
+// With an expert map the staged size stays: a lightly loaded rank copies
+// about one row per token, and its fixed per-tile index work then dominates
+// (measured slower with 64-row tiles).
+inline int coarse_copy_tokens_per_tile(int topk) {
+    int t = kCoarseCopyTileRows / topk;
+    return t < 1 ? 1 : t;
+}
+
 inline size_t staged_workspace_bytes(int64_t rows, int64_t num_tiles, int buckets) {
     size_t b = align_up(sizeof(int32_t) * (size_t)rows, kWorkspaceAlign);
     b += align_up(sizeof(int32_t) * (size_t)(buckets + 1) * (size_t)num_tiles, kWorkspaceAlign);
@@ -139,28 +154,34 @@ inline size_t coarse_workspace_bytes(int num_coarse, int buckets) {
     return align_up(sizeof(int32_t) * (size_t)num_coarse * (size_t)(buckets + 1), kWorkspaceAlign);
 }
 
+inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int map_entries, bool index_only = false);
+
 // Workspace of a call with max_num_tokens tokens; every call with fewer tokens
-// needs no more: the schedules go fused -> coarse -> staged as the row count
-// grows, a coarse call needs at most max_coarse_tiles(B) histogram rows, and
-// the staged size grows with the row and tile counts (the tile size depends
-// on topk only).
+// needs no more.  A coarse call needs at most max_coarse_tiles histogram rows
+// for the tile size it uses (the staged size, or the copy size without a map);
+// a call takes the staged schedule only when the coarse one does not apply,
+// which holds for every larger row count too, and the staged size grows with
+// the row count -- so the plans at max_num_tokens bound the staged case.
 inline size_t workspace_bound(int64_t max_num_tokens, int topk, int buckets, int map_entries) {
     const int64_t rows = max_num_tokens * topk;
     if (rows <= kFusedMaxRows) return 0;
-    const int tpt = staged_tokens_per_tile(topk);
-    const int tile_rows = tpt * topk;
-    const int nmax = max_coarse_tiles(buckets, tile_rows, map_entries);
-    const size_t coarse = nmax > 0 ? coarse_workspace_bytes(nmax, buckets) : 0;
-    if (coarse_rows_for(rows, buckets, tile_rows, map_entries) > 0) return coarse;
-    const int64_t tiles = (max_num_tokens + tpt - 1) / tpt;
-    const size_t staged = staged_workspace_bytes(rows, tiles, buckets);
-    return staged > coarse ? staged : coarse;
+    size_t b = 0;
+    const int sizes[2] = {staged_tokens_per_tile(topk), coarse_copy_tokens_per_tile(topk)};
+    for (int i = 0; i < (map_entries == 0 ? 2 : 1); ++i) {
+        const int nmax = max_coarse_tiles(buckets, sizes[i] * topk, map_entries);
+        if (nmax > 0 && coarse_workspace_bytes(nmax, buckets) > b) b = coarse_workspace_bytes(nmax, buckets);
+    }
+    for (bool index_only : {false, true}) {
+        const size_t w = plan_permute(max_num_tokens, topk, buckets, map_entries, index_only).ws_bytes;
+        if (w > b) b = w;
+    }
+    return b;
 }
 
 // index_only: no rows are copied (the quantising permute moves them in a
 // second kernel), so fewer, larger tiles: every fused workgroup counts all ids,
 // and without a row copy to hide behind that count is the kernel's cost.
-inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int map_entries, bool index_only = false) {
+inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int map_entries, bool index_only) {
     PermutePlan p;
     p.rows = num_tokens * topk;
     p.nbits = key_bits(buckets);
@@ -176,13 +197,17 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int m
     } else {
         p.fused = false;
         p.tokens_per_tile = staged_tokens_per_tile(topk);
+        const int small = coarse_copy_tokens_per_tile(topk);
+        if (!index_only && map_entries == 0 && small < p.tokens_per_tile &&
+            coarse_rows_for(p.rows, buckets, small * topk, map_entries) > 0)
+            p.tokens_per_tile = small;
     }
     if (!p.fused && index_only) {
         // Without a row copy the fixed index work of each tile is the cost, so
-        // the coarse schedule takes tiles kIndexOnlyTileScale times larger
-        // (whole tokens, at most kMaxTileRows rows) where it still applies
+        // the coarse schedule takes tiles kIndexOnlyTileScale times the staged
+        // size (whole tokens, at most kMaxTileRows rows) where it still applies
         // with them; the histogram then has no more rows than with the
-        // standard tiles, so the workspace bound holds.
+        // staged-size tiles, so the workspace bound holds.
         int64_t big = (int64_t)p.tokens_per_tile * kIndexOnlyTileScale;
         const int64_t cap = kMaxTileRows / topk;
         if (big > cap) big = cap;

@@ -10,6 +10,13 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # The sanitizer test runs the host checks against a sanitizer build of the C ABI.
+    lib = os.environ.get("MOE_TEST_PERMUTE_LIB")
+    if lib:
+        from mixture_experts_token_amd import binding
+
+        binding.LIB_PATH = lib
+        binding._lib = None
 
 
 def gpu_available() -> bool:

@@ -340,7 +340,7 @@ def test_streaming_probe_library_checks_arguments():
     """The bench's ceiling probe (libhbm_probe.so) loads and rejects bad sizes before any launch."""
     import os
 
-    path = os.path.join(os.path.dirname(binding.LIB_PATH), "libhbm_probe.so")
+    path = os.path.join(os.path.dirname(os.path.abspath(binding.__file__)), "libhbm_probe.so")
     probe = ctypes.CDLL(path)
     for fn in (probe.hbm_probe_fanout, probe.hbm_probe_reduce):
         fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,

@@ -99,6 +99,10 @@ int main() {
   // the named workloads take the schedules the design notes describe
   CHECK(plan_permute(4096, 2, 8, 0).fused, "mixtral fused");
   CHECK(plan_permute(8192, 8, 128, 0).coarse, "qwen3 coarse");
+  CHECK(plan_permute(8192, 8, 128, 0).tile_rows == 64, "qwen3 coarse copy tiles of 64 rows");
+  CHECK(plan_permute(16384, 8, 256, 0).tile_rows == 64, "dsv3 coarse copy tiles of 64 rows");
+  CHECK(plan_permute(8192, 8, 128, 0, true).tile_rows == 512, "qwen3 index-only tiles of 512 rows");
+  CHECK(plan_permute(16384, 8, 32, 256).tile_rows == 128, "expert map: staged-size tiles");
   CHECK(plan_permute(16384, 8, 256, 0).coarse, "dsv3 coarse");
   CHECK(plan_permute(256, 8, 256, 0).fused, "decode fused");
   CHECK(!plan_permute(140000, 2, 16, 0).coarse && !plan_permute(140000, 2, 16, 0).fused, "large staged");
@@ -113,6 +117,7 @@ def test_plans_respect_kernel_bounds(tmp_path):
     src = tmp_path / "plan_driver.cpp"
     src.write_text(DRIVER)
     exe = tmp_path / "plan_driver"
-    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-I", CSRC, "-o", str(exe), str(src)], check=True)
+    extra = os.environ.get("MOE_TEST_SANITIZE_FLAGS", "").split()  # set by the sanitizer test
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", *extra, "-I", CSRC, "-o", str(exe), str(src)], check=True)
     res = subprocess.run([str(exe)], capture_output=True, text=True)
     assert res.returncode == 0, res.stdout[-3000:]
