@@ -137,6 +137,33 @@ moe_status_t moe_permute(const void *hidden_states, int32_t dtype, const float *
                          void *stream);
 
 /*
+ * moe_permute_static_scratch -- moe_permute for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results without `workspace` /
+ * `workspace_bytes`.  The workspace is a static device array of the library,
+ * MOE_STATIC_SCRATCH_BYTES bytes per GPU, held from library load until the
+ * process ends; the call allocates nothing (its first call on a device looks
+ * up that device's copy with hipGetSymbolAddress).
+ *   - Limit: a call whose moe_permute would need more than
+ *     MOE_STATIC_SCRATCH_BYTES of workspace (moe_permute_workspace_size) returns
+ *     MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  Up to 16384
+ *     expanded rows no workspace is used at all; up to a few hundred thousand
+ *     rows (the coarse schedule) it needs at most 32 KiB.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *     GPU (other streams, other threads, other processes' contexts excepted)
+ *     race and must be ordered by the caller.  The kernels initialise every
+ *     workspace word they read, so the contents left by an earlier call never
+ *     matter.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)4 << 20)
+moe_status_t moe_permute_static_scratch(const void *hidden_states, int32_t dtype, const float *token_scale,
+                                        const void *topk_ids, int32_t topk_ids_dtype, int64_t num_tokens,
+                                        int64_t hidden_size, int32_t topk, int32_t num_experts,
+                                        void *permuted_hidden_states, float *permuted_scale,
+                                        int64_t *expert_first_token_offset, int32_t *permuted_idx,
+                                        int32_t *inv_permuted_idx, void *stream);
+
+/*
  * moe_permute_local_workspace_size -- as moe_permute_workspace_size, for
  * moe_permute_local with this num_local_experts.  Pure host function; returns
  * 0 outside the limits (those of moe_permute, and

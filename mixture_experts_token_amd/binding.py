@@ -8,7 +8,7 @@ is missing the first call raises.
 The entry points carry the C names: ``moe_permute_supported``,
 ``moe_permute_workspace_size``, ``moe_permute``, ``moe_unpermute``,
 ``moe_permute_local_workspace_size``, ``moe_permute_local``,
-``moe_permute_quant_fp8``, ``moe_grouped_gemm_bf16``.
+``moe_permute_quant_fp8``, ``moe_grouped_gemm_bf16``, ``moe_permute_static_scratch``.
 ``MoEPermuteScratch`` follows the preallocated-buffer design of the prhub
 summary of vLLM PR #43014 (section "key code snippets", MoEPermuteScratch):
 every buffer is allocated once for ``max_num_tokens`` and reused by each call.
@@ -61,6 +61,8 @@ def load_library() -> ctypes.CDLL:
         lib.moe_permute_workspace_size.restype = sz
         lib.moe_permute.argtypes = [p, i32, p, p, i32, i64, i64, i32, i32, p, p, p, p, p, p, sz, p]
         lib.moe_permute.restype = ctypes.c_int
+        lib.moe_permute_static_scratch.argtypes = [p, i32, p, p, i32, i64, i64, i32, i32, p, p, p, p, p, p]
+        lib.moe_permute_static_scratch.restype = ctypes.c_int
         lib.moe_permute_local_workspace_size.argtypes = [i64, i32, i32, i32]
         lib.moe_permute_local_workspace_size.restype = sz
         lib.moe_permute_local.argtypes = [p, i32, p, p, i32, i64, i64, i32, i32, p, i32, p, p, p, p, p, p, sz, p]
@@ -244,6 +246,31 @@ def moe_permute(hidden_states, topk_ids, num_experts: int, permuted_hidden_state
         _ptr(workspace), ws_bytes, _stream(stream, topk_ids))
     if status != MOE_OK:
         raise MoEError(status, "moe_permute")
+
+
+MOE_STATIC_SCRATCH_BYTES = 4 << 20  # the library's static workspace per GPU (moe_permute_static_scratch)
+
+
+def moe_permute_static_scratch(hidden_states, topk_ids, num_experts: int, permuted_hidden_states,
+                               expert_first_token_offset, permuted_idx, inv_permuted_idx, token_scale=None,
+                               permuted_scale=None, stream=None) -> None:
+    """moe_permute without a workspace argument, for callers that cannot allocate.
+
+    The library's static per-GPU array (MOE_STATIC_SCRATCH_BYTES) is the
+    workspace; calls that overlap on one GPU race.  A call that needs more
+    workspace than that raises MoEError (MOE_ERR_WORKSPACE_TOO_SMALL).
+    """
+    hidden, code, hsize, _, ids_code = _permute_args(
+        hidden_states, topk_ids, None, expert_first_token_offset, permuted_idx, inv_permuted_idx,
+        int(num_experts) + 1, permuted_hidden_states, token_scale, permuted_scale)
+    _permute_done(topk_ids)
+    n, topk = topk_ids.shape
+    status = load_library().moe_permute_static_scratch(
+        _ptr(hidden), code, _ptr(token_scale), _ptr(topk_ids), ids_code, n, hsize, topk, int(num_experts),
+        _ptr(permuted_hidden_states) if hsize else None, _ptr(permuted_scale),
+        _ptr(expert_first_token_offset), _ptr(permuted_idx), _ptr(inv_permuted_idx), _stream(stream, topk_ids))
+    if status != MOE_OK:
+        raise MoEError(status, "moe_permute_static_scratch")
 
 
 def moe_permute_local(hidden_states, topk_ids, num_experts: int, expert_map, num_local_experts: int,

@@ -65,6 +65,8 @@ hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t value, hip
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, int num_cus, hipStream_t stream);
 hipError_t launch_quant_scatter(const QuantArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream);
+// Device address of the current device's static workspace (kStaticScratchBytes).
+hipError_t static_scratch_address(void** ptr);
 // One schedule each (u: 16-byte vectors per lane in the row copy).
 hipError_t launch_permute_fused(const PermuteArgs& a, const PermutePlan& p, int u, hipStream_t stream);
 hipError_t launch_permute_coarse(const PermuteArgs& a, const PermutePlan& p, void* workspace, int u,

@@ -2,8 +2,9 @@
 //
 // Every argument check runs on the host before anything touches HIP, so a
 // rejected call has no side effect and the checks work on a host with no GPU.
-// The only HIP calls are the kernel launches (and, in moe_permute_supported,
-// the device queries).
+// The only HIP calls are the kernel launches, the device queries of
+// moe_permute_supported and the grouped GEMM, and (after every check of a
+// moe_permute_static_scratch call) the lookup of the static workspace.
 
 #include "moe_permute.h"
 
@@ -107,7 +108,7 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
                           int32_t num_experts, const int32_t* expert_map, int32_t num_local_experts,
                           void* permuted_hidden_states, float* permuted_scale, int64_t* expert_first_token_offset,
                           int32_t* permuted_idx, int32_t* inv_permuted_idx, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, void* stream, bool static_workspace = false) {
     const int64_t eb = element_bytes(dtype);
     if (eb == 0) return MOE_ERR_INVALID_ARG;
     if (!sizes_ok(num_tokens, topk, num_experts)) return MOE_ERR_INVALID_ARG;
@@ -141,10 +142,16 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
 
     const moe::PermutePlan plan =
         moe::plan_permute(num_tokens, topk, buckets, map_entries, hidden_size == 0 && token_scale == nullptr);
-    if (workspace_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    if (plan.ws_bytes > 0) {
-        if (workspace == nullptr) return MOE_ERR_INVALID_ARG;
-        if (!aligned(workspace, 16)) return MOE_ERR_MISALIGNED;
+    if (static_workspace) {
+        // the library's static array stands in for the caller's workspace
+        if (plan.ws_bytes > moe::kStaticScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+        workspace = nullptr;
+    } else {
+        if (workspace_bytes < plan.ws_bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+        if (plan.ws_bytes > 0) {
+            if (workspace == nullptr) return MOE_ERR_INVALID_ARG;
+            if (!aligned(workspace, 16)) return MOE_ERR_MISALIGNED;
+        }
     }
 
     const uint64_t rows = (uint64_t)plan.rows;
@@ -164,6 +171,10 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
         {expert_map, 4ull * (uint64_t)map_entries},
     };
     if (any_overlap(outs, 6, ins, 4)) return MOE_ERR_INVALID_ARG;
+    // Every check has passed; only now, and only when the plan uses a
+    // workspace, look up this device's static array (once per device).
+    if (static_workspace && plan.ws_bytes > 0 && moe::static_scratch_address(&workspace) != hipSuccess)
+        return MOE_ERR_HIP;
 
     moe::PermuteArgs a;
     a.hidden_states = copy_rows ? hidden_states : nullptr;
@@ -196,6 +207,19 @@ moe_status_t moe_permute(const void* hidden_states, int32_t dtype, const float* 
     return permute_impl(hidden_states, dtype, token_scale, topk_ids, topk_ids_dtype, num_tokens, hidden_size, topk,
                         num_experts, nullptr, 0, permuted_hidden_states, permuted_scale, expert_first_token_offset,
                         permuted_idx, inv_permuted_idx, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_permute_static_scratch(const void* hidden_states, int32_t dtype, const float* token_scale,
+                                        const void* topk_ids, int32_t topk_ids_dtype, int64_t num_tokens,
+                                        int64_t hidden_size, int32_t topk, int32_t num_experts,
+                                        void* permuted_hidden_states, float* permuted_scale,
+                                        int64_t* expert_first_token_offset, int32_t* permuted_idx,
+                                        int32_t* inv_permuted_idx, void* stream) {
+    // moe_permute's checks and plan; the workspace is the device's static
+    // array (no allocation: it exists from library load).
+    return permute_impl(hidden_states, dtype, token_scale, topk_ids, topk_ids_dtype, num_tokens, hidden_size, topk,
+                        num_experts, nullptr, 0, permuted_hidden_states, permuted_scale, expert_first_token_offset,
+                        permuted_idx, inv_permuted_idx, nullptr, 0, stream, true);
 }
 
 moe_status_t moe_permute_local(const void* hidden_states, int32_t dtype, const float* token_scale,

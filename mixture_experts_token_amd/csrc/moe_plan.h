@@ -44,6 +44,7 @@ constexpr int kCoarseCopyTileRows = 64;            // coarse tiles of a copying 
 constexpr int kFusedTargetBlocks = 512;
 constexpr int kMaxTileRows = 1024;                 // LDS staging bound for one tile
 constexpr size_t kWorkspaceAlign = 256;
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;  // workspace of moe_permute_static_scratch
 constexpr int kQuantMaxRowVecs = 1024;             // quantise-scatter: a wave holds the whole row (16 KiB)
 constexpr int kIndexOnlyTileScale = 4;             // coarse tiles of an index-only permute, vs the staged ones
 

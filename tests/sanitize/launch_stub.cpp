@@ -43,6 +43,11 @@ long moe_stub_launches(void) { return g_launches.load(); }
 
 namespace moe {
 
+hipError_t static_scratch_address(void** ptr) {
+    *ptr = nullptr;
+    return hipErrorNoDevice;
+}
+
 hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t, hipStream_t) {
     require(off != nullptr && num_experts >= 1 && num_experts <= kMaxExperts, "fill offsets");
     return hipSuccess;

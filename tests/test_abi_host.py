@@ -49,8 +49,8 @@ host_only = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer checks run on
 def test_header_declares_the_boundary():
     assert declared_functions() == ["moe_grouped_gemm_bf16", "moe_permute", "moe_permute_local",
                                     "moe_permute_local_workspace_size", "moe_permute_quant_fp8",
-                                    "moe_permute_supported", "moe_permute_workspace_size", "moe_status_string",
-                                    "moe_unpermute"]
+                                    "moe_permute_static_scratch", "moe_permute_supported",
+                                    "moe_permute_workspace_size", "moe_status_string", "moe_unpermute"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -351,3 +351,19 @@ def test_streaming_probe_library_checks_arguments():
         assert fn(addr(0), addr(1), 10, 24, 2, 1, None) == 1
         assert fn(addr(0), addr(1), 10, 64, 0, 1, None) == 1
         assert fn(addr(0), addr(1), 10, 64, 2, 8, None) == 1  # variant out of range
+
+
+@host_only
+def test_static_scratch_rejects_calls_beyond_its_array(lib):
+    """moe_permute_static_scratch: a call whose workspace would exceed the
+    static array is refused on the host; other checks are moe_permute's."""
+    fake = ctypes.c_void_p(1 << 20)
+    n, k, e = 600000, 2, 16
+    assert lib.moe_permute_workspace_size(n, k, e) > binding.MOE_STATIC_SCRATCH_BYTES
+    st = lib.moe_permute_static_scratch(None, BF16, None, fake, I32, n, 0, k, e, None, None, fake,
+                                        ctypes.c_void_p((1 << 20) + (1 << 24)), ctypes.c_void_p((1 << 20) + (2 << 24)),
+                                        None)
+    assert st == TOO_SMALL
+    # moe_permute's own checks still apply (here: topk > num_experts)
+    assert lib.moe_permute_static_scratch(None, BF16, None, fake, I32, 8, 0, 9, 8, None, None, fake, fake, fake,
+                                          None) == INVALID
