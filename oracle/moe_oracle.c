@@ -402,6 +402,12 @@ int oracle_quantize_fp8_rows(const void *x, int x_is_bf16, int64_t rows, int64_t
                 float v = x_is_bf16 ? (float)oracle_bf16_to_double(((const uint16_t *)x)[r * h + i])
                                     : ((const float *)x)[r * h + i];
                 float q = v / scale;
+                /* A NaN quotient (a NaN element, or an infinite one divided by an
+                   infinite scale) takes the one code 0x7F.  IEEE 754 leaves the sign
+                   of a NaN that arithmetic produces unspecified, and x86 (negative
+                   default NaN) and the GPU (positive) differ, so a code that copied
+                   it would depend on the machine.  The format codec keeps a NaN's
+                   sign because it converts bits, not an arithmetic result. */
                 codes[r * h + i] = isnan(q) ? 0x7Fu : oracle_double_to_e4m3((double)q);
             }
         }
