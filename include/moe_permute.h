@@ -111,7 +111,8 @@ size_t moe_permute_workspace_size(int64_t max_num_tokens, int32_t topk, int32_t 
  *                            such and range-checked, never truncated; this removes the
  *                            separate int64 -> int32 cast pass that the summary of vLLM
  *                            PR #43014 shows in prepare_topk_ids ("key code snippets").
- *   num_tokens, hidden_size, topk, num_experts   sizes (hidden_size 0: indices only)
+ *   num_tokens, hidden_size, topk, num_experts   sizes (hidden_size 0: no rows move;
+ *                            the indices, and the scales when token_scale is given, do)
  *   permuted_hidden_states   [N*topk, hidden_size] of `dtype` (out); ignored when hidden_size == 0
  *   permuted_scale           [N*topk] float (out); non-NULL exactly when token_scale is
  *   expert_first_token_offset [num_experts + 1] int64 (out)

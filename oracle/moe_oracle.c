@@ -136,8 +136,9 @@ void oracle_gather_rows(const uint8_t *hidden_states, int64_t row_bytes,
 {
     for (int64_t j = 0; j < num_rows; ++j) {
         int64_t t = permuted_idx[j] / topk;
-        memcpy(permuted_hidden_states + j * row_bytes, hidden_states + t * row_bytes,
-               (size_t)row_bytes);
+        if (row_bytes > 0)
+            memcpy(permuted_hidden_states + j * row_bytes, hidden_states + t * row_bytes,
+                   (size_t)row_bytes);
         if (token_scale != NULL && permuted_scale != NULL)
             permuted_scale[j] = token_scale[t];
     }
@@ -180,7 +181,9 @@ int oracle_moe_permute(const uint8_t *hidden_states, int64_t row_bytes,
                                             expert_first_token_offset, permuted_idx,
                                             inv_permuted_idx);
     }
-    if (status == ORACLE_OK && row_bytes > 0)
+    /* A token's scale moves with it to every destination, also when its row is
+       zero bytes wide (a call that moves indices and scales only). */
+    if (status == ORACLE_OK && (row_bytes > 0 || token_scale != NULL))
         oracle_gather_rows(hidden_states, row_bytes, token_scale, permuted_idx,
                            num_tokens * topk, topk, permuted_hidden_states,
                            permuted_scale);
@@ -254,7 +257,7 @@ int oracle_moe_permute_local(const uint8_t *hidden_states, int64_t row_bytes,
             permuted_idx[j] = (int32_t)r;
             inv_permuted_idx[r] = (int32_t)j;
         }
-        if (row_bytes > 0)
+        if (row_bytes > 0 || token_scale != NULL)
             oracle_gather_rows(hidden_states, row_bytes, token_scale, permuted_idx,
                                expert_first_token_offset[num_local_experts], topk,
                                permuted_hidden_states, permuted_scale);

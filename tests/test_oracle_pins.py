@@ -783,3 +783,27 @@ def test_grouped_gemm_rejects_bad_offsets():
         oracle.grouped_gemm_bf16(x, w, np.array([0, 3, 2], np.int64))
     with pytest.raises(oracle.OracleError):
         oracle.grouped_gemm_bf16(x, w, np.array([1, 2, 3], np.int64))
+
+
+@pytest.mark.parametrize("local", [False, True])
+def test_scales_move_on_an_indices_only_call(local):
+    """Rows zero bytes wide: the indices are the usual ones and each token's
+    scale still reaches every destination of its rows (slot j gets the scale of
+    token perm[j] // topk), with and without an expert map."""
+    rng = np.random.default_rng(12)
+    n, k, e = 9, 3, 5
+    ids = np.stack([rng.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    scale = (rng.random(n) + 0.5).astype(np.float32)
+    empty = np.zeros((n, 0), np.float32)
+    if local:
+        emap = np.array([0, -1, 1, -1, 0], np.int32)
+        got = oracle.permute_local(empty, ids, e, emap, 2, token_scale=scale)
+        full = oracle.permute_local(np.zeros((n, 4), np.float32), ids, e, emap, 2, token_scale=scale)
+    else:
+        got = oracle.permute(empty, ids, e, token_scale=scale)
+        full = oracle.permute(np.zeros((n, 4), np.float32), ids, e, token_scale=scale)
+    m = int(got["expert_first_token_offset"][-1])
+    perm = got["permuted_idx"][:m]
+    assert got["permuted_scale"][:m].tolist() == [float(scale[r // k]) for r in perm]
+    np.testing.assert_array_equal(got["permuted_idx"], full["permuted_idx"])
+    np.testing.assert_array_equal(got["permuted_scale"], full["permuted_scale"])
