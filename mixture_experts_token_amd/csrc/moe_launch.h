@@ -68,6 +68,7 @@ hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* work
 // Device address of the current device's static workspace (kStaticScratchBytes).
 hipError_t static_scratch_address(void** ptr);
 // One schedule each (u: 16-byte vectors per lane in the row copy).
+hipError_t launch_permute_wave(const PermuteArgs& a, const PermutePlan& p, int u, hipStream_t stream);
 hipError_t launch_permute_fused(const PermuteArgs& a, const PermutePlan& p, int u, hipStream_t stream);
 hipError_t launch_permute_coarse(const PermuteArgs& a, const PermutePlan& p, void* workspace, int u,
                                  hipStream_t stream);

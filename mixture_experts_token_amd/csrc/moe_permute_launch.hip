@@ -48,6 +48,7 @@ hipError_t static_scratch_address(void** ptr) {
 hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream) {
     const int u = a.topk >= 4 ? choose_unroll(a.row_vecs, kCopyUnrollsWideFanout, 4)
                               : choose_unroll(a.row_vecs, kCopyUnrolls, 8);
+    if (p.wave) return launch_permute_wave(a, p, u, stream);
     if (p.fused) return launch_permute_fused(a, p, u, stream);
     if (p.coarse) return launch_permute_coarse(a, p, workspace, u, stream);
     return launch_permute_staged(a, p, workspace, u, stream);

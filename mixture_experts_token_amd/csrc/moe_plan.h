@@ -3,6 +3,9 @@
 // Pure C++ with no HIP call, so the size query and the argument checks work on
 // a host without a GPU.  The plan fixes, for one call:
 //   * which permute schedule runs:
+//       wave   -- one kernel of one-wave workgroups for at most kWaveMaxRows
+//                 rows without an expert map (decode): every wave computes
+//                 the whole index itself, with no workgroup barrier;
 //       fused  -- one kernel; every workgroup counts all expert ids itself
 //                 (cheap while N*topk is small, and it avoids extra launches);
 //       coarse -- two kernels: expert counts per coarse tile (a few dozen),
@@ -39,6 +42,8 @@ constexpr int64_t kMaxGridBlocks = int64_t(1) << 20;  // beyond this, waves loop
 constexpr int kScanPerThread = 8;                  // tile counts one scan thread holds per pass
 constexpr int kMaxExperts = 1024;
 constexpr int64_t kFusedMaxRows = 16384;           // fused schedule up to this many expanded rows
+constexpr int64_t kWaveMaxRows = 128;              // wave schedule up to this many rows (2 ids per lane)
+constexpr int64_t kWaveMaxChunkBlocks = 4096;      // wave schedule grid (chunks per token); waves loop beyond
 constexpr int kStagedTileRows = 128;               // target expanded rows per staged tile
 constexpr int kCoarseCopyTileRows = 64;            // coarse tiles of a copying permute without an expert map
 constexpr int kFusedTargetBlocks = 512;
@@ -72,6 +77,7 @@ inline int key_bits(int buckets) {
 }
 
 struct PermutePlan {
+    bool wave = false;            // one-wave workgroups, whole index per wave (no workspace)
     bool fused = false;
     bool coarse = false;          // two-kernel schedule (only when !fused)
     int coarse_rows = 0;          // expanded rows per coarse tile (a multiple of tile_rows)
@@ -186,6 +192,13 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int m
     PermutePlan p;
     p.rows = num_tokens * topk;
     p.nbits = key_bits(buckets);
+    if (p.rows >= 1 && p.rows <= kWaveMaxRows && map_entries == 0) {
+        p.wave = true;
+        p.tokens_per_tile = (int)num_tokens;
+        p.tile_rows = (int)p.rows;
+        p.num_tiles = 1;
+        return p;
+    }
     if (p.rows <= kFusedMaxRows) {
         p.fused = true;
         // Enough workgroups to spread the row copy, at most kFusedThreads rows per tile.
@@ -237,6 +250,7 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int m
 
 // Dynamic LDS bytes of each kernel for one tile shape (B buckets; the map,
 // when there is one, sits after everything else).
+inline size_t wave_lds_bytes(int experts, int rows) { return sizeof(int) * ((size_t)experts + (size_t)rows); }
 inline size_t fused_lds_bytes(int buckets, int tile_rows, int map_entries) {
     return sizeof(int) *
            ((size_t)(2 + kFusedThreads / kWaveSize) * buckets + (size_t)tile_rows + 16 + (size_t)map_entries);

@@ -62,6 +62,7 @@ hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* work
     return hipSuccess;
 }
 
+hipError_t launch_permute_wave(const PermuteArgs&, const PermutePlan&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_permute_fused(const PermuteArgs&, const PermutePlan&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_permute_coarse(const PermuteArgs&, const PermutePlan&, void*, int, hipStream_t) {
     return hipErrorNoDevice;

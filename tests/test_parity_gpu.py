@@ -147,8 +147,15 @@ EDGE = [
     (513, 8, 256, 16, "fp8_e4m3", "distinct"),
     (2600, 8, 256, 7168, "fp8_e4m3", "distinct"),
     (140000, 2, 16, 8, "bf16", "dups"),        # > 2048 tiles: the tile scan takes several passes
+    # the wave schedule (at most 128 rows, one wave per workgroup) holds 1 or 2 ids per lane
+    (64, 1, 5, 32, "fp8_e4m3", "dups"),        # 64 rows: one batch, fp8 codes with scales
+    (65, 1, 5, 32, "fp8_e4m3", "dups"),        # 65 rows: two
+    (32, 4, 9, 1040, "bf16", "dups"),          # 128 rows, the largest wave call; 130-vector rows, ragged
+    (4, 32, 1024, 96, "bf16", "distinct"),     # 128 rows over 1024 experts (16 per lane in the scan)
     # the fused kernel holds 1, 4, 16 or 32 id batches of 512 per thread: each side of each switch
-    (64, 8, 256, 16, "bf16", "distinct"),      # 512 rows: one batch
+    (43, 3, 7, 200, "f32", "distinct"),        # 129 rows: the first fused call, one batch
+    (32, 8, 64, 32, "bf16", "one_expert"),     # 256 rows, every row one expert
+    (64, 8, 256, 7168, "fp8_e4m3", "empties"),  # 512 rows: one batch (decode N = 64)
     (65, 8, 256, 16, "bf16", "distinct"),      # 520 rows: four
     (1024, 2, 8, 16, "bf16", "dups"),          # 2048 rows: four
     (1025, 2, 8, 16, "bf16", "dups"),          # 2050 rows: sixteen
@@ -214,6 +221,18 @@ def test_index_only_permute(hip_device, n, k, e):
     outs = gpu_permute(None, ids, e)
     torch.cuda.synchronize()
     assert_permute_equal(outs, oracle_permute(None, ids, e), check_rows=False)
+
+
+@pytest.mark.parametrize("n,k,e", [(5, 8, 256), (700, 4, 32)])
+def test_index_only_permute_moves_scales(hip_device, n, k, e):
+    """hidden_size 0 with per-token scales: no rows, the scales still move."""
+    rng = np.random.default_rng(6)
+    ids = torch.from_numpy(_edge_ids(rng, n, k, e, "distinct").astype(np.int32)).to(hip_device)
+    scale = torch.rand(n, device=hip_device) + 0.25
+    _say("index-only with scales N=%d topk=%d E=%d" % (n, k, e))
+    outs = gpu_permute(None, ids, e, token_scale=scale)
+    torch.cuda.synchronize()
+    assert_permute_equal(outs, oracle_permute(None, ids, e, scale), check_rows=False)
 
 
 def test_zero_tokens(hip_device):

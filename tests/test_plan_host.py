@@ -9,6 +9,8 @@ walks a grid of shapes and asserts, for every plan:
     tile <= kCoarseMaxRowsPerTile, LDS of the scatter kernel <= 64 KiB;
   * staged: each grid dimension of the rank and scatter kernels within 32-bit
     work-item counts, up to the largest accepted row count;
+  * wave: exactly the calls of at most kWaveMaxRows rows without a map, no
+    workspace, LDS within bounds;
   * the workspace query bounds the requirement of every smaller call and is
     monotone in the token count.
 The grid covers the plain sort over E experts and the local-expert sort over
@@ -75,7 +77,11 @@ int main() {
       CHECK(p.nbits >= 0 && (1 << p.nbits) >= B, "key bits");
       CHECK(p.tile_rows == p.tokens_per_tile * K, "tile rows");
       CHECK(p.tile_rows <= kMaxTileRows, "N=%lld K=%d tile rows %d", N, K, p.tile_rows);
-      if (p.fused) {
+      CHECK(p.wave == (N * K <= kWaveMaxRows && M == 0), "N=%lld K=%d M=%d wave schedule", N, K, M);
+      if (p.wave) {
+        CHECK(p.rows <= 2 * kWaveSize && p.ws_bytes == 0 && !p.fused && !p.coarse, "wave plan");
+        CHECK(wave_lds_bytes(E, (int)p.rows) <= 4 * (size_t)kMaxLdsInts, "wave lds");
+      } else if (p.fused) {
         CHECK(p.rows <= kFusedMaxRows, "fused rows");
         CHECK(fused_lds_bytes(B, p.tile_rows, M) <= 4 * kMaxLdsInts, "fused lds");
       } else if (p.coarse) {
@@ -104,7 +110,10 @@ int main() {
   CHECK(plan_permute(8192, 8, 128, 0, true).tile_rows == 512, "qwen3 index-only tiles of 512 rows");
   CHECK(plan_permute(16384, 8, 32, 256).tile_rows == 128, "expert map: staged-size tiles");
   CHECK(plan_permute(16384, 8, 256, 0).coarse, "dsv3 coarse");
-  CHECK(plan_permute(256, 8, 256, 0).fused, "decode fused");
+  CHECK(plan_permute(256, 8, 256, 0).fused, "decode N=256 fused");
+  CHECK(plan_permute(16, 8, 256, 0).wave && plan_permute(1, 8, 256, 0).wave, "decode N<=16 wave");
+  CHECK(plan_permute(17, 8, 256, 0).fused && plan_permute(64, 8, 256, 0).fused, "decode N>16 fused");
+  CHECK(plan_permute(16, 8, 256, 256).fused, "decode with an expert map: fused");
   CHECK(!plan_permute(140000, 2, 16, 0).coarse && !plan_permute(140000, 2, 16, 0).fused, "large staged");
   CHECK(plan_permute(16384, 8, 32, 256).coarse, "dsv3 one of eight expert ranks: coarse");
   std::printf("%s (%d failures)\n", fails ? "FAILED" : "ok", fails);
