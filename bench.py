@@ -7,7 +7,8 @@ The headline workload is the largest single-GPU shape, DeepSeek-V3-shaped:
 N=16384 tokens, hidden 7168 bf16, 256 experts, topk 8, Zipf(1.2) routing with
 empty experts.  With ``--ep N`` the step is one expert-parallel rank's share:
 the local-expert permute (moe_permute_local, rank R's experts of an N-way
-split) and the unpermute of its output (remote slots skipped).
+split) and the unpermute of its output (moe_unpermute_local: remote slots
+skipped).
 
 Prints ONE JSON line.  ``value`` is whole-step achieved HBM bandwidth:
 algorithmic bytes of permute + unpermute (each input read once, each output
@@ -119,7 +120,7 @@ def load_traffic(workload: str, op: str):
     if not entry:
         return None, None
     kernels = entry.get("kernels")
-    if rec.get("kernel_source_sha256") != kernel_source_digest(op):
+    if entry.get("kernel_source_sha256", rec.get("kernel_source_sha256")) != kernel_source_digest(op):
         return None, kernels
     return entry.get("hbm_bytes_per_call"), kernels
 
@@ -313,7 +314,7 @@ def run_workload(args, w, dev) -> dict:
                                       s["inv"], wsp, token_scale=s["scale"], permuted_scale=s["sp"])
 
     def unpermute(s):
-        binding.moe_unpermute(s["y"], wts, s["inv"], s["out"])
+        (binding.moe_unpermute if local is None else binding.moe_unpermute_local)(s["y"], wts, s["inv"], s["out"])
 
     def step(i):
         permute(sets[i % nsets])

@@ -194,8 +194,9 @@ size_t moe_permute_local_workspace_size(int64_t max_num_tokens, int32_t topk, in
  *   permuted_idx, permuted_hidden_states, permuted_scale: the first M entries
  *                     / rows are written, the rest of each buffer is untouched
  *   inv_permuted_idx  [N*topk]: the slot of a local row, -1 for every other row
- * Hidden rows of tokens with no local row are not read.  moe_unpermute skips
- * the -1 entries, so its output is this rank's share of each token's sum.
+ * Hidden rows of tokens with no local row are not read.  moe_unpermute_local
+ * (or moe_unpermute) skips the -1 entries, so its output is this rank's share
+ * of each token's sum.
  * All other arguments, conventions and limits are those of moe_permute
  * (buffers are still sized for N*topk rows; workspace from
  * moe_permute_local_workspace_size).  A topk_ids value outside
@@ -304,6 +305,20 @@ moe_status_t moe_grouped_gemm_bf16(const void *x, const void *w, const int64_t *
 moe_status_t moe_unpermute(const void *expanded_output, int32_t dtype, const float *topk_weights,
                            const int32_t *inv_permuted_idx, int64_t num_tokens,
                            int64_t hidden_size, int32_t topk, void *output, void *stream);
+
+/*
+ * moe_unpermute_local -- moe_unpermute for the inverse index of an expert
+ * split: the same reduction (vLLM PR #14568, PR description), arguments,
+ * result and errors, scheduled for inverse indices written by
+ * moe_permute_local, where most of a token's topk entries are -1.  With one
+ * or two live entries per token the reduction is latency bound and uses every
+ * wave slot of the chip; moe_unpermute limits large topk-8 reductions to
+ * fewer resident waves, which is faster when every entry is live.  Either
+ * entry point is correct for any inverse index.
+ */
+moe_status_t moe_unpermute_local(const void *expanded_output, int32_t dtype, const float *topk_weights,
+                                 const int32_t *inv_permuted_idx, int64_t num_tokens,
+                                 int64_t hidden_size, int32_t topk, void *output, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *moe_status_string(moe_status_t status);

@@ -6,7 +6,7 @@ stream, and raises on a non-OK status.  There is no fallback: if the library
 is missing the first call raises.
 
 The entry points carry the C names: ``moe_permute_supported``,
-``moe_permute_workspace_size``, ``moe_permute``, ``moe_unpermute``,
+``moe_permute_workspace_size``, ``moe_permute``, ``moe_unpermute``, ``moe_unpermute_local``,
 ``moe_permute_local_workspace_size``, ``moe_permute_local``,
 ``moe_permute_quant_fp8``, ``moe_grouped_gemm_bf16``, ``moe_permute_static_scratch``.
 ``MoEPermuteScratch`` follows the preallocated-buffer design of the prhub
@@ -72,8 +72,9 @@ def load_library() -> ctypes.CDLL:
         lib.moe_permute_quant_fp8.restype = ctypes.c_int
         lib.moe_grouped_gemm_bf16.argtypes = [p, p, p, i32, i64, i64, i64, p, p]
         lib.moe_grouped_gemm_bf16.restype = ctypes.c_int
-        lib.moe_unpermute.argtypes = [p, i32, p, p, i64, i64, i32, p, p]
-        lib.moe_unpermute.restype = ctypes.c_int
+        for fn in (lib.moe_unpermute, lib.moe_unpermute_local):
+            fn.argtypes = [p, i32, p, p, i64, i64, i32, p, p]
+            fn.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -371,6 +372,16 @@ def moe_unpermute(expanded_output, topk_weights, inv_permuted_idx, output, strea
     ``topk_weights`` float32 [N, topk], ``inv_permuted_idx`` int32 [N*topk],
     ``output`` [N, H] of the same type as ``expanded_output``.
     """
+    _unpermute("moe_unpermute", expanded_output, topk_weights, inv_permuted_idx, output, stream)
+
+
+def moe_unpermute_local(expanded_output, topk_weights, inv_permuted_idx, output, stream=None) -> None:
+    """moe_unpermute scheduled for the inverse index of ``moe_permute_local``
+    (most entries -1); same arguments and result."""
+    _unpermute("moe_unpermute_local", expanded_output, topk_weights, inv_permuted_idx, output, stream)
+
+
+def _unpermute(name, expanded_output, topk_weights, inv_permuted_idx, output, stream) -> None:
     import torch
 
     if topk_weights is None or topk_weights.dim() != 2:
@@ -385,11 +396,11 @@ def moe_unpermute(expanded_output, topk_weights, inv_permuted_idx, output, strea
     _check(inv_permuted_idx, "inv_permuted_idx", (torch.int32,), n * topk, dev)
     _check(output, "output", (expanded_output.dtype,), n * h, dev)
     _require_gpu(dev)
-    status = load_library().moe_unpermute(
+    status = getattr(load_library(), name)(
         _ptr(expanded_output), _dtype_code(expanded_output), _ptr(topk_weights), _ptr(inv_permuted_idx),
         n, expanded_output.shape[-1], topk, _ptr(output), _stream(stream, output))
     if status != MOE_OK:
-        raise MoEError(status, "moe_unpermute")
+        raise MoEError(status, name)
 
 
 class MoEPermuteScratch:

@@ -35,6 +35,7 @@ struct UnpermuteArgs {
     int64_t row_vecs;
     int32_t topk;
     void* output;                   // [N, row_vecs * 16 bytes]
+    bool few_live;                  // most slots are expected to be -1 (an expert split): no occupancy cap
 };
 
 struct QuantArgs {

@@ -338,9 +338,9 @@ moe_status_t moe_grouped_gemm_bf16(const void* x, const void* w, const int64_t* 
                                                                                                  : MOE_ERR_HIP;
 }
 
-moe_status_t moe_unpermute(const void* expanded_output, int32_t dtype, const float* topk_weights,
-                           const int32_t* inv_permuted_idx, int64_t num_tokens, int64_t hidden_size, int32_t topk,
-                           void* output, void* stream) {
+static moe_status_t unpermute_impl(const void* expanded_output, int32_t dtype, const float* topk_weights,
+                                   const int32_t* inv_permuted_idx, int64_t num_tokens, int64_t hidden_size,
+                                   int32_t topk, void* output, void* stream, bool few_live) {
     const int64_t eb = element_bytes(dtype);
     if (eb == 0) return MOE_ERR_INVALID_ARG;
     if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -372,9 +372,24 @@ moe_status_t moe_unpermute(const void* expanded_output, int32_t dtype, const flo
     a.row_vecs = row_bytes / 16;
     a.topk = topk;
     a.output = output;
+    a.few_live = few_live;
     return moe::launch_unpermute(a, dtype == MOE_DTYPE_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
                ? MOE_OK
                : MOE_ERR_HIP;
+}
+
+moe_status_t moe_unpermute(const void* expanded_output, int32_t dtype, const float* topk_weights,
+                           const int32_t* inv_permuted_idx, int64_t num_tokens, int64_t hidden_size, int32_t topk,
+                           void* output, void* stream) {
+    return unpermute_impl(expanded_output, dtype, topk_weights, inv_permuted_idx, num_tokens, hidden_size, topk,
+                          output, stream, false);
+}
+
+moe_status_t moe_unpermute_local(const void* expanded_output, int32_t dtype, const float* topk_weights,
+                                 const int32_t* inv_permuted_idx, int64_t num_tokens, int64_t hidden_size,
+                                 int32_t topk, void* output, void* stream) {
+    return unpermute_impl(expanded_output, dtype, topk_weights, inv_permuted_idx, num_tokens, hidden_size, topk,
+                          output, stream, true);
 }
 
 }  // extern "C"

@@ -242,19 +242,23 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict_
     }
 }
 
-// Occupancy cap for large topk-8 reductions.  A topk-8 wave keeps 8 KiB of
-// row loads in flight (eight 1 KiB chunks); with every wave slot of a CU
-// filled that is 256 KiB per CU, and large grids then ran slower than with
-// fewer waves.  At the DSv3 shape (N = 16384, rows of 14 KiB, 57344
-// workgroups) three workgroups of four waves per CU (96 KiB of loads in
-// flight per CU) measured 369 -> 350 us for the unpermute alone and
-// 807 -> 766 us for the permute + unpermute step: the permute after it runs
-// faster as well.  Two, four, five and six workgroups per CU were slower than
-// three.  Small grids need every slot to cover memory latency (Qwen3 shape,
-// 8192 workgroups: fastest uncapped), so the cap applies from
-// kUnpermuteCapMinBlocks workgroups on.  The cap is imposed through dynamic
-// LDS that the kernel never touches: each workgroup reserves just over a
-// quarter of the CU's LDS, so at most three fit on a CU.
+// Occupancy cap for large topk-8 reductions whose slots are all live.  At the
+// DSv3 shape (N = 16384, rows of 14 KiB, 57344 workgroups) three workgroups
+// of four waves per CU measured 367 -> 350 us for the unpermute alone and
+// 802 -> 765 us for the permute + unpermute step (the permute after it runs
+// faster as well); two, four, five and six workgroups per CU were slower than
+// three.  What helps is fewer resident waves, not fewer bytes in flight:
+// waves that issue their eight row loads in groups of four or two (every CU
+// slot filled) measured the same as all eight at once, 366-367 us, and so
+// did waves that sum chunks of two tokens at once.  Small grids need every
+// slot to cover memory latency (Qwen3 shape, 8192 workgroups: fastest
+// uncapped), so the cap applies from kUnpermuteCapMinBlocks workgroups on.
+// Inverse indices of an expert split (moe_unpermute_local) are not capped:
+// with one or two live slots per token a wave is latency bound, and the cap
+// made one rank's unpermute at the DSv3 shape, 8-way split, 110 -> 163 us.
+// The cap is imposed through dynamic LDS that the kernel never touches: each
+// workgroup reserves just over a quarter of the CU's LDS, so at most three
+// fit on a CU.
 constexpr int kUnpermuteCapTopk = 8;
 constexpr int64_t kUnpermuteCapMinBlocks = 16384;
 constexpr int kUnpermuteCapWorkgroups = 3;
@@ -285,8 +289,9 @@ static hipError_t launch_unpermute_t(const UnpermuteArgs& a, hipStream_t stream)
     const int64_t items = a.num_tokens * nchunks;
     const int64_t blocks_needed = (items + 3) / 4;
     const int64_t blocks = blocks_needed < kMaxGridBlocks ? blocks_needed : kMaxGridBlocks;
-    const size_t lds =
-        KC == kUnpermuteCapTopk && blocks >= kUnpermuteCapMinBlocks ? unpermute_cap_lds_bytes() : 0;
+    const size_t lds = !a.few_live && KC == kUnpermuteCapTopk && blocks >= kUnpermuteCapMinBlocks
+                           ? unpermute_cap_lds_bytes()
+                           : 0;
     hipLaunchKernelGGL((unpermute_kernel<kBF16, KC, U, G>), dim3((unsigned)blocks), dim3(256), lds, stream,
                        reinterpret_cast<const u32x4*>(a.expanded_output), a.topk_weights, a.inv_permuted_idx,
                        reinterpret_cast<u32x4*>(a.output), a.num_tokens, a.row_vecs, a.topk, blocks * 4);

@@ -50,10 +50,11 @@ def gpu_permute(hidden, ids, num_experts, token_scale=None, workspace=None, stre
     return outs
 
 
-def gpu_unpermute(y, weights, inv, stream=None):
+def gpu_unpermute(y, weights, inv, stream=None, local=False):
+    """moe_unpermute, or moe_unpermute_local (local=True), into a poisoned output."""
     n = weights.shape[0]
     out = poisoned((n, y.shape[1]), y.dtype, y.device)
-    binding.moe_unpermute(y, weights, inv, out, stream=stream)
+    (binding.moe_unpermute_local if local else binding.moe_unpermute)(y, weights, inv, out, stream=stream)
     return out
 
 

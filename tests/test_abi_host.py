@@ -50,7 +50,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == ["moe_grouped_gemm_bf16", "moe_permute", "moe_permute_local",
                                     "moe_permute_local_workspace_size", "moe_permute_quant_fp8",
                                     "moe_permute_static_scratch", "moe_permute_supported",
-                                    "moe_permute_workspace_size", "moe_status_string", "moe_unpermute"]
+                                    "moe_permute_workspace_size", "moe_status_string", "moe_unpermute",
+                                    "moe_unpermute_local"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -290,11 +291,14 @@ def test_grouped_gemm_zero_rows_is_a_no_op(lib):
     assert gemm_call(lib, rows=0, x=None, y=None) == OK
 
 
-def unpermute_call(lib, **kw):
+def unpermute_call(lib, fn="moe_unpermute", **kw):
     args = dict(y=addr(0), dtype=BF16, w=addr(1), inv=addr(2), n=4096, h=4096, k=2, out=addr(3), stream=None)
     args.update(kw)
-    return lib.moe_unpermute(args["y"], args["dtype"], args["w"], args["inv"], args["n"], args["h"], args["k"],
-                             args["out"], args["stream"])
+    return getattr(lib, fn)(args["y"], args["dtype"], args["w"], args["inv"], args["n"], args["h"], args["k"],
+                            args["out"], args["stream"])
+
+
+UNPERMUTE_FNS = ["moe_unpermute", "moe_unpermute_local"]
 
 
 @host_only
@@ -315,12 +319,14 @@ def unpermute_call(lib, **kw):
     (dict(w=addr(1, 2)), MISALIGNED),
     (dict(out=addr(0)), INVALID),       # output aliases the input
 ])
-def test_unpermute_rejects(lib, kw, status):
-    assert unpermute_call(lib, **kw) == status
+@pytest.mark.parametrize("fn", UNPERMUTE_FNS)
+def test_unpermute_rejects(lib, fn, kw, status):
+    assert unpermute_call(lib, fn, **kw) == status
 
 
-def test_unpermute_zero_tokens_is_a_no_op(lib):
-    assert unpermute_call(lib, n=0, y=None, w=None, inv=None, out=None) == OK
+@pytest.mark.parametrize("fn", UNPERMUTE_FNS)
+def test_unpermute_zero_tokens_is_a_no_op(lib, fn):
+    assert unpermute_call(lib, fn, n=0, y=None, w=None, inv=None, out=None) == OK
 
 
 def test_status_strings(lib):

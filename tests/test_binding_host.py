@@ -45,9 +45,13 @@ def test_valid_permute_on_cpu_is_rejected_only_for_the_device():
         B.moe_permute(**_permute_bufs())
 
 
-def test_valid_unpermute_on_cpu_is_rejected_only_for_the_device():
+UNPERMUTES = [B.moe_unpermute, B.moe_unpermute_local]
+
+
+@pytest.mark.parametrize("fn", UNPERMUTES, ids=lambda f: f.__name__)
+def test_valid_unpermute_on_cpu_is_rejected_only_for_the_device(fn):
     with pytest.raises(TypeError, match="GPU tensors"):
-        B.moe_unpermute(**_unpermute_bufs())
+        fn(**_unpermute_bufs())
 
 
 @pytest.mark.parametrize("key,bad,exc", [
@@ -101,18 +105,20 @@ def test_permute_rejects_a_buffer_on_another_device():
     ("expanded_output", torch.zeros((N * K - 1, H), dtype=torch.bfloat16), ValueError),
     ("output", torch.zeros((N, 2 * H), dtype=torch.bfloat16)[:, ::2], ValueError),
 ])
-def test_unpermute_rejects_wrong_buffers(key, bad, exc):
+@pytest.mark.parametrize("fn", UNPERMUTES, ids=lambda f: f.__name__)
+def test_unpermute_rejects_wrong_buffers(fn, key, bad, exc):
     bufs = _unpermute_bufs()
     bufs[key] = bad
     with pytest.raises(exc):
-        B.moe_unpermute(**bufs)
+        fn(**bufs)
 
 
-def test_unpermute_rejects_a_buffer_on_another_device():
+@pytest.mark.parametrize("fn", UNPERMUTES, ids=lambda f: f.__name__)
+def test_unpermute_rejects_a_buffer_on_another_device(fn):
     bufs = _unpermute_bufs()
     bufs["output"] = torch.empty((N, H), dtype=torch.bfloat16, device="meta")
     with pytest.raises(TypeError, match="meta"):
-        B.moe_unpermute(**bufs)
+        fn(**bufs)
 
 
 def _local_bufs():

@@ -6,6 +6,9 @@ other rows get inverse index -1, are not copied, and add nothing when
 unpermuted.  Bar as for the plain permute: offsets, indices, rows and scales
 bit-exact (the permuted buffers past the local rows must keep their poison);
 unpermute within 2^-7 * max(1, |ref|) for bf16, 1e-5 * max(1, |ref|) for fp32.
+Both reductions of a local inverse index, moe_unpermute_local and
+moe_unpermute (different occupancy, same kernel arithmetic), must agree bit
+for bit.
 """
 
 import numpy as np
@@ -37,6 +40,12 @@ def _inputs(name, dev, seed=0, n=None):
     return w, inp
 
 
+def _assert_same_bits(a, b):
+    assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                       b.view(torch.uint8) if b.dtype == torch.bfloat16 else b.view(torch.int32)), \
+        "moe_unpermute_local and moe_unpermute differ"
+
+
 def _unpermute_ref(y, wts, inv, k, dtype):
     """Oracle unpermute of every token (a -1 slot adds nothing)."""
     return oracle.unpermute(y, wts, inv, dtype)
@@ -63,12 +72,14 @@ def test_local_workload_parity(hip_device, name, ep, rank, layout, n):
     _say("local %s N=%d E=%d topk=%d ep=%d rank=%d %s" % (name, w.num_tokens, w.num_experts, w.topk, ep, rank, layout))
     outs = gpu_permute_local(inp["hidden_states"], inp["topk_ids"], w.num_experts, emap, nl,
                              token_scale=inp["token_scale"])
-    out = gpu_unpermute(inp["expert_output"], inp["topk_weights"], outs["inv_permuted_idx"])
+    out = gpu_unpermute(inp["expert_output"], inp["topk_weights"], outs["inv_permuted_idx"], local=True)
+    out_plain = gpu_unpermute(inp["expert_output"], inp["topk_weights"], outs["inv_permuted_idx"])
     torch.cuda.synchronize()
     ref = oracle_permute_local(inp["hidden_states"], inp["topk_ids"], w.num_experts, emap, nl, inp["token_scale"])
     assert_permute_local_equal(outs, ref)
     y, wts, inv = to_np(inp["expert_output"]), to_np(inp["topk_weights"]), ref["inv_permuted_idx"]
     assert_unpermute_close(to_np(out), _unpermute_ref(y, wts, inv, w.topk, w.output_dtype), w.output_dtype)
+    _assert_same_bits(out, out_plain)
 
 
 def _ids(rng, n, k, e, mode):
@@ -125,11 +136,13 @@ def test_local_edge_parity(hip_device, n, k, e, h, dtype, mode, kind):
     wts = torch.rand((n, k), generator=torch.Generator().manual_seed(n + 2)).to(dev)
     _say("local edge N=%d topk=%d E=%d H=%d %s %s %s" % (n, k, e, h, dtype, mode, kind))
     outs = gpu_permute_local(x, ids, e, emap, nl)
-    out = gpu_unpermute(y, wts, outs["inv_permuted_idx"])
+    out = gpu_unpermute(y, wts, outs["inv_permuted_idx"], local=True)
+    out_plain = gpu_unpermute(y, wts, outs["inv_permuted_idx"])
     torch.cuda.synchronize()
     ref = oracle_permute_local(x, ids, e, emap, nl)
     assert_permute_local_equal(outs, ref)
     assert_unpermute_close(to_np(out), oracle.unpermute(to_np(y), to_np(wts), ref["inv_permuted_idx"], dtype), dtype)
+    _assert_same_bits(out, out_plain)
     if kind == "identity":  # every expert local: exactly the plain permute
         plain = gpu_permute(x, ids, e)
         torch.cuda.synchronize()
@@ -207,8 +220,9 @@ def test_local_scratch_reuse_and_ranks_cover_every_slot(hip_device):
     assert covered.tolist() == [1] * w.num_rows
 
 
+@pytest.mark.parametrize("local", [False, True], ids=["unpermute", "unpermute_local"])
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 8])
-def test_unpermute_minus_one_slots_skip_and_others_nan(hip_device, k):
+def test_unpermute_minus_one_slots_skip_and_others_nan(hip_device, k, local):
     """-1 slots add nothing (their rows are not read); any other out-of-range
     index still turns its token into NaN."""
     n, h = 64, 128
@@ -223,8 +237,8 @@ def test_unpermute_minus_one_slots_skip_and_others_nan(hip_device, k):
     wts[3, 0] = float("inf")             # weight of a -1 slot is never used
     inv[3 * k] = -1
     inv_np[3 * k] = -1
-    _say("unpermute -1 slots topk=%d" % k)
-    out = gpu_unpermute(y, wts, inv)
+    _say("unpermute -1 slots topk=%d local=%s" % (k, local))
+    out = gpu_unpermute(y, wts, inv, local=local)
     torch.cuda.synchronize()
     o = to_np(out)
     of = out.float().cpu()
@@ -245,8 +259,9 @@ REMOTE_ROWS = [(2, 1560, "bf16"), (8, 1000, "f32"), (3, 1560, "bf16"), (1, 4096,
                (6, 1560, "bf16")]
 
 
+@pytest.mark.parametrize("local", [False, True], ids=["unpermute", "unpermute_local"])
 @pytest.mark.parametrize("k,h,dtype", REMOTE_ROWS, ids=["-".join(map(str, c)) for c in REMOTE_ROWS])
-def test_unpermute_tokens_with_no_local_slot_get_whole_zero_rows(hip_device, k, h, dtype):
+def test_unpermute_tokens_with_no_local_slot_get_whole_zero_rows(hip_device, k, h, dtype, local):
     """Tokens whose every slot is -1 get rows of +0.0 over the whole row (the
     output is poisoned first, so an unwritten chunk shows); tokens with some
     local slots are summed as usual; a token with one bad index among -1 slots
@@ -268,8 +283,8 @@ def test_unpermute_tokens_with_no_local_slot_get_whole_zero_rows(hip_device, k, 
     y = torch.randn((n * k, h), generator=torch.Generator().manual_seed(h)).to(tdt).to(hip_device)
     wts = torch.rand((n, k), generator=torch.Generator().manual_seed(k)).to(hip_device)
     inv = torch.from_numpy(inv_np).to(hip_device)
-    _say("unpermute zero rows topk=%d H=%d %s remote=%d" % (k, h, dtype, int(remote.sum())))
-    out = gpu_unpermute(y, wts, inv)
+    _say("unpermute zero rows topk=%d H=%d %s remote=%d local=%s" % (k, h, dtype, int(remote.sum()), local))
+    out = gpu_unpermute(y, wts, inv, local=local)
     torch.cuda.synchronize()
     o = to_np(out)
     assert torch.isnan(out[bad_t].float().cpu()).all()
