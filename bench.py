@@ -90,8 +90,9 @@ def algorithmic_bytes(w, local=None, id_bytes: int = 4, quant_groups: int = 0) -
 # Sources whose kernels a counter summary measured: a summary stays valid while
 # these files are unchanged.
 DIGEST_FILES = {
-    "permute": ["moe_permute_device.h", "moe_permute_wave.hip", "moe_permute_fused.hip", "moe_permute_coarse.hip", "moe_permute_staged.hip",
-                "moe_permute_launch.hip", "moe_launch.h", "moe_plan.h"],
+    "permute": ["moe_permute_device.h", "moe_permute_wave.hip", "moe_permute_fused.hip", "moe_permute_coarse.hip",
+                "moe_permute_staged.hip", "moe_permute_rows.hip", "moe_permute_launch.hip", "moe_launch.h",
+                "moe_plan.h"],
     "unpermute": ["moe_unpermute.hip", "moe_launch.h", "moe_plan.h"],
     "gemm": ["moe_gemm_kernels.hip", "moe_launch.h", "moe_plan.h"],
 }

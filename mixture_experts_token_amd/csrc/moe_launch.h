@@ -75,6 +75,8 @@ hipError_t launch_permute_coarse(const PermuteArgs& a, const PermutePlan& p, voi
                                  hipStream_t stream);
 hipError_t launch_permute_staged(const PermuteArgs& a, const PermutePlan& p, void* workspace, int u,
                                  hipStream_t stream);
+// Row copy of the split schedule; reads the inverse index and offsets the index pass wrote.
+hipError_t launch_permute_rows(const PermuteArgs& a, hipStream_t stream);
 hipError_t launch_unpermute(const UnpermuteArgs& a, bool bf16, hipStream_t stream);
 
 }  // namespace moe

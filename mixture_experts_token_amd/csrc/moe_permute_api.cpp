@@ -140,8 +140,10 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
     if (hidden_size > 0 && (!aligned(hidden_states, 16) || !aligned(permuted_hidden_states, 16)))
         return MOE_ERR_MISALIGNED;
 
-    const moe::PermutePlan plan =
-        moe::plan_permute(num_tokens, topk, buckets, map_entries, hidden_size == 0 && token_scale == nullptr);
+    const bool split = moe::split_copy_applies(num_tokens, topk, row_bytes, map_entries);
+    moe::PermutePlan plan = moe::plan_permute(num_tokens, topk, buckets, map_entries,
+                                              (hidden_size == 0 || split) && token_scale == nullptr);
+    plan.split_copy = split;
     if (static_workspace) {
         // the library's static array stands in for the caller's workspace
         if (plan.ws_bytes > moe::kStaticScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;

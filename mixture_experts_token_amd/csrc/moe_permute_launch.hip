@@ -46,6 +46,18 @@ hipError_t static_scratch_address(void** ptr) {
 }
 
 hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream) {
+    if (p.split_copy) {
+        // the index (and the scales) first, as an index-only call, then the rows
+        PermuteArgs ai = a;
+        ai.hidden_states = nullptr;
+        ai.permuted_hidden_states = nullptr;
+        ai.row_vecs = 0;
+        PermutePlan pi = p;
+        pi.split_copy = false;
+        const hipError_t e = launch_permute(ai, pi, workspace, stream);
+        if (e != hipSuccess) return e;
+        return launch_permute_rows(a, stream);
+    }
     const int u = a.topk >= 4 ? choose_unroll(a.row_vecs, kCopyUnrollsWideFanout, 4)
                               : choose_unroll(a.row_vecs, kCopyUnrolls, 8);
     if (p.wave) return launch_permute_wave(a, p, u, stream);

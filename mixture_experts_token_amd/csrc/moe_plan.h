@@ -50,6 +50,13 @@ constexpr int kFusedTargetBlocks = 512;
 constexpr int kMaxTileRows = 1024;                 // LDS staging bound for one tile
 constexpr size_t kWorkspaceAlign = 256;
 constexpr size_t kStaticScratchBytes = size_t(4) << 20;  // workspace of moe_permute_static_scratch
+// Expanded-row bytes (N * topk * row bytes) from which a permute without an
+// expert map takes the split schedule: the index-only schedule, then a
+// separate row copy (moe_permute_rows.hip).  The index pass costs about
+// 10 us at these sizes and the separate copy saves about 13 us per GB moved
+// (DSv3 shape, 2.1 GB: 434 -> 416 us); the Qwen3 shape (0.3 GB) measured
+// 58 -> 61 us with it.
+constexpr int64_t kSplitCopyMinBytes = int64_t(1) << 30;
 constexpr int kQuantMaxRowVecs = 1024;             // quantise-scatter: a wave holds the whole row (16 KiB)
 constexpr int kIndexOnlyTileScale = 4;             // coarse tiles of an index-only permute, vs the staged ones
 
@@ -78,6 +85,7 @@ inline int key_bits(int buckets) {
 
 struct PermutePlan {
     bool wave = false;            // one-wave workgroups, whole index per wave (no workspace)
+    bool split_copy = false;      // index-only schedule below, then the separate row copy
     bool fused = false;
     bool coarse = false;          // two-kernel schedule (only when !fused)
     int coarse_rows = 0;          // expanded rows per coarse tile (a multiple of tile_rows)
@@ -162,6 +170,11 @@ inline size_t coarse_workspace_bytes(int num_coarse, int buckets) {
 }
 
 inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int map_entries, bool index_only = false);
+
+// Whether a permute copying rows of row_bytes takes the split schedule.
+inline bool split_copy_applies(int64_t num_tokens, int topk, int64_t row_bytes, int map_entries) {
+    return map_entries == 0 && row_bytes > 0 && num_tokens * topk * row_bytes >= kSplitCopyMinBytes;
+}
 
 // Workspace of a call with max_num_tokens tokens; every call with fewer tokens
 // needs no more.  A coarse call needs at most max_coarse_tiles histogram rows

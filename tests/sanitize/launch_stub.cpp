@@ -71,6 +71,8 @@ hipError_t launch_permute_staged(const PermuteArgs&, const PermutePlan&, void*, 
     return hipErrorNoDevice;
 }
 
+hipError_t launch_permute_rows(const PermuteArgs&, hipStream_t) { return hipErrorNoDevice; }
+
 hipError_t launch_unpermute(const UnpermuteArgs& a, bool, hipStream_t) {
     require(a.expanded_output != nullptr && a.topk_weights != nullptr && a.inv_permuted_idx != nullptr &&
                 a.output != nullptr && a.num_tokens > 0 && a.row_vecs > 0,

@@ -167,8 +167,10 @@ def test_permute_rejects(lib, kw, status):
 
 @host_only
 def test_permute_workspace_boundary(lib):
+    # rows of 2 KiB: 0.33 GB of expanded rows, below the split schedule's
+    # threshold, so the call takes the copying plan the size is tight for
     need = lib.moe_permute_workspace_size(20000, 8, 256)
-    assert permute_call(lib, n=20000, k=8, e=256, ws_bytes=need - 1) == TOO_SMALL
+    assert permute_call(lib, n=20000, k=8, e=256, h=1024, ws_bytes=need - 1) == TOO_SMALL
 
 
 def test_local_workspace_size_pure_and_monotone(lib):

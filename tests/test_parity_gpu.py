@@ -247,6 +247,64 @@ def test_zero_tokens(hip_device):
     assert out.shape == (0, 64)
 
 
+# ----------------------------------------------------------------------------
+# Split schedule: from 2^30 bytes of expanded rows (no expert map) the index is
+# written by the index-only schedule and a separate kernel copies the rows.
+# The DSv3-shaped call (topk 8) is compared in full above; these cover the
+# other copy kernels (topk 4 and 2, and a runtime topk), a ragged last chunk,
+# the threshold itself, moved scales and the rejected-id path.  Indices are
+# compared with the oracle in full; rows and scales against a gather of the
+# inputs by the (already verified) permuted_idx, on the device.
+# ----------------------------------------------------------------------------
+SPLIT_CASES = [
+    # (N, topk, E, H bf16): N*topk*H*2 bytes >= 2^30
+    (65536, 3, 64, 2816),    # runtime-topk kernel; rows of 352 vectors: a ragged second chunk
+    (65536, 4, 128, 2048),   # exactly 2^30 bytes: the first size that splits
+    (131072, 2, 8, 4096),    # topk 2 (non-temporal row stores)
+]
+
+
+def _distinct_ids(rng, n, k, e):
+    return np.argsort(rng.random((n, e)), axis=1)[:, :k].astype(np.int32)
+
+
+@pytest.mark.parametrize("n,k,e,h", SPLIT_CASES, ids=["-".join(map(str, c)) for c in SPLIT_CASES])
+def test_split_schedule_parity(hip_device, n, k, e, h):
+    assert n * k * h * 2 >= 1 << 30
+    rng = np.random.default_rng(n + k)
+    ids_np = _distinct_ids(rng, n, k, e)
+    ids = torch.from_numpy(ids_np).to(hip_device)
+    g = torch.Generator(device=hip_device).manual_seed(k)
+    x = torch.randn((n, h), device=hip_device, generator=g).to(torch.bfloat16)
+    scale = torch.rand(n, device=hip_device, generator=g) + 0.5
+    _say("split schedule N=%d topk=%d E=%d H=%d" % (n, k, e, h))
+    outs = gpu_permute(x, ids, e, token_scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle_permute(None, ids, e)
+    for key in ("expert_first_token_offset", "permuted_idx", "inv_permuted_idx"):
+        np.testing.assert_array_equal(to_np(outs[key]), ref[key], err_msg=key)
+    src = outs["permuted_idx"].long() // k
+    assert torch.equal(outs["permuted_hidden_states"].view(torch.int16), x.view(torch.int16)[src])
+    assert torch.equal(outs["permuted_scale"], scale[src])
+
+
+def test_split_schedule_rejected_id_writes_nothing(hip_device):
+    """DSv3 shape (split schedule) with one expert id out of range: offsets -1,
+    and the index and all 1.88 GB of row buffer keep their poison."""
+    w = W.WORKLOADS["dsv3"]
+    rng = np.random.default_rng(11)
+    ids_np = _distinct_ids(rng, w.num_tokens, w.topk, w.num_experts)
+    ids_np[w.num_tokens - 5, 3] = w.num_experts
+    ids = torch.from_numpy(ids_np).to(hip_device)
+    x = torch.randn((w.num_tokens, w.hidden_size), device=hip_device).to(torch.bfloat16)
+    _say("split schedule, bad id")
+    outs = gpu_permute(x, ids, w.num_experts)
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == [-1] * (w.num_experts + 1)
+    for key in ("permuted_idx", "inv_permuted_idx", "permuted_hidden_states"):
+        assert bool((outs[key].view(torch.uint8) == POISON).all()), key
+
+
 @pytest.mark.parametrize("n,k,e,bad", [(50, 2, 8, 8), (50, 2, 8, -1), (4000, 8, 64, 64), (4000, 8, 64, -7)])
 def test_out_of_range_expert_id_is_reported(hip_device, n, k, e, bad):
     """The kernels' own check: offsets become -1 and nothing else is written."""

@@ -116,6 +116,13 @@ int main() {
   CHECK(plan_permute(16, 8, 256, 256).fused, "decode with an expert map: fused");
   CHECK(!plan_permute(140000, 2, 16, 0).coarse && !plan_permute(140000, 2, 16, 0).fused, "large staged");
   CHECK(plan_permute(16384, 8, 32, 256).coarse, "dsv3 one of eight expert ranks: coarse");
+  CHECK(split_copy_applies(16384, 8, 7168 * 2, 0), "dsv3 bf16 rows: split copy");
+  CHECK(!split_copy_applies(16384, 8, 7168 * 2, 256), "dsv3 with an expert map: no split copy");
+  CHECK(!split_copy_applies(8192, 8, 2048 * 2, 0), "qwen3: no split copy");
+  CHECK(!split_copy_applies(4096, 2, 4096 * 2, 0), "mixtral: no split copy");
+  CHECK(!split_copy_applies(1 << 20, 8, 0, 0), "index only: no split copy");
+  CHECK(split_copy_applies(1, 1, kSplitCopyMinBytes, 0) && !split_copy_applies(1, 1, kSplitCopyMinBytes - 16, 0),
+        "split copy from kSplitCopyMinBytes on");
   std::printf("%s (%d failures)\n", fails ? "FAILED" : "ok", fails);
   return fails ? 1 : 0;
 }
