@@ -138,6 +138,13 @@ def load_probe():
         fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                        ctypes.c_void_p]
         fn.restype = ctypes.c_int
+    lib.hbm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.hbm_probe_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.hbm_probe_read.restype = lib.hbm_probe_write.restype = ctypes.c_int
+    lib.hbm_probe_fanout_source.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
+    lib.hbm_probe_fanout_source.restype = ctypes.c_int
     return lib
 
 
@@ -398,6 +405,45 @@ def run_workload(args, w, dev) -> dict:
                    "unpermute_GBps": round(red_bytes / (red_us * 1e-6) / 1e9, 1),
                    "step_GBps": round(step_ceiling, 1),
                    "pct_of_step_ceiling": round(100 * value / step_ceiling, 2)}
+        if args.direction_split:
+            # Each operation's bytes split into their two directions, each timed
+            # alone (read-only and write-only probes, fastest variant), beside
+            # the mixed probe and the operation itself.
+            def probe_dir(i, read, buf, rows, row_bytes, variant):
+                s = sets[i % nsets]
+                stream = torch._C._cuda_getCurrentRawStream(dev_index)
+                if read:
+                    rc = probe.hbm_probe_read(s[buf].data_ptr(), s["xp"].data_ptr(), rows, row_bytes, variant, stream)
+                else:
+                    rc = probe.hbm_probe_write(s[buf].data_ptr(), rows, row_bytes, variant, stream)
+                assert rc == 0, rc
+
+            def fastest(read, buf, rows, row_bytes):
+                return min(timed(lambda i: probe_dir(i, read, buf, rows, row_bytes, v), k)[0]
+                           for v in ((0, 2, 4, 6) if read else range(8)))
+
+            def split(read_buf, read_rows, read_row, write_buf, write_rows, write_row, mixed_us, op_us):
+                r_us = fastest(True, read_buf, read_rows, read_row)
+                w_us = fastest(False, write_buf, write_rows, write_row)
+                return {"read_bytes": read_rows * read_row, "read_alone_us": round(r_us, 3),
+                        "write_bytes": write_rows * write_row, "write_alone_us": round(w_us, 3),
+                        "sum_alone_us": round(r_us + w_us, 3), "mixed_probe_us": round(mixed_us, 3),
+                        "operation_us": round(op_us, 3)}
+
+            def fan_source(i, source_rows):
+                s = sets[i % nsets]
+                rc = probe.hbm_probe_fanout_source(s["x"].data_ptr(), s["xp"].data_ptr(), w.num_tokens, xrow,
+                                                   w.topk, source_rows, torch._C._cuda_getCurrentRawStream(dev_index))
+                assert rc == 0, rc
+
+            ceiling["direction_split"] = {
+                "permute": split("x", w.num_tokens, xrow, "xp", w.num_rows, xrow, fan_us, perm_avg),
+                "unpermute": split("y", w.num_rows, yrow, "out", w.num_tokens, yrow, red_us, unperm_avg)}
+            # the fan-out's writes with no reads, and with reads of a few rows
+            # that stay in L2 (64) or in the last-level cache (2048)
+            ceiling["direction_split"]["permute"]["fanout_writes_by_source_rows_us"] = {
+                str(sr): round(timed(lambda i: fan_source(i, sr), k)[0], 3)
+                for sr in (0, 64, 2048) if sr <= w.num_tokens}
         torch.cuda.synchronize(dev)
 
     # The same steps with every output buffer and the workspace allocated per
@@ -641,6 +687,8 @@ def main() -> int:
                     help="skip the token sweep (the other workloads and the decode sizes, timed in the same run)")
     ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--direction-split", action="store_true",
+                    help="also time each operation's reads alone and writes alone (streaming probes)")
     ap.add_argument("--sets", type=int, default=None, help="buffer sets to rotate (default: enough to beat the LLC)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before timing, run a plain elementwise copy kernel (negation) over a fresh MIB-MiB "
