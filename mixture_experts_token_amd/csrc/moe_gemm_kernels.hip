@@ -15,8 +15,8 @@
 //     per step;
 //   * both operands go from global memory straight into LDS (16 bytes per
 //     lane, no register round trip), 128-byte rows with the 16-byte k-vectors
-//     of row r stored in slot (kvec ^ r % 8), so the fragment reads of 32
-//     consecutive rows hit every bank once; the wide tiles load through buffer
+//     of row r stored in slot kvec ^ (r % 8) ^ (bit 3 of r), so the fragment
+//     reads of 16 consecutive rows hit every bank once; the wide tiles load through buffer
 //     resources (one lane offset register per operand, row group and k step
 //     in the scalar offset) and spread a step's loads over its four 16-wide k
 //     slices instead of issuing them all after the barrier;
@@ -147,22 +147,32 @@ __device__ __forceinline__ TileCoord tile_coord(int64_t id, const int64_t* __res
     return c;
 }
 
+// LDS slot of k-vector kvec of tile row `row`: the 16-byte k-vectors of a
+// 128-byte row are XOR-swizzled by the row.  A 128-byte row spans half of the
+// LDS banks, so two rows share a bank line and a 16-lane phase of a 16-byte
+// read touches 16 consecutive rows: the row's bit 3 flips the slot as well, so
+// rows r and r + 8 (same row % 8, same bank half) land in different banks.
+// With only row % 8, half of the LDS cycles of the fragment reads were bank
+// conflicts (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = 0.50 at the Mixtral
+// shape); with this slot none (0.00), grouped GEMM 2048 -> 1989 us.
+__device__ __forceinline__ int kslot(int row, int kvec) { return kvec ^ (row % 8) ^ ((row / 8) & 1); }
+
 // Operand tiles (ROWS rows x 64 bf16 = 128 bytes per row per k-step) go from
 // global memory straight into LDS, one 1 KiB instruction (8 rows) at a time:
 // lane L of an instruction writes slot L % 8 of row L / 8 of its group and
-// reads that row's k-vector (L % 8) ^ (row % 8) -- the XOR swizzle that keeps
-// the fragment reads of 32 consecutive rows free of bank conflicts.
+// reads the k-vector of that row that belongs in that slot (kslot is its own
+// inverse in kvec).
 // One 8-row group: `row` is this lane's row (group start + L / 8), `srow` the
 // row it reads (clamped into the valid rows), `lds_group` the group's LDS rows.
 __device__ __forceinline__ void group_to_lds(__bf16* lds_group, const u32x4* __restrict__ src_row0,
                                              int64_t row_stride_vecs, int row, int srow, int64_t kvec0, int lane) {
-    const u32x4* g = src_row0 + (int64_t)srow * row_stride_vecs + kvec0 + ((lane % 8) ^ (row % 8));
+    const u32x4* g = src_row0 + (int64_t)srow * row_stride_vecs + kvec0 + kslot(row, lane % 8);
     __builtin_amdgcn_global_load_lds(g, lds_group, 16, 0, 0);
 }
 
 // One 8-row group of the same load through a buffer resource whose base is
 // the tile's first row: lane L reads row L / 8 of the group, k-vector
-// (L % 8) ^ (L / 8) (groups are 8-aligned, so row % 8 = L / 8); the group row
+// kslot(group row + L / 8, L % 8) (groups are 8-aligned); the group row
 // and the k step go into the scalar offset.  With kClamp, rows past
 // rows_valid re-read the last valid row (the group start is clamped too, so
 // the lane offset never goes negative): every step issues the same number of
@@ -170,7 +180,7 @@ __device__ __forceinline__ void group_to_lds(__bf16* lds_group, const u32x4* __r
 template <bool kClamp>
 __device__ __forceinline__ void group_to_lds_buf(__bf16* lds_group, __amdgpu_buffer_rsrc_t rsrc, int stride_bytes,
                                                  int grow, int rows_valid, int step, int lane) {
-    const int chunk = ((lane % 8) ^ (lane / 8)) * 16;
+    const int chunk = kslot(grow + lane / 8, lane % 8) * 16;
     int g0 = grow, r = lane / 8;
     if (kClamp) {
         g0 = grow < rows_valid ? grow : rows_valid - 1;
@@ -183,13 +193,13 @@ __device__ __forceinline__ void group_to_lds_buf(__bf16* lds_group, __amdgpu_buf
 
 // Fragment of 8 consecutive k (k-vector kvec) of tile row `row`.
 __device__ __forceinline__ bf16x8 lds_frag(const __bf16* lds, int row, int kvec) {
-    return *reinterpret_cast<const bf16x8*>(lds + row * kBK + ((kvec ^ (row % 8)) * 8));
+    return *reinterpret_cast<const bf16x8*>(lds + row * kBK + kslot(row, kvec) * 8);
 }
 
 // LDS byte address of the 16-byte fragment vector (row, kvec) of a stage: a
 // generic address of LDS memory holds the LDS byte offset in its low 32 bits.
 __device__ __forceinline__ uint32_t lds_frag_addr(const __bf16* lds, int row, int kvec) {
-    return (uint32_t)(uintptr_t)(lds + row * kBK + ((kvec ^ (row % 8)) * 8));
+    return (uint32_t)(uintptr_t)(lds + row * kBK + kslot(row, kvec) * 8);
 }
 
 // The four fragment reads of one 16-wide k slice (two row fragments, two
