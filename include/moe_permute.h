@@ -311,10 +311,12 @@ moe_status_t moe_unpermute(const void *expanded_output, int32_t dtype, const flo
  * split: the same reduction (vLLM PR #14568, PR description), arguments,
  * result and errors, scheduled for inverse indices written by
  * moe_permute_local, where most of a token's topk entries are -1.  With one
- * or two live entries per token the reduction is latency bound and uses every
- * wave slot of the chip; moe_unpermute limits large topk-8 reductions to
- * fewer resident waves, which is faster when every entry is live.  Either
- * entry point is correct for any inverse index.
+ * or two live entries per token the reduction is latency bound: it uses
+ * every wave slot of the chip, and at topk 8 on large calls a wave sums
+ * several chunks of a token row from its live entries at once.
+ * moe_unpermute limits large topk-8 reductions to fewer resident waves,
+ * which is faster when every entry is live.  Either entry point is correct
+ * for any inverse index and gives the same bits.
  */
 moe_status_t moe_unpermute_local(const void *expanded_output, int32_t dtype, const float *topk_weights,
                                  const int32_t *inv_permuted_idx, int64_t num_tokens,

@@ -242,6 +242,147 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const u32x4* __restrict_
     }
 }
 
+// ----------------------------------------------------------------------------
+// Span schedule for the inverse index of an expert split (moe_unpermute_local,
+// topk 8).  With one or two live slots per token, one wave per 1 KiB chunk
+// keeps only 1-2 KiB of row loads in flight and the reduction is latency
+// bound.  Here a wave owns a span of kSpanChunks chunks of one token, gathers
+// the token's live slots (ascending k) and sums P chunks at a time, P chosen
+// so that live slots x P is about eight row loads in flight: one slot takes
+// all four chunks at once, two slots four, three or four slots two, five or
+// more one.  The loads of the next P chunks are issued before the stores of
+// the current ones (one counter covers both on this chip, in issue order, so
+// waiting for loads issued after a store would wait for the store too).
+// Terms are added in ascending k exactly as the per-chunk kernel adds them
+// (a -1 slot there adds 0 * 0, which leaves a sum that started at +0 unchanged),
+// so both schedules give the same bits.
+// ----------------------------------------------------------------------------
+constexpr int kSpanChunks = 4;
+// Spans (tokens x spans per token) from which the span schedule is used: the
+// DSv3 shape (16384 tokens x 4 spans) took one 8-way rank's unpermute
+// 110 -> 95 us and the other ranks 69 -> 66 and 73 -> 69 us; the Qwen3 shape
+// (8192 tokens x 1 span, 4-way split) ran slower with it (18 -> 21 us), too
+// few waves for the machine.
+constexpr int64_t kSpanMinItems = 32768;
+
+template <int LC, int P>
+__device__ __forceinline__ void span_load(const u32x4* __restrict__ y, int64_t rv, int64_t c0, int64_t c_end,
+                                          const int32_t (&jc)[LC], int nlive, int lane, u32x4 (&v)[LC][P]) {
+#pragma unroll
+    for (int l = 0; l < LC; ++l) {
+        const u32x4* src = y + (int64_t)jc[l] * rv;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int64_t idx = (c0 + p) * kWaveSize + lane;
+            const bool ok = l < nlive && c0 + p < c_end && idx < rv;
+            v[l][p] = ok ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+// The span [c_begin, c_end) of token row orow from the nlive compacted slots.
+template <bool kBF16, int LC, int P>
+__device__ __forceinline__ void span_sum(const u32x4* __restrict__ y, u32x4* __restrict__ orow, int64_t rv,
+                                         int64_t c_begin, int64_t c_end, const int32_t (&jc)[LC],
+                                         const float (&wc)[LC], int nlive, int lane) {
+    constexpr int kEl = kBF16 ? 8 : 4;
+    u32x4 v[LC][P];
+    span_load<LC, P>(y, rv, c_begin, c_end, jc, nlive, lane, v);
+    for (int64_t c0 = c_begin; c0 < c_end; c0 += P) {
+        float acc[P][1][kEl];
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int e = 0; e < kEl; ++e) acc[p][0][e] = 0.0f;
+#pragma unroll
+        for (int l = 0; l < LC; ++l) {
+            if (l < nlive) {
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    const u32x4 one[1] = {v[l][p]};
+                    accumulate<kBF16, 1>(acc[p], one, wc[l]);
+                }
+            }
+        }
+        if (c0 + P < c_end) span_load<LC, P>(y, rv, c0 + P, c_end, jc, nlive, lane, v);
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            if (c0 + p < c_end) store_outputs<kBF16, 1>(orow, rv, (c0 + p) * kWaveSize + lane, acc[p], false);
+    }
+}
+
+// Compacts the live slots (mask bit k: slot k live) into the first LC entries,
+// ascending k, with selects only (a run-time index into the slot arrays would
+// put them in scratch or LDS), then sums the span.
+template <bool kBF16, int LC, int P>
+__device__ __forceinline__ void span_compact(const u32x4* __restrict__ y, u32x4* __restrict__ orow, int64_t rv,
+                                             int64_t c_begin, int64_t c_end, const int32_t (&j)[8],
+                                             const float (&wk)[8], uint32_t mask, int lane) {
+    int32_t jc[LC];
+    float wc[LC];
+#pragma unroll
+    for (int l = 0; l < LC; ++l) {
+        jc[l] = 0;
+        wc[l] = 0.0f;
+    }
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const bool live = (mask >> k) & 1u;
+#pragma unroll
+        for (int l = 0; l < LC; ++l) {
+            const bool here = live && n == l;
+            jc[l] = here ? j[k] : jc[l];
+            wc[l] = here ? wk[k] : wc[l];
+        }
+        n += live ? 1 : 0;
+    }
+    span_sum<kBF16, LC, P>(y, orow, rv, c_begin, c_end, jc, wc, n < LC ? n : LC, lane);
+}
+
+template <bool kBF16>
+__global__ __launch_bounds__(256) void unpermute_span_kernel(const u32x4* __restrict__ y,
+                                                             const float* __restrict__ wts,
+                                                             const int32_t* __restrict__ inv,
+                                                             u32x4* __restrict__ out, int64_t num_tokens,
+                                                             int64_t rv, int64_t total_waves) {
+    constexpr int K = 8;
+    constexpr int C = kSpanChunks;
+    const int64_t nchunks = (rv + kWaveSize - 1) / kWaveSize;
+    const int64_t nspans = (nchunks + C - 1) / C;
+    const int64_t items = num_tokens * nspans;
+    const int64_t R = num_tokens * K;
+    const int lane = (int)(threadIdx.x % kWaveSize);
+    for (int64_t item = (int64_t)blockIdx.x * (256 / kWaveSize) + wave_index(); item < items; item += total_waves) {
+        const int64_t t = __builtin_amdgcn_readfirstlane((int)(item / nspans));
+        const int64_t c_begin = (item - t * nspans) * C;
+        const int64_t c_end = c_begin + C < nchunks ? c_begin + C : nchunks;
+        int32_t j[K];
+        float wk[K];
+        uint32_t mask = 0;
+        bool bad = false;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            j[k] = inv[t * K + k];
+            wk[k] = wts[t * K + k];
+            bad |= !(j[k] >= -1 && (int64_t)j[k] < R);
+            mask |= (j[k] >= 0 ? 1u : 0u) << k;
+        }
+        u32x4* orow = out + t * rv;
+        if (bad || mask == 0) {  // NaN row (bad index) or zero row (every slot remote)
+            const uint32_t fill = bad ? (kBF16 ? 0x7FC07FC0u : 0x7FC00000u) : 0u;
+            for (int64_t idx = c_begin * kWaveSize + lane; idx < c_end * kWaveSize && idx < rv; idx += kWaveSize)
+                __builtin_nontemporal_store(u32x4{fill, fill, fill, fill}, orow + idx);
+            continue;
+        }
+        const int live = __builtin_popcount(mask);
+        if (live >= 5) span_compact<kBF16, 8, 1>(y, orow, rv, c_begin, c_end, j, wk, mask, lane);
+        else if (live >= 3) span_compact<kBF16, 4, 2>(y, orow, rv, c_begin, c_end, j, wk, mask, lane);
+        else if (live == 2) span_compact<kBF16, 2, C>(y, orow, rv, c_begin, c_end, j, wk, mask, lane);
+        else span_compact<kBF16, 1, C>(y, orow, rv, c_begin, c_end, j, wk, mask, lane);
+    }
+}
+
 // Occupancy cap for large topk-8 reductions whose slots are all live.  At the
 // DSv3 shape (N = 16384, rows of 14 KiB, 57344 workgroups) three workgroups
 // of four waves per CU measured 367 -> 350 us for the unpermute alone and
@@ -283,8 +424,22 @@ static size_t unpermute_cap_lds_bytes() {
     return (size_t)(v / (kUnpermuteCapWorkgroups + 1)) + 1;
 }
 
+template <bool kBF16>
+static hipError_t launch_unpermute_span(const UnpermuteArgs& a, int64_t items, hipStream_t stream) {
+    const int64_t blocks_needed = (items + 3) / 4;
+    const int64_t blocks = blocks_needed < kMaxGridBlocks ? blocks_needed : kMaxGridBlocks;
+    hipLaunchKernelGGL((unpermute_span_kernel<kBF16>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const u32x4*>(a.expanded_output), a.topk_weights, a.inv_permuted_idx,
+                       reinterpret_cast<u32x4*>(a.output), a.num_tokens, a.row_vecs, blocks * 4);
+    return hipGetLastError();
+}
+
 template <bool kBF16, int KC, int U, int G>
 static hipError_t launch_unpermute_t(const UnpermuteArgs& a, hipStream_t stream) {
+    if (KC == 8 && a.few_live) {
+        const int64_t spans = a.num_tokens * (((a.row_vecs + kWaveSize - 1) / kWaveSize + kSpanChunks - 1) / kSpanChunks);
+        if (spans >= kSpanMinItems) return launch_unpermute_span<kBF16>(a, spans, stream);
+    }
     const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
     const int64_t items = a.num_tokens * nchunks;
     const int64_t blocks_needed = (items + 3) / 4;

@@ -296,3 +296,55 @@ def test_unpermute_tokens_with_no_local_slot_get_whole_zero_rows(hip_device, k, 
     ref = oracle.unpermute(to_np(y), to_np(wts), valid, dtype)
     keep = [t for t in range(n) if t != bad_t]
     assert_unpermute_close(o[keep], ref[keep], dtype)
+
+
+# (N, H, dtype): the span schedule of moe_unpermute_local (topk 8, at least
+# 32768 spans of 4 chunks): rows of 17 chunks, the last one a single vector.
+SPAN_CASES = [(8192, 8200, "bf16"), (8192, 4100, "f32")]
+
+
+@pytest.mark.parametrize("n,h,dtype", SPAN_CASES, ids=["-".join(map(str, c)) for c in SPAN_CASES])
+def test_unpermute_local_span_schedule(hip_device, n, h, dtype):
+    """moe_unpermute_local at a size that takes its span schedule, on an
+    expert-split inverse index (each slot live with probability 1/6, some
+    tokens with every slot remote, one token with a bad index): bit-equal to
+    moe_unpermute, and equal to the oracle on a sample of tokens of every
+    live-slot count."""
+    k = 8
+    rng = np.random.default_rng(n + h)
+    rows = n * k
+    inv_np = np.full(rows, -1, dtype=np.int32)
+    live = rng.random(rows) < 1.0 / 6
+    live[np.arange(0, 40) * k] = False        # tokens 0..39: every slot remote
+    for t in range(40):
+        live[t * k:(t + 1) * k] = False
+    live[(40 * k):(41 * k)] = True             # token 40: all eight live
+    inv_np[live] = rng.permutation(rows)[:int(live.sum())].astype(np.int32)
+    bad_t = 77
+    inv_np[bad_t * k + 5] = rows + 3
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    g = torch.Generator(device=hip_device).manual_seed(h)
+    y = torch.randn((rows, h), device=hip_device, generator=g).to(tdt)
+    wts = torch.rand((n, k), device=hip_device, generator=g)
+    inv = torch.from_numpy(inv_np).to(hip_device)
+    _say("unpermute_local span schedule N=%d H=%d %s" % (n, h, dtype))
+    out = gpu_unpermute(y, wts, inv, local=True)
+    out_plain = gpu_unpermute(y, wts, inv)
+    torch.cuda.synchronize()
+    _assert_same_bits(out, out_plain)
+    o = to_np(out)
+    assert torch.isnan(out[bad_t].float().cpu()).all()
+    assert np.all(o[:40].view(np.uint8) == 0)
+    # oracle on sampled tokens: their referenced rows gathered into a compact problem
+    counts = live.reshape(n, k).sum(axis=1)
+    sample = [t for c in range(0, k + 1) for t in np.nonzero(counts == c)[0][:6] if t != bad_t]
+    sample = np.array(sorted(set(sample + list(rng.choice(n, 40, replace=False)))) , dtype=np.int64)
+    sample = sample[sample != bad_t]
+    sub_inv = inv_np.reshape(n, k)[sample].reshape(-1)
+    used = sub_inv[sub_inv >= 0]
+    remap = np.full(sub_inv.shape, -1, dtype=np.int32)
+    remap[sub_inv >= 0] = np.arange(used.size, dtype=np.int32)
+    y_sub = np.zeros((sample.size * k, h), dtype=to_np(y[:1]).dtype)
+    y_sub[:used.size] = to_np(y[torch.from_numpy(used.astype(np.int64)).to(hip_device)])
+    ref = oracle.unpermute(y_sub, to_np(wts)[sample], remap, dtype)
+    assert_unpermute_close(o[sample], ref, dtype)
