@@ -498,7 +498,24 @@ hipError_t launch_gemm_tiles(const GemmArgs& a, int num_cus, hipStream_t stream)
 
 }  // namespace
 
+// The tiled kernel runs at most min(max_rows, num_experts + max_rows / 128)
+// row tiles times n / 256 column tiles, one workgroup per CU.  When that
+// cannot fill the CUs and the experts average at most 16 rows (decode: a row
+// or a few per expert), the skinny kernel streams the weights with one wave
+// per 32 columns instead: decode N=1 (8 rows, 128 tiles) 126 -> 91 us.  With
+// enough tiles the tiled kernel streams faster (decode N=16: 1009 us tiled,
+// 1139 us skinny; N=256: 2419 vs 3014), and with more rows per expert the
+// skinny kernel would stream each expert's weights once per 16 rows.
+constexpr int64_t kSkinnyMaxRowsPerExpert = 16;
+
+static bool gemm_takes_skinny(int64_t max_rows, int num_experts, int64_t n, int num_cus) {
+    const int64_t bound = num_experts + max_rows / 128;
+    const int64_t row_tiles = max_rows < bound ? max_rows : bound;
+    return max_rows <= kSkinnyMaxRowsPerExpert * num_experts && row_tiles * ((n + 255) / 256) < num_cus;
+}
+
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, int num_cus, hipStream_t stream) {
+    if (gemm_takes_skinny(a.max_rows, a.num_experts, a.n, num_cus)) return launch_grouped_gemm_skinny(a, num_cus, stream);
     if (a.n % 256 == 0) return launch_gemm_tiles<GemmShape<128, 256, 2, 4, 3, 1, true>>(a, num_cus, stream);
     return launch_gemm_tiles<GemmShape<128, 128, 2, 2, 2, 2, false>>(a, num_cus, stream);
 }

@@ -64,6 +64,8 @@ struct GemmArgs {
 
 hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t value, hipStream_t stream);
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, int num_cus, hipStream_t stream);
+// The grouped GEMM for experts with few rows each (called by launch_grouped_gemm_bf16).
+hipError_t launch_grouped_gemm_skinny(const GemmArgs& a, int num_cus, hipStream_t stream);
 hipError_t launch_quant_scatter(const QuantArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream);
 // Device address of the current device's static workspace (kStaticScratchBytes).

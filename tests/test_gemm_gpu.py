@@ -164,3 +164,93 @@ def test_grouped_gemm_full_size_sampled_rows(hip_device, name, n):
         wr = to_np(wts[int(ex):int(ex) + 1])
         ref = oracle.grouped_gemm_bf16(xr, wr, np.array([0, 1], np.int64))
         assert_gemm_close(to_np(y[int(j):int(j) + 1]), ref, xr, wr, np.array([0, 1], np.int64))
+
+
+# ----------------------------------------------------------------------------
+# Skinny kernel: taken when the experts average at most 16 rows and the tiled
+# kernel's most tiles, min(max_rows, E + max_rows // 128) x ceil(n / 256), are
+# fewer than the CUs; one wave per 32 output columns of an expert and 16 of
+# its rows, weights streamed from global memory into the MFMA operands.
+# ----------------------------------------------------------------------------
+def _takes_skinny(max_rows, e, n):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return max_rows <= 16 * e and min(max_rows, e + max_rows // 128) * ((n + 255) // 256) < cus
+
+
+SKINNY_CASES = [
+    # (experts, per-expert row counts or a mode with a total, n, k, spare rows)
+    (8, [0, 1, 33, 40, 0, 20, 2, 0], 256, 832, 16),   # 13 k chunks: whole rounds, then a tail; 2 row groups
+    (8, [8] * 8, 128, 512, 0),                         # exactly two rounds of 4 chunks
+    (16, ("skewed", 200), 384, 256, 16),               # 4 chunks: the tail path only
+    (4, [0, 0, 0, 1], 128, 64, 3),                     # one row, one chunk
+    (200, ("even", 1600), 128, 320, 0),                # 200 experts, 5 chunks
+]
+
+
+def _skinny_offsets(rng, e, spec):
+    if isinstance(spec, tuple):
+        return _offsets(rng, e, spec[1], spec[0])
+    return np.concatenate([[0], np.cumsum(spec)]).astype(np.int64)
+
+
+@pytest.mark.parametrize("e,spec,n,k,spare", SKINNY_CASES, ids=["skinny-%d-%d-%d" % (c[0], c[2], c[3]) for c in SKINNY_CASES])
+def test_grouped_gemm_skinny_parity(hip_device, e, spec, n, k, spare):
+    rng = np.random.default_rng(n + k + e)
+    off = _skinny_offsets(rng, e, spec)
+    rows = int(off[-1])
+    assert _takes_skinny(rows + spare, e, n)
+    g = torch.Generator().manual_seed(rows * 7 + k)
+    x = _bf16(torch.randn((rows, k), generator=g))
+    w = _bf16(torch.randn((e, n, k), generator=g) * k**-0.5)
+    xs = torch.cat([x, _bf16(torch.randn((spare, k), generator=g))]).to(hip_device)
+    y = poisoned((rows + spare, n), torch.bfloat16, hip_device)
+    _say("skinny grouped gemm E=%d rows=%d n=%d k=%d" % (e, rows, n, k))
+    binding.moe_grouped_gemm_bf16(xs, w.to(hip_device), torch.from_numpy(off).to(hip_device), y)
+    torch.cuda.synchronize()
+    got = to_np(y)
+    ref = oracle.grouped_gemm_bf16(to_np(x), to_np(w), off)
+    assert_gemm_close(got[:rows], ref, to_np(x), to_np(w), off)
+    assert np.all(got[rows:].view(np.uint8) == POISON)
+
+
+def test_grouped_gemm_skinny_rejected_offsets_write_nothing(hip_device):
+    x = _bf16(torch.randn((64, 128))).to(hip_device)
+    w = _bf16(torch.randn((8, 128, 128))).to(hip_device)
+    for bad in ([-1] * 9, [0, 4, 3, 5, 6, 7, 8, 9, 10], [0, 1, 2, 3, 4, 5, 6, 7, 65], [2] * 9):
+        y = poisoned((64, 128), torch.bfloat16, hip_device)
+        _say("skinny grouped gemm bad offsets %s" % bad)
+        binding.moe_grouped_gemm_bf16(x, w, torch.tensor(bad, dtype=torch.int64, device=hip_device), y)
+        torch.cuda.synchronize()
+        assert np.all(to_np(y).view(np.uint8) == POISON)
+
+
+@pytest.mark.parametrize("tokens", [1, 4, 256])
+def test_grouped_gemm_decode_shape_sampled(hip_device, tokens):
+    """The decode shape (topk 8, 256 experts, n=4096, k=7168) at N=1 (skinny
+    kernel), 4 and 256 tokens (tiled): every expert's rows on the device; the
+    oracle checks a sample of experts (the ones with the most and the fewest
+    rows, and up to four others)."""
+    w8 = W.WORKLOADS["decode"].with_tokens(tokens)
+    ids_np, _ = W.make_routing(w8, 0)
+    e, n, k = w8.num_experts, 4096, w8.hidden_size
+    counts = np.bincount(ids_np.reshape(-1), minlength=e)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    rows = int(off[-1])
+    g = torch.Generator(device=hip_device).manual_seed(9)
+    x = _bf16(torch.randn((rows, k), device=hip_device, generator=g))
+    w = _bf16(torch.randn((e, n, k), device=hip_device, generator=g) * k**-0.5)
+    y = poisoned((rows, n), torch.bfloat16, hip_device)
+    _say("grouped gemm decode shape N=%d rows=%d skinny=%s" % (tokens, rows, _takes_skinny(rows, e, n)))
+    assert _takes_skinny(rows, e, n) == (tokens == 1)
+    binding.moe_grouped_gemm_bf16(x, w, torch.from_numpy(off).to(hip_device), y)
+    torch.cuda.synchronize()
+    used = np.nonzero(counts)[0]
+    pick = sorted(set([int(used[np.argmax(counts[used])]), int(used[np.argmin(counts[used])])] +
+                      [int(v) for v in np.random.default_rng(1).choice(used, min(4, used.size), replace=False)]))
+    sub_rows = np.concatenate([np.arange(off[p], off[p + 1]) for p in pick])
+    sub_off = np.concatenate([[0], np.cumsum(counts[pick])]).astype(np.int64)
+    xs = to_np(x[torch.from_numpy(sub_rows).to(hip_device)])
+    ws = to_np(w[torch.tensor(pick, device=hip_device)])
+    ref = oracle.grouped_gemm_bf16(xs, ws, sub_off)
+    got = to_np(y)[sub_rows]
+    assert_gemm_close(got, ref, xs, ws, sub_off)
