@@ -67,6 +67,9 @@ hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, int num_cus, hipStream_t 
 // The grouped GEMM for experts with few rows each (called by launch_grouped_gemm_bf16).
 hipError_t launch_grouped_gemm_skinny(const GemmArgs& a, int num_cus, hipStream_t stream);
 hipError_t launch_quant_scatter(const QuantArgs& a, bool bf16, hipStream_t stream);
+// Decode sizes (the wave plan, no expert map): index permute and quantise-scatter in one kernel.
+hipError_t launch_quant_permute_wave(const PermuteArgs& a, const QuantArgs& q, const PermutePlan& p, bool bf16,
+                                     hipStream_t stream);
 hipError_t launch_permute(const PermuteArgs& a, const PermutePlan& p, void* workspace, hipStream_t stream);
 // Device address of the current device's static workspace (kStaticScratchBytes).
 hipError_t static_scratch_address(void** ptr);

@@ -108,7 +108,9 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
                           int32_t num_experts, const int32_t* expert_map, int32_t num_local_experts,
                           void* permuted_hidden_states, float* permuted_scale, int64_t* expert_first_token_offset,
                           int32_t* permuted_idx, int32_t* inv_permuted_idx, void* workspace,
-                          size_t workspace_bytes, void* stream, bool static_workspace = false) {
+                          size_t workspace_bytes, void* stream, bool static_workspace = false,
+                          const moe::QuantArgs* fuse_quant = nullptr, bool quant_bf16 = false,
+                          bool* quant_fused = nullptr) {
     const int64_t eb = element_bytes(dtype);
     if (eb == 0) return MOE_ERR_INVALID_ARG;
     if (!sizes_ok(num_tokens, topk, num_experts)) return MOE_ERR_INVALID_ARG;
@@ -194,6 +196,12 @@ moe_status_t permute_impl(const void* hidden_states, int32_t dtype, const float*
     a.expert_first_token_offset = expert_first_token_offset;
     a.permuted_idx = permuted_idx;
     a.inv_permuted_idx = inv_permuted_idx;
+    if (fuse_quant != nullptr && plan.wave && !mapped) {
+        // decode sizes: index permute and quantise-scatter in one kernel
+        *quant_fused = true;
+        return moe::launch_quant_permute_wave(a, *fuse_quant, plan, quant_bf16, s) == hipSuccess ? MOE_OK
+                                                                                                : MOE_ERR_HIP;
+    }
     return moe::launch_permute(a, plan, workspace, s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -282,12 +290,8 @@ moe_status_t moe_permute_quant_fp8(const void* hidden_states, int32_t dtype, con
         };
         if (any_overlap(outs, 2, others, 7)) return MOE_ERR_INVALID_ARG;
     }
-    // Index permute (no rows moved), then the quantise-scatter.
-    const moe_status_t st = permute_impl(nullptr, dtype, nullptr, topk_ids, topk_ids_dtype, num_tokens, 0, topk,
-                                         num_experts, expert_map, num_local_experts, nullptr, nullptr,
-                                         expert_first_token_offset, permuted_idx, inv_permuted_idx, workspace,
-                                         workspace_bytes, stream);
-    if (st != MOE_OK || num_tokens == 0) return st;
+    // Index permute (no rows moved), then the quantise-scatter; at decode sizes
+    // (the wave plan, no expert map) one kernel does both.
     moe::QuantArgs q;
     q.hidden_states = hidden_states;
     q.inv_permuted_idx = inv_permuted_idx;
@@ -299,6 +303,12 @@ moe_status_t moe_permute_quant_fp8(const void* hidden_states, int32_t dtype, con
     q.all_local = expert_map == nullptr;
     q.permuted_codes = permuted_codes;
     q.permuted_scale = permuted_scale;
+    bool fused = false;
+    const moe_status_t st = permute_impl(nullptr, dtype, nullptr, topk_ids, topk_ids_dtype, num_tokens, 0, topk,
+                                         num_experts, expert_map, num_local_experts, nullptr, nullptr,
+                                         expert_first_token_offset, permuted_idx, inv_permuted_idx, workspace,
+                                         workspace_bytes, stream, false, &q, dtype == MOE_DTYPE_BF16, &fused);
+    if (st != MOE_OK || num_tokens == 0 || fused) return st;
     return moe::launch_quant_scatter(q, dtype == MOE_DTYPE_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
                ? MOE_OK
                : MOE_ERR_HIP;

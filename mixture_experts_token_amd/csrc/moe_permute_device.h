@@ -72,6 +72,102 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ----------------------------------------------------------------------------
+// Wave schedule index pass (decode sizes, no expert map): one wave holds all R
+// <= 64 * kPer expert ids of the call (id[j] is row j * 64 + lane; rows past R
+// hold any valid load and are ignored) and computes the whole index itself:
+//   * stable ranks: rows walked in batches of 64 in ascending order; inside a
+//     batch the lanes with the same expert are found with one ballot per id
+//     bit and a row's rank is the count of such lanes below it (mbcnt) plus
+//     the rows of its expert in earlier batches (a running count in LDS,
+//     advanced by the lowest lane of each equal-key group);
+//   * the running counts end as the rows per expert; their exclusive scan
+//     (wave shuffles) gives the offsets, and destination = offset + rank.
+// run: LDS [E]; dest_s: LDS [R], filled with each row's destination.  When
+// `writer`, the offsets, permuted_idx, inv_permuted_idx (and, with kScale,
+// the per-token scales sc moved to their rows) are written.  Returns false
+// when an id is outside [0, E): the writer has then set every offset to -1
+// and nothing else is written.  The same answer in every wave, since every
+// wave sees every id.
+// ----------------------------------------------------------------------------
+// Orders the LDS accesses of this wave (the compiler must not move them across
+// it; the hardware completes one wave's LDS operations in order).
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local"); }
+
+template <int kPer, bool kScale>
+__device__ __forceinline__ bool wave_index_pass(int E, int R, int nbits, const int (&id)[kPer],
+                                                const float (&sc)[kPer], int* run, int* dest_s, bool writer,
+                                                int64_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                int32_t* __restrict__ inv, float* __restrict__ pscale) {
+    const int lane = (int)(threadIdx.x % kWaveSize);
+    for (int e = lane; e < E; e += kWaveSize) run[e] = 0;
+    wave_lds_fence();
+
+    // Stable ranks, batch by batch; run[e] ends as the rows of expert e.
+    int rank[kPer];
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        rank[j] = 0;
+        if (j * kWaveSize < R) {  // wave-uniform
+            const int r = j * kWaveSize + lane;
+            const bool live = r < R;
+            const bool ok = live && (unsigned)id[j] < (unsigned)E;
+            bad |= live && !ok;
+            const uint64_t same = lanes_with_same_key(id[j], ok, nbits);
+            const int below = lanes_below(same);
+            if (ok) {
+                const int c = run[id[j]];
+                rank[j] = c + below;
+                if (below == 0) run[id[j]] = c + (int)__popcll(same);
+            }
+            wave_lds_fence();
+        }
+    }
+    if (__ballot(bad) != 0) {
+        if (writer)
+            for (int e = lane; e <= E; e += kWaveSize) offsets[e] = -1;
+        return false;
+    }
+
+    // Exclusive scan of the counts in place: lane l owns experts [l*per, l*per + per).
+    const int per = (E + kWaveSize - 1) / kWaveSize;
+    const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
+    int s = 0;
+    for (int e = e0; e < e1; ++e) s += run[e];
+    int x = s;
+#pragma unroll
+    for (int d = 1; d < kWaveSize; d <<= 1) {
+        const int y = __shfl_up(x, d, kWaveSize);
+        if (lane >= d) x += y;
+    }
+    int acc = x - s;
+    for (int e = e0; e < e1; ++e) {
+        const int c = run[e];
+        run[e] = acc;
+        if (writer) offsets[e] = acc;
+        acc += c;
+    }
+    if (writer && lane == 0) offsets[E] = R;
+    wave_lds_fence();
+
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int r = j * kWaveSize + lane;
+        if (r < R) {
+            const int d = run[id[j]] + rank[j];
+            dest_s[r] = d;
+            if (writer) {
+                inv[r] = d;
+                perm[d] = r;
+                if constexpr (kScale) pscale[d] = sc[j];
+            }
+        }
+    }
+    wave_lds_fence();
+    return true;
+}
+
+// ----------------------------------------------------------------------------
 // Sort keys.  Without a map a row's key is its expert id.  With a local-expert
 // map (expert parallelism: the offsets cover this rank's experts only) the key
 // is the expert's local id, and a row whose expert lives on another rank gets

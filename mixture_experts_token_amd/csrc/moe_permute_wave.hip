@@ -17,9 +17,10 @@
 //   * the running counts end as the rows per expert; their exclusive scan
 //     (wave shuffles) gives the offsets, and destination = offset + rank.
 // LDS operations of one wave complete in order, so the wave needs no barrier.
-// Workgroups redundantly compute the index (at most 128 ids each) and
-// each copies its own row chunks of one token (grid: chunks x tokens);
-// workgroup (0, 0) writes the index outputs.
+// Workgroups redundantly compute the index (at most 128 ids each,
+// wave_index_pass in moe_permute_device.h) and each copies its own row chunks
+// of one token (grid: chunks x tokens); workgroup (0, 0) writes the index
+// outputs.
 
 #include <hip/hip_runtime.h>
 
@@ -28,10 +29,6 @@
 #include "moe_permute_device.h"
 
 namespace moe {
-
-// Orders the LDS accesses of this wave (the compiler must not move them across
-// it; the hardware completes one wave's LDS operations in order).
-__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local"); }
 
 // kPer: expert ids each lane holds (N*topk <= 64*kPer), chosen by the launcher.
 // kScale: per-token scales move with the rows (loaded with the ids, so the
@@ -88,71 +85,9 @@ __global__ __launch_bounds__(kWaveSize) void permute_wave_kernel(PermuteArgs a, 
     int64_t chunk = blockIdx.x;  // < the row's chunk count when kRows (the grid never exceeds it)
     if constexpr (kRows) load_chunk(chunk);
 
-    for (int e = lane; e < E; e += kWaveSize) run[e] = 0;
-    wave_lds_fence();
-
-    // Stable ranks, batch by batch; run[e] ends as the rows of expert e.
-    int rank[kPer];
-    bool bad = false;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        rank[j] = 0;
-        if (j * kWaveSize < R) {  // wave-uniform
-            const int r = j * kWaveSize + lane;
-            const bool live = r < R;
-            const bool ok = live && (unsigned)id[j] < (unsigned)E;
-            bad |= live && !ok;
-            const uint64_t same = lanes_with_same_key(id[j], ok, nbits);
-            const int below = lanes_below(same);
-            if (ok) {
-                const int c = run[id[j]];
-                rank[j] = c + below;
-                if (below == 0) run[id[j]] = c + (int)__popcll(same);
-            }
-            wave_lds_fence();
-        }
-    }
-    if (__ballot(bad) != 0) {  // every workgroup saw every id: all stop here
-        if (writer)
-            for (int e = lane; e <= E; e += kWaveSize) a.expert_first_token_offset[e] = -1;
-        return;
-    }
-
-    // Exclusive scan of the counts in place: lane l owns experts [l*per, l*per + per).
-    const int per = (E + kWaveSize - 1) / kWaveSize;
-    const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
-    int s = 0;
-    for (int e = e0; e < e1; ++e) s += run[e];
-    int x = s;
-#pragma unroll
-    for (int d = 1; d < kWaveSize; d <<= 1) {
-        const int y = __shfl_up(x, d, kWaveSize);
-        if (lane >= d) x += y;
-    }
-    int acc = x - s;
-    for (int e = e0; e < e1; ++e) {
-        const int c = run[e];
-        run[e] = acc;
-        if (writer) a.expert_first_token_offset[e] = acc;
-        acc += c;
-    }
-    if (writer && lane == 0) a.expert_first_token_offset[E] = R;
-    wave_lds_fence();
-
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int r = j * kWaveSize + lane;
-        if (r < R) {
-            const int d = run[id[j]] + rank[j];
-            dest_s[r] = d;
-            if (writer) {
-                a.inv_permuted_idx[r] = d;
-                a.permuted_idx[d] = r;
-                if constexpr (kScale) a.permuted_scale[d] = sc[j];
-            }
-        }
-    }
-    wave_lds_fence();
+    if (!wave_index_pass<kPer, kScale>(E, R, nbits, id, sc, run, dest_s, writer, a.expert_first_token_offset,
+                                       a.permuted_idx, a.inv_permuted_idx, a.permuted_scale))
+        return;  // a rejected id: every workgroup saw it and stops here
 
     // Row copy of token t: chunk `chunk`, then chunk + gridDim.x, ...; the
     // next chunk's loads are issued before the current one is stored.

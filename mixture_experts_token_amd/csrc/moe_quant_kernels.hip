@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "moe_launch.h"
+#include "moe_permute_device.h"
 #include "moe_plan.h"
 
 namespace moe {
@@ -264,7 +265,118 @@ hipError_t launch_quant_dtype(const QuantArgs& a, hipStream_t stream) {
     return launch_quant_ut<kBF16, 1, 1024>(a, stream);  // rv <= 1024 (checked on the host)
 }
 
+// ----------------------------------------------------------------------------
+// Decode sizes (N*topk <= kWaveMaxRows, no expert map): the index permute and
+// the quantise-scatter in one kernel of one-wave workgroups, as the wave
+// schedule of the plain permute does it.  Grid: chunks of 64 input vectors x
+// tokens.  Every wave computes the whole index (wave_index_pass; workgroup
+// (0, 0) writes it), then quantises its chunk of its token and stores the
+// codes (and scales) at the token's topk destinations.  With one scale per
+// token each wave also reads the whole row for the amax (kRowPer vectors per
+// lane, from L2 after the first wave); with group scales a chunk holds whole
+// groups (a group is at most 64 vectors, aligned).  The arithmetic is the
+// quantise-scatter's (vec_amax, max over the group or row, __fdiv_rn,
+// vec_codes).
+// ----------------------------------------------------------------------------
+template <bool kBF16, typename IdT, int kPer, int kRowPer>
+__global__ __launch_bounds__(kWaveSize) void quant_permute_wave_kernel(PermuteArgs a, QuantArgs q, int nbits) {
+    constexpr int kEpv = kBF16 ? 8 : 4;  // elements (and code bytes) per 16-byte input vector
+    extern __shared__ int smem[];
+    const int E = a.num_experts;
+    const int K = a.topk;
+    const int R = (int)(a.num_tokens * K);
+    int* run = smem;
+    int* dest_s = run + E;
+    const int lane = (int)threadIdx.x;
+    const IdT* ids = static_cast<const IdT*>(a.topk_ids);
+    const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
+
+    // Independent loads first: the ids, this wave's input vector, the row.
+    int id[kPer];
+    float sc_unused[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int r = j * kWaveSize + lane;
+        id[j] = load_id(ids, r < R ? r : R - 1);
+    }
+    const int64_t rv = q.row_vecs;
+    const int t = (int)blockIdx.y;
+    const u32x4* src = static_cast<const u32x4*>(q.hidden_states) + (int64_t)t * rv;
+    const int64_t idx = (int64_t)blockIdx.x * kWaveSize + lane;  // blockIdx.x < ceil(rv / 64)
+    const u32x4 v = __builtin_nontemporal_load(src + (idx < rv ? idx : rv - 1));
+    u32x4 row[kRowPer > 0 ? kRowPer : 1];
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+        const int64_t i = (int64_t)j * kWaveSize + lane;
+        row[j] = src[i < rv ? i : rv - 1];  // duplicates past the row end do not change a maximum
+    }
+
+    if (!wave_index_pass<kPer, false>(E, R, nbits, id, sc_unused, run, dest_s, writer, a.expert_first_token_offset,
+                                      a.permuted_idx, a.inv_permuted_idx, nullptr))
+        return;  // a rejected id: nothing but the offsets (-1) is written
+
+    float m;
+    if constexpr (kRowPer > 0) {  // one scale per token
+        m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kRowPer; ++j) {
+            const float b = vec_amax<kBF16>(row[j]);
+            m = b > m ? b : m;
+        }
+#pragma unroll
+        for (int s = 1; s < kWaveSize; s <<= 1) m = max_xor(m, s);
+    } else {
+        m = idx < rv ? vec_amax<kBF16>(v) : 0.0f;
+        for (int s = 1; s < q.group_vecs; s <<= 1) m = max_xor(m, s);
+    }
+    const float scale = m > 0.0f ? __fdiv_rn(m, kE4M3Max) : 1.0f;
+    const u32x2 c = vec_codes<kBF16>(v, scale);
+    const int64_t row_bytes = rv * kEpv;
+    const int64_t groups = q.group_vecs > 0 ? rv / q.group_vecs : 1;
+    for (int k = 0; k < K; ++k) {
+        const int d = dest_s[t * K + k];
+        if (idx < rv) {
+            uint8_t* orow = q.permuted_codes + (int64_t)d * row_bytes;
+            if constexpr (kBF16) __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(orow) + idx);
+            else __builtin_nontemporal_store(c.x, reinterpret_cast<uint32_t*>(orow) + idx);
+            if (kRowPer == 0 && idx % q.group_vecs == 0) q.permuted_scale[(int64_t)d * groups + idx / q.group_vecs] = scale;
+        }
+        if (kRowPer > 0 && blockIdx.x == 0 && lane == 0) q.permuted_scale[d] = scale;
+    }
+}
+
+template <bool kBF16, typename IdT, int kPer>
+static hipError_t launch_quant_wave_p(const PermuteArgs& a, const QuantArgs& q, const PermutePlan& p,
+                                      hipStream_t stream) {
+    const dim3 grid((unsigned)((q.row_vecs + kWaveSize - 1) / kWaveSize), (unsigned)a.num_tokens);
+    const size_t lds = wave_lds_bytes(a.num_experts, (int)p.rows);
+#define MOE_QW(RP) hipLaunchKernelGGL((quant_permute_wave_kernel<kBF16, IdT, kPer, RP>), grid, dim3(kWaveSize), lds, \
+                                      stream, a, q, p.nbits)
+    if (q.group_vecs > 0) MOE_QW(0);
+    else if (q.row_vecs <= 4 * kWaveSize) MOE_QW(4);
+    else MOE_QW(16);  // row_vecs <= kQuantMaxRowVecs = 16 * 64
+#undef MOE_QW
+    return hipGetLastError();
+}
+
+template <bool kBF16, typename IdT>
+static hipError_t launch_quant_wave_i(const PermuteArgs& a, const QuantArgs& q, const PermutePlan& p,
+                                      hipStream_t stream) {
+    static_assert(kWaveMaxRows == 2 * kWaveSize && kQuantMaxRowVecs == 16 * kWaveSize,
+                  "ids per lane and row vectors per lane of the decode quantising permute");
+    if (p.rows <= kWaveSize) return launch_quant_wave_p<kBF16, IdT, 1>(a, q, p, stream);
+    return launch_quant_wave_p<kBF16, IdT, 2>(a, q, p, stream);
+}
+
 }  // namespace
+
+hipError_t launch_quant_permute_wave(const PermuteArgs& a, const QuantArgs& q, const PermutePlan& p, bool bf16,
+                                     hipStream_t stream) {
+    if (bf16) return a.ids64 ? launch_quant_wave_i<true, int64_t>(a, q, p, stream)
+                             : launch_quant_wave_i<true, int32_t>(a, q, p, stream);
+    return a.ids64 ? launch_quant_wave_i<false, int64_t>(a, q, p, stream)
+                   : launch_quant_wave_i<false, int32_t>(a, q, p, stream);
+}
 
 hipError_t launch_quant_scatter(const QuantArgs& a, bool bf16, hipStream_t stream) {
     if (a.num_tokens == 0) return hipSuccess;

@@ -80,6 +80,16 @@ hipError_t launch_unpermute(const UnpermuteArgs& a, bool, hipStream_t) {
     return hipSuccess;
 }
 
+hipError_t launch_quant_permute_wave(const PermuteArgs& a, const QuantArgs& q, const PermutePlan& p, bool,
+                                     hipStream_t) {
+    require(a.topk_ids != nullptr && a.permuted_idx != nullptr && a.inv_permuted_idx != nullptr &&
+                a.expert_first_token_offset != nullptr && p.wave && p.rows == a.num_tokens * a.topk &&
+                a.expert_map == nullptr && q.hidden_states != nullptr && q.permuted_codes != nullptr &&
+                q.permuted_scale != nullptr && q.row_vecs > 0 && q.row_vecs <= kQuantMaxRowVecs,
+            "quant permute wave");
+    return hipSuccess;
+}
+
 hipError_t launch_quant_scatter(const QuantArgs& a, bool, hipStream_t) {
     require(a.hidden_states != nullptr && a.permuted_codes != nullptr && a.permuted_scale != nullptr &&
                 a.row_vecs > 0 && a.row_vecs <= kQuantMaxRowVecs,

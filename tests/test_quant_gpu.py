@@ -189,3 +189,40 @@ def test_quant_zero_tokens(hip_device):
     outs = gpu_quant(x, ids, 4)
     torch.cuda.synchronize()
     assert to_np(outs["expert_first_token_offset"]).tolist() == [0] * 5
+
+
+# Decode sizes (N*topk <= 128, no expert map) take the one-kernel quantising
+# permute: one or two ids per lane, rows read whole for a per-token scale
+# (4 or 16 vectors per lane) or groups within a 64-vector chunk.
+WAVE_CASES = [
+    # (N, topk, E, H, dtype, group, ids dtype)
+    (16, 8, 256, 7168, torch.bfloat16, 0, torch.int32),     # 128 rows: two ids per lane
+    (16, 8, 256, 7168, torch.bfloat16, 128, torch.int32),
+    (9, 8, 64, 2048, torch.float32, 0, torch.int32),         # f32 rows of 512 vectors
+    (5, 4, 16, 256, torch.bfloat16, 32, torch.int32),        # a single, partly filled chunk
+    (3, 8, 256, 4096, torch.bfloat16, 0, torch.int64),
+    (2, 8, 256, 8192, torch.bfloat16, 0, torch.int32),       # the largest row: 1024 vectors
+    (1, 8, 256, 7168, torch.bfloat16, 64, torch.int64),
+]
+
+
+@pytest.mark.parametrize("n,k,e,h,dtype,group,idt", WAVE_CASES, ids=["-".join(map(str, c[:4])) + "-%s-g%d-%s" % (
+    str(c[4]).split(".")[-1], c[5], str(c[6]).split(".")[-1]) for c in WAVE_CASES])
+def test_quant_decode_sizes_one_kernel(hip_device, n, k, e, h, dtype, group, idt):
+    rng = np.random.default_rng(n * 31 + h)
+    ids = torch.from_numpy(np.argsort(rng.random((n, e)), axis=1)[:, :k]).to(idt).to(hip_device)
+    g = torch.Generator(device="cpu").manual_seed(n + h)
+    mag = torch.exp(torch.randn((n, 1), generator=g) * 3)
+    x = (torch.randn((n, h), generator=g) * mag).to(dtype).to(hip_device)
+    _say("quant decode size N=%d topk=%d H=%d group=%d" % (n, k, h, group))
+    outs = gpu_quant(x, ids, e, group)
+    torch.cuda.synchronize()
+    assert_quant_equal(outs, oracle_quant(x, ids, e, group))
+    bad = ids.clone()
+    bad[n - 1, k - 1] = e if idt == torch.int32 else 2**32 + 1
+    outs = gpu_quant(x, bad, e, group)
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == [-1] * (e + 1)
+    assert np.all(to_np(outs["permuted_hidden_states"]) == POISON)
+    assert np.all(to_np(outs["permuted_scale"]).view(np.uint32) == 0xFFFFFFFF)
+    assert np.all(to_np(outs["permuted_idx"]).view(np.uint32) == 0xFFFFFFFF)
