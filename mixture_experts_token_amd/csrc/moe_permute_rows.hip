@@ -16,7 +16,9 @@
 // The index pass sets every offset to -1 and writes no index when it meets an
 // invalid expert id; the copy then reads expert_first_token_offset[0] (0 after
 // a valid index pass) and writes nothing.  Every destination is checked
-// against [0, N*topk) as well.
+// against [0, N*topk) as well.  With an expert map (kMap) a row of another
+// rank has destination -1 and is skipped, and a token with no local row is
+// not read: its wave reads the destinations first.
 
 #include <hip/hip_runtime.h>
 
@@ -32,7 +34,7 @@ namespace moe {
 // nothing), then the wave-uniform destinations are read; the loads are in
 // bounds whatever the index pass found, so the check of its result waits
 // until they are in flight.
-template <int U, bool kNTStore, int KC>
+template <int U, bool kNTStore, int KC, bool kMap>
 __global__ __launch_bounds__(256) void permute_rows_kernel(const u32x4* __restrict__ x,
                                                            const int32_t* __restrict__ inv,
                                                            const int64_t* __restrict__ off,
@@ -47,6 +49,12 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const u32x4* __restri
         const int64_t t = __builtin_amdgcn_readfirstlane((int)(item / nchunks));
         const int64_t base = (item - t * nchunks) * (U * kWaveSize) + lane;
         const u32x4* src = x + t * rv;
+        if constexpr (kMap) {
+            // tokens with no local row are not read
+            bool any = false;
+            for (int k = 0; k < K; ++k) any |= inv[t * K + k] >= 0;
+            if (!any) continue;
+        }
         u32x4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -92,31 +100,32 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const u32x4* __restri
 // one, two, three, six and eight (413-425 us for the others, 405 us here).
 constexpr int kRowsCopyUnroll = 4;
 
-template <bool kNT, int KC>
+template <bool kNT, int KC, bool kMap>
 static void launch_rows_k(const PermuteArgs& a, hipStream_t stream) {
     constexpr int U = kRowsCopyUnroll;
     const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
     const int64_t items = a.num_tokens * nchunks;
     const int64_t needed = (items + 3) / 4;
     const int64_t blocks = needed < kMaxGridBlocks ? needed : kMaxGridBlocks;
-    hipLaunchKernelGGL((permute_rows_kernel<U, kNT, KC>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((permute_rows_kernel<U, kNT, KC, kMap>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const u32x4*>(a.hidden_states), a.inv_permuted_idx, a.expert_first_token_offset,
                        static_cast<u32x4*>(a.permuted_hidden_states), a.num_tokens, a.row_vecs, a.topk, blocks * 4);
 }
 
-template <bool kNT>
+template <bool kNT, bool kMap>
 static void launch_rows_nt(const PermuteArgs& a, hipStream_t stream) {
     switch (a.topk) {
-        case 8: launch_rows_k<kNT, 8>(a, stream); break;
-        case 4: launch_rows_k<kNT, 4>(a, stream); break;
-        case 2: launch_rows_k<kNT, 2>(a, stream); break;
-        default: launch_rows_k<kNT, 0>(a, stream); break;
+        case 8: launch_rows_k<kNT, 8, kMap>(a, stream); break;
+        case 4: launch_rows_k<kNT, 4, kMap>(a, stream); break;
+        case 2: launch_rows_k<kNT, 2, kMap>(a, stream); break;
+        default: launch_rows_k<kNT, 0, kMap>(a, stream); break;
     }
 }
 
 hipError_t launch_permute_rows(const PermuteArgs& a, hipStream_t stream) {
-    if (plain_row_stores(a)) launch_rows_nt<false>(a, stream);
-    else launch_rows_nt<true>(a, stream);
+    const bool m = a.expert_map != nullptr;
+    if (plain_row_stores(a)) { if (m) launch_rows_nt<false, true>(a, stream); else launch_rows_nt<false, false>(a, stream); }
+    else { if (m) launch_rows_nt<true, true>(a, stream); else launch_rows_nt<true, false>(a, stream); }
     return hipGetLastError();
 }
 

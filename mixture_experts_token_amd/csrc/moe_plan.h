@@ -57,6 +57,14 @@ constexpr size_t kStaticScratchBytes = size_t(4) << 20;  // workspace of moe_per
 // (DSv3 shape, 2.1 GB: 434 -> 416 us); the Qwen3 shape (0.3 GB) measured
 // 58 -> 61 us with it.
 constexpr int64_t kSplitCopyMinBytes = int64_t(1) << 30;
+// With an expert map (a rank's share: about N * topk / ranks rows), from
+// this many bytes of token rows (N * row bytes) at topk >= 4.  DSv3 shape,
+// 8-way split: the three measured ranks' permutes 121 -> 115, 51 -> 46 and
+// 56 -> 51 us; below it the index pass costs more than it saves (Qwen3 shape,
+// 34 MB of token rows, 4- and 8-way: 25 -> 27 and 19 -> 21 us; Mixtral shape,
+// topk 2, 2-way: 13 -> 20 us).
+constexpr int64_t kSplitMapMinTokenBytes = int64_t(128) << 20;
+constexpr int kSplitMapMinTopk = 4;
 constexpr int kQuantMaxRowVecs = 1024;             // quantise-scatter: a wave holds the whole row (16 KiB)
 constexpr int kIndexOnlyTileScale = 4;             // coarse tiles of an index-only permute, vs the staged ones
 
@@ -173,7 +181,9 @@ inline PermutePlan plan_permute(int64_t num_tokens, int topk, int buckets, int m
 
 // Whether a permute copying rows of row_bytes takes the split schedule.
 inline bool split_copy_applies(int64_t num_tokens, int topk, int64_t row_bytes, int map_entries) {
-    return map_entries == 0 && row_bytes > 0 && num_tokens * topk * row_bytes >= kSplitCopyMinBytes;
+    if (row_bytes <= 0) return false;
+    if (map_entries > 0) return topk >= kSplitMapMinTopk && num_tokens * row_bytes >= kSplitMapMinTokenBytes;
+    return num_tokens * topk * row_bytes >= kSplitCopyMinBytes;
 }
 
 // Workspace of a call with max_num_tokens tokens; every call with fewer tokens

@@ -348,3 +348,31 @@ def test_unpermute_local_span_schedule(hip_device, n, h, dtype):
     y_sub[:used.size] = to_np(y[torch.from_numpy(used.astype(np.int64)).to(hip_device)])
     ref = oracle.unpermute(y_sub, to_np(wts)[sample], remap, dtype)
     assert_unpermute_close(o[sample], ref, dtype)
+
+
+def test_local_split_schedule_with_scales_and_bad_id(hip_device):
+    """A local permute large enough for the split schedule (16384 tokens of
+    14 KiB, topk 8): with per-token scales against the oracle in full (the
+    buffers past the local rows keep their poison), then with one expert id
+    out of range (offsets -1, nothing else written)."""
+    w = W.WORKLOADS["dsv3"]
+    n, k, e, h = w.num_tokens, w.topk, w.num_experts, w.hidden_size
+    assert n * h * 2 >= 128 << 20
+    ids_np, _ = W.make_routing(w, seed=5)
+    ids = torch.from_numpy(ids_np).to(hip_device)
+    g = torch.Generator(device=hip_device).manual_seed(3)
+    x = torch.randn((n, h), device=hip_device, generator=g).to(torch.bfloat16)
+    scale = torch.rand(n, device=hip_device, generator=g) + 0.25
+    emap, nl = W.expert_map_for(e, 8, 3, "shuffled")
+    _say("local split schedule dsv3 ep8 rank 3 shuffled, scales")
+    outs = gpu_permute_local(x, ids, e, emap, nl, token_scale=scale)
+    torch.cuda.synchronize()
+    assert_permute_local_equal(outs, oracle_permute_local(x, ids, e, emap, nl, scale))
+    bad = ids_np.copy()
+    bad[n // 3, 2] = e + 7
+    _say("local split schedule, bad id")
+    outs = gpu_permute_local(x, torch.from_numpy(bad).to(hip_device), e, emap, nl, token_scale=scale)
+    torch.cuda.synchronize()
+    assert to_np(outs["expert_first_token_offset"]).tolist() == [-1] * (nl + 1)
+    for key in ("permuted_idx", "inv_permuted_idx", "permuted_hidden_states", "permuted_scale"):
+        assert bool((outs[key].view(torch.uint8) == POISON).all()), key

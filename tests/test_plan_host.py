@@ -117,7 +117,9 @@ int main() {
   CHECK(!plan_permute(140000, 2, 16, 0).coarse && !plan_permute(140000, 2, 16, 0).fused, "large staged");
   CHECK(plan_permute(16384, 8, 32, 256).coarse, "dsv3 one of eight expert ranks: coarse");
   CHECK(split_copy_applies(16384, 8, 7168 * 2, 0), "dsv3 bf16 rows: split copy");
-  CHECK(!split_copy_applies(16384, 8, 7168 * 2, 256), "dsv3 with an expert map: no split copy");
+  CHECK(split_copy_applies(16384, 8, 7168 * 2, 256), "dsv3 with an expert map: split copy");
+  CHECK(!split_copy_applies(8192, 8, 2048 * 2, 128), "qwen3 with an expert map: no split copy");
+  CHECK(!split_copy_applies(16384, 2, 4096 * 2, 8), "topk 2 with an expert map: no split copy");
   CHECK(!split_copy_applies(8192, 8, 2048 * 2, 0), "qwen3: no split copy");
   CHECK(!split_copy_applies(4096, 2, 4096 * 2, 0), "mixtral: no split copy");
   CHECK(!split_copy_applies(1 << 20, 8, 0, 0), "index only: no split copy");
