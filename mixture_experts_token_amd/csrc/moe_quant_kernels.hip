@@ -99,13 +99,16 @@ __device__ __forceinline__ u32x2 vec_codes(const u32x4& v, float scale) {
 // TPT threads per token (64: one wave; 256 or 1024: several waves whose
 // amax meets in LDS), BT = max(TPT, 256) threads per block, BT / TPT tokens
 // per block.  Thread gt of a token holds vectors gt, gt + TPT, ...  (U of
-// them, U*TPT >= row_vecs).  group_vecs: vectors per scale group (a power of
-// two <= 64, so a group is an aligned run of lanes of one wave), or 0 for one
-// scale per token.  kAllLocal (no expert map): every token has topk
+// them, U*TPT >= row_vecs); with kPair (bf16, U even) it holds the adjacent
+// pairs 2 (gt + TPT p), 2 (gt + TPT p) + 1 instead, so the 16 codes of a pair
+// go out as one 16-byte store (8-byte stores of single vectors measured
+// 4-10 % slower on the Mixtral and Qwen3 shapes).  group_vecs: vectors per
+// scale group (a power of two <= 64, so a group is an aligned run of lanes of
+// one wave; at least 2 with kPair), or 0 for one scale per token.  kAllLocal (no expert map): every token has topk
 // destinations, so its row is loaded before anything else is read and the
 // check for a rejected id (off[0] < 0: write nothing) follows the loads; with
 // a map the destinations are read first and tokens without one are skipped.
-template <bool kBF16, int U, int TPT, bool kNTStore, bool kAllLocal>
+template <bool kBF16, int U, int TPT, bool kNTStore, bool kAllLocal, bool kPair>
 __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ inv, const int64_t* __restrict__ off,
     uint8_t* __restrict__ codes, float* __restrict__ scales, int64_t num_tokens, int64_t rv, int topk,
@@ -114,6 +117,7 @@ __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
     constexpr int TB = BT / TPT;           // tokens per block
     constexpr int WPT = TPT / 64;          // waves per token
     constexpr int kEpv = kBF16 ? 8 : 4;    // elements (and code bytes) per 16-byte input vector
+    static_assert(!kPair || (kBF16 && U % 2 == 0), "pairs: bf16 rows, an even number of vectors per thread");
     __shared__ float red_s[WPT > 1 ? WPT : 1];
     if constexpr (!kAllLocal) {
         if (off[0] < 0) return;            // the index permute rejected an id: write nothing
@@ -138,10 +142,17 @@ __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
         }
         u32x4 v[U];
         const u32x4* src = x + tt * rv;
+        auto vidx = [&](int u) -> int64_t {  // the vector in this thread's slot u
+            if constexpr (kPair) return 2 * (gt + (int64_t)TPT * (u / 2)) + u % 2;
+            else return gt + (int64_t)TPT * u;
+        };
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t idx = gt + (int64_t)TPT * u;
-            v[u] = idx < rv ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+            const int64_t idx = vidx(u);
+            // a pair's second load reads the lines its first one brought in, so
+            // those go through the cache
+            if constexpr (kPair) v[u] = idx < rv ? src[idx] : u32x4{0u, 0u, 0u, 0u};
+            else v[u] = idx < rv ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
         }
         if constexpr (kAllLocal) {
             // the index permute rejected an id: write nothing.  The empty asm
@@ -172,11 +183,22 @@ __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u) sc[u] = scale;
         } else {
+            if constexpr (kPair) {  // a group is group_vecs / 2 lanes of pairs
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float m = vec_amax<kBF16>(v[u]);
-                for (int s = 1; s < group_vecs; s <<= 1) m = max_xor(m, s);
-                sc[u] = m > 0.0f ? __fdiv_rn(m, kE4M3Max) : 1.0f;
+                for (int u = 0; u < U; u += 2) {
+                    float m = vec_amax<kBF16>(v[u]);
+                    const float m1 = vec_amax<kBF16>(v[u + 1]);
+                    m = m1 > m ? m1 : m;
+                    for (int s = 1; s < group_vecs / 2; s <<= 1) m = max_xor(m, s);
+                    sc[u] = sc[u + 1] = m > 0.0f ? __fdiv_rn(m, kE4M3Max) : 1.0f;
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float m = vec_amax<kBF16>(v[u]);
+                    for (int s = 1; s < group_vecs; s <<= 1) m = max_xor(m, s);
+                    sc[u] = m > 0.0f ? __fdiv_rn(m, kE4M3Max) : 1.0f;
+                }
             }
         }
         u32x2 c[U];
@@ -186,9 +208,21 @@ __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
             const int32_t d = inv[tt * topk + k];
             if (!(d >= 0 && (int64_t)d < rows)) continue;
             uint8_t* orow = codes + (int64_t)d * row_bytes;
+            if constexpr (kPair) {
+#pragma unroll
+                for (int u = 0; u < U; u += 2) {
+                    const int64_t idx = vidx(u);  // even; rv is even, so idx + 1 < rv too
+                    if (idx >= rv) continue;
+                    u32x4* o = reinterpret_cast<u32x4*>(orow) + idx / 2;
+                    const u32x4 cc = {c[u].x, c[u].y, c[u + 1].x, c[u + 1].y};
+                    if constexpr (kNTStore) __builtin_nontemporal_store(cc, o);
+                    else *o = cc;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t idx = gt + (int64_t)TPT * u;
+                if constexpr (kPair) break;
+                const int64_t idx = vidx(u);
                 if (idx >= rv) continue;
                 if constexpr (kBF16) {
                     u32x2* o = reinterpret_cast<u32x2*>(orow) + idx;
@@ -206,7 +240,7 @@ __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
             } else {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int64_t idx = gt + (int64_t)TPT * u;
+                    const int64_t idx = vidx(u);
                     if (idx < rv && idx % group_vecs == 0) srow[idx / group_vecs] = sc[u];
                 }
             }
@@ -214,8 +248,8 @@ __global__ __launch_bounds__(TPT > 256 ? TPT : 256) void quant_scatter_kernel(
     }
 }
 
-template <bool kBF16, int U, int TPT>
-hipError_t launch_quant_ut(const QuantArgs& a, hipStream_t stream) {
+template <bool kBF16, int U, int TPT, bool kPair>
+hipError_t launch_quant_up(const QuantArgs& a, hipStream_t stream) {
     constexpr int BT = TPT > 256 ? TPT : 256;
     constexpr int64_t TB = BT / TPT;
     const int64_t blocks_needed = (a.num_tokens + TB - 1) / TB;
@@ -223,7 +257,8 @@ hipError_t launch_quant_ut(const QuantArgs& a, hipStream_t stream) {
     // Plain stores for wide fan-out into large outputs, as in the permute row copy.
     const bool plain = a.topk >= 4 && a.num_tokens * a.topk * a.row_vecs * (kBF16 ? 8 : 4) >= (int64_t(32) << 20);
     auto go = [&](auto nt_store, auto all_local) {
-        hipLaunchKernelGGL((quant_scatter_kernel<kBF16, U, TPT, decltype(nt_store)::value, decltype(all_local)::value>),
+        hipLaunchKernelGGL((quant_scatter_kernel<kBF16, U, TPT, decltype(nt_store)::value, decltype(all_local)::value,
+                                                 kPair>),
                            dim3((unsigned)blocks), dim3(BT), 0, stream,
                            reinterpret_cast<const u32x4*>(a.hidden_states), a.inv_permuted_idx,
                            a.expert_first_token_offset, a.permuted_codes, a.permuted_scale, a.num_tokens, a.row_vecs,
@@ -237,6 +272,16 @@ hipError_t launch_quant_ut(const QuantArgs& a, hipStream_t stream) {
         else go(std::true_type{}, std::false_type{});
     }
     return hipGetLastError();
+}
+
+// Adjacent pairs whenever they apply: bf16 rows of an even vector count, an
+// even number of vectors per thread and no single-vector scale groups.
+template <bool kBF16, int U, int TPT>
+hipError_t launch_quant_ut(const QuantArgs& a, hipStream_t stream) {
+    if constexpr (kBF16 && U % 2 == 0) {
+        if (a.row_vecs % 2 == 0 && a.group_vecs != 1) return launch_quant_up<kBF16, U, TPT, true>(a, stream);
+    }
+    return launch_quant_up<kBF16, U, TPT, false>(a, stream);
 }
 
 // Threads per token: one wave for short rows while tokens alone fill the

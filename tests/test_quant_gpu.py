@@ -6,6 +6,8 @@ and permutes the codes with their scales.  Bar: offsets, indices, codes and
 scales bit-exact; with an expert map, nothing past the local rows written.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -70,10 +72,12 @@ def assert_quant_equal(outs, ref):
     assert np.all(codes[m:] == POISON) and np.all(sc[m:] == 0xFFFFFFFF) and np.all(perm[m:].view(np.uint32) == 0xFFFFFFFF)
 
 
-def _inputs(name, dev, n=None, dtype=torch.bfloat16):
+def _inputs(name, dev, n=None, dtype=torch.bfloat16, hidden=None):
     w = W.WORKLOADS[name]
     if n is not None:
         w = w.with_tokens(n)
+    if hidden is not None:
+        w = dataclasses.replace(w, hidden_size=hidden)
     ids_np, _ = W.make_routing(w, seed=0)
     g = torch.Generator(device="cpu").manual_seed(w.num_tokens * 7 + w.hidden_size)
     # a spread of row magnitudes so scales differ by orders of magnitude
@@ -108,6 +112,33 @@ def test_quant_parity(hip_device, name, n, group, dtype, ep):
     outs = gpu_quant(x, ids, w.num_experts, group, emap, nl or 0)
     torch.cuda.synchronize()
     assert_quant_equal(outs, oracle_quant(x, ids, w.num_experts, group, emap, nl))
+
+
+# The quantise-scatter holds adjacent vector pairs per thread (one 16-byte
+# code store per pair) for bf16 rows of an even vector count, an even number
+# of vectors per thread and scale groups of at least two vectors; single
+# vectors otherwise.  (tokens, hidden, group): one wave per token, pairs, 8
+# rows of vectors per group of 16 elements; single vectors for 8-element
+# groups; an odd vector count; an even count that leaves pair slots idle; one
+# wave with two and three vectors per thread.
+PAIR_CASES = [
+    (2000, 2048, 16),
+    (500, 4096, 8),
+    (300, 2056, 0),
+    (300, 2064, 0),
+    (300, 2064, 16),
+    (2000, 1024, 0),
+    (2000, 1040, 0),
+]
+
+
+@pytest.mark.parametrize("n,hidden,group", PAIR_CASES, ids=["-".join(map(str, c)) for c in PAIR_CASES])
+def test_quant_pair_layout_edges(hip_device, n, hidden, group):
+    w, ids, x = _inputs("mixtral", hip_device, n, torch.bfloat16, hidden)
+    _say("quant pairs N=%d H=%d group=%d" % (w.num_tokens, w.hidden_size, group))
+    outs = gpu_quant(x, ids, w.num_experts, group)
+    torch.cuda.synchronize()
+    assert_quant_equal(outs, oracle_quant(x, ids, w.num_experts, group))
 
 
 @pytest.mark.parametrize("group", [0, 128])
