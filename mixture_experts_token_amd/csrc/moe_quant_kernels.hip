@@ -101,8 +101,7 @@ __device__ __forceinline__ u32x2 vec_codes(const u32x4& v, float scale) {
 // per block.  Thread gt of a token holds vectors gt, gt + TPT, ...  (U of
 // them, U*TPT >= row_vecs); with kPair (bf16, U even) it holds the adjacent
 // pairs 2 (gt + TPT p), 2 (gt + TPT p) + 1 instead, so the 16 codes of a pair
-// go out as one 16-byte store (8-byte stores of single vectors measured
-// 4-10 % slower on the Mixtral and Qwen3 shapes).  group_vecs: vectors per
+// go out as one 16-byte store.  group_vecs: vectors per
 // scale group (a power of two <= 64, so a group is an aligned run of lanes of
 // one wave; at least 2 with kPair), or 0 for one scale per token.  kAllLocal (no expert map): every token has topk
 // destinations, so its row is loaded before anything else is read and the
@@ -274,11 +273,14 @@ hipError_t launch_quant_up(const QuantArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Adjacent pairs whenever they apply: bf16 rows of an even vector count, an
-// even number of vectors per thread and no single-vector scale groups.
+// Adjacent pairs for several waves per token (bf16 rows of an even vector
+// count, an even number of vectors per thread, no single-vector scale
+// groups): Mixtral-shaped rows, cold in HBM, 21.5 -> 20.6 us per token scale
+// and 22.8 -> 20.6 us for groups of 128.  One wave per token keeps single
+// vectors: with pairs the Qwen3 shape measured 42.6 -> 44.7 us.
 template <bool kBF16, int U, int TPT>
 hipError_t launch_quant_ut(const QuantArgs& a, hipStream_t stream) {
-    if constexpr (kBF16 && U % 2 == 0) {
+    if constexpr (kBF16 && U % 2 == 0 && TPT > 64) {
         if (a.row_vecs % 2 == 0 && a.group_vecs != 1) return launch_quant_up<kBF16, U, TPT, true>(a, stream);
     }
     return launch_quant_up<kBF16, U, TPT, false>(a, stream);

@@ -114,21 +114,22 @@ def test_quant_parity(hip_device, name, n, group, dtype, ep):
     assert_quant_equal(outs, oracle_quant(x, ids, w.num_experts, group, emap, nl))
 
 
-# The quantise-scatter holds adjacent vector pairs per thread (one 16-byte
-# code store per pair) for bf16 rows of an even vector count, an even number
-# of vectors per thread and scale groups of at least two vectors; single
-# vectors otherwise.  (tokens, hidden, group): one wave per token, pairs, 8
-# rows of vectors per group of 16 elements; single vectors for 8-element
-# groups; an odd vector count; an even count that leaves pair slots idle; one
-# wave with two and three vectors per thread.
+# With several waves per token the quantise-scatter holds adjacent vector
+# pairs per thread (one 16-byte code store per pair) for bf16 rows of an even
+# vector count, an even number of vectors per thread and scale groups of at
+# least two vectors; single vectors otherwise.  (tokens, hidden, group): pairs
+# with one pair per 16-element group; single vectors for 8-element groups; an
+# odd vector count; an even count that leaves pair slots idle, per token and
+# per 16 elements; four vectors per thread with a ragged tail; one wave per
+# token (single vectors).
 PAIR_CASES = [
-    (2000, 2048, 16),
+    (500, 4096, 16),
     (500, 4096, 8),
     (300, 2056, 0),
     (300, 2064, 0),
     (300, 2064, 16),
+    (100, 6160, 0),
     (2000, 1024, 0),
-    (2000, 1040, 0),
 ]
 
 
