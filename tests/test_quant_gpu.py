@@ -114,22 +114,22 @@ def test_quant_parity(hip_device, name, n, group, dtype, ep):
     assert_quant_equal(outs, oracle_quant(x, ids, w.num_experts, group, emap, nl))
 
 
-# With several waves per token the quantise-scatter holds adjacent vector
-# pairs per thread (one 16-byte code store per pair) for bf16 rows of an even
+# The quantise-scatter holds adjacent vector pairs per thread with several
+# waves per token (one 16-byte code store per pair) for bf16 rows of an even
 # vector count, an even number of vectors per thread and scale groups of at
-# least two vectors; single vectors otherwise.  (tokens, hidden, group): pairs
-# with one pair per 16-element group; single vectors for 8-element groups; an
-# odd vector count; an even count that leaves pair slots idle, per token and
-# per 16 elements; four vectors per thread with a ragged tail; one wave per
-# token (single vectors).
+# least two vectors; single vectors otherwise.  (tokens, hidden, group), topk
+# 2: pairs with one pair per 16-element group; single vectors for 8-element
+# groups; an odd vector count; an even count that leaves pair slots idle, per
+# token and per 16 elements; four vectors per thread with a ragged tail; one
+# wave per token.
 PAIR_CASES = [
-    (500, 4096, 16),
-    (500, 4096, 8),
-    (300, 2056, 0),
-    (300, 2064, 0),
-    (300, 2064, 16),
+    (9000, 4096, 16),
+    (9000, 4096, 8),
+    (9000, 2056, 0),
+    (9000, 2064, 0),
+    (9000, 2064, 16),
     (100, 6160, 0),
-    (2000, 1024, 0),
+    (9000, 1024, 0),
 ]
 
 
@@ -140,6 +140,63 @@ def test_quant_pair_layout_edges(hip_device, n, hidden, group):
     outs = gpu_quant(x, ids, w.num_experts, group)
     torch.cuda.synchronize()
     assert_quant_equal(outs, oracle_quant(x, ids, w.num_experts, group))
+
+
+# Row counts of the fused index plan (above the one-kernel decode plan, at
+# most 16384 rows): the index permute, then the quantise-scatter.  (tokens,
+# topk, experts, hidden, dtype, group, expert split (ep, rank, layout) or
+# None, ids dtype): the largest fused row count; f32 rows of 128 and 512
+# vectors; a ragged row of 257 vectors; groups of 16 elements (two vectors);
+# an expert split (tokens with no local row are not read); int64 ids.
+FUSED_CASES = [
+    (8192, 2, 8, 1024, torch.bfloat16, 0, None, torch.int32),
+    (1000, 2, 8, 512, torch.float32, 0, None, torch.int32),
+    (1000, 2, 8, 2048, torch.float32, 64, None, torch.int32),
+    (700, 4, 16, 2056, torch.bfloat16, 0, None, torch.int32),
+    (700, 4, 16, 2064, torch.bfloat16, 16, None, torch.int32),
+    (4096, 2, 8, 4096, torch.bfloat16, 0, (2, 0, "contiguous"), torch.int32),
+    (3000, 4, 64, 2048, torch.bfloat16, 128, (4, 1, "round_robin"), torch.int64),
+]
+
+
+@pytest.mark.parametrize("n,k,e,h,dtype,group,ep,idt", FUSED_CASES,
+                         ids=["-".join(map(str, c[:6])) + ("-ep" if c[6] else "") for c in FUSED_CASES])
+def test_quant_fused_plan(hip_device, n, k, e, h, dtype, group, ep, idt):
+    w = dataclasses.replace(W.WORKLOADS["mixtral"], num_tokens=n, topk=k, num_experts=e, hidden_size=h)
+    ids_np, _ = W.make_routing(w, seed=1)
+    ids = torch.from_numpy(ids_np).to(idt).to(hip_device)
+    g = torch.Generator(device="cpu").manual_seed(n + h)
+    mag = torch.exp(torch.randn((n, 1), generator=g) * 3)
+    x = (torch.randn((n, h), generator=g) * mag).to(dtype).to(hip_device)
+    emap, nl = (None, None) if ep is None else W.expert_map_for(e, *ep)
+    _say("quant fused plan N=%d K=%d E=%d H=%d %s group=%d ep=%s" % (n, k, e, h, dtype, group, ep))
+    outs = gpu_quant(x, ids, e, group, emap, nl or 0)
+    torch.cuda.synchronize()
+    assert_quant_equal(outs, oracle_quant(x, ids, e, group, emap, nl))
+
+
+def test_quant_fused_plan_non_finite_and_boundaries(hip_device):
+    """Non-finite, zero and E4M3 rounding-boundary rows at a fused-plan row
+    count (400 rows: above the one-kernel decode plan)."""
+    row = _e4m3_boundary_row()
+    h = row.size
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((200, h)).astype(np.float32) * 10
+    x[0] = row
+    x[1] = -row
+    x[2] = 0.0
+    x[3] = -0.0
+    x[4, 3] = np.nan
+    x[5, 7] = np.inf
+    x[6, ::2] = np.nan
+    x[7, 9] = -np.inf
+    xt = torch.from_numpy(x).to(hip_device)
+    ids = torch.from_numpy(np.stack([np.arange(200) % 5, (np.arange(200) + 2) % 5], 1).astype(np.int32)).to(hip_device)
+    _say("quant fused plan non-finite H=%d" % h)
+    for group in (0, 4):
+        outs = gpu_quant(xt, ids, 5, group)
+        torch.cuda.synchronize()
+        assert_quant_equal(outs, oracle_quant(xt, ids, 5, group))
 
 
 @pytest.mark.parametrize("group", [0, 128])
