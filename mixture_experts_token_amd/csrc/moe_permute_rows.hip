@@ -98,11 +98,15 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const u32x4* __restri
 
 // Four vectors per lane (a 4 KiB chunk): measured at the DSv3 shape against
 // one, two, three, six and eight (413-425 us for the others, 405 us here).
+// With an expert map two (2 KiB chunks): one rank of an 8-way DSv3 split,
+// ranks 0, 3 and 7: 116.0 -> 113.9, 46.4 -> 45.1 and 51.7 -> 49.5 us against
+// four (one: 107.3, 59.4 and 61.8 us; eight: 117.5, 47.7 and 53.2 us).
 constexpr int kRowsCopyUnroll = 4;
+constexpr int kRowsCopyUnrollMap = 2;
 
 template <bool kNT, int KC, bool kMap>
 static void launch_rows_k(const PermuteArgs& a, hipStream_t stream) {
-    constexpr int U = kRowsCopyUnroll;
+    constexpr int U = kMap ? kRowsCopyUnrollMap : kRowsCopyUnroll;
     const int64_t nchunks = (a.row_vecs + U * kWaveSize - 1) / (U * kWaveSize);
     const int64_t items = a.num_tokens * nchunks;
     const int64_t needed = (items + 3) / 4;
