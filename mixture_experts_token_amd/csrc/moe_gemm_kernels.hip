@@ -498,23 +498,34 @@ hipError_t launch_gemm_tiles(const GemmArgs& a, int num_cus, hipStream_t stream)
 
 }  // namespace
 
-// The tiled kernel runs at most min(max_rows, num_experts + max_rows / 128)
-// row tiles times n / 256 column tiles, one workgroup per CU.  When that
-// cannot fill the CUs and the experts average at most 16 rows (decode: a row
-// or a few per expert), the skinny kernel streams the weights with one wave
-// per 32 columns instead: decode N=1 (8 rows, 128 tiles) 126 -> 91 us.  With
-// enough tiles the tiled kernel streams faster (decode N=16: 1009 us tiled,
-// 1139 us skinny; N=256: 2419 vs 3014), and with more rows per expert the
-// skinny kernel would stream each expert's weights once per 16 rows.
+// Kernel choice from what the host knows (rows M = max_rows, experts E, n, k).
+// The tiled kernel runs at most min(M, E + M / 128) row tiles times n / 256
+// column tiles, one workgroup per CU.  At decode sizes the work is streaming
+// the experts' weights, and two streaming kernels do it faster:
+//  * M <= E (one row per expert on average) and k a multiple of 512 up to
+//    8192: the row-streaming kernel (each weight row read whole; two x rows
+//    per item).  Against the tiled kernel (DSv3 shape, n 4096, k 7168):
+//    N=1 83 -> 70 us (the LDS-staged kernel), N=4 300 -> 261, N=16
+//    1008 -> 861, N=32 (M = E) 1598 -> 1483; Mixtral N=4 236 -> 184, Qwen3
+//    N=16 106 -> 97.  At M = 2E it ties (Mixtral N=8 378 / 380, Qwen3 N=32
+//    155 / 156) and beyond loses (DSv3 N=64 2210 / 2590): experts with more
+//    rows stream their weights once per two rows.
+//  * otherwise M <= 4E, or M <= 16E with fewer tiles than CUs: the LDS-staged
+//    kernel (16 x rows per item).  Against the tiled kernel: DSv3 N=16
+//    1008 / 965 us, N=64 2210 / 2156, N=128 (4E) 2393 / 2400; Mixtral N=8
+//    378 / 334, N=16 344 / 336; Qwen3 N=64 183 / 161.
 constexpr int64_t kSkinnyMaxRowsPerExpert = 16;
+constexpr int64_t kSkinnyAnyRowsPerExpert = 4;
 
 static bool gemm_takes_skinny(int64_t max_rows, int num_experts, int64_t n, int num_cus) {
     const int64_t bound = num_experts + max_rows / 128;
     const int64_t row_tiles = max_rows < bound ? max_rows : bound;
-    return max_rows <= kSkinnyMaxRowsPerExpert * num_experts && row_tiles * ((n + 255) / 256) < num_cus;
+    return max_rows <= kSkinnyAnyRowsPerExpert * num_experts ||
+           (max_rows <= kSkinnyMaxRowsPerExpert * num_experts && row_tiles * ((n + 255) / 256) < num_cus);
 }
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, int num_cus, hipStream_t stream) {
+    if (a.max_rows <= a.num_experts && gemm_rowstream_fits(a.k)) return launch_grouped_gemm_rowstream(a, num_cus, stream);
     if (gemm_takes_skinny(a.max_rows, a.num_experts, a.n, num_cus)) return launch_grouped_gemm_skinny(a, num_cus, stream);
     if (a.n % 256 == 0) return launch_gemm_tiles<GemmShape<128, 256, 2, 4, 3, 1, true>>(a, num_cus, stream);
     return launch_gemm_tiles<GemmShape<128, 128, 2, 2, 2, 2, false>>(a, num_cus, stream);

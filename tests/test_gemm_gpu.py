@@ -167,23 +167,45 @@ def test_grouped_gemm_full_size_sampled_rows(hip_device, name, n):
 
 
 # ----------------------------------------------------------------------------
-# Skinny kernel: taken when the experts average at most 16 rows and the tiled
-# kernel's most tiles, min(max_rows, E + max_rows // 128) x ceil(n / 256), are
-# fewer than the CUs; one wave per 32 output columns of an expert and 16 of
-# its rows, weights streamed from global memory into the MFMA operands.
+# Decode-size kernels, chosen from the host's sizes (M rows, E experts):
+#  * row-streaming: M <= E and k a multiple of 512 up to 8192; one wave per
+#    32 weight rows of an expert and up to two of its rows, each weight row
+#    read whole into bf16 dot products, a cross-lane sum per row;
+#  * LDS-staged: M <= 4E, or M <= 16E with fewer tiled-kernel tiles,
+#    min(M, E + M // 128) x ceil(n / 256), than CUs; one wave per 32 output
+#    columns of an expert and 16 of its rows, weights staged through LDS in
+#    512-byte runs of the 32 rows;
+#  * otherwise the tiled kernel.
 # ----------------------------------------------------------------------------
-def _takes_skinny(max_rows, e, n):
+def _kernel_for(max_rows, e, n, k):
+    if max_rows <= e and k % 512 == 0 and k <= 8192:
+        return "rowstream"
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return max_rows <= 16 * e and min(max_rows, e + max_rows // 128) * ((n + 255) // 256) < cus
+    tiles = min(max_rows, e + max_rows // 128) * ((n + 255) // 256)
+    if max_rows <= 4 * e or (max_rows <= 16 * e and tiles < cus):
+        return "skinny"
+    return "tiled"
 
 
 SKINNY_CASES = [
     # (experts, per-expert row counts or a mode with a total, n, k, spare rows)
-    (8, [0, 1, 33, 40, 0, 20, 2, 0], 256, 832, 16),   # 13 k chunks: whole rounds, then a tail; 2 row groups
-    (8, [8] * 8, 128, 512, 0),                         # exactly two rounds of 4 chunks
-    (16, ("skewed", 200), 384, 256, 16),               # 4 chunks: the tail path only
-    (4, [0, 0, 0, 1], 128, 64, 3),                     # one row, one chunk
-    (200, ("even", 1600), 128, 320, 0),                # 200 experts, 5 chunks
+    (8, [0, 1, 33, 40, 0, 20, 2, 0], 256, 832, 16),   # 13 k chunks: 3 whole stages and one chunk; 2 row groups
+    (8, [8] * 8, 128, 512, 0),                         # exactly two stages
+    (16, ("skewed", 200), 384, 256, 16),               # one stage
+    (4, [0, 0, 0, 1], 128, 64, 3),                     # one row, one chunk (a partial stage)
+    (200, ("even", 1600), 128, 320, 0),                # 200 experts, 5 chunks: a whole stage and one chunk
+    (8, [3] * 8, 128, 640, 0),                         # 10 chunks: an odd stage count, the last stage partial
+    (4, [1, 0, 2, 1], 128, 8704, 0),                   # k past the row-streaming kernel's 8192: 34 stages
+    (8, [4] * 8, 8192, 512, 0),                        # M = 4E with as many tiles as CUs
+]
+
+ROWSTREAM_CASES = [
+    # (experts, per-expert row counts or a mode with a total, n, k, spare rows)
+    (8, [0, 2, 1, 0, 0, 3, 0, 1], 128, 512, 1),        # a 3-row expert: a 2-row and a 1-row item; 16 rows in flight
+    (16, [1] * 10 + [0] * 6, 256, 1024, 6),            # one row each; 2 loads per row
+    (64, ("even", 60), 384, 4608, 4),                  # 9 loads per row: one row in flight
+    (4, [1, 0, 2, 1], 128, 8192, 0),                   # the largest k: 16 loads per row
+    (3, [0, 0, 3], 4096, 2560, 0),                     # one expert with all rows, 128 column blocks
 ]
 
 
@@ -193,24 +215,47 @@ def _skinny_offsets(rng, e, spec):
     return np.concatenate([[0], np.cumsum(spec)]).astype(np.int64)
 
 
-@pytest.mark.parametrize("e,spec,n,k,spare", SKINNY_CASES, ids=["skinny-%d-%d-%d" % (c[0], c[2], c[3]) for c in SKINNY_CASES])
-def test_grouped_gemm_skinny_parity(hip_device, e, spec, n, k, spare):
+def _decode_kernel_parity(hip_device, e, spec, n, k, spare, kernel):
     rng = np.random.default_rng(n + k + e)
     off = _skinny_offsets(rng, e, spec)
     rows = int(off[-1])
-    assert _takes_skinny(rows + spare, e, n)
+    assert _kernel_for(rows + spare, e, n, k) == kernel
     g = torch.Generator().manual_seed(rows * 7 + k)
     x = _bf16(torch.randn((rows, k), generator=g))
     w = _bf16(torch.randn((e, n, k), generator=g) * k**-0.5)
     xs = torch.cat([x, _bf16(torch.randn((spare, k), generator=g))]).to(hip_device)
     y = poisoned((rows + spare, n), torch.bfloat16, hip_device)
-    _say("skinny grouped gemm E=%d rows=%d n=%d k=%d" % (e, rows, n, k))
+    _say("%s grouped gemm E=%d rows=%d n=%d k=%d" % (kernel, e, rows, n, k))
     binding.moe_grouped_gemm_bf16(xs, w.to(hip_device), torch.from_numpy(off).to(hip_device), y)
     torch.cuda.synchronize()
     got = to_np(y)
     ref = oracle.grouped_gemm_bf16(to_np(x), to_np(w), off)
     assert_gemm_close(got[:rows], ref, to_np(x), to_np(w), off)
     assert np.all(got[rows:].view(np.uint8) == POISON)
+
+
+@pytest.mark.parametrize("e,spec,n,k,spare", SKINNY_CASES, ids=["skinny-%d-%d-%d" % (c[0], c[2], c[3]) for c in SKINNY_CASES])
+def test_grouped_gemm_skinny_parity(hip_device, e, spec, n, k, spare):
+    _decode_kernel_parity(hip_device, e, spec, n, k, spare, "skinny")
+
+
+@pytest.mark.parametrize("e,spec,n,k,spare", ROWSTREAM_CASES,
+                         ids=["rowstream-%d-%d-%d" % (c[0], c[2], c[3]) for c in ROWSTREAM_CASES])
+def test_grouped_gemm_rowstream_parity(hip_device, e, spec, n, k, spare):
+    _decode_kernel_parity(hip_device, e, spec, n, k, spare, "rowstream")
+
+
+@pytest.mark.parametrize("kernel,n,k", [("skinny", 128, 128), ("rowstream", 128, 512)])
+def test_grouped_gemm_decode_kernels_rejected_offsets_write_nothing(hip_device, kernel, n, k):
+    x = _bf16(torch.randn((8, k))).to(hip_device)
+    w = _bf16(torch.randn((8, n, k))).to(hip_device)
+    assert _kernel_for(8, 8, n, k) == kernel
+    for bad in ([-1] * 9, [0, 1, 0, 2, 3, 4, 5, 6, 7], [0, 1, 2, 3, 4, 5, 6, 7, 9], [1] * 9):
+        y = poisoned((8, n), torch.bfloat16, hip_device)
+        _say("%s grouped gemm bad offsets %s" % (kernel, bad))
+        binding.moe_grouped_gemm_bf16(x, w, torch.tensor(bad, dtype=torch.int64, device=hip_device), y)
+        torch.cuda.synchronize()
+        assert np.all(to_np(y).view(np.uint8) == POISON)
 
 
 def test_grouped_gemm_skinny_rejected_offsets_write_nothing(hip_device):
@@ -226,10 +271,10 @@ def test_grouped_gemm_skinny_rejected_offsets_write_nothing(hip_device):
 
 @pytest.mark.parametrize("tokens", [1, 4, 256])
 def test_grouped_gemm_decode_shape_sampled(hip_device, tokens):
-    """The decode shape (topk 8, 256 experts, n=4096, k=7168) at N=1 (skinny
-    kernel), 4 and 256 tokens (tiled): every expert's rows on the device; the
-    oracle checks a sample of experts (the ones with the most and the fewest
-    rows, and up to four others)."""
+    """The decode shape (topk 8, 256 experts, n=4096, k=7168) at N=1 and 4
+    (row-streaming kernel) and 256 tokens (tiled): every expert's rows on the
+    device; the oracle checks a sample of experts (the ones with the most and
+    the fewest rows, and up to four others)."""
     w8 = W.WORKLOADS["decode"].with_tokens(tokens)
     ids_np, _ = W.make_routing(w8, 0)
     e, n, k = w8.num_experts, 4096, w8.hidden_size
@@ -240,8 +285,9 @@ def test_grouped_gemm_decode_shape_sampled(hip_device, tokens):
     x = _bf16(torch.randn((rows, k), device=hip_device, generator=g))
     w = _bf16(torch.randn((e, n, k), device=hip_device, generator=g) * k**-0.5)
     y = poisoned((rows, n), torch.bfloat16, hip_device)
-    _say("grouped gemm decode shape N=%d rows=%d skinny=%s" % (tokens, rows, _takes_skinny(rows, e, n)))
-    assert _takes_skinny(rows, e, n) == (tokens == 1)
+    kernel = _kernel_for(rows, e, n, k)
+    _say("grouped gemm decode shape N=%d rows=%d kernel=%s" % (tokens, rows, kernel))
+    assert kernel == ("tiled" if tokens == 256 else "rowstream")
     binding.moe_grouped_gemm_bf16(x, w, torch.from_numpy(off).to(hip_device), y)
     torch.cuda.synchronize()
     used = np.nonzero(counts)[0]
