@@ -514,6 +514,10 @@ hipError_t launch_gemm_tiles(const GemmArgs& a, int num_cus, hipStream_t stream)
 //    kernel (16 x rows per item).  Against the tiled kernel: DSv3 N=16
 //    1008 / 965 us, N=64 2210 / 2156, N=128 (4E) 2393 / 2400; Mixtral N=8
 //    378 / 334, N=16 344 / 336; Qwen3 N=64 183 / 161.
+// The row-streaming kernel and its k range (moe_gemm_skinny.hip).
+hipError_t launch_grouped_gemm_rowstream(const GemmArgs& a, int num_cus, hipStream_t stream);
+bool gemm_rowstream_fits(int64_t k);
+
 constexpr int64_t kSkinnyMaxRowsPerExpert = 16;
 constexpr int64_t kSkinnyAnyRowsPerExpert = 4;
 

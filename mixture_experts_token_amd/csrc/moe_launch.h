@@ -64,13 +64,8 @@ struct GemmArgs {
 
 hipError_t launch_fill_offsets(int64_t* off, int num_experts, int64_t value, hipStream_t stream);
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, int num_cus, hipStream_t stream);
-// The grouped GEMM for experts with few rows each (called by launch_grouped_gemm_bf16):
-// weights streamed through LDS stages into the matrix cores, or, for at most
-// one row per expert on average and k a multiple of 512 up to 8192
-// (gemm_rowstream_fits), each weight row streamed whole into bf16 dot products.
+// The grouped GEMM for experts with few rows each (called by launch_grouped_gemm_bf16).
 hipError_t launch_grouped_gemm_skinny(const GemmArgs& a, int num_cus, hipStream_t stream);
-hipError_t launch_grouped_gemm_rowstream(const GemmArgs& a, int num_cus, hipStream_t stream);
-bool gemm_rowstream_fits(int64_t k);
 hipError_t launch_quant_scatter(const QuantArgs& a, bool bf16, hipStream_t stream);
 // Decode sizes (the wave plan, no expert map): index permute and quantise-scatter in one kernel.
 hipError_t launch_quant_permute_wave(const PermuteArgs& a, const QuantArgs& q, const PermutePlan& p, bool bf16,
