@@ -62,6 +62,22 @@ __device__ __forceinline__ int wave_index() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWaveSize));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active), by
+// DPP moves: shifts by 1, 2, 4 and 8 lanes within each 16-lane row, then lane
+// 15 of rows 0 and 2 added into rows 1 and 3, and lane 31 into rows 2 and 3.
+// Lanes whose source lies outside the row (or whose row the mask leaves out)
+// add 0.  Six dependent VALU steps; the same sum through lane shuffles took six
+// LDS-crossbar round trips.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
 // Workgroup barrier that orders LDS only.  Global loads issued before it stay
 // in flight (no wait on the vector-memory counter); nothing in these kernels
 // communicates through global memory inside one launch.
@@ -81,7 +97,7 @@ __device__ __forceinline__ void lds_barrier() {
 //     the rows of its expert in earlier batches (a running count in LDS,
 //     advanced by the lowest lane of each equal-key group);
 //   * the running counts end as the rows per expert; their exclusive scan
-//     (wave shuffles) gives the offsets, and destination = offset + rank.
+//     (DPP lane moves) gives the offsets, and destination = offset + rank.
 // run: LDS [E]; dest_s: LDS [R], filled with each row's destination.  When
 // `writer`, the offsets, permuted_idx, inv_permuted_idx (and, with kScale,
 // the per-token scales sc moved to their rows) are written.  Returns false
@@ -134,12 +150,7 @@ __device__ __forceinline__ bool wave_index_pass(int E, int R, int nbits, const i
     const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
     int s = 0;
     for (int e = e0; e < e1; ++e) s += run[e];
-    int x = s;
-#pragma unroll
-    for (int d = 1; d < kWaveSize; d <<= 1) {
-        const int y = __shfl_up(x, d, kWaveSize);
-        if (lane >= d) x += y;
-    }
+    const int x = wave_inclusive_scan(s);
     int acc = x - s;
     for (int e = e0; e < e1; ++e) {
         const int c = run[e];
@@ -237,12 +248,7 @@ __device__ int block_exclusive_scan(int* data, int n, int* tmp) {
     const int beg = min(tid * per, n), end = min(beg + per, n);
     int s = 0;
     for (int i = beg; i < end; ++i) s += data[i];
-    int x = s;
-#pragma unroll
-    for (int d = 1; d < kWaveSize; d <<= 1) {
-        const int y = __shfl_up(x, d, kWaveSize);
-        if (lane >= d) x += y;
-    }
+    const int x = wave_inclusive_scan(s);
     if (lane == kWaveSize - 1) tmp[w] = x;
     lds_barrier();
     int before = 0, total = 0;
@@ -548,12 +554,7 @@ __device__ __forceinline__ void expert_bases(int B, int* wave_s, int* base_s, in
         }
         s += tot[q];
     }
-    int x = s;
-#pragma unroll
-    for (int d = 1; d < kWaveSize; d <<= 1) {
-        const int y = __shfl_up(x, d, kWaveSize);
-        if (lane >= d) x += y;
-    }
+    const int x = wave_inclusive_scan(s);
     if (lane == kWaveSize - 1) scan_tmp[w] = x;
     lds_barrier();
     int excl = x - s, total = 0;

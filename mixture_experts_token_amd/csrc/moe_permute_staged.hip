@@ -84,12 +84,7 @@ __global__ __launch_bounds__(NT) void permute_scan_tiles_kernel(int32_t* tile_hi
             v[p] = s;  // exclusive within the thread
             s += c;
         }
-        int x = s;
-#pragma unroll
-        for (int d = 1; d < kWaveSize; d <<= 1) {
-            const int y = __shfl_up(x, d, kWaveSize);
-            if (lane >= d) x += y;
-        }
+        const int x = wave_inclusive_scan(s);
         if (lane == kWaveSize - 1) tmp[w] = x;
         lds_barrier();
         int before = carry, pass_total = 0;
