@@ -314,19 +314,19 @@ hipError_t launch_skinny(const GemmArgs& a, int num_cus, hipStream_t stream) {
 
 // ----------------------------------------------------------------------------
 // Row-streaming kernel for experts with one or two rows (decode at a token or
-// a few): one wave owns COLS consecutive weight rows of one expert (a single
-// contiguous COLS x k block of w) and up to two of its x rows, and reads the
-// block front to back, 1 KiB per load, RA weight rows in flight.  Each lane
+// a few): one wave owns COLS (8) consecutive weight rows of one expert (a
+// single contiguous COLS x k block of w) and up to two of its x rows, and reads
+// the block front to back, 1 KiB per load, RA weight rows in flight.  Each lane
 // multiplies its 16-byte weight vectors with the matching x vectors (held in
 // registers for the whole item) by bf16 dot products into fp32, and a row's 64
-// lane sums are added across the wave when the row ends.  No LDS and no
+// lane sums are added across the wave (DPP) when the row ends.  No LDS and no
 // matrix cores: with one x row the matrix cores would idle on a 16-row tile,
 // and streaming each weight row whole keeps the HBM reads sequential, which
 // the 16-row fragment layout of the other kernels cannot.
 // KV64 = k / 512: loads per weight row (k a multiple of 512, at most 8192).
 // ----------------------------------------------------------------------------
 constexpr int kRsRowsX = 2;     // x rows per item
-constexpr int kRsCols = 32;     // weight rows (output columns) per item
+constexpr int kRsCols = 8;      // weight rows (output columns) per item
 constexpr int kRsThreads = 256;
 constexpr int kRsMaxKv64 = 16;  // k <= 8192
 
@@ -344,10 +344,22 @@ __device__ __forceinline__ float dot8(const u32x4& wv, const u32x4& xv, float ac
     return acc;
 }
 
+// Sum over the 64 lanes of a wave (every lane active): the DPP inclusive scan
+// of the permute's index passes on float bits (row shifts 1, 2, 4, 8, then the
+// broadcasts of lanes 15 and 31; lanes without a source add +0), lane 63's
+// value read out.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    return v;
+    v = dpp_add<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_add<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_add<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_add<0x142, 0xa>(v);  // row_bcast:15
+    v = dpp_add<0x143, 0xc>(v);  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 template <int KV64, int RA, int COLS>
@@ -475,13 +487,19 @@ __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
     }
 }
 
-// RA = rows in flight: about 16 loads (16 KiB) per wave, a power of two so
-// that the 32 rows of an item are whole rounds.  Measured at the DSv3 decode
-// shape (N=1, k 7168, 14 loads per row): one row in flight 70.5 us, two 73.2;
-// 16 or 32 rows per item the same.
+// RA = rows in flight: about 16 loads (16 KiB) per wave, a power of two that
+// divides the 8 rows of an item.  Measured at the DSv3 decode shape (N=1, k
+// 7168, 14 loads per row, 32 rows per item): one row in flight 70.5 us, two
+// 73.2.  Rows per item, 32 / 16 / 8 / 4 (same box): DSv3 N=1 70.5 / 70.4 /
+// 69.8 / 69.6 us, N=16 860 / 861 / 859 / 857; Mixtral N=1 72.1 / 80.0 / 70.8 /
+// 69.9, N=4 182 / 187 / 171 / 169; Qwen3 N=1 13.9 / 10.5 / 10.1 / 9.8, N=16
+// 94.5 / 90.5 / 82.6 / 84.3: more, shorter items fill the CUs when the experts
+// with rows have few weight rows between them, and 8 rows re-read each x row
+// from L2 half as often as 4.
 template <int KV64>
-hipError_t launch_rowstream_k(const GemmArgs& a, int num_cus, hipStream_t stream) {
-    constexpr int RA = KV64 > 8 ? 1 : KV64 > 4 ? 2 : KV64 > 2 ? 4 : KV64 > 1 ? 8 : 16;
+hipError_t launch_rowstream_kc(const GemmArgs& a, int num_cus, hipStream_t stream) {
+    constexpr int RA0 = KV64 > 8 ? 1 : KV64 > 4 ? 2 : KV64 > 2 ? 4 : KV64 > 1 ? 8 : 16;
+    constexpr int RA = RA0 < kRsCols ? RA0 : kRsCols;
     const int64_t blocks = (int64_t)num_cus * 2;  // two workgroups per CU fit (at most 221 VGPRs)
     hipLaunchKernelGGL((grouped_gemm_rowstream_kernel<KV64, RA, kRsCols>), dim3((unsigned)blocks), dim3(kRsThreads),
                        0, stream, reinterpret_cast<const u32x4*>(a.x), reinterpret_cast<const u32x4*>(a.w), a.offsets,
@@ -506,22 +524,22 @@ hipError_t launch_grouped_gemm_skinny(const GemmArgs& a, int num_cus, hipStream_
 
 hipError_t launch_grouped_gemm_rowstream(const GemmArgs& a, int num_cus, hipStream_t stream) {
     switch (a.k / 512) {
-        case 1: return launch_rowstream_k<1>(a, num_cus, stream);
-        case 2: return launch_rowstream_k<2>(a, num_cus, stream);
-        case 3: return launch_rowstream_k<3>(a, num_cus, stream);
-        case 4: return launch_rowstream_k<4>(a, num_cus, stream);
-        case 5: return launch_rowstream_k<5>(a, num_cus, stream);
-        case 6: return launch_rowstream_k<6>(a, num_cus, stream);
-        case 7: return launch_rowstream_k<7>(a, num_cus, stream);
-        case 8: return launch_rowstream_k<8>(a, num_cus, stream);
-        case 9: return launch_rowstream_k<9>(a, num_cus, stream);
-        case 10: return launch_rowstream_k<10>(a, num_cus, stream);
-        case 11: return launch_rowstream_k<11>(a, num_cus, stream);
-        case 12: return launch_rowstream_k<12>(a, num_cus, stream);
-        case 13: return launch_rowstream_k<13>(a, num_cus, stream);
-        case 14: return launch_rowstream_k<14>(a, num_cus, stream);
-        case 15: return launch_rowstream_k<15>(a, num_cus, stream);
-        case 16: return launch_rowstream_k<16>(a, num_cus, stream);
+        case 1: return launch_rowstream_kc<1>(a, num_cus, stream);
+        case 2: return launch_rowstream_kc<2>(a, num_cus, stream);
+        case 3: return launch_rowstream_kc<3>(a, num_cus, stream);
+        case 4: return launch_rowstream_kc<4>(a, num_cus, stream);
+        case 5: return launch_rowstream_kc<5>(a, num_cus, stream);
+        case 6: return launch_rowstream_kc<6>(a, num_cus, stream);
+        case 7: return launch_rowstream_kc<7>(a, num_cus, stream);
+        case 8: return launch_rowstream_kc<8>(a, num_cus, stream);
+        case 9: return launch_rowstream_kc<9>(a, num_cus, stream);
+        case 10: return launch_rowstream_kc<10>(a, num_cus, stream);
+        case 11: return launch_rowstream_kc<11>(a, num_cus, stream);
+        case 12: return launch_rowstream_kc<12>(a, num_cus, stream);
+        case 13: return launch_rowstream_kc<13>(a, num_cus, stream);
+        case 14: return launch_rowstream_kc<14>(a, num_cus, stream);
+        case 15: return launch_rowstream_kc<15>(a, num_cus, stream);
+        case 16: return launch_rowstream_kc<16>(a, num_cus, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -169,7 +169,7 @@ def test_grouped_gemm_full_size_sampled_rows(hip_device, name, n):
 # ----------------------------------------------------------------------------
 # Decode-size kernels, chosen from the host's sizes (M rows, E experts):
 #  * row-streaming: M <= E and k a multiple of 512 up to 8192; one wave per
-#    32 weight rows of an expert and up to two of its rows, each weight row
+#    8 weight rows of an expert and up to two of its rows, each weight row
 #    read whole into bf16 dot products, a cross-lane sum per row;
 #  * LDS-staged: M <= 4E, or M <= 16E with fewer tiled-kernel tiles,
 #    min(M, E + M // 128) x ceil(n / 256), than CUs; one wave per 32 output
