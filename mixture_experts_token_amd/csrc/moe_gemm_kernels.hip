@@ -245,6 +245,10 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
     uint16_t* __restrict__ y, int num_experts, int64_t max_rows, int64_t n, int64_t k) {
     constexpr int BM = S::BM, BN = S::BN, MT = S::MT, NT = S::NT, STAGES = S::STAGES;
     constexpr int kThreads = S::kThreads;
+    // The tile's results go out through the idle weight stages when a stage
+    // holds 64 rows of the tile (128 x 256 tiles, two waves down the rows).
+    constexpr bool kStagedOut = S::FAST && BM == 128 && BN == 256 && S::WM == 2 && BN * kBK * 2 == 64 * 512 &&
+                                (BM / S::kWaves) % 2 == 0 && 64 % (BM / S::kWaves) == 0;
     // Each stage of each operand is its own LDS object, so the compiler's
     // wait tracking can tell a stage being filled from the ones being read.
     constexpr int kA2 = STAGES > 2 ? BM * kBK : 8, kB2 = STAGES > 2 ? BN * kBK : 8;
@@ -465,6 +469,50 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
         // Epilogue: for the 32 x 32 tile (weight rows n, x rows m), lane l,
         // register r holds n = (l / 32) * 4 + (r / 4) * 8 + r % 4, m = l % 32:
         // registers 4j .. 4j+3 are four consecutive output columns of row m.
+        if constexpr (kStagedOut) {
+            // Through LDS: each wave writes its bf16 results into the idle
+            // weight stages (tile rows 0-63 in b_s0, 64-127 in b_s1, 512 bytes
+            // a row, the 16-byte unit u of row r at slot u ^ (r % 32), so the
+            // 32 rows of one 8-byte write land in 32 different slots), then
+            // every wave stores whole rows, two 512-byte rows per instruction.
+            // Stored straight from the MFMA layout, each instruction wrote 16
+            // bytes into each of 32 rows.
+            lds_barrier();  // every wave is done reading the stages
+            __bf16* half = wm == 0 ? b_s0 : b_s1;
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                const int r = mi * 32 + lane % 32;  // row within the half
+#pragma unroll
+                for (int ni = 0; ni < NT; ++ni) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int c = wn * S::kWaveN + ni * 32 + (lane / 32) * 4 + j * 8;
+                        const uint32_t lo =
+                            bf16_bits_rne(acc[mi][ni][4 * j]) | (bf16_bits_rne(acc[mi][ni][4 * j + 1]) << 16);
+                        const uint32_t hi =
+                            bf16_bits_rne(acc[mi][ni][4 * j + 2]) | (bf16_bits_rne(acc[mi][ni][4 * j + 3]) << 16);
+                        char* slot = reinterpret_cast<char*>(half) + r * 512 + (((c / 8) ^ (r % 32)) * 16) + (c % 8) * 2;
+                        *reinterpret_cast<uint2*>(slot) = make_uint2(lo, hi);
+                    }
+                }
+            }
+            lds_barrier();
+            constexpr int kRowsPerWave = BM / S::kWaves;
+            const int u = lane % 32;
+            const __bf16* hb = wave * kRowsPerWave < 64 ? b_s0 : b_s1;  // the wave's rows lie in one half
+            u32x4 v[kRowsPerWave / 2];
+#pragma unroll
+            for (int i = 0; i < kRowsPerWave / 2; ++i) {  // all reads first, then the stores
+                const int r = (wave * kRowsPerWave + 2 * i + lane / 32) % 64;
+                v[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(hb) + r * 512 +
+                                                      ((u ^ (r % 32)) * 16));
+            }
+#pragma unroll
+            for (int i = 0; i < kRowsPerWave / 2; ++i) {
+                const int row = wave * kRowsPerWave + 2 * i + lane / 32;  // row of the tile
+                if (row < tc.rows) *reinterpret_cast<u32x4*>(y + (tc.row0 + row) * n + tc.col0 + u * 8) = v[i];
+            }
+        } else {
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
             const int row = wm * S::kWaveM + mi * 32 + lane % 32;
@@ -481,6 +529,7 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
                     *reinterpret_cast<uint2*>(yrow + col) = make_uint2(lo, hi);
                 }
             }
+        }
         }
     }
 }
