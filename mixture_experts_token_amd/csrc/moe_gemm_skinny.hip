@@ -21,6 +21,11 @@
 // registers with its weights.  Experts with more than 16 rows take several
 // row groups, each streaming the weight rows again.
 //
+// With at most one row per expert on average a second kernel takes over
+// (grouped_gemm_rowstream_kernel, below): one wave reads 8 whole weight rows
+// front to back and multiplies them with up to two x rows by bf16 dot
+// products, without LDS or matrix cores, so every HBM stream is sequential.
+//
 // MFMA operands (v_mfma_f32_16x16x32_bf16, weight fragment first): for the
 // k half h (32 k) of a 64-wide chunk, lane l holds 8 consecutive k (k-vector
 // 4h + l / 16 of the chunk) of weight row l % 16 of a 16-row block and of x
@@ -500,7 +505,7 @@ template <int KV64>
 hipError_t launch_rowstream_kc(const GemmArgs& a, int num_cus, hipStream_t stream) {
     constexpr int RA0 = KV64 > 8 ? 1 : KV64 > 4 ? 2 : KV64 > 2 ? 4 : KV64 > 1 ? 8 : 16;
     constexpr int RA = RA0 < kRsCols ? RA0 : kRsCols;
-    const int64_t blocks = (int64_t)num_cus * 2;  // two workgroups per CU fit (at most 221 VGPRs)
+    const int64_t blocks = (int64_t)num_cus * 2;  // two workgroups per CU fit (at most 215 VGPRs)
     hipLaunchKernelGGL((grouped_gemm_rowstream_kernel<KV64, RA, kRsCols>), dim3((unsigned)blocks), dim3(kRsThreads),
                        0, stream, reinterpret_cast<const u32x4*>(a.x), reinterpret_cast<const u32x4*>(a.w), a.offsets,
                        reinterpret_cast<uint16_t*>(a.y), a.num_experts, a.max_rows, a.n);
