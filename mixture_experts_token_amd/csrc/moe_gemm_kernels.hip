@@ -556,16 +556,20 @@ hipError_t launch_gemm_tiles(const GemmArgs& a, int num_cus, hipStream_t stream)
 //    per item).  Against the tiled kernel (DSv3 shape, n 4096, k 7168):
 //    N=1 83 -> 70 us (the LDS-staged kernel), N=4 300 -> 261, N=16
 //    1008 -> 861, N=32 (M = E) 1598 -> 1483; Mixtral N=4 236 -> 184, Qwen3
-//    N=16 106 -> 97.  At M = 2E it ties (Mixtral N=8 378 / 380, Qwen3 N=32
-//    155 / 156) and beyond loses (DSv3 N=64 2210 / 2590): experts with more
-//    rows stream their weights once per two rows.
+//    N=16 106 -> 97.  Two x rows per item stream an expert's weights once per
+//    two of its rows, so past M = E it depends on the routing (DSv3 N=64
+//    2210 / 2590 against the tiled kernel).
+//  * E < M <= 2E and k a multiple of 512 up to 4096: the same kernel with
+//    four x rows per item.  Against the LDS-staged kernel: Mixtral N=6 and 8
+//    330 -> 311 and 331 -> 312 us, Qwen3 N=24 and 32 139 -> 103 and
+//    154 -> 113; at 3E it lost (Mixtral 330 -> 354).
 //  * otherwise M <= 4E, or M <= 16E with fewer tiles than CUs: the LDS-staged
 //    kernel (16 x rows per item).  Against the tiled kernel: DSv3 N=16
 //    1008 / 965 us, N=64 2210 / 2156, N=128 (4E) 2393 / 2400; Mixtral N=8
 //    378 / 334, N=16 344 / 336; Qwen3 N=64 183 / 161.
-// The row-streaming kernel and its k range (moe_gemm_skinny.hip).
-hipError_t launch_grouped_gemm_rowstream(const GemmArgs& a, int num_cus, hipStream_t stream);
-bool gemm_rowstream_fits(int64_t k);
+// The row-streaming kernel (2 or 4 x rows per item) and its k range (moe_gemm_skinny.hip).
+hipError_t launch_grouped_gemm_rowstream(const GemmArgs& a, int num_cus, int x_rows, hipStream_t stream);
+bool gemm_rowstream_fits(int64_t k, int x_rows);
 
 constexpr int64_t kSkinnyMaxRowsPerExpert = 16;
 constexpr int64_t kSkinnyAnyRowsPerExpert = 4;
@@ -578,7 +582,9 @@ static bool gemm_takes_skinny(int64_t max_rows, int num_experts, int64_t n, int 
 }
 
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& a, int num_cus, hipStream_t stream) {
-    if (a.max_rows <= a.num_experts && gemm_rowstream_fits(a.k)) return launch_grouped_gemm_rowstream(a, num_cus, stream);
+    if (a.max_rows <= a.num_experts && gemm_rowstream_fits(a.k, 2)) return launch_grouped_gemm_rowstream(a, num_cus, 2, stream);
+    if (a.max_rows <= 2 * (int64_t)a.num_experts && gemm_rowstream_fits(a.k, 4))
+        return launch_grouped_gemm_rowstream(a, num_cus, 4, stream);
     if (gemm_takes_skinny(a.max_rows, a.num_experts, a.n, num_cus)) return launch_grouped_gemm_skinny(a, num_cus, stream);
     if (a.n % 256 == 0) return launch_gemm_tiles<GemmShape<128, 256, 2, 4, 3, 1, true>>(a, num_cus, stream);
     return launch_gemm_tiles<GemmShape<128, 128, 2, 2, 2, 2, false>>(a, num_cus, stream);

@@ -21,9 +21,9 @@
 // registers with its weights.  Experts with more than 16 rows take several
 // row groups, each streaming the weight rows again.
 //
-// With at most one row per expert on average a second kernel takes over
+// With at most one or two rows per expert on average a second kernel takes over
 // (grouped_gemm_rowstream_kernel, below): one wave reads 8 whole weight rows
-// front to back and multiplies them with up to two x rows by bf16 dot
+// front to back and multiplies them with up to two or four x rows by bf16 dot
 // products, without LDS or matrix cores, so every HBM stream is sequential.
 //
 // MFMA operands (v_mfma_f32_16x16x32_bf16, weight fragment first): for the
@@ -318,9 +318,9 @@ hipError_t launch_skinny(const GemmArgs& a, int num_cus, hipStream_t stream) {
 }
 
 // ----------------------------------------------------------------------------
-// Row-streaming kernel for experts with one or two rows (decode at a token or
-// a few): one wave owns COLS (8) consecutive weight rows of one expert (a
-// single contiguous COLS x k block of w) and up to two of its x rows, and reads
+// Row-streaming kernel for experts with one to four rows (decode at a token
+// or a few): one wave owns COLS (8) consecutive weight rows of one expert (a
+// single contiguous COLS x k block of w) and up to XR (2 or 4) of its x rows, and reads
 // the block front to back, 1 KiB per load, RA weight rows in flight.  Each lane
 // multiplies its 16-byte weight vectors with the matching x vectors (held in
 // registers for the whole item) by bf16 dot products into fp32, and a row's 64
@@ -330,10 +330,10 @@ hipError_t launch_skinny(const GemmArgs& a, int num_cus, hipStream_t stream) {
 // the 16-row fragment layout of the other kernels cannot.
 // KV64 = k / 512: loads per weight row (k a multiple of 512, at most 8192).
 // ----------------------------------------------------------------------------
-constexpr int kRsRowsX = 2;     // x rows per item
 constexpr int kRsCols = 8;      // weight rows (output columns) per item
 constexpr int kRsThreads = 256;
 constexpr int kRsMaxKv64 = 16;  // k <= 8192
+constexpr int kRsMaxKv64X4 = 8; // k <= 4096 with four x rows per item
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -367,7 +367,7 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-template <int KV64, int RA, int COLS>
+template <int KV64, int RA, int COLS, int XR>
 __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
     const u32x4* __restrict__ x, const u32x4* __restrict__ w, const int64_t* __restrict__ off,
     uint16_t* __restrict__ y, int num_experts, int64_t max_rows, int64_t n) {
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
         if (e < num_experts) {
             const int64_t cnt = off[e + 1] - off[e];
             bad |= cnt < 0;
-            cnt_t[q] = cnt > 0 ? (cnt + kRsRowsX - 1) / kRsRowsX * nblocks : 0;
+            cnt_t[q] = cnt > 0 ? (cnt + XR - 1) / XR * nblocks : 0;
         }
         sum += cnt_t[q];
     }
@@ -433,15 +433,15 @@ __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
         const int64_t local = id - item_pre[e];
         const int64_t group = local / nblocks;
         const int64_t col0 = uniform64((local - group * nblocks) * COLS);
-        const int64_t row0 = uniform64(off[e] + group * kRsRowsX);
+        const int64_t row0 = uniform64(off[e] + group * XR);
         const int64_t cnt = off[e + 1] - off[e];
-        const int rows = (int)uniform64(cnt - group * kRsRowsX < kRsRowsX ? cnt - group * kRsRowsX : kRsRowsX);
+        const int rows = (int)uniform64(cnt - group * XR < XR ? cnt - group * XR : XR);
 
         // x vectors i * 64 + lane of the item's rows (a missing second row
         // repeats the first: its sums are not stored).
-        u32x4 xr[kRsRowsX][KV64];
+        u32x4 xr[XR][KV64];
 #pragma unroll
-        for (int r = 0; r < kRsRowsX; ++r)
+        for (int r = 0; r < XR; ++r)
 #pragma unroll
             for (int i = 0; i < KV64; ++i) xr[r][i] = x[(row0 + (r < rows ? r : 0)) * kv + i * 64 + lane];
         // Weight rows col0 .. col0 + COLS - 1: one contiguous block.
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
                 __builtin_amdgcn_sched_barrier(0);  // issued in the loop's order (see below)
             }
 
-        float res[kRsRowsX] = {};
+        float res[XR] = {};
         for (int j0 = 0; j0 < COLS; j0 += RA) {
 #pragma unroll
             for (int a = 0; a < RA; ++a) {
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
                 // the last row is read again (not summed), so every step
                 // issues the same loads and each wait is for one row.
                 const int jn = j + RA < COLS ? j + RA : COLS - 1;
-                float acc[kRsRowsX] = {};
+                float acc[XR] = {};
 #pragma unroll
                 for (int i = 0; i < KV64; ++i) {
                     // Use a vector, then refill its registers: a sliding
@@ -472,12 +472,12 @@ __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
                     // the compiler from hoisting the refills above the uses,
                     // which would make it wait for the whole window first.
 #pragma unroll
-                    for (int r = 0; r < kRsRowsX; ++r) acc[r] = dot8(ring[a][i], xr[r][i], acc[r]);
+                    for (int r = 0; r < XR; ++r) acc[r] = dot8(ring[a][i], xr[r][i], acc[r]);
                     ring[a][i] = __builtin_nontemporal_load(wb + ((int64_t)jn * KV64 + i) * 64);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
-                for (int r = 0; r < kRsRowsX; ++r) {
+                for (int r = 0; r < XR; ++r) {
                     const float t = wave_sum(acc[r]);
                     if (lane == j) res[r] = t;
                 }
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
         // Lane c holds output column col0 + c of each x row.
         if (lane < COLS) {
 #pragma unroll
-            for (int r = 0; r < kRsRowsX; ++r)
+            for (int r = 0; r < XR; ++r)
                 if (r < rows) y[(row0 + r) * n + col0 + lane] = (uint16_t)bf16_rne(res[r]);
         }
     }
@@ -501,20 +501,33 @@ __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
 // 94.5 / 90.5 / 82.6 / 84.3: more, shorter items fill the CUs when the experts
 // with rows have few weight rows between them, and 8 rows re-read each x row
 // from L2 half as often as 4.
-template <int KV64>
-hipError_t launch_rowstream_kc(const GemmArgs& a, int num_cus, hipStream_t stream) {
+template <int KV64, int XR>
+hipError_t launch_rowstream_kx(const GemmArgs& a, int num_cus, hipStream_t stream) {
     constexpr int RA0 = KV64 > 8 ? 1 : KV64 > 4 ? 2 : KV64 > 2 ? 4 : KV64 > 1 ? 8 : 16;
     constexpr int RA = RA0 < kRsCols ? RA0 : kRsCols;
     const int64_t blocks = (int64_t)num_cus * 2;  // two workgroups per CU fit (at most 215 VGPRs)
-    hipLaunchKernelGGL((grouped_gemm_rowstream_kernel<KV64, RA, kRsCols>), dim3((unsigned)blocks), dim3(kRsThreads),
-                       0, stream, reinterpret_cast<const u32x4*>(a.x), reinterpret_cast<const u32x4*>(a.w), a.offsets,
-                       reinterpret_cast<uint16_t*>(a.y), a.num_experts, a.max_rows, a.n);
+    hipLaunchKernelGGL((grouped_gemm_rowstream_kernel<KV64, RA, kRsCols, XR>), dim3((unsigned)blocks),
+                       dim3(kRsThreads), 0, stream, reinterpret_cast<const u32x4*>(a.x),
+                       reinterpret_cast<const u32x4*>(a.w), a.offsets, reinterpret_cast<uint16_t*>(a.y),
+                       a.num_experts, a.max_rows, a.n);
     return hipGetLastError();
+}
+
+// Four x rows per item only up to k 4096 (KV64 8): more x registers would
+// not leave two waves per SIMD.
+template <int KV64>
+hipError_t launch_rowstream_kc(const GemmArgs& a, int num_cus, int x_rows, hipStream_t stream) {
+    if constexpr (KV64 <= kRsMaxKv64X4) {
+        if (x_rows == 4) return launch_rowstream_kx<KV64, 4>(a, num_cus, stream);
+    }
+    return launch_rowstream_kx<KV64, 2>(a, num_cus, stream);
 }
 
 }  // namespace
 
-bool gemm_rowstream_fits(int64_t k) { return k % 512 == 0 && k <= 512 * kRsMaxKv64; }
+bool gemm_rowstream_fits(int64_t k, int x_rows) {
+    return k % 512 == 0 && k <= 512 * (x_rows == 4 ? kRsMaxKv64X4 : kRsMaxKv64);
+}
 
 // Persistent grid, one workgroup per CU (its waves' LDS stages fill the LDS);
 // each wave walks its items.  Stages of 512 bytes of 32 weight rows, two per
@@ -527,24 +540,24 @@ hipError_t launch_grouped_gemm_skinny(const GemmArgs& a, int num_cus, hipStream_
     return launch_skinny<SkShape<32, 32, 2, 4>>(a, num_cus, stream);
 }
 
-hipError_t launch_grouped_gemm_rowstream(const GemmArgs& a, int num_cus, hipStream_t stream) {
+hipError_t launch_grouped_gemm_rowstream(const GemmArgs& a, int num_cus, int x_rows, hipStream_t stream) {
     switch (a.k / 512) {
-        case 1: return launch_rowstream_kc<1>(a, num_cus, stream);
-        case 2: return launch_rowstream_kc<2>(a, num_cus, stream);
-        case 3: return launch_rowstream_kc<3>(a, num_cus, stream);
-        case 4: return launch_rowstream_kc<4>(a, num_cus, stream);
-        case 5: return launch_rowstream_kc<5>(a, num_cus, stream);
-        case 6: return launch_rowstream_kc<6>(a, num_cus, stream);
-        case 7: return launch_rowstream_kc<7>(a, num_cus, stream);
-        case 8: return launch_rowstream_kc<8>(a, num_cus, stream);
-        case 9: return launch_rowstream_kc<9>(a, num_cus, stream);
-        case 10: return launch_rowstream_kc<10>(a, num_cus, stream);
-        case 11: return launch_rowstream_kc<11>(a, num_cus, stream);
-        case 12: return launch_rowstream_kc<12>(a, num_cus, stream);
-        case 13: return launch_rowstream_kc<13>(a, num_cus, stream);
-        case 14: return launch_rowstream_kc<14>(a, num_cus, stream);
-        case 15: return launch_rowstream_kc<15>(a, num_cus, stream);
-        case 16: return launch_rowstream_kc<16>(a, num_cus, stream);
+        case 1: return launch_rowstream_kc<1>(a, num_cus, x_rows, stream);
+        case 2: return launch_rowstream_kc<2>(a, num_cus, x_rows, stream);
+        case 3: return launch_rowstream_kc<3>(a, num_cus, x_rows, stream);
+        case 4: return launch_rowstream_kc<4>(a, num_cus, x_rows, stream);
+        case 5: return launch_rowstream_kc<5>(a, num_cus, x_rows, stream);
+        case 6: return launch_rowstream_kc<6>(a, num_cus, x_rows, stream);
+        case 7: return launch_rowstream_kc<7>(a, num_cus, x_rows, stream);
+        case 8: return launch_rowstream_kc<8>(a, num_cus, x_rows, stream);
+        case 9: return launch_rowstream_kc<9>(a, num_cus, x_rows, stream);
+        case 10: return launch_rowstream_kc<10>(a, num_cus, x_rows, stream);
+        case 11: return launch_rowstream_kc<11>(a, num_cus, x_rows, stream);
+        case 12: return launch_rowstream_kc<12>(a, num_cus, x_rows, stream);
+        case 13: return launch_rowstream_kc<13>(a, num_cus, x_rows, stream);
+        case 14: return launch_rowstream_kc<14>(a, num_cus, x_rows, stream);
+        case 15: return launch_rowstream_kc<15>(a, num_cus, x_rows, stream);
+        case 16: return launch_rowstream_kc<16>(a, num_cus, x_rows, stream);
         default: return hipErrorInvalidValue;
     }
 }

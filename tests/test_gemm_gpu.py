@@ -168,9 +168,10 @@ def test_grouped_gemm_full_size_sampled_rows(hip_device, name, n):
 
 # ----------------------------------------------------------------------------
 # Decode-size kernels, chosen from the host's sizes (M rows, E experts):
-#  * row-streaming: M <= E and k a multiple of 512 up to 8192; one wave per
-#    8 weight rows of an expert and up to two of its rows, each weight row
-#    read whole into bf16 dot products, a cross-lane sum per row;
+#  * row-streaming: M <= E and k a multiple of 512 up to 8192 (two x rows per
+#    item), or E < M <= 2E and k a multiple of 512 up to 4096 (four x rows per
+#    item); one wave per 8 weight rows of an expert, each weight row read
+#    whole into bf16 dot products, a cross-lane sum per row;
 #  * LDS-staged: M <= 4E, or M <= 16E with fewer tiled-kernel tiles,
 #    min(M, E + M // 128) x ceil(n / 256), than CUs; one wave per 32 output
 #    columns of an expert and 16 of its rows, weights staged through LDS in
@@ -180,6 +181,8 @@ def test_grouped_gemm_full_size_sampled_rows(hip_device, name, n):
 def _kernel_for(max_rows, e, n, k):
     if max_rows <= e and k % 512 == 0 and k <= 8192:
         return "rowstream"
+    if max_rows <= 2 * e and k % 512 == 0 and k <= 4096:
+        return "rowstream4"
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     tiles = min(max_rows, e + max_rows // 128) * ((n + 255) // 256)
     if max_rows <= 4 * e or (max_rows <= 16 * e and tiles < cus):
@@ -197,6 +200,7 @@ SKINNY_CASES = [
     (8, [3] * 8, 128, 640, 0),                         # 10 chunks: an odd stage count, the last stage partial
     (4, [1, 0, 2, 1], 128, 8704, 0),                   # k past the row-streaming kernel's 8192: 34 stages
     (8, [4] * 8, 8192, 512, 0),                        # M = 4E with as many tiles as CUs
+    (4, [5, 1, 0, 2], 128, 4608, 0),                   # M = 2E, k past the four-row kernel's 4096
 ]
 
 ROWSTREAM_CASES = [
@@ -206,6 +210,13 @@ ROWSTREAM_CASES = [
     (64, ("even", 60), 384, 4608, 4),                  # 9 loads per row: one row in flight
     (4, [1, 0, 2, 1], 128, 8192, 0),                   # the largest k: 16 loads per row
     (3, [0, 0, 3], 4096, 2560, 0),                     # one expert with all rows, 128 column blocks
+]
+
+ROWSTREAM4_CASES = [
+    # four x rows per item (E < M <= 2E)
+    (8, [3, 0, 4, 1, 0, 2, 3, 1], 256, 1024, 2),       # 14 rows; a 4-row and a 3-row expert
+    (4, [5, 1, 0, 2], 128, 512, 0),                    # a 5-row expert: a 4-row and a 1-row item
+    (16, ("even", 30), 384, 4096, 0),                  # the largest k with four x rows
 ]
 
 
@@ -243,6 +254,12 @@ def test_grouped_gemm_skinny_parity(hip_device, e, spec, n, k, spare):
                          ids=["rowstream-%d-%d-%d" % (c[0], c[2], c[3]) for c in ROWSTREAM_CASES])
 def test_grouped_gemm_rowstream_parity(hip_device, e, spec, n, k, spare):
     _decode_kernel_parity(hip_device, e, spec, n, k, spare, "rowstream")
+
+
+@pytest.mark.parametrize("e,spec,n,k,spare", ROWSTREAM4_CASES,
+                         ids=["rowstream4-%d-%d-%d" % (c[0], c[2], c[3]) for c in ROWSTREAM4_CASES])
+def test_grouped_gemm_rowstream4_parity(hip_device, e, spec, n, k, spare):
+    _decode_kernel_parity(hip_device, e, spec, n, k, spare, "rowstream4")
 
 
 @pytest.mark.parametrize("kernel,n,k", [("skinny", 128, 128), ("rowstream", 128, 512)])
