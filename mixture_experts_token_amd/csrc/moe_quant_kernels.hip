@@ -79,15 +79,39 @@ __device__ __forceinline__ float max_xor(float m, int lane_mask) {
     return o > m ? o : m;
 }
 
+// x / scale for bf16 x, giving the code of the correctly rounded quotient
+// with one division per scale instead of one per element: the reciprocal r =
+// 1 / scale (correctly rounded), q0 = x * r, and the FMA correction step of
+// Markstein's division, q = q0 + r * (x - q0 * scale), the sign taken from x
+// (an exact zero otherwise loses the sign of -0).  Used for scales in
+// [2^-100, 2^126]: an exhaustive host check over every finite bf16 x and every
+// scale that a bf16 amax gives (tests/quant_division_check.c) finds the quotient
+// bit-identical to the division wherever it can reach a nonzero E4M3 code
+// (|x / scale| >= 2^-11) and of the same sign elsewhere; below 2^-100
+// (amax < 448 * 2^-100) remainders of subnormal x lose bits, so the division
+// stays.  Bf16 inputs only (f32 inputs cannot be checked exhaustively).
+struct Bf16Quotient {
+    float scale, r;
+    bool fast;
+    __device__ __forceinline__ explicit Bf16Quotient(float s)
+        : scale(s), r(0.0f), fast(s >= 0x1p-100f && s <= 0x1p+126f) {
+        if (fast) r = __fdiv_rn(1.0f, s);
+    }
+    __device__ __forceinline__ float operator()(float x) const {
+        if (!fast) return __fdiv_rn(x, scale);
+        const float q0 = x * r;
+        return copysignf(fmaf(fmaf(-q0, scale, x), r, q0), x);
+    }
+};
+
 // Codes of one 16-byte vector: 8 bf16 -> 8 bytes, or 4 f32 -> 4 bytes (in .x).
 template <bool kBF16>
 __device__ __forceinline__ u32x2 vec_codes(const u32x4& v, float scale) {
     u32x2 out;
     if constexpr (kBF16) {
-        out.x = e4m3_pack4(__fdiv_rn(bf16_lo(v[0]), scale), __fdiv_rn(bf16_hi(v[0]), scale),
-                           __fdiv_rn(bf16_lo(v[1]), scale), __fdiv_rn(bf16_hi(v[1]), scale));
-        out.y = e4m3_pack4(__fdiv_rn(bf16_lo(v[2]), scale), __fdiv_rn(bf16_hi(v[2]), scale),
-                           __fdiv_rn(bf16_lo(v[3]), scale), __fdiv_rn(bf16_hi(v[3]), scale));
+        const Bf16Quotient q(scale);
+        out.x = e4m3_pack4(q(bf16_lo(v[0])), q(bf16_hi(v[0])), q(bf16_lo(v[1])), q(bf16_hi(v[1])));
+        out.y = e4m3_pack4(q(bf16_lo(v[2])), q(bf16_hi(v[2])), q(bf16_lo(v[3])), q(bf16_hi(v[3])));
     } else {
         out.x = e4m3_pack4(__fdiv_rn(__uint_as_float(v[0]), scale), __fdiv_rn(__uint_as_float(v[1]), scale),
                            __fdiv_rn(__uint_as_float(v[2]), scale), __fdiv_rn(__uint_as_float(v[3]), scale));
