@@ -346,8 +346,8 @@ hipError_t launch_quant_dtype(const QuantArgs& a, hipStream_t stream) {
 // token each wave also reads the whole row for the amax (kRowPer vectors per
 // lane, from L2 after the first wave); with group scales a chunk holds whole
 // groups (a group is at most 64 vectors, aligned).  The arithmetic is the
-// quantise-scatter's (vec_amax, max over the group or row, __fdiv_rn,
-// vec_codes).
+// quantise-scatter's (vec_amax, max over the group or row, the scale by
+// __fdiv_rn, vec_codes).
 // ----------------------------------------------------------------------------
 template <bool kBF16, typename IdT, int kPer, int kRowPer>
 __global__ __launch_bounds__(kWaveSize) void quant_permute_wave_kernel(PermuteArgs a, QuantArgs q, int nbits) {
