@@ -199,6 +199,45 @@ def test_quant_fused_plan_non_finite_and_boundaries(hip_device):
         assert_quant_equal(outs, oracle_quant(xt, ids, 5, group))
 
 
+def _bf16_from_bits(bits):
+    return torch.from_numpy(np.asarray(bits, np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def test_quant_bf16_scale_ranges(hip_device):
+    """Bf16 rows whose scales fall on both sides of the bound of the kernels'
+    reciprocal-and-FMA quotient (scales in [2^-100, 2^126]; below it the
+    division per element stays): tiny rows, rows around the bound, subnormal
+    values beside normal ones, signed zeros, values near the bf16 maximum,
+    NaN beside finite values, and rows of log-uniform magnitudes; one scale per
+    token and 8-element groups (one 16-byte vector each, so scales change
+    within a wave).  400 rows
+    (above the one-kernel decode plan) and 8 rows (the decode plan)."""
+    h = 512
+    rng = np.random.default_rng(11)
+    rows = []
+    rows.append(rng.standard_normal(h) * 1e-30)                    # amax ~1e-30: below the bound
+    rows.append(rng.standard_normal(h) * 2.0**-91)                 # amax around 448 * 2^-100
+    r = rng.standard_normal(h) * 2.0**-128; r[5] = 2.0**-120; rows.append(r)   # subnormals, tiny scale
+    r = rng.standard_normal(h) * 2.0**-128; r[5] = 1.0; rows.append(r)         # subnormals, scale 1/448
+    rows.append(rng.uniform(-3.3e38, 3.3e38, h))                   # near the bf16 maximum
+    r = np.zeros(h); r[1::2] = -0.0; r[7] = 1.0; rows.append(r)   # signed zeros beside 1
+    r = rng.standard_normal(h); r[3] = np.nan; r[10] = 2.5; rows.append(r)    # NaN beside finite values
+    while len(rows) < 200:                                          # log-uniform magnitudes per element
+        rows.append(rng.choice([-1.0, 1.0], h) * np.exp2(rng.uniform(-140, 120, h)))
+    xb = torch.from_numpy(np.stack(rows).astype(np.float32)).to(torch.bfloat16)
+    signed_zeros = _bf16_from_bits(np.where(np.arange(h) % 2 == 1, 0x8000, 0)).to(torch.bfloat16)
+    signed_zeros[7] = 1.0
+    xb[5] = signed_zeros
+    x = xb.to(hip_device)
+    for n in (200, 8):
+        ids = torch.from_numpy(np.stack([np.arange(n) % 5, (np.arange(n) + 2) % 5], 1).astype(np.int32)).to(hip_device)
+        for group in (0, 8):
+            _say("quant bf16 scale ranges N=%d group=%d" % (n, group))
+            outs = gpu_quant(x[:n].contiguous(), ids, 5, group)
+            torch.cuda.synchronize()
+            assert_quant_equal(outs, oracle_quant(x[:n].contiguous(), ids, 5, group))
+
+
 @pytest.mark.parametrize("group", [0, 128])
 def test_quant_dsv3_full_size(hip_device, group):
     """DSv3 shape at full size: offsets, indices, and the codes and scales of
