@@ -261,8 +261,10 @@ moe_status_t moe_permute_quant_fp8(const void *hidden_states, int32_t dtype, con
  * contiguous for a grouped GEMM, whose expanded output the unpermute then
  * reduces).  For every expert e and permuted row j in [off[e], off[e+1]):
  *     y[j][c] = sum over i of x[j][i] * w[e][c][i]
- * bf16 inputs, fp32 accumulation on the matrix cores, rounded once to bf16
- * (round to nearest even).  y is in permuted order, ready for moe_unpermute.
+ * bf16 inputs, fp32 accumulation (on the matrix cores; at decode sizes, with
+ * one or two rows per expert on average, by bf16 dot products on the vector
+ * units), rounded once to bf16 (round to nearest even); the order of the fp32
+ * sums is not specified.  y is in permuted order, ready for moe_unpermute.
  *
  *   x                 [max_rows, k] bf16, permuted rows (e.g. permuted_hidden_states)
  *   w                 [num_experts, n, k] bf16 (expert e: n output rows of k, a
