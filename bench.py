@@ -94,7 +94,7 @@ DIGEST_FILES = {
                 "moe_permute_staged.hip", "moe_permute_rows.hip", "moe_permute_launch.hip", "moe_launch.h",
                 "moe_plan.h"],
     "unpermute": ["moe_unpermute.hip", "moe_launch.h", "moe_plan.h"],
-    "gemm": ["moe_gemm_kernels.hip", "moe_gemm_skinny.hip", "moe_launch.h", "moe_plan.h"],
+    "gemm": ["moe_gemm_kernels.hip", "moe_gemm_skinny.hip", "moe_gemm_device.h", "moe_launch.h", "moe_plan.h"],
 }
 
 

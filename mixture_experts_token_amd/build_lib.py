@@ -26,7 +26,7 @@ PROBE_LIB = os.path.join(PKG, "libhbm_probe.so")
 
 SOURCES = ["moe_permute_wave.hip", "moe_permute_fused.hip", "moe_permute_coarse.hip", "moe_permute_staged.hip",
            "moe_permute_rows.hip", "moe_permute_launch.hip", "moe_unpermute.hip", "moe_quant_kernels.hip", "moe_gemm_kernels.hip", "moe_gemm_skinny.hip", "moe_permute_api.cpp"]
-HEADERS = ["moe_launch.h", "moe_plan.h", "moe_permute_device.h"]
+HEADERS = ["moe_launch.h", "moe_plan.h", "moe_permute_device.h", "moe_gemm_device.h"]
 PROBE_SOURCES = ["hbm_probe.hip"]  # streaming-ceiling kernels used by bench.py only
 
 HIPCC_FLAGS = [

@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "moe_launch.h"
+#include "moe_gemm_device.h"
 #include "moe_plan.h"
 
 namespace moe {
@@ -259,8 +260,7 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
     __shared__ __attribute__((aligned(1024))) __bf16 b_s1[BN * kBK];
     __shared__ __attribute__((aligned(1024))) __bf16 b_s2[kB2];
     __shared__ int64_t tile_pre[kMaxExperts + 1];
-    __shared__ int64_t part[kThreads];
-    __shared__ int bad_s;
+    __shared__ int64_t part[kThreads / 64];  // per-wave totals of the item prefix
 
     const int tid = threadIdx.x;
     const int lane = tid % 64;
@@ -296,27 +296,16 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
         s += cnt_t[q];
     }
     if (tid == 0) bad |= off[0] != 0 || off[num_experts] > max_rows;
-    if (tid == 0) bad_s = 0;
-    part[tid] = s;
-    __syncthreads();
-    if (bad) atomicOr(&bad_s, 1);
-    for (int d = 1; d < kThreads; d <<= 1) {
-        const int64_t v = tid >= d ? part[tid - d] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    int64_t excl = part[tid] - s;
+    int64_t total;
+    int64_t excl = block_exclusive_prefix64<kThreads>(s, part, total);
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int e = tid * kPer + q;
         if (e < num_experts) tile_pre[e] = excl;
         excl += cnt_t[q];
     }
-    if (tid == 0) tile_pre[num_experts] = part[kThreads - 1];
-    __syncthreads();
-    if (bad_s) return;
-    const int64_t total = tile_pre[num_experts];
+    if (tid == 0) tile_pre[num_experts] = total;
+    if (__syncthreads_or(bad)) return;  // also publishes tile_pre
 
     auto stage_a = [&](auto st) __attribute__((always_inline)) -> __bf16* {
         if constexpr (decltype(st)::value == 0) return a_s0;

@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "moe_launch.h"
+#include "moe_gemm_device.h"
 #include "moe_plan.h"
 
 namespace moe {
@@ -198,8 +199,7 @@ __global__ __launch_bounds__(S::kThreads) void grouped_gemm_skinny_kernel(
     // read only by asm fragment reads.
     __shared__ __attribute__((aligned(1024))) u32x4 stage_s[S::kWaves][S::kStages][S::kStageVecs];
     __shared__ int64_t item_pre[kMaxExperts + 1];
-    __shared__ int64_t part[kThreads];
-    __shared__ int bad_s;
+    __shared__ int64_t part[kThreads / 64];  // per-wave totals of the item prefix
     const int tid = threadIdx.x;
     const int lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -225,27 +225,16 @@ __global__ __launch_bounds__(S::kThreads) void grouped_gemm_skinny_kernel(
         sum += cnt_t[q];
     }
     if (tid == 0) bad |= off[0] != 0 || off[num_experts] > max_rows;
-    if (tid == 0) bad_s = 0;
-    part[tid] = sum;
-    __syncthreads();
-    if (bad) atomicOr(&bad_s, 1);
-    for (int d = 1; d < kThreads; d <<= 1) {
-        const int64_t v = tid >= d ? part[tid - d] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    int64_t excl = part[tid] - sum;
+    int64_t total;
+    int64_t excl = block_exclusive_prefix64<kThreads>(sum, part, total);
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int e = tid * kPer + q;
         if (e < num_experts) item_pre[e] = excl;
         excl += cnt_t[q];
     }
-    if (tid == 0) item_pre[num_experts] = part[kThreads - 1];
-    __syncthreads();
-    if (bad_s) return;
-    const int64_t total = item_pre[num_experts];
+    if (tid == 0) item_pre[num_experts] = total;
+    if (__syncthreads_or(bad)) return;  // also publishes item_pre
     const int64_t total_waves = (int64_t)gridDim.x * S::kWaves;
 
     for (int64_t id = (int64_t)blockIdx.x * S::kWaves + wave; id < total; id += total_waves) {
@@ -375,8 +364,7 @@ __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
     constexpr int kWaves = kRsThreads / 64;
     constexpr int kv = KV64 * 64;  // 16-byte vectors per row
     __shared__ int64_t item_pre[kMaxExperts + 1];
-    __shared__ int64_t part[kRsThreads];
-    __shared__ int bad_s;
+    __shared__ int64_t part[kRsThreads / 64];  // per-wave totals of the item prefix
     const int tid = threadIdx.x;
     const int lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -399,27 +387,16 @@ __global__ __launch_bounds__(kRsThreads) void grouped_gemm_rowstream_kernel(
         sum += cnt_t[q];
     }
     if (tid == 0) bad |= off[0] != 0 || off[num_experts] > max_rows;
-    if (tid == 0) bad_s = 0;
-    part[tid] = sum;
-    __syncthreads();
-    if (bad) atomicOr(&bad_s, 1);
-    for (int d = 1; d < kRsThreads; d <<= 1) {
-        const int64_t v = tid >= d ? part[tid - d] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    int64_t excl = part[tid] - sum;
+    int64_t total;
+    int64_t excl = block_exclusive_prefix64<kRsThreads>(sum, part, total);
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
         const int e = tid * kPer + q;
         if (e < num_experts) item_pre[e] = excl;
         excl += cnt_t[q];
     }
-    if (tid == 0) item_pre[num_experts] = part[kRsThreads - 1];
-    __syncthreads();
-    if (bad_s) return;
-    const int64_t total = item_pre[num_experts];
+    if (tid == 0) item_pre[num_experts] = total;
+    if (__syncthreads_or(bad)) return;  // also publishes item_pre
     const int64_t total_waves = (int64_t)gridDim.x * kWaves;
 
     for (int64_t id = (int64_t)blockIdx.x * kWaves + wave; id < total; id += total_waves) {
