@@ -225,6 +225,15 @@ __device__ __forceinline__ void lds_read_slice(uint32_t a0, uint32_t a1, uint32_
         : "memory");
 }
 
+// A copy the compiler cannot see through or move out of a loop: per-lane
+// values derived from it are recomputed where they are used instead of being
+// hoisted out of the k-loop and kept live across it.
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 template <int I>
 using Int = std::integral_constant<int, I>;
 
@@ -318,6 +327,11 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
         else return b_s2;
     };
 
+    // This lane's byte offset of its first fragment (k slice 0) within a stage
+    // of the row tile and of the weight tile.
+    const uint32_t a_lane_off = lds_frag_addr(a_s0, wm * S::kWaveM + lane % 32, lane / 32) - lds_frag_addr(a_s0, 0, 0);
+    const uint32_t b_lane_off = lds_frag_addr(b_s0, wn * S::kWaveN + lane % 32, lane / 32) - lds_frag_addr(b_s0, 0, 0);
+
     // Persistent walk: iteration i covers tiles [i*G, (i+1)*G), G = gridDim.x;
     // XCD x (blocks b with b % 8 == x) takes the contiguous chunk x*G/8 ...
     const int64_t G = gridDim.x;
@@ -376,6 +390,14 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
         auto compute_step = [&](auto st, auto&& hook) __attribute__((always_inline)) {
             const __bf16* as = stage_a(st);
             const __bf16* bs = stage_b(st);
+            // Explicit fragment addresses: rows 32 apart have the same row % 8
+            // and bit 3, so both fragments of an operand share one slot (4 KiB
+            // apart); slice kk's slot is slice 0's XOR 2 kk (address bits 5-6).
+            // Two opaque per-lane offsets per step, instead of the 16 addresses
+            // per stage the compiler kept live through the loop (246 -> 201 VGPRs,
+            // Mixtral- / Qwen3- / DSv3-shaped 2-5 % faster, bit-identical).
+            const uint32_t a_off = opaque_u32(a_lane_off), b_off = opaque_u32(b_lane_off);
+            const uint32_t as_addr = lds_frag_addr(as, 0, 0), bs_addr = lds_frag_addr(bs, 0, 0);
 #pragma unroll
             for (int kk = 0; kk < kBK / 16; ++kk) {
                 const int kvec = kk * 2 + lane / 32;
@@ -383,11 +405,9 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
                 if constexpr (S::FAST) {
                     static_assert(MT == 2 && NT == 2, "lds_read_slice reads 2 + 2 fragments");
                     u32x4 fa[MT], fb[NT];
-                    lds_read_slice(lds_frag_addr(as, wm * S::kWaveM + lane % 32, kvec),
-                                   lds_frag_addr(as, wm * S::kWaveM + 32 + lane % 32, kvec),
-                                   lds_frag_addr(bs, wn * S::kWaveN + lane % 32, kvec),
-                                   lds_frag_addr(bs, wn * S::kWaveN + 32 + lane % 32, kvec), fa[0], fa[1], fb[0],
-                                   fb[1]);
+                    const uint32_t a0 = as_addr + (a_off ^ (uint32_t)(kk * 32));
+                    const uint32_t b0 = bs_addr + (b_off ^ (uint32_t)(kk * 32));
+                    lds_read_slice(a0, a0 + 32 * kBK * 2, b0, b0 + 32 * kBK * 2, fa[0], fa[1], fb[0], fb[1]);
 #pragma unroll
                     for (int mi = 0; mi < MT; ++mi) af[mi] = __builtin_bit_cast(bf16x8, fa[mi]);
 #pragma unroll
@@ -418,14 +438,16 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
         static_for<0, STAGES - 1>([&](auto st) __attribute__((always_inline)) {
             if (decltype(st)::value < ksteps) load_part(decltype(st)::value, st, Int<0>{}, Int<kGA + kGB>{});
         });
-        auto step = [&](int64_t ks, auto st) __attribute__((always_inline)) {
+        // full: the caller knows that step ks + STAGES - 1 exists (no branch on it).
+        auto step = [&](int64_t ks, auto st, auto full) __attribute__((always_inline)) {
             constexpr int kSt = decltype(st)::value;
-            if (STAGES == 3 && ks + 1 < ksteps) wait_vmem<(STAGES == 3 ? 1 : 0) * S::kLoadsPerStep>();
+            constexpr bool kFull = decltype(full)::value;
+            if (STAGES == 3 && (kFull || ks + 1 < ksteps)) wait_vmem<(STAGES == 3 ? 1 : 0) * S::kLoadsPerStep>();
             else wait_vmem<0>();
             lds_barrier();
             constexpr auto nst = Int<(kSt + STAGES - 1) % STAGES>{};
             const int64_t nstep = ks + STAGES - 1;
-            if (nstep < ksteps) {
+            if (kFull || nstep < ksteps) {
                 if constexpr (S::FAST) {
                     // the next step's loads go out a quarter at a time, one
                     // part before each k slice's MFMAs
@@ -447,12 +469,19 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
         };
         // Whole rounds of STAGES steps, then the last ksteps % STAGES steps
         // (stages 0, 1, ... again): the accumulators see no branch inside a round.
+        // Rounds in which every step refills a stage have no branch inside.
         int64_t ks = 0;
+        for (; ks + 2 * STAGES - 1 <= ksteps; ks += STAGES)
+            static_for<0, STAGES>([&](auto st) __attribute__((always_inline)) {
+                step(ks + decltype(st)::value, st, Int<1>{});
+            });
         for (; ks + STAGES <= ksteps; ks += STAGES)
-            static_for<0, STAGES>([&](auto st) __attribute__((always_inline)) { step(ks + decltype(st)::value, st); });
-        if (ks < ksteps) step(ks, Int<0>{});
+            static_for<0, STAGES>([&](auto st) __attribute__((always_inline)) {
+                step(ks + decltype(st)::value, st, Int<0>{});
+            });
+        if (ks < ksteps) step(ks, Int<0>{}, Int<0>{});
         if constexpr (STAGES == 3) {
-            if (ks + 1 < ksteps) step(ks + 1, Int<1>{});
+            if (ks + 1 < ksteps) step(ks + 1, Int<1>{}, Int<0>{});
         }
 
         // Epilogue: for the 32 x 32 tile (weight rows n, x rows m), lane l,
