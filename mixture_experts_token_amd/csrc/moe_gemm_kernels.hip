@@ -240,6 +240,20 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
     return r;
 }
 
+// The same for a wave whose second row fragment holds no rows of the tile:
+// one row fragment and the two weight fragments.
+__device__ __forceinline__ void lds_read_slice3(uint32_t a0, uint32_t b0, uint32_t b1, u32x4& fa0, u32x4& fb0,
+                                                u32x4& fb1) {
+    asm volatile(
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b128 %1, %4\n\t"
+        "ds_read_b128 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fa0), "=&v"(fb0), "=&v"(fb1)
+        : "v"(a0), "v"(b0), "v"(b1)
+        : "memory");
+}
+
 template <int I>
 using Int = std::integral_constant<int, I>;
 
@@ -393,7 +407,9 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
         };
         // One k-step from stage st: four 16-wide k slices; hook(kk) runs
         // before slice kk's MFMAs (it issues part of the next step's loads).
-        auto compute_step = [&](auto st, auto&& hook) __attribute__((always_inline)) {
+        // mf: the 32-row fragments of this wave's block that hold rows of the
+        // tile (the others' results are never stored, so their MFMAs are skipped).
+        auto compute_step = [&](auto st, auto mf, auto&& hook) __attribute__((always_inline)) {
             const __bf16* as = stage_a(st);
             const __bf16* bs = stage_b(st);
             // Explicit fragment addresses: rows 32 apart have the same row % 8
@@ -413,7 +429,14 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
                     u32x4 fa[MT], fb[NT];
                     const uint32_t a0 = as_addr + (a_off ^ (uint32_t)(kk * 32));
                     const uint32_t b0 = bs_addr + (b_off ^ (uint32_t)(kk * 32));
-                    lds_read_slice(a0, a0 + 32 * kBK * 2, b0, b0 + 32 * kBK * 2, fa[0], fa[1], fb[0], fb[1]);
+                    if constexpr (decltype(mf)::value == 2) {
+                        lds_read_slice(a0, a0 + 32 * kBK * 2, b0, b0 + 32 * kBK * 2, fa[0], fa[1], fb[0], fb[1]);
+                    } else if constexpr (decltype(mf)::value == 1) {
+                        lds_read_slice3(a0, b0, b0 + 32 * kBK * 2, fa[0], fb[0], fb[1]);
+                        fa[1] = fa[0];  // not used
+                    } else {
+                        fa[0] = fa[1] = fb[0] = fb[1] = u32x4{};  // not used: no MFMAs, no reads
+                    }
 #pragma unroll
                     for (int mi = 0; mi < MT; ++mi) af[mi] = __builtin_bit_cast(bf16x8, fa[mi]);
 #pragma unroll
@@ -426,7 +449,7 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
                 }
                 hook(kk);
 #pragma unroll
-                for (int mi = 0; mi < MT; ++mi)
+                for (int mi = 0; mi < decltype(mf)::value; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < NT; ++ni)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
@@ -445,7 +468,7 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
             if (decltype(st)::value < ksteps) load_part(decltype(st)::value, st, Int<0>{}, Int<kGA + kGB>{});
         });
         // full: the caller knows that step ks + STAGES - 1 exists (no branch on it).
-        auto step = [&](int64_t ks, auto st, auto full) __attribute__((always_inline)) {
+        auto step = [&](int64_t ks, auto st, auto full, auto mf) __attribute__((always_inline)) {
             constexpr int kSt = decltype(st)::value;
             constexpr bool kFull = decltype(full)::value;
             if (STAGES == 3 && (kFull || ks + 1 < ksteps)) wait_vmem<(STAGES == 3 ? 1 : 0) * S::kLoadsPerStep>();
@@ -458,7 +481,7 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
                     // the next step's loads go out a quarter at a time, one
                     // part before each k slice's MFMAs
                     constexpr int n4 = kGA + kGB;
-                    compute_step(st, [&](int kk) __attribute__((always_inline)) {
+                    compute_step(st, mf, [&](int kk) __attribute__((always_inline)) {
                         if (kk == 0) load_part(nstep, nst, Int<0>{}, Int<n4 / 4>{});
                         else if (kk == 1) load_part(nstep, nst, Int<n4 / 4>{}, Int<n4 / 2>{});
                         else if (kk == 2) load_part(nstep, nst, Int<n4 / 2>{}, Int<3 * n4 / 4>{});
@@ -467,27 +490,42 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
                 } else {
                     load_part(nstep, nst, Int<0>{}, Int<kGA + kGB>{});
                     __builtin_amdgcn_sched_barrier(0);  // the loads go out before this step's LDS reads
-                    compute_step(st, [](int) __attribute__((always_inline)) {});
+                    compute_step(st, mf, [](int) __attribute__((always_inline)) {});
                 }
             } else {
-                compute_step(st, [](int) __attribute__((always_inline)) {});
+                compute_step(st, mf, [](int) __attribute__((always_inline)) {});
             }
         };
-        // Whole rounds of STAGES steps, then the last ksteps % STAGES steps
-        // (stages 0, 1, ... again): the accumulators see no branch inside a round.
-        // Rounds in which every step refills a stage have no branch inside.
-        int64_t ks = 0;
-        for (; ks + 2 * STAGES - 1 <= ksteps; ks += STAGES)
-            static_for<0, STAGES>([&](auto st) __attribute__((always_inline)) {
-                step(ks + decltype(st)::value, st, Int<1>{});
-            });
-        for (; ks + STAGES <= ksteps; ks += STAGES)
-            static_for<0, STAGES>([&](auto st) __attribute__((always_inline)) {
-                step(ks + decltype(st)::value, st, Int<0>{});
-            });
-        if (ks < ksteps) step(ks, Int<0>{}, Int<0>{});
-        if constexpr (STAGES == 3) {
-            if (ks + 1 < ksteps) step(ks + 1, Int<1>{}, Int<0>{});
+        // Whole rounds of STAGES steps (those in which every step refills a
+        // stage have no branch inside), then the last ksteps % STAGES steps
+        // (stages 0, 1, ... again).
+        auto k_loop = [&](auto mf) __attribute__((always_inline)) {
+            int64_t ks = 0;
+            for (; ks + 2 * STAGES - 1 <= ksteps; ks += STAGES)
+                static_for<0, STAGES>([&](auto st) __attribute__((always_inline)) {
+                    step(ks + decltype(st)::value, st, Int<1>{}, mf);
+                });
+            for (; ks + STAGES <= ksteps; ks += STAGES)
+                static_for<0, STAGES>([&](auto st) __attribute__((always_inline)) {
+                    step(ks + decltype(st)::value, st, Int<0>{}, mf);
+                });
+            if (ks < ksteps) step(ks, Int<0>{}, Int<0>{}, mf);
+            if constexpr (STAGES == 3) {
+                if (ks + 1 < ksteps) step(ks + 1, Int<1>{}, Int<0>{}, mf);
+            }
+        };
+        if constexpr (S::FAST && MT == 2) {
+            // One k-loop per count of this wave's fragments that hold rows
+            // (a wave-uniform choice per tile; every version has the same
+            // barriers): the last row tile of an expert is often mostly empty.
+            const int wave_rows = rows_valid - wm * S::kWaveM;
+            const int wave_frags =
+                __builtin_amdgcn_readfirstlane(wave_rows > 32 ? 2 : wave_rows > 0 ? 1 : 0);
+            if (wave_frags == 2) k_loop(Int<2>{});
+            else if (wave_frags == 1) k_loop(Int<1>{});
+            else k_loop(Int<0>{});
+        } else {
+            k_loop(Int<MT>{});
         }
 
         // Epilogue: for the 32 x 32 tile (weight rows n, x rows m), lane l,
