@@ -27,8 +27,8 @@
 //   * the tile list lives on the device: the offsets come from the permute, so
 //     every workgroup derives the per-expert tile counts from them (prefix in
 //     LDS) and walks tiles persistently.  Order: per expert, groups of 8 row
-//     tiles (the last group 8-15: it takes the remainder), all column tiles of
-//     a group, row tiles fastest -- a group's rows
+//     tiles (a remainder of 1-3 tiles joins the last group), all column tiles
+//     of a group, row tiles fastest -- a group's rows
 //     and a column tile's weights are reused while they are cached; the
 //     concurrently running tiles are split into one contiguous chunk per XCD
 //     (workgroups are dispatched round-robin over the 8 XCDs), so each XCD's
@@ -52,7 +52,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64;
-constexpr int kGroupM = 8;             // row tiles per group in the tile order (the last group: 8-15)
+constexpr int kGroupM = 8;             // row tiles per group in the tile order (the last group: 1-11)
 constexpr int kXcds = 8;
 
 // Tile shape: BM x BN outputs per workgroup of WM x WN waves, each wave a
@@ -136,10 +136,11 @@ __device__ __forceinline__ TileCoord tile_coord(int64_t id, const int64_t* __res
     const int64_t local = id - tile_pre[e];
     const int64_t cnt = off[e + 1] - off[e];
     const int64_t mt = (cnt + BM - 1) / BM;
-    // Groups of kGroupM row tiles; the last group also takes the remainder
-    // (up to 2 kGroupM - 1 tiles), so that no short group streams all of the
-    // expert's weight column tiles again for one or two row tiles.
-    const int64_t ng = mt / kGroupM > 0 ? mt / kGroupM : 1;
+    // Groups of kGroupM row tiles; a remainder of 1-3 row tiles joins the last
+    // group, so that no short group streams all of the expert's weight column
+    // tiles again for one to three row tiles (a longer remainder keeps its own
+    // group: larger groups fetch more row bytes per column tile).
+    const int64_t ng = mt % kGroupM <= 3 && mt / kGroupM > 0 ? mt / kGroupM : (mt + kGroupM - 1) / kGroupM;
     const int64_t g0 = local / (kGroupM * n_tiles);
     const int64_t g = g0 < ng - 1 ? g0 : ng - 1;
     const int64_t gsize = g == ng - 1 ? mt - g * kGroupM : kGroupM;
