@@ -358,10 +358,15 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
     const int64_t G = gridDim.x;
     const int64_t per_xcd = G / kXcds;
     const int64_t slot = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    // Each tile's coordinates are worked out during the previous tile (after its
+    // first loads are issued), so the dependent LDS search and offset loads are
+    // off the path between two tiles.
+    TileCoord tc_next{};
+    if (slot < total) tc_next = tile_coord<BM, BN>(slot, off, tile_pre, num_experts, n_tiles);
     for (int64_t base = 0; base < total; base += G) {
         const int64_t id = base + slot;
         if (id >= total) break;
-        const TileCoord tc = tile_coord<BM, BN>(id, off, tile_pre, num_experts, n_tiles);
+        const TileCoord tc = tc_next;
         const u32x4* xrow0 = x + tc.row0 * kv;
         const u32x4* wrow0 = w + ((int64_t)tc.expert * n + tc.col0) * kv;
         const int rows_valid = (int)tc.rows;
@@ -468,6 +473,11 @@ __global__ __launch_bounds__(S::kThreads, S::PER_CU) void grouped_gemm_bf16_kern
         static_for<0, STAGES - 1>([&](auto st) __attribute__((always_inline)) {
             if (decltype(st)::value < ksteps) load_part(decltype(st)::value, st, Int<0>{}, Int<kGA + kGB>{});
         });
+        if (id + G < total) {
+            tc_next = tile_coord<BM, BN>(id + G, off, tile_pre, num_experts, n_tiles);
+            // computed here, not moved down to its use after the k-loop
+            asm volatile("" ::"s"(tc_next.expert), "s"(tc_next.row0), "s"(tc_next.rows), "s"(tc_next.col0));
+        }
         // full: the caller knows that step ks + STAGES - 1 exists (no branch on it).
         auto step = [&](int64_t ks, auto st, auto full, auto mf) __attribute__((always_inline)) {
             constexpr int kSt = decltype(st)::value;
